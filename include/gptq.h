@@ -1,0 +1,161 @@
+/*
+ * gptq.h -- C ABI of libgptq.so, the MI355X (gfx950) GPTQ weight-only GEMM.
+ *
+ * What it computes (page "Enhancing vLLM's support for the GPTQv2 format:
+ * analysis and implementation", sections "Weight quantization of LLMs",
+ * "From GPTQv1 to GPTQv2" and "Adjustment details"):
+ *
+ *   g(k)      = g_idx ? g_idx[k] : k / group_size
+ *   q[k,n]    = b-bit field k of column n of qweight
+ *   z[g,n]    = b-bit field n of row g of qzeros  + (is_v2 ? 0 : 1)
+ *   W^[k,n]   = fp16_round((q[k,n] - z[g(k),n]) * scales[g(k),n])
+ *   out[m,n]  = fp16_round( sum_k x[m,k] * W^[k,n] )   (fp32 accumulation)
+ *
+ * Data layout (all row-major, caller-owned device memory):
+ *   x        fp16  [M, K]
+ *   qweight  int32 [K*bits/32, N]  packed along K: column n's K fields form one
+ *                                  LSB-first bitstream of bits-wide fields;
+ *                                  word r holds stream bits [32r, 32r+32).  For
+ *                                  bits = 3 one 32-value chunk spans three
+ *                                  consecutive rows (fields 10 and 21 straddle).
+ *   qzeros   int32 [G, N*bits/32]  packed along N, same bitstream rule per row.
+ *   scales   fp16  [G, N]
+ *   g_idx    int32 [K] or NULL     group of every row k (act-order); NULL means
+ *                                  k / group_size.
+ *   out      fp16  [M, N]          written, never accumulated into.
+ * with G = K / group_size.  The int32 words are bit containers (no sign).
+ *
+ * Ownership and streams: the library keeps no pointer after a call returns.
+ * Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ * asynchronous: buffers must stay valid until that work completes, and a
+ * device-side fault surfaces at the caller's next synchronisation.  The only
+ * library-owned state is a split-K workspace per (device, stream), allocated on
+ * the first M <= 16 call on that pair (so that call must not be inside a HIP
+ * graph capture), reused afterwards and freed by gptq_release().  Calls that
+ * overlap on the same stream are serialised by the stream; concurrent calls on
+ * different streams use different workspaces.
+ *
+ * Errors: every function returns GPTQ_OK (0) or a negative gptq_status code;
+ * nothing is launched when an argument check fails, and no C++ exception
+ * crosses the ABI.  M == 0 returns GPTQ_OK without launching.
+ *
+ * Preconditions that are not checked: g_idx entries lie in [0, G) (an entry
+ * outside is clamped into range, so memory stays in bounds but the result is
+ * unspecified); scales are finite; out does not alias an input.
+ */
+#ifndef GPTQ_H_
+#define GPTQ_H_
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define GPTQ_API __attribute__((visibility("default")))
+#else
+#define GPTQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gptq_status {
+  GPTQ_OK = 0,
+  GPTQ_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
+  GPTQ_ERR_BAD_BITS = -2,    /* bits not in {2, 3, 4, 8} */
+  GPTQ_ERR_BAD_SHAPE = -3,   /* M < 0, N <= 0, K <= 0, K % 32, N % 32, or a size limit */
+  GPTQ_ERR_BAD_GROUP = -4,   /* group_size <= 0 or K % group_size != 0 */
+  GPTQ_ERR_MISALIGNED = -5,  /* x, qweight, out not 16-byte aligned; scales not 8; qzeros, g_idx not 4 */
+  GPTQ_ERR_NO_MEM = -6,      /* device memory for a workspace or temporary could not be allocated */
+  GPTQ_ERR_LAUNCH = -7,      /* a kernel launch failed */
+  GPTQ_ERR_DEVICE = -8,      /* no current HIP device or a HIP runtime call failed */
+  GPTQ_ERR_BAD_ARG = -9      /* is_v2 / sym not 0 or 1, or a gptq_gemm_ex option out of range */
+} gptq_status;
+
+/* Size limits (GPTQ_ERR_BAD_SHAPE beyond them): M <= 2^24, N and K <= 2^20,
+ * and M*K, K*N, M*N each below 2^31 elements. */
+
+/*
+ * y = x . dequant(W): the GPTQ weight-only GEMM (the `gptq_gemm` call of the
+ * page above, whose `use_v2_format` flag is `is_v2` here).
+ *   bits        2, 3, 4 or 8.
+ *   group_size  rows per quantization group; K % group_size == 0.
+ *   is_v2       1: zeros are stored as is (GPTQv2); 0: stored zero + 1 (GPTQv1).
+ *               Mandatory: there is no default and no format detection.
+ *   M, N, K     x is [M,K], out is [M,N]; N % 32 == 0 and K % 32 == 0.
+ *   stream      hipStream_t as void*.
+ * M <= 16 runs the split-K decode kernel; larger M runs the MFMA prefill kernel.
+ */
+GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros,
+              const void* scales, const int32_t* g_idx, int bits, int group_size,
+              int is_v2, int64_t M, int64_t N, int64_t K, void* out, void* stream);
+
+/*
+ * gptq_gemm with explicit kernel choice, for tests and tuning.
+ *   path     0 = automatic (as gptq_gemm), 1 = decode kernel (requires M <= 16),
+ *            2 = prefill kernel (any M).
+ *   split_k  0 = automatic; > 0 = number of K slices the decode kernel reduces
+ *            across workgroups (clamped to the number of 32-row chunks).
+ * Other values give GPTQ_ERR_BAD_ARG.
+ */
+GPTQ_API int gptq_gemm_ex(const void* x, const int32_t* qweight, const int32_t* qzeros,
+                 const void* scales, const int32_t* g_idx, int bits, int group_size,
+                 int is_v2, int64_t M, int64_t N, int64_t K, void* out, void* stream,
+                 int path, int split_k);
+
+/*
+ * W^ = dequant(W) into w_out, fp16 [K, N] row-major (the "reconstruct" kernel
+ * of the page's "Adjustment details" section).  Bit-exact: one round-to-
+ * nearest-even of the exact product (q - z) * s per element, fp16 subnormals
+ * kept.  Same arguments and checks as gptq_gemm minus x and M.
+ */
+GPTQ_API int gptq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                 const int32_t* g_idx, int bits, int group_size, int is_v2,
+                 int64_t N, int64_t K, void* w_out, void* stream);
+
+/*
+ * Argument checks of gptq_gemm / gptq_dequant only: pure host code, touches no
+ * device and no pointer target.  Returns the code the full call would return
+ * for these arguments before any HIP call.
+ */
+GPTQ_API int gptq_gemm_check(const void* x, const int32_t* qweight, const int32_t* qzeros,
+                    const void* scales, const int32_t* g_idx, int bits, int group_size,
+                    int is_v2, int64_t M, int64_t N, int64_t K, const void* out);
+GPTQ_API int gptq_dequant_check(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                       const int32_t* g_idx, int bits, int group_size, int is_v2,
+                       int64_t N, int64_t K, const void* w_out);
+
+/*
+ * Min/max round-to-nearest quantization of W (fp32 [K, N] row-major, device)
+ * into qweight, qzeros and scales with the layout above (page "Enhancing
+ * vLLM's support for the GPTQv2 format", sections "Weight quantization of
+ * LLMs" and "From GPTQv1 to GPTQv2"):
+ *   scale = fp16((wmax - wmin) / (2^b - 1)), computed in fp64 (0 becomes 1.0)
+ *   zero  = clamp(-round(wmin / scale), 0, 2^b - 1)   (sym: wmax = -wmin =
+ *           max|w| and zero = round((2^b - 1) / 2) = 2^(b-1))
+ *   q     = clamp(round(w / scale) + zero, 0, 2^b - 1)
+ *   stored zero = is_v2 ? zero : clamp(zero - 1, 0, 2^b - 1)
+ * round() is half-to-even and every division that decides an integer is done
+ * in fp64 with the stored fp16 scale.  g_idx (nullable) assigns rows to groups
+ * as in gptq_gemm.  sym and is_v2 are 0 or 1.  Alignment: 4 bytes for w,
+ * qweight, qzeros, g_idx; 2 bytes for scales.  Enqueues two kernels and a
+ * stream-ordered temporary of G*N bytes on `stream`.
+ */
+GPTQ_API int gptq_quantize(const float* w, const int32_t* g_idx, int bits, int group_size,
+                           int sym, int is_v2, int64_t N, int64_t K, int32_t* qweight,
+                           int32_t* qzeros, void* scales, void* stream);
+
+/* Static text for a gptq_status code ("unknown error" for other values). */
+GPTQ_API const char* gptq_strerror(int code);
+
+/* Frees every library-owned workspace on every device.  The caller must make
+ * sure no enqueued gptq work is still running. */
+GPTQ_API void gptq_release(void);
+
+/* Library ABI version: 1. */
+GPTQ_API int gptq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_H_ */

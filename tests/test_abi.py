@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gptq.h declares, and its argument checks return the documented codes
+(the *_check entry points are pure host code and touch no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_bit_gptq_amd as gq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gptq.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(gq.library_path()),
+                               reason="libgptq.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"GPTQ_API\s+[A-Za-z_][A-Za-z0-9_\s\*]*?\b(gptq_[a-z_]+)\s*\(", text)
+
+
+def declared_status():
+    text = open(HEADER).read()
+    return {int(v): k for k, v in re.findall(r"\b(GPTQ_[A-Z_]+)\s*=\s*(-?\d+)", text)}
+
+
+def test_header_declares_api():
+    names = declared_functions()
+    for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check",
+              "gptq_dequant_check", "gptq_strerror", "gptq_release", "gptq_abi_version"):
+        assert f in names
+    assert declared_status() == gq.STATUS
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gq.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert gq.library().gptq_abi_version() == 1
+
+
+@needs_lib
+def test_strerror_covers_every_code():
+    lib = gq.library()
+    for code in gq.STATUS:
+        assert lib.gptq_strerror(code).decode()
+    assert lib.gptq_strerror(12345).decode() == "unknown error"
+
+
+# fake, suitably aligned addresses: the check functions never dereference them
+X, QW, QZ, SC, GI, OUT = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000
+
+
+def gemm_check(x=X, qw=QW, qz=QZ, sc=SC, gi=None, bits=4, gs=128, v2=1, M=1, N=4096, K=4096, out=OUT):
+    return gq.library().gptq_gemm_check(x, qw, qz, sc, gi, bits, gs, v2, M, N, K, out)
+
+
+@needs_lib
+def test_gemm_check_codes():
+    assert gemm_check() == 0
+    assert gemm_check(gi=GI) == 0
+    assert gemm_check(M=0, x=None, out=None) == 0
+    assert gemm_check(x=None) == -1
+    assert gemm_check(qw=None) == -1
+    assert gemm_check(qz=None) == -1
+    assert gemm_check(sc=None) == -1
+    assert gemm_check(out=None) == -1
+    for b in (0, 1, 5, 6, 7, 16):
+        assert gemm_check(bits=b) == -2
+    assert gemm_check(M=-1) == -3
+    assert gemm_check(N=0) == -3
+    assert gemm_check(K=0) == -3
+    assert gemm_check(N=48) == -3
+    assert gemm_check(K=4112, gs=16) == -3
+    assert gemm_check(K=1 << 21, gs=128) == -3
+    assert gemm_check(M=1 << 20, K=4096) == -3       # M*K >= 2^31
+    assert gemm_check(gs=0) == -4
+    assert gemm_check(gs=-128) == -4
+    assert gemm_check(gs=96) == -4                    # 4096 % 96 != 0
+    assert gemm_check(x=X + 8) == -5
+    assert gemm_check(qw=QW + 4) == -5
+    assert gemm_check(out=OUT + 2) == -5
+    assert gemm_check(sc=SC + 4) == -5
+    assert gemm_check(qz=QZ + 2) == -5
+    assert gemm_check(gi=GI + 2) == -5
+    assert gemm_check(v2=2) == -9
+    assert gemm_check(bits=3, N=32, K=96, gs=32) == 0
+
+
+@needs_lib
+def test_dequant_check_codes():
+    lib = gq.library()
+    ok = lambda **kw: lib.gptq_dequant_check(kw.get("qw", QW), kw.get("qz", QZ), kw.get("sc", SC),
+                                             kw.get("gi"), kw.get("bits", 3), kw.get("gs", 128),
+                                             kw.get("v2", 0), kw.get("N", 5120), kw.get("K", 13824),
+                                             kw.get("out", OUT))
+    assert ok() == 0
+    assert ok(out=None) == -1
+    assert ok(bits=1) == -2
+    assert ok(N=5121) == -3
+    assert ok(gs=100) == -4
+    assert ok(out=OUT + 8) == -5
+
+
+@needs_lib
+def test_invalid_calls_return_before_any_launch():
+    """gptq_gemm / gptq_dequant with bad arguments fail in the host checks, so
+    they are safe to call without a GPU."""
+    lib = gq.library()
+    assert lib.gptq_gemm(X, QW, QZ, SC, None, 5, 128, 1, 1, 4096, 4096, OUT, None) == -2
+    assert lib.gptq_gemm_ex(X, QW, QZ, SC, None, 4, 128, 1, 17, 4096, 4096, OUT, None, 1, 0) == -9
+    assert lib.gptq_gemm_ex(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, None, 3, 0) == -9
+    assert lib.gptq_gemm_ex(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, None, 0, -1) == -9
+    assert lib.gptq_dequant(QW, QZ, SC, None, 4, 100, 1, 4096, 4096, OUT, None) == -4
+    assert lib.gptq_gemm(X, QW, QZ, SC, None, 4, 128, 1, 0, 4096, 4096, OUT, None) == 0   # M == 0
+
+
+def test_python_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    qw = torch.zeros((512, 64), dtype=torch.int32)
+    qz = torch.zeros((32, 8), dtype=torch.int32)
+    sc = torch.zeros((32, 64), dtype=torch.float16)
+    x = torch.zeros((1, 4096), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        gq.gemm(x, qw, qz, sc, None, 5, 128, True)
+    with pytest.raises(ValueError):
+        gq.gemm(x, qw, qz, sc, None, 4, 128, True)          # CPU tensors are rejected

@@ -1,0 +1,211 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+- gptq_dequant must match the oracle bit for bit (compared as uint16);
+- gptq_gemm must satisfy max|y - y_ref| <= 5e-3 * rms(y_ref), y_ref in fp64
+  (tolerance of the GEMM target; fp32 accumulation on the GPU).
+
+Inputs are seeded draws from ``workload`` quantized and packed by the oracle;
+nothing the GPU computes is ever fed back to the oracle.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_bit_gptq_amd as gq
+from workload import WORKLOADS, draw_layer, draw_workload_layer, random_words
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+BITS = (2, 3, 4, 8)
+TOL = 5e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gq.library()
+    return torch.device("cuda:0")
+
+
+def upload(L, dev):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return (t(L.qweight), t(L.qzeros), t(L.scales), None if L.g_idx is None else t(L.g_idx))
+
+
+def quantized(K, N, M, bits, gs, sym, is_v2, act, seed=0, outliers=0.0, sigma=0.02):
+    d = draw_layer(K, N, M, sigma=sigma, group_size=gs, outlier_rate=outliers, act_order=act, seed=seed)
+    L = oracle.quantize_layer(d.W, bits, gs, sym, is_v2, d.g_idx)
+    return d, L
+
+
+def assert_close(y_gpu, y_ref, what=""):
+    y = y_gpu.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(y).all(), what
+    rms = np.sqrt(np.mean(y_ref ** 2))
+    err = np.max(np.abs(y - y_ref))
+    assert err <= TOL * rms, f"{what}: max err {err:.3e} > {TOL} * rms {rms:.3e}"
+
+
+# ------------------------------------------------------------------ dequant, bit-exact
+DQ_GRID = list(itertools.product(BITS, (False, True), (False, True), (False, True), (32, 64, 128)))
+
+
+@pytest.mark.parametrize("bits,is_v2,sym,act,gs", DQ_GRID)
+def test_dequant_bit_exact(dev, bits, is_v2, sym, act, gs):
+    K, N = 256, 160                     # 2.5 column tiles, 8 chunks
+    d, L = quantized(K, N, 1, bits, gs, sym, is_v2, act, seed=bits + 7 * gs)
+    qw, qz, sc, gi = upload(L, dev)
+    w = gq.dequant(qw, qz, sc, gi, bits, gs, is_v2)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_ref(L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, is_v2, K, N)
+    assert np.array_equal(w.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("bits,is_v2", list(itertools.product(BITS, (False, True))))
+def test_dequant_random_words_and_subnormals(dev, bits, is_v2):
+    """Every field value (incl. top bits set, v1 zero 2^b - 1 -> 2^b) and scales
+    whose products are fp16 subnormals."""
+    K, N, gs = 192, 96, 64
+    rng = np.random.default_rng(bits * 3 + is_v2)
+    qweight = random_words(rng, (K * bits // 32, N))
+    qzeros = random_words(rng, (K // gs, N * bits // 32))
+    scales = (rng.standard_normal((K // gs, N)) * 0.05).astype(np.float16)
+    scales[0, :32] = np.float16(2.0 ** -24) * np.arange(1, 33).astype(np.float16)
+    scales[1, :8] = np.float16(-6.0e-8)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    w = gq.dequant(t(qweight), t(qzeros), t(scales), None, bits, gs, is_v2)
+    ref = oracle.dequant_ref(qweight, qzeros, scales, None, bits, gs, is_v2, K, N)
+    assert np.array_equal(w.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+
+
+def test_dequant_v2_data_read_as_v1(dev):
+    """Reading GPTQv2 zeros with is_v2 = 0 gives exactly the oracle's v1 reading
+    (the misread of the v2 format is reproducible, never silent noise)."""
+    bits, K, N, gs = 2, 256, 64, 64
+    d, L = quantized(K, N, 1, bits, gs, False, True, False, seed=4, outliers=0.02)
+    qw, qz, sc, gi = upload(L, dev)
+    w = gq.dequant(qw, qz, sc, gi, bits, gs, False)
+    ref_v1 = oracle.dequant_ref(L.qweight, L.qzeros, L.scales, None, bits, gs, False, K, N)
+    ref_v2 = oracle.dequant_ref(L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N)
+    assert np.array_equal(w.cpu().numpy().view(np.uint16), ref_v1.view(np.uint16))
+    assert not np.array_equal(ref_v1.view(np.uint16), ref_v2.view(np.uint16))
+
+
+# ------------------------------------------------------------------ GEMM, small grid
+GEMM_GRID = list(itertools.product(BITS, (False, True), (False, True), (32, 128)))
+
+
+@pytest.mark.parametrize("bits,is_v2,act,gs", GEMM_GRID)
+def test_gemm_small_grid(dev, bits, is_v2, act, gs):
+    K, N = 512, 160
+    for sym in (False, True):
+        d, L = quantized(K, N, 40, bits, gs, sym, is_v2, act, seed=bits * 11 + gs)
+        qw, qz, sc, gi = upload(L, dev)
+        xt = torch.from_numpy(d.x).to(dev)
+        for M in (1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 40):
+            ref = oracle.gptq_gemm_ref(d.x[:M], L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, is_v2, K, N)
+            paths = [gq.PATH_AUTO, gq.PATH_PREFILL] + ([gq.PATH_DECODE] if M <= 16 else [])
+            for p in paths:
+                y = gq.gemm(xt[:M].contiguous(), qw, qz, sc, gi, bits, gs, is_v2, path=p)
+                assert_close(y, ref, f"M={M} path={p} sym={sym}")
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("K,N,gs", [(96, 32, 32), (96, 96, 96), (288, 224, 96), (256, 64, 16), (544, 96, 32),
+                                    (1024, 32, 1024)])
+def test_gemm_ragged_and_group_shapes(dev, bits, K, N, gs):
+    """Ragged K (not a multiple of the 128-row wave step or the 64-row prefill
+    tile), N with a half column tile, and group sizes 16 / 96 / K that are not
+    multiples of the 32- and 64-row pipelines (per-element path)."""
+    d, L = quantized(K, N, 33, bits, gs, False, True, False, seed=K + N + gs)
+    qw, qz, sc, gi = upload(L, dev)
+    xt = torch.from_numpy(d.x).to(dev)
+    for M in (1, 7, 16, 33):
+        ref = oracle.gptq_gemm_ref(d.x[:M], L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N)
+        for p in ([gq.PATH_DECODE] if M <= 16 else []) + [gq.PATH_PREFILL]:
+            y = gq.gemm(xt[:M].contiguous(), qw, qz, sc, gi, bits, gs, True, path=p)
+            assert_close(y, ref, f"M={M} path={p}")
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 5, 16, 1000])
+def test_decode_split_k_and_determinism(dev, split_k):
+    bits, K, N, gs = 4, 2048, 320, 128
+    d, L = quantized(K, N, 16, bits, gs, True, False, False, seed=21)
+    qw, qz, sc, gi = upload(L, dev)
+    xt = torch.from_numpy(d.x).to(dev)
+    for M in (1, 4, 16):
+        ref = oracle.gptq_gemm_ref(d.x[:M], L.qweight, L.qzeros, L.scales, None, bits, gs, False, K, N)
+        x = xt[:M].contiguous()
+        y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, split_k=split_k)
+        y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, split_k=split_k)
+        assert_close(y1, ref, f"M={M} split_k={split_k}")
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_gemm_closed_forms(dev):
+    """One-hot rows of x pick rows of W^ (exact up to fp16 output rounding,
+    which is the identity for fp16 inputs); x = 0 gives 0."""
+    bits, K, N, gs = 4, 256, 128, 64
+    d, L = quantized(K, N, 1, bits, gs, False, True, False, seed=3)
+    qw, qz, sc, gi = upload(L, dev)
+    w_ref = oracle.dequant_ref(L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N)
+    x = np.zeros((20, K), dtype=np.float16)
+    ks = [0, 1, 31, 32, 63, 64, 100, 127, 128, 129, 200, 255, 7, 8, 9, 15, 16, 17, 250, 40]
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    xt = torch.from_numpy(x).to(dev)
+    for p, Ms in ((gq.PATH_DECODE, (1, 16)), (gq.PATH_PREFILL, (20,))):
+        for M in Ms:
+            y = gq.gemm(xt[:M].contiguous(), qw, qz, sc, gi, bits, gs, True, path=p).cpu().numpy()
+            assert np.array_equal(y.view(np.uint16), w_ref[ks[:M]].view(np.uint16)), (p, M)
+    y0 = gq.gemm(torch.zeros((5, K), dtype=torch.float16, device=dev), qw, qz, sc, gi, bits, gs, True)
+    assert (y0 == 0).all()
+
+
+def test_gemm_m_zero(dev):
+    d, L = quantized(64, 32, 1, 4, 32, False, True, False)
+    qw, qz, sc, gi = upload(L, dev)
+    y = gq.gemm(torch.zeros((0, 64), dtype=torch.float16, device=dev), qw, qz, sc, gi, 4, 32, True)
+    assert tuple(y.shape) == (0, 32)
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled columns
+def workload_cases():
+    cases = []
+    for name, wl in WORKLOADS.items():
+        for layer in wl.layers:
+            for M in wl.Ms:
+                cases.append(pytest.param(name, layer.name, M, id=f"{name}-{layer.name}-M{M}"))
+    return cases
+
+
+@pytest.mark.parametrize("wname,lname,M", workload_cases())
+def test_workload_full_size(dev, wname, lname, M):
+    wl = WORKLOADS[wname]
+    layer = next(l for l in wl.layers if l.name == lname)
+    K, N = layer.K, layer.N
+    d = draw_workload_layer(wl, layer, M, seed=0)
+    L = oracle.quantize_layer(d.W, wl.bits, wl.group_size, wl.sym, wl.is_v2, d.g_idx)
+    del d.W
+    if wl.bits == 2 and wl.outlier_rate > 0:
+        assert set(np.unique(L.zero)) == {0, 1, 2, 3}
+    qw, qz, sc, gi = upload(L, dev)
+    xt = torch.from_numpy(d.x).to(dev)
+    y = gq.gemm(xt, qw, qz, sc, gi, wl.bits, wl.group_size, wl.is_v2).cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(1)
+    cols = np.unique(np.concatenate([rng.choice(N, 48, replace=False), [0, 1, 2, 3, N - 4, N - 3, N - 2, N - 1]]))
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, wl.bits, wl.group_size, wl.is_v2,
+                               K, N, cols=cols)
+    assert np.isfinite(y).all()
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.max(np.abs(y[:, cols] - ref))
+    assert err <= TOL * rms, f"max err {err:.3e} > {TOL} * rms {rms:.3e}"
+    # dequant, bit-exact on the same sampled columns
+    w = gq.dequant(qw, qz, sc, gi, wl.bits, wl.group_size, wl.is_v2)[:, torch.from_numpy(cols).to(dev)]
+    w_ref = oracle.dequant_ref(L.qweight, L.qzeros, L.scales, L.g_idx, wl.bits, wl.group_size, wl.is_v2, K, N,
+                               cols=cols)
+    assert np.array_equal(w.cpu().numpy().view(np.uint16), w_ref.view(np.uint16))

@@ -1,0 +1,213 @@
+"""GPTQ weight-only GEMM for AMD MI355X (gfx950): Python binding of libgptq.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gptq.h``.  PyTorch supplies
+device memory and the current stream.  If the compiled library is missing the
+functions raise ``RuntimeError``; there is no CPU fallback.
+
+    out = gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
+    w   = dequant(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+__all__ = ["gemm", "dequant", "quantize", "release", "library", "library_path", "GptqError",
+           "STATUS", "PATH_AUTO", "PATH_DECODE", "PATH_PREFILL"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "_lib", "libgptq.so")
+_lock = threading.Lock()
+_lib = None
+
+PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+
+STATUS = {
+    0: "GPTQ_OK", -1: "GPTQ_ERR_NULL_PTR", -2: "GPTQ_ERR_BAD_BITS", -3: "GPTQ_ERR_BAD_SHAPE",
+    -4: "GPTQ_ERR_BAD_GROUP", -5: "GPTQ_ERR_MISALIGNED", -6: "GPTQ_ERR_NO_MEM",
+    -7: "GPTQ_ERR_LAUNCH", -8: "GPTQ_ERR_DEVICE", -9: "GPTQ_ERR_BAD_ARG",
+}
+
+
+class GptqError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> ctypes.CDLL:
+    """Load libgptq.so (built in-tree by ``weight_only_bit_gptq_amd.build_lib``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"libgptq.so is not built ({_LIB_PATH}); run "
+                               "`python -m weight_only_bit_gptq_amd.build_lib`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32p, i64, i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        gemm_args = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, vp]
+        lib.gptq_gemm.argtypes = gemm_args
+        lib.gptq_gemm.restype = i32
+        lib.gptq_gemm_ex.argtypes = gemm_args + [i32, i32]
+        lib.gptq_gemm_ex.restype = i32
+        lib.gptq_dequant.argtypes = [i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, vp, vp]
+        lib.gptq_dequant.restype = i32
+        lib.gptq_gemm_check.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp]
+        lib.gptq_gemm_check.restype = i32
+        lib.gptq_dequant_check.argtypes = [i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, vp]
+        lib.gptq_dequant_check.restype = i32
+        lib.gptq_quantize.argtypes = [vp, i32p, i32, i32, i32, i32, i64, i64, i32p, i32p, vp, vp]
+        lib.gptq_quantize.restype = i32
+        lib.gptq_strerror.argtypes = [i32]
+        lib.gptq_strerror.restype = ctypes.c_char_p
+        lib.gptq_release.argtypes = []
+        lib.gptq_release.restype = None
+        lib.gptq_abi_version.argtypes = []
+        lib.gptq_abi_version.restype = i32
+        if lib.gptq_abi_version() != 1:
+            raise RuntimeError("libgptq.so ABI version mismatch")
+        _lib = lib
+        return lib
+
+
+def _raise(code: int):
+    if code != 0:
+        msg = library().gptq_strerror(code).decode()
+        raise GptqError(code, msg)
+
+
+def _check_tensor(name, t, dtype, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K=None):
+    import torch
+    if bits not in (2, 3, 4, 8):
+        raise ValueError("bits must be 2, 3, 4 or 8")
+    if is_v2 not in (0, 1, True, False):
+        raise ValueError("is_v2 must be a bool")
+    dev = qweight.device if isinstance(qweight, torch.Tensor) else None
+    _check_tensor("qweight", qweight, torch.int32, dev)
+    _check_tensor("qzeros", qzeros, torch.int32, dev)
+    _check_tensor("scales", scales, torch.float16, dev)
+    if g_idx is not None:
+        _check_tensor("g_idx", g_idx, torch.int32, dev)
+    if qweight.dim() != 2 or qzeros.dim() != 2 or scales.dim() != 2:
+        raise ValueError("qweight, qzeros and scales must be 2-D")
+    N = qweight.shape[1]
+    if K is None:
+        K = qweight.shape[0] * 32 // bits
+    if qweight.shape[0] * 32 != K * bits:
+        raise ValueError(f"qweight has {qweight.shape[0]} rows, expected K*bits/32 = {K * bits / 32}")
+    if group_size <= 0 or K % group_size:
+        raise ValueError("group_size must divide K")
+    G = K // group_size
+    if tuple(scales.shape) != (G, N):
+        raise ValueError(f"scales must be [{G}, {N}], got {tuple(scales.shape)}")
+    if tuple(qzeros.shape) != (G, N * bits // 32) or (N * bits) % 32:
+        raise ValueError(f"qzeros must be [{G}, {N * bits // 32}], got {tuple(qzeros.shape)}")
+    if g_idx is not None and tuple(g_idx.shape) != (K,):
+        raise ValueError(f"g_idx must be [{K}]")
+    return dev, N, K
+
+
+def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,
+         is_v2: bool, *, out=None, path: int = PATH_AUTO, split_k: int = 0):
+    """out[M, N] (fp16) = x[M, K] (fp16) . dequant(qweight, qzeros, scales, g_idx).
+
+    Enqueued on the current HIP stream of x's device (asynchronous)."""
+    import torch
+    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
+    _check_tensor("x", x, torch.float16, dev)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M, {K}], got {tuple(x.shape)}")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    else:
+        _check_tensor("out", out, torch.float16, dev)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be [{M}, {N}]")
+    lib = library()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        code = lib.gptq_gemm_ex(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                                None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
+                                int(bool(is_v2)), M, N, K, out.data_ptr(), stream, int(path), int(split_k))
+    _raise(code)
+    return out
+
+
+def dequant(qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,
+            is_v2: bool, *, out=None):
+    """W^ [K, N] fp16, bit-exact dequantization of the packed weights."""
+    import torch
+    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
+    if out is None:
+        out = torch.empty((K, N), dtype=torch.float16, device=dev)
+    else:
+        _check_tensor("out", out, torch.float16, dev)
+        if tuple(out.shape) != (K, N):
+            raise ValueError(f"out must be [{K}, {N}]")
+    lib = library()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        code = lib.gptq_dequant(qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                                None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
+                                int(bool(is_v2)), N, K, out.data_ptr(), stream)
+    _raise(code)
+    return out
+
+
+def quantize(w, g_idx: Optional[object], bits: int, group_size: int, sym: bool, is_v2: bool):
+    """Min/max round-to-nearest quantization of W [K, N] (fp32, GPU) into
+    (qweight int32 [K*b/32, N], qzeros int32 [G, N*b/32], scales fp16 [G, N])."""
+    import torch
+    if bits not in (2, 3, 4, 8):
+        raise ValueError("bits must be 2, 3, 4 or 8")
+    dev = w.device if isinstance(w, torch.Tensor) else None
+    _check_tensor("w", w, torch.float32, dev)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [K, N]")
+    K, N = w.shape
+    if K % 32 or N % 32 or group_size <= 0 or K % group_size:
+        raise ValueError("need K % 32 == 0, N % 32 == 0 and group_size dividing K")
+    if g_idx is not None:
+        _check_tensor("g_idx", g_idx, torch.int32, dev)
+        if tuple(g_idx.shape) != (K,):
+            raise ValueError(f"g_idx must be [{K}]")
+    G = K // group_size
+    qweight = torch.empty((K * bits // 32, N), dtype=torch.int32, device=dev)
+    qzeros = torch.empty((G, N * bits // 32), dtype=torch.int32, device=dev)
+    scales = torch.empty((G, N), dtype=torch.float16, device=dev)
+    lib = library()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        code = lib.gptq_quantize(w.data_ptr(), None if g_idx is None else g_idx.data_ptr(), int(bits),
+                                 int(group_size), int(bool(sym)), int(bool(is_v2)), N, K, qweight.data_ptr(),
+                                 qzeros.data_ptr(), scales.data_ptr(), stream)
+    _raise(code)
+    return qweight, qzeros, scales
+
+
+def release():
+    """Free the library's split-K workspaces (call with no gptq work in flight)."""
+    library().gptq_release()

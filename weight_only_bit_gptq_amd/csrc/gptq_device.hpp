@@ -1,0 +1,165 @@
+// Device-side building blocks shared by the dequant, decode and prefill kernels.
+//
+// Packed layout (page "Enhancing vLLM's support for the GPTQv2 format",
+// sections "Weight quantization of LLMs" and "Adjustment details"): qweight is
+// int32 [K*b/32, N], each column's K b-bit fields an LSB-first bitstream, so one
+// 128-bit load of row r gives the same packed word of four adjacent columns.
+//
+// The unit of work is a 32-row chunk c (k in [32c, 32c+32)) split into four
+// 8-row blocks kb.  An 8-row block of one column is exactly the B operand one
+// lane holds for a gfx950 16x16x32 (or 32x32x16) f16 MFMA: eight k values of
+// one column.  The block's eight b-bit fields sit in:
+//   b = 2: half (kb & 1) of word 2c + (kb >> 1)
+//   b = 3: bits [24kb, 24kb+24) of the 96-bit chunk in words 3c .. 3c+2
+//   b = 4: word 4c + kb
+//   b = 8: words 8c + 2kb and 8c + 2kb + 1
+//
+// Fields become fp16 with the exponent trick: OR-ing a field (shifted by s
+// bits) into the mantissa of 1024.0 gives exactly 1024 + 2^s * q.  Each 32-bit
+// result holds two fields of one column ("magic pair"); the eight halves of a
+// block come out in the field order F[] below, with multiplier MUL[v] for the
+// pair in register v.  Callers reorder and scale the other MFMA operand (x) to
+// match, so no instruction is spent putting fields back in k order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMagicPair = 0x64006400u;   // fp16 1024.0 in both halves
+constexpr float kMagic = 1024.0f;
+
+// Field order of the eight halves of a block and the power-of-two multiplier of
+// each register's pair, per bit width.
+template <int BITS> struct Block;
+template <> struct Block<2> {
+  static constexpr int F[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+  static constexpr int MUL[4] = {1, 4, 16, 64};
+  static constexpr int LOADS = 1;               // 128-bit qweight rows per block
+};
+template <> struct Block<3> {
+  static constexpr int F[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+  static constexpr int MUL[4] = {1, 8, 64, 8};
+  static constexpr int LOADS = 2;
+};
+template <> struct Block<4> {
+  static constexpr int F[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+  static constexpr int MUL[4] = {1, 16, 1, 16};
+  static constexpr int LOADS = 1;
+};
+template <> struct Block<8> {
+  static constexpr int F[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+  static constexpr int MUL[4] = {1, 1, 1, 1};
+  static constexpr int LOADS = 2;
+};
+
+// qweight rows holding block kb of chunk c (second row only for LOADS == 2).
+template <int BITS> __device__ __forceinline__ int block_row0(int c, int kb) {
+  if constexpr (BITS == 2) return 2 * c + (kb >> 1);
+  else if constexpr (BITS == 3) return 3 * c + ((24 * kb) >> 5);
+  else if constexpr (BITS == 4) return 4 * c + kb;
+  else return 8 * c + 2 * kb;
+}
+template <int BITS> __device__ __forceinline__ int block_row1(int c, int kb) {
+  if constexpr (BITS == 3) { int w = (24 * kb) >> 5; return 3 * c + (w < 2 ? w + 1 : 2); }
+  else if constexpr (BITS == 8) return 8 * c + 2 * kb + 1;
+  else return block_row0<BITS>(c, kb);
+}
+
+// Lane-constant selector for unpack_block: byte selector (b = 2) or funnel
+// shift (b = 3); unused otherwise.
+template <int BITS> __device__ __forceinline__ uint32_t block_sel(int kb) {
+  if constexpr (BITS == 2) return (kb & 1) ? 0x0C030C02u : 0x0C010C00u;
+  else if constexpr (BITS == 3) return (uint32_t)((24 * kb) & 31);
+  else return 0u;
+}
+
+// Eight fields of one column's block -> four magic pairs (see file comment).
+// w0 / w1 are the column's words from block_row0 / block_row1.
+template <int BITS>
+__device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, uint32_t sel, uint32_t p[4]) {
+  if constexpr (BITS == 4) {
+    const uint32_t t = w0 >> 8;
+    p[0] = (w0 & 0x000F000Fu) | kMagicPair;   // f0, f4
+    p[1] = (w0 & 0x00F000F0u) | kMagicPair;   // 16 f1, 16 f5
+    p[2] = (t & 0x000F000Fu) | kMagicPair;    // f2, f6
+    p[3] = (t & 0x00F000F0u) | kMagicPair;    // 16 f3, 16 f7
+  } else if constexpr (BITS == 2) {
+    // spread the block's two bytes to bytes 0 and 2 (f0..f3 low, f4..f7 high)
+    const uint32_t t = __builtin_amdgcn_perm(0u, w0, sel);
+    p[0] = (t & 0x00030003u) | kMagicPair;    // f0, f4
+    p[1] = (t & 0x000C000Cu) | kMagicPair;    // 4 f1, 4 f5
+    p[2] = (t & 0x00300030u) | kMagicPair;    // 16 f2, 16 f6
+    p[3] = (t & 0x00C000C0u) | kMagicPair;    // 64 f3, 64 f7
+  } else if constexpr (BITS == 3) {
+    // 24-bit block: f0..f3 in bits 0..11 stay, f4..f7 (bits 12..23) move to 16..27
+    const uint32_t s = __builtin_amdgcn_alignbit(w1, w0, sel);
+    const uint32_t t = (s & 0x0000FFFFu) | ((s << 4) & 0xFFFF0000u);
+    const uint32_t t6 = t >> 6;
+    p[0] = (t & 0x00070007u) | kMagicPair;    // f0, f4
+    p[1] = (t & 0x00380038u) | kMagicPair;    // 8 f1, 8 f5
+    p[2] = (t & 0x01C001C0u) | kMagicPair;    // 64 f2, 64 f6
+    p[3] = (t6 & 0x00380038u) | kMagicPair;   // 8 f3, 8 f7
+  } else {
+    p[0] = (w0 & 0x00FF00FFu) | kMagicPair;          // f0, f2
+    p[1] = ((w0 >> 8) & 0x00FF00FFu) | kMagicPair;   // f1, f3
+    p[2] = (w1 & 0x00FF00FFu) | kMagicPair;          // f4, f6
+    p[3] = ((w1 >> 8) & 0x00FF00FFu) | kMagicPair;   // f5, f7
+  }
+}
+
+__device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Magic pair of register v -> exact (q - z) in both halves:
+// (1024 + MUL q) / MUL - (1024 / MUL + z); every step is exact in fp16.
+template <int BITS>
+__device__ __forceinline__ half2_t pair_minus_zero(uint32_t p, int v, half2_t neg_off) {
+  const _Float16 inv = (_Float16)(1.0f / (float)Block<BITS>::MUL[v]);
+  return as_half2(p) * half2_t{inv, inv} + neg_off;
+}
+
+// -(1024 / MUL_v + z) for a zero point z (exact in fp16 for every bit width).
+template <int BITS>
+__device__ __forceinline__ _Float16 neg_offset(int v, int z) {
+  return (_Float16)(-(kMagic / (float)Block<BITS>::MUL[v] + (float)z));
+}
+
+// Zero points of the four adjacent columns n .. n+3 (n % 4 == 0) of group row g,
+// as four b-bit fields in the low 4b bits of the result.
+template <int BITS>
+__device__ __forceinline__ uint32_t load_zero4(const int32_t* __restrict__ qzeros, int64_t row_words,
+                                               int g, int n) {
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(qzeros) + (int64_t)g * row_words;
+  if constexpr (BITS == 3) {
+    const int base = 3 * (n >> 5);
+    const int bit = 3 * (n & 31);
+    const int w = bit >> 5;
+    const uint32_t lo = row[base + w];
+    const uint32_t hi = row[base + (w < 2 ? w + 1 : 2)];
+    return __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(bit & 31)) & 0xFFFu;
+  } else {
+    const int bit = n * BITS;
+    const uint32_t word = row[bit >> 5];
+    if constexpr (BITS == 8) return word;
+    else return (word >> (bit & 31)) & ((1u << (4 * BITS)) - 1u);
+  }
+}
+
+__device__ __forceinline__ int field_of4(uint32_t z4, int j, int bits) {
+  return (int)((z4 >> (bits * j)) & ((1u << bits) - 1u));
+}
+
+// Round-to-nearest-even fp32 -> fp16 with subnormals (hardware conversion).
+__device__ __forceinline__ _Float16 f32_to_f16(float f) { return (_Float16)f; }
+
+}  // namespace gptq

@@ -1,0 +1,190 @@
+// gptq_quantize: min/max round-to-nearest quantization of W [K, N] (fp32) into
+// the packed GPTQ tensors (qweight, qzeros, scales).
+//
+// Formulas (page "Enhancing vLLM's support for the GPTQv2 format", section
+// "Weight quantization of LLMs"): scale = (wmax - wmin) / (2^b - 1),
+// zero = -round(wmin / scale), q = clamp(round(w / scale) + zero); symmetric
+// groups take wmax = -wmin = max|w| and zero = round((2^b - 1) / 2).  Storage
+// of the zero (section "From GPTQv1 to GPTQv2"): v2 stores zero, v1 stores
+// clamp(zero - 1).  Readings of what the page leaves open: round() is
+// round-half-even; zero and q are clamped to [0, 2^b - 1]; the scale is
+// computed in fp64, stored as fp16 (nearest-even) and the stored value is the
+// one used for zero and q; a stored scale of 0 becomes 1; every division and
+// rounding that decides an integer runs in fp64.
+//
+// Two kernels on the caller's stream:
+//   params: one thread per (group, column): min/max over the group's rows,
+//           scale, true zero (to a stream-ordered temporary), and the packed
+//           stored zeros of the block's 256 columns.
+//   pack:   one thread per (32-row chunk, column): the chunk's 32 codes packed
+//           LSB-first into b consecutive qweight rows.
+#include <hip/hip_runtime.h>
+
+#include "gptq_kernels.hpp"
+
+namespace gptq {
+
+// fp64 -> fp16 bits, round to nearest even, subnormals kept, overflow to inf.
+__device__ __forceinline__ uint16_t f64_to_f16_bits(double d) {
+  const uint64_t u = (uint64_t)__double_as_longlong(d);
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  const int exp = (int)((u >> 52) & 0x7FF);
+  const uint64_t mant = u & ((1ull << 52) - 1);
+  if (exp == 0x7FF) return sign | 0x7C00u | (mant ? 0x200u : 0u);
+  if (exp == 0) return sign;                      // fp64 subnormal: far below fp16 range
+  const int e = exp - 1023;
+  if (e > 15) return sign | 0x7C00u;
+  const uint64_t sig = mant | (1ull << 52);
+  const int shift = (e >= -14) ? 42 : 28 - e;     // keep 11 bits, or align to 2^-24
+  if (shift >= 64) return sign;
+  uint64_t q = sig >> shift;
+  const uint64_t rem = sig & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (e >= -14) {
+    int he = e + 15;
+    if (q == (1ull << 11)) { q = 1ull << 10; ++he; }
+    if (he >= 31) return sign | 0x7C00u;
+    return (uint16_t)(sign | (he << 10) | (uint16_t)(q & 0x3FF));
+  }
+  return (uint16_t)(sign | q);                    // q == 1024 is the smallest normal
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+  return (double)__builtin_bit_cast(_Float16, h);
+}
+
+struct QuantArgs {
+  const float* w;          // [K, N]
+  const int32_t* g_idx;    // nullable
+  int32_t* qweight;        // [K*b/32, N]
+  int32_t* qzeros;         // [G, N*b/32]
+  uint16_t* scales;        // [G, N] fp16 bits
+  uint8_t* zero_tmp;       // [G, N] true zero points
+  int N, K, G, group_size, bits, sym, is_v2;
+};
+
+__global__ __launch_bounds__(256) void quant_params_kernel(QuantArgs a) {
+  __shared__ int32_t gl[256];
+  __shared__ uint32_t zs[256];
+  const int tid = threadIdx.x;
+  const int n0 = blockIdx.x * 256;
+  const int n = n0 + tid;
+  const int g = blockIdx.y;
+  const bool ok = n < a.N;
+  const int qmax = (1 << a.bits) - 1;
+
+  float wmin = 0.f, wmax = 0.f;
+  bool any = false;
+  auto take = [&](int k) {
+    if (!ok) return;
+    const float v = a.w[(int64_t)k * a.N + n];
+    if (!any) { wmin = v; wmax = v; any = true; }
+    else { wmin = fminf(wmin, v); wmax = fmaxf(wmax, v); }
+  };
+  if (a.g_idx) {
+    for (int k0 = 0; k0 < a.K; k0 += 256) {
+      __syncthreads();
+      gl[tid] = (k0 + tid < a.K) ? a.g_idx[k0 + tid] : -1;
+      __syncthreads();
+      const int kn = min(256, a.K - k0);
+      for (int i = 0; i < kn; ++i)
+        if (gl[i] == g) take(k0 + i);
+    }
+  } else {
+    for (int k = g * a.group_size; k < (g + 1) * a.group_size; ++k) take(k);
+  }
+
+  double lo = (double)wmin, hi = (double)wmax;     // an empty group acts as all-zero
+  if (a.sym) {
+    const double wabs = fmax(fabs(lo), fabs(hi));
+    hi = wabs;
+    lo = -wabs;
+  }
+  uint16_t sbits = f64_to_f16_bits((hi - lo) / (double)qmax);
+  if ((sbits & 0x7FFFu) == 0) sbits = 0x3C00u;       // degenerate group: scale 1.0
+  const double s = f16_bits_to_f64(sbits);
+  int zero;
+  if (a.sym) {
+    zero = (int)rint((double)qmax / 2.0);
+  } else {
+    double z = -rint(lo / s);
+    z = z < 0.0 ? 0.0 : (z > (double)qmax ? (double)qmax : z);
+    zero = (int)z;
+  }
+  if (ok) {
+    a.scales[(int64_t)g * a.N + n] = sbits;
+    a.zero_tmp[(int64_t)g * a.N + n] = (uint8_t)zero;
+  }
+  int stored = a.is_v2 ? zero : zero - 1;
+  stored = stored < 0 ? 0 : stored;
+  zs[tid] = (uint32_t)stored;
+  __syncthreads();
+
+  // pack the stored zeros of this block's columns: word t = stream bits [32t, 32t+32)
+  const int ncols = min(256, a.N - n0);
+  const int nwords = ncols * a.bits / 32;
+  if (tid < nwords) {
+    uint32_t word = 0;
+    const int bit0 = 32 * tid;
+    const int f_first = bit0 / a.bits;
+    const int f_last = (bit0 + 31) / a.bits;
+    for (int f = f_first; f <= f_last && f < ncols; ++f) {
+      const int pos = f * a.bits - bit0;            // may be negative (straddles in from below)
+      const uint64_t v = (uint64_t)zs[f];
+      word |= (uint32_t)(pos >= 0 ? (v << pos) : (v >> -pos));
+    }
+    a.qzeros[(int64_t)g * (a.N * a.bits / 32) + (n0 * a.bits) / 32 + tid] = (int32_t)word;
+  }
+}
+
+__global__ __launch_bounds__(256) void quant_pack_kernel(QuantArgs a) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  if (n >= a.N) return;
+  const int qmax = (1 << a.bits) - 1;
+  uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // 32 fields * b bits = b words
+  for (int i = 0; i < 32; ++i) {
+    const int k = 32 * c + i;
+    const int g = group_of(a.g_idx, k, a.group_size, a.G);
+    const double s = f16_bits_to_f64(a.scales[(int64_t)g * a.N + n]);
+    const int zero = a.zero_tmp[(int64_t)g * a.N + n];
+    double qd = rint((double)a.w[(int64_t)k * a.N + n] / s) + (double)zero;
+    qd = qd < 0.0 ? 0.0 : (qd > (double)qmax ? (double)qmax : qd);
+    const uint64_t q = (uint64_t)qd;
+    const int bit = i * a.bits;
+    const int wi = bit >> 5, off = bit & 31;
+    words[wi] |= (uint32_t)(q << off);
+    if (off + a.bits > 32) words[wi + 1] |= (uint32_t)(q >> (32 - off));
+  }
+  for (int i = 0; i < a.bits; ++i) a.qweight[(int64_t)(c * a.bits + i) * a.N + n] = (int32_t)words[i];
+}
+
+hipError_t launch_quantize(const float* w, const int32_t* g_idx, int bits, int group_size, int sym, int is_v2,
+                           int N, int K, int32_t* qweight, int32_t* qzeros, void* scales, hipStream_t stream) {
+  QuantArgs a{};
+  a.w = w;
+  a.g_idx = g_idx;
+  a.qweight = qweight;
+  a.qzeros = qzeros;
+  a.scales = static_cast<uint16_t*>(scales);
+  a.N = N;
+  a.K = K;
+  a.G = K / group_size;
+  a.group_size = group_size;
+  a.bits = bits;
+  a.sym = sym;
+  a.is_v2 = is_v2;
+  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&a.zero_tmp), (size_t)a.G * N, stream);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(quant_params_kernel, dim3((N + 255) / 256, a.G), dim3(256), 0, stream, a);
+  err = hipGetLastError();
+  if (err == hipSuccess) {
+    hipLaunchKernelGGL(quant_pack_kernel, dim3((N + 255) / 256, K / 32), dim3(256), 0, stream, a);
+    err = hipGetLastError();
+  }
+  const hipError_t ferr = hipFreeAsync(a.zero_tmp, stream);
+  return err != hipSuccess ? err : ferr;
+}
+
+}  // namespace gptq

@@ -11,7 +11,8 @@ total) are rotated so the 256 MB Infinity Cache cannot serve them.
 
 The JSON line also carries:
   roofline      the decode kernel: algorithmic bytes per launch (weights + x +
-                y) / its mean launch time from HIP events around each launch,
+                y) / its mean launch time (HIP events around replays of a HIP
+                graph of that layer's launches over the rotated copies),
                 against 8 TB/s;
   prefill       the 70B-MLP M=2048 GEMMs (4-bit g128 sym v1, 8-bit g128 asym
                 v2): TFLOP/s against 2.5 PFLOP/s dense fp16 MFMA;
@@ -68,6 +69,10 @@ def make_layer(torch, gq, wl, layer, M, dev):
 
 
 def bench_decode(torch, gq, args, dev):
+    """Decode step timing.  Launches are captured in HIP graphs so the Python
+    binding's per-call overhead stays out of the timed region: one graph holds
+    R steps (R rotated weight copies x 4 layers); per-layer graphs hold R launches
+    of one layer and give the kernel's mean launch time."""
     from workload import WORKLOADS
     wl = WORKLOADS["llama7b_decode_w4g128"]
     base = [make_layer(torch, gq, wl, l, 1, dev) for l in wl.layers]
@@ -76,47 +81,58 @@ def bench_decode(torch, gq, args, dev):
     sets = [base] + [[{**L, "qweight": L["qweight"].clone(), "qzeros": L["qzeros"].clone(),
                        "scales": L["scales"].clone()} for L in base] for _ in range(copies - 1)]
     outs = [torch.empty((1, L["N"]), dtype=torch.float16, device=dev) for L in base]
-    stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
-        s = sets[i % len(sets)]
-        for j, L in enumerate(s):
-            if ev is not None:
-                ev[2 * j].record(stream)
-            gq.gemm(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits, wl.group_size, wl.is_v2,
-                    out=outs[j])
-            if ev is not None:
-                ev[2 * j + 1].record(stream)
+    def launch(r, j):
+        L = sets[r][j]
+        gq.gemm(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits, wl.group_size, wl.is_v2,
+                out=outs[j])
 
-    for i in range(args.warmup):
-        step(i)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for i in range(max(args.warmup, 1)):          # also allocates the split-K workspace of `side`
+            for j in range(len(base)):
+                launch(i % copies, j)
     torch.cuda.synchronize()
 
-    # timed region: whole steps, back to back
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all, stream=side):
+        for r in range(copies):
+            for j in range(len(base)):
+                launch(r, j)
+    g_layer = []
+    for j in range(len(base)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for r in range(copies):
+                launch(r, j)
+        g_layer.append(g)
 
-    # per-launch event pairs for the decode kernel's mean launch time
-    nrep = max(1, min(args.steps, 100))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(base))] for _ in range(nrep)]
-    for i in range(nrep):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    per_layer_ms = [float(np.mean([evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(nrep)]))
-                    for j in range(len(base))]
+    def timed(graph, reps):
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream(dev)
+        e0.record(st)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    replays = max(1, -(-args.steps // copies))
+    steps = replays * copies
+    ms_per_step = timed(g_all, replays) / steps
+    per_layer_ms = [timed(g, replays) / steps for g in g_layer]
 
     alg = [layer_bytes(L["K"], L["N"], wl.bits, wl.group_size) + 2 * L["K"] + 2 * L["N"] for L in base]
     mean_launch_ms = float(np.mean(per_layer_ms))
     achieved = (sum(alg) / len(alg)) / (mean_launch_ms * 1e-3) / 1e9
     layers = [{"layer": l.name, "K": l.K, "N": l.N, "alg_bytes": a, "us": round(t * 1e3, 2),
                "GBps": round(a / (t * 1e-3) / 1e9, 1)} for l, a, t in zip(wl.layers, alg, per_layer_ms)]
-    return dict(wl=wl, wbytes=wbytes, copies=copies, ms_per_step=ms_per_step, achieved=achieved,
+    del g_all, g_layer
+    return dict(wl=wl, wbytes=wbytes, copies=copies, ms_per_step=ms_per_step, achieved=achieved, steps=steps,
                 mean_launch_us=mean_launch_ms * 1e3, layers=layers, base=base)
 
 
@@ -235,7 +251,7 @@ def main():
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": dec["steps"],
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 5),
         "higher_is_better": True,

@@ -25,15 +25,14 @@
  *   out      fp16  [M, N]          written, never accumulated into.
  * with G = K / group_size.  The int32 words are bit containers (no sign).
  *
- * Ownership and streams: the library keeps no pointer after a call returns.
- * Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ * Ownership and streams: the library keeps no pointer after a call returns
+ * and owns no device memory between calls (gptq_quantize alone uses a
+ * stream-ordered temporary that is freed on the same stream).  Work is
+ * enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
  * asynchronous: buffers must stay valid until that work completes, and a
- * device-side fault surfaces at the caller's next synchronisation.  The only
- * library-owned state is a split-K workspace per (device, stream), allocated on
- * the first M <= 16 call on that pair (so that call must not be inside a HIP
- * graph capture), reused afterwards and freed by gptq_release().  Calls that
- * overlap on the same stream are serialised by the stream; concurrent calls on
- * different streams use different workspaces.
+ * device-side fault surfaces at the caller's next synchronisation.  The GEMM
+ * and dequant entry points allocate nothing, so they may be captured in a HIP
+ * graph.
  *
  * Errors: every function returns GPTQ_OK (0) or a negative gptq_status code;
  * nothing is launched when an argument check fails, and no C++ exception
@@ -64,8 +63,8 @@ typedef enum gptq_status {
   GPTQ_ERR_BAD_BITS = -2,    /* bits not in {2, 3, 4, 8} */
   GPTQ_ERR_BAD_SHAPE = -3,   /* M < 0, N <= 0, K <= 0, K % 32, N % 32, or a size limit */
   GPTQ_ERR_BAD_GROUP = -4,   /* group_size <= 0 or K % group_size != 0 */
-  GPTQ_ERR_MISALIGNED = -5,  /* x, qweight, out not 16-byte aligned; scales not 8; qzeros, g_idx not 4 */
-  GPTQ_ERR_NO_MEM = -6,      /* device memory for a workspace or temporary could not be allocated */
+  GPTQ_ERR_MISALIGNED = -5,  /* x, qweight, g_idx, out not 16-byte aligned; scales not 8; qzeros not 4 */
+  GPTQ_ERR_NO_MEM = -6,      /* the quantizer's temporary could not be allocated */
   GPTQ_ERR_LAUNCH = -7,      /* a kernel launch failed */
   GPTQ_ERR_DEVICE = -8,      /* no current HIP device or a HIP runtime call failed */
   GPTQ_ERR_BAD_ARG = -9      /* is_v2 / sym not 0 or 1, or a gptq_gemm_ex option out of range */
@@ -83,7 +82,8 @@ typedef enum gptq_status {
  *               Mandatory: there is no default and no format detection.
  *   M, N, K     x is [M,K], out is [M,N]; N % 32 == 0 and K % 32 == 0.
  *   stream      hipStream_t as void*.
- * M <= 16 runs the split-K decode kernel; larger M runs the MFMA prefill kernel.
+ * M <= 16 runs the decode kernel (workgroups own full-K column tiles, MFMA
+ * with M padded to 16); larger M runs the MFMA prefill kernel.
  */
 GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros,
               const void* scales, const int32_t* g_idx, int bits, int group_size,
@@ -91,16 +91,17 @@ GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qze
 
 /*
  * gptq_gemm with explicit kernel choice, for tests and tuning.
- *   path     0 = automatic (as gptq_gemm), 1 = decode kernel (requires M <= 16),
- *            2 = prefill kernel (any M).
- *   split_k  0 = automatic; > 0 = number of K slices the decode kernel reduces
- *            across workgroups (clamped to the number of 32-row chunks).
+ *   path          0 = automatic (as gptq_gemm), 1 = decode kernel (requires
+ *                 M <= 16), 2 = prefill kernel (any M).
+ *   decode_waves  0 = automatic; 1..16 = waves per decode workgroup (each
+ *                 workgroup owns a column tile for all of K; its waves split K;
+ *                 values above 8 are clamped to 8).
  * Other values give GPTQ_ERR_BAD_ARG.
  */
 GPTQ_API int gptq_gemm_ex(const void* x, const int32_t* qweight, const int32_t* qzeros,
                  const void* scales, const int32_t* g_idx, int bits, int group_size,
                  int is_v2, int64_t M, int64_t N, int64_t K, void* out, void* stream,
-                 int path, int split_k);
+                 int path, int decode_waves);
 
 /*
  * W^ = dequant(W) into w_out, fp16 [K, N] row-major (the "reconstruct" kernel
@@ -113,13 +114,18 @@ GPTQ_API int gptq_dequant(const int32_t* qweight, const int32_t* qzeros, const v
                  int64_t N, int64_t K, void* w_out, void* stream);
 
 /*
- * Argument checks of gptq_gemm / gptq_dequant only: pure host code, touches no
- * device and no pointer target.  Returns the code the full call would return
- * for these arguments before any HIP call.
+ * Argument checks of gptq_gemm / gptq_gemm_ex / gptq_dequant only (the GEMM
+ * checks also pick the kernel and its launch shape): pure host code, touches
+ * no device and no pointer target.  Returns the code the full call would return for these
+ * arguments before any HIP call.
  */
 GPTQ_API int gptq_gemm_check(const void* x, const int32_t* qweight, const int32_t* qzeros,
                     const void* scales, const int32_t* g_idx, int bits, int group_size,
                     int is_v2, int64_t M, int64_t N, int64_t K, const void* out);
+GPTQ_API int gptq_gemm_ex_check(const void* x, const int32_t* qweight, const int32_t* qzeros,
+                       const void* scales, const int32_t* g_idx, int bits, int group_size,
+                       int is_v2, int64_t M, int64_t N, int64_t K, const void* out,
+                       int path, int decode_waves);
 GPTQ_API int gptq_dequant_check(const int32_t* qweight, const int32_t* qzeros, const void* scales,
                        const int32_t* g_idx, int bits, int group_size, int is_v2,
                        int64_t N, int64_t K, const void* w_out);
@@ -147,8 +153,8 @@ GPTQ_API int gptq_quantize(const float* w, const int32_t* g_idx, int bits, int g
 /* Static text for a gptq_status code ("unknown error" for other values). */
 GPTQ_API const char* gptq_strerror(int code);
 
-/* Frees every library-owned workspace on every device.  The caller must make
- * sure no enqueued gptq work is still running. */
+/* Releases library-owned device memory.  The library keeps none between calls,
+ * so this is a no-op kept for callers that pair it with their teardown. */
 GPTQ_API void gptq_release(void);
 
 /* Library ABI version: 1. */

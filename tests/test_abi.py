@@ -28,7 +28,7 @@ def declared_status():
 
 def test_header_declares_api():
     names = declared_functions()
-    for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check",
+    for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check", "gptq_gemm_ex_check",
               "gptq_dequant_check", "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
     assert declared_status() == gq.STATUS
@@ -86,6 +86,7 @@ def test_gemm_check_codes():
     assert gemm_check(sc=SC + 4) == -5
     assert gemm_check(qz=QZ + 2) == -5
     assert gemm_check(gi=GI + 2) == -5
+    assert gemm_check(gi=GI + 4) == -5
     assert gemm_check(v2=2) == -9
     assert gemm_check(bits=3, N=32, K=96, gs=32) == 0
 
@@ -114,6 +115,7 @@ def test_invalid_calls_return_before_any_launch():
     assert lib.gptq_gemm_ex(X, QW, QZ, SC, None, 4, 128, 1, 17, 4096, 4096, OUT, None, 1, 0) == -9
     assert lib.gptq_gemm_ex(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, None, 3, 0) == -9
     assert lib.gptq_gemm_ex(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, None, 0, -1) == -9
+    assert lib.gptq_gemm_ex(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, None, 0, 17) == -9
     assert lib.gptq_dequant(QW, QZ, SC, None, 4, 100, 1, 4096, 4096, OUT, None) == -4
     assert lib.gptq_gemm(X, QW, QZ, SC, None, 4, 128, 1, 0, 4096, 4096, OUT, None) == 0   # M == 0
 
@@ -128,3 +130,38 @@ def test_python_binding_rejects_bad_tensors():
         gq.gemm(x, qw, qz, sc, None, 5, 128, True)
     with pytest.raises(ValueError):
         gq.gemm(x, qw, qz, sc, None, 4, 128, True)          # CPU tensors are rejected
+
+
+@needs_lib
+def test_every_decode_shape_has_a_launch_plan():
+    """Kernel choice and launch shape (pure host) succeed for every bit width,
+    M in 1..16, both scale paths and the layer shapes the workloads use, plus
+    ragged small ones."""
+    shapes = [(4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096), (12288, 4096), (5120, 13824),
+              (13824, 5120), (8192, 28672), (28672, 8192), (96, 32), (256, 160), (1024, 32), (32768, 64)]
+    for bits in (2, 3, 4, 8):
+        for K, N in shapes:
+            for gi in (None, GI):
+                for gs in (32, 128):
+                    if K % gs:
+                        continue
+                    for M in list(range(1, 17)) + [17, 2048]:
+                        rc = gemm_check(gi=gi, bits=bits, gs=gs, M=M, N=N, K=K)
+                        assert rc == 0, (bits, K, N, gi, gs, M, rc)
+
+
+@needs_lib
+def test_forced_decode_always_has_a_launch_plan():
+    """path = decode must find a launch shape for every M <= 16 and every waves
+    setting, on the shapes the GPU tests force it on."""
+    lib = gq.library()
+    shapes = [(512, 160, 32), (512, 160, 128), (96, 32, 32), (96, 96, 96), (288, 224, 96), (256, 64, 16),
+              (544, 96, 32), (1024, 32, 1024), (2048, 320, 128), (8192, 256, 128), (8192, 4608, 128),
+              (8192, 17408, 128), (4096, 12288, 64), (12288, 4096, 64), (5120, 13824, 128), (13824, 5120, 128)]
+    for bits in (2, 3, 4, 8):
+        for K, N, gs in shapes:
+            for gi in (None, GI):
+                for M in range(1, 17):
+                    for waves in (0, 1, 2, 3, 4, 8, 16):
+                        rc = lib.gptq_gemm_ex_check(X, QW, QZ, SC, gi, bits, gs, 1, M, N, K, OUT, 1, waves)
+                        assert rc == 0, (bits, K, N, gs, gi, M, waves, rc)

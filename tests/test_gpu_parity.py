@@ -131,19 +131,38 @@ def test_gemm_ragged_and_group_shapes(dev, bits, K, N, gs):
             assert_close(y, ref, f"M={M} path={p}")
 
 
-@pytest.mark.parametrize("split_k", [1, 2, 3, 5, 16, 1000])
-def test_decode_split_k_and_determinism(dev, split_k):
+@pytest.mark.parametrize("waves", [1, 2, 3, 4, 8, 16])
+def test_decode_waves_and_determinism(dev, waves):
+    """Every waves-per-workgroup split of K gives the oracle's result, and
+    repeated calls are bit-identical (fixed reduction order)."""
     bits, K, N, gs = 4, 2048, 320, 128
     d, L = quantized(K, N, 16, bits, gs, True, False, False, seed=21)
     qw, qz, sc, gi = upload(L, dev)
     xt = torch.from_numpy(d.x).to(dev)
-    for M in (1, 4, 16):
+    for M in (1, 2, 3, 4, 16):
         ref = oracle.gptq_gemm_ref(d.x[:M], L.qweight, L.qzeros, L.scales, None, bits, gs, False, K, N)
         x = xt[:M].contiguous()
-        y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, split_k=split_k)
-        y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, split_k=split_k)
-        assert_close(y1, ref, f"M={M} split_k={split_k}")
+        y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, decode_waves=waves)
+        y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, decode_waves=waves)
+        assert_close(y1, ref, f"M={M} waves={waves}")
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_multi_phase_k(dev, bits, M):
+    """K long enough that M * K x-rows are staged in several LDS phases, with
+    column tile widths of 16, 32 and 64 (N chosen to select each)."""
+    K, gs = 8192, 128
+    for N in (256, 4096 + 512, 16384 + 1024):
+        if N > 5000 and bits != 4:
+            continue
+        d, L = quantized(K, N, M, bits, gs, False, True, False, seed=N + bits)
+        qw, qz, sc, gi = upload(L, dev)
+        cols = np.arange(0, N, max(1, N // 96))
+        ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N, cols=cols)
+        y = gq.gemm(torch.from_numpy(d.x).to(dev), qw, qz, sc, gi, bits, gs, True, path=gq.PATH_DECODE)
+        assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, f"N={N}")
 
 
 def test_gemm_closed_forms(dev):
@@ -190,10 +209,13 @@ def test_workload_full_size(dev, wname, lname, M):
     K, N = layer.K, layer.N
     d = draw_workload_layer(wl, layer, M, seed=0)
     L = oracle.quantize_layer(d.W, wl.bits, wl.group_size, wl.sym, wl.is_v2, d.g_idx)
-    del d.W
     if wl.bits == 2 and wl.outlier_rate > 0:
         assert set(np.unique(L.zero)) == {0, 1, 2, 3}
     qw, qz, sc, gi = upload(L, dev)
+    # the library's quantizer reproduces the oracle's packed tensors exactly
+    gqw, gqz, gsc = gq.quantize(torch.from_numpy(d.W).to(dev), gi, wl.bits, wl.group_size, wl.sym, wl.is_v2)
+    assert torch.equal(gqw, qw) and torch.equal(gqz, qz) and torch.equal(gsc.view(torch.int16), sc.view(torch.int16))
+    del gqw, gqz, gsc, d.W
     xt = torch.from_numpy(d.x).to(dev)
     y = gq.gemm(xt, qw, qz, sc, gi, wl.bits, wl.group_size, wl.is_v2).cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(1)
@@ -209,3 +231,25 @@ def test_workload_full_size(dev, wname, lname, M):
     w_ref = oracle.dequant_ref(L.qweight, L.qzeros, L.scales, L.g_idx, wl.bits, wl.group_size, wl.is_v2, K, N,
                                cols=cols)
     assert np.array_equal(w.cpu().numpy().view(np.uint16), w_ref.view(np.uint16))
+
+
+# ------------------------------------------------------------------ quantize + pack, bit-exact
+QZ_GRID = list(itertools.product(BITS, (False, True), (False, True), (False, True)))
+
+
+@pytest.mark.parametrize("bits,sym,is_v2,act", QZ_GRID)
+def test_quantize_bit_exact(dev, bits, sym, is_v2, act):
+    """gptq_quantize reproduces the oracle's min/max quantizer and packers bit for
+    bit (codes decided in fp64 on both sides)."""
+    for K, N, gs in ((512, 544, 64), (256, 96, 128), (96, 32, 32)):
+        d = draw_layer(K, N, 1, sigma=0.02, group_size=gs, outlier_rate=0.01, act_order=act, seed=bits + K)
+        W = d.W.copy()
+        W[:, 3] = 0.125                      # constant column: degenerate group -> scale 1
+        W[:gs, 5] = 1e-9                     # scale underflows to 0 in fp16 -> 1
+        W[:, 7] *= 1e-4                      # fp16-subnormal scales
+        L = oracle.quantize_layer(W, bits, gs, sym, is_v2, d.g_idx)
+        gi = None if d.g_idx is None else torch.from_numpy(d.g_idx).to(dev)
+        qw, qz, sc = gq.quantize(torch.from_numpy(W).to(dev), gi, bits, gs, sym, is_v2)
+        assert np.array_equal(qw.cpu().numpy(), L.qweight), (K, N, gs, "qweight")
+        assert np.array_equal(qz.cpu().numpy(), L.qzeros), (K, N, gs, "qzeros")
+        assert np.array_equal(sc.cpu().numpy().view(np.uint16), L.scales.view(np.uint16)), (K, N, gs, "scales")

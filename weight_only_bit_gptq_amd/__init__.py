@@ -62,6 +62,8 @@ def library() -> ctypes.CDLL:
         lib.gptq_dequant.restype = i32
         lib.gptq_gemm_check.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp]
         lib.gptq_gemm_check.restype = i32
+        lib.gptq_gemm_ex_check.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, i32, i32]
+        lib.gptq_gemm_ex_check.restype = i32
         lib.gptq_dequant_check.argtypes = [i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, vp]
         lib.gptq_dequant_check.restype = i32
         lib.gptq_quantize.argtypes = [vp, i32p, i32, i32, i32, i32, i64, i64, i32p, i32p, vp, vp]
@@ -130,7 +132,7 @@ def _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K=None):
 
 
 def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,
-         is_v2: bool, *, out=None, path: int = PATH_AUTO, split_k: int = 0):
+         is_v2: bool, *, out=None, path: int = PATH_AUTO, decode_waves: int = 0):
     """out[M, N] (fp16) = x[M, K] (fp16) . dequant(qweight, qzeros, scales, g_idx).
 
     Enqueued on the current HIP stream of x's device (asynchronous)."""
@@ -151,7 +153,7 @@ def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_s
         stream = torch.cuda.current_stream(dev).cuda_stream
         code = lib.gptq_gemm_ex(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
                                 None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
-                                int(bool(is_v2)), M, N, K, out.data_ptr(), stream, int(path), int(split_k))
+                                int(bool(is_v2)), M, N, K, out.data_ptr(), stream, int(path), int(decode_waves))
     _raise(code)
     return out
 
@@ -209,5 +211,5 @@ def quantize(w, g_idx: Optional[object], bits: int, group_size: int, sym: bool, 
 
 
 def release():
-    """Free the library's split-K workspaces (call with no gptq work in flight)."""
+    """Release library-owned device memory (none is kept between calls)."""
     library().gptq_release()

@@ -1,16 +1,16 @@
-// extern "C" entry points of libgptq.so: argument checks, kernel choice,
-// split-K workspace and launches on the caller's stream.  No exception leaves
-// this file; every failure is a gptq_status code.
+// extern "C" entry points of libgptq.so: argument checks, kernel choice and
+// launch shape, and launches on the caller's stream.  No exception leaves this
+// file; every failure is a gptq_status code.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <numeric>
 #include <cstdlib>
-#include <map>
-#include <mutex>
 #include <new>
 #include <utility>
 
-#include "../../include/gptq.h"
+#include "gptq.h"
 #include "gptq_kernels.hpp"
 
 namespace {
@@ -27,7 +27,7 @@ int check_weights(const int32_t* qweight, const int32_t* qzeros, const void* sca
   if (N > ((int64_t)1 << 20) || K > ((int64_t)1 << 20) || N * K >= kMaxElems) return GPTQ_ERR_BAD_SHAPE;
   if (group_size <= 0 || K % group_size != 0) return GPTQ_ERR_BAD_GROUP;
   if (is_v2 != 0 && is_v2 != 1) return GPTQ_ERR_BAD_ARG;
-  if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4) || (g_idx && !aligned(g_idx, 4)))
+  if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4) || (g_idx && !aligned(g_idx, 16)))
     return GPTQ_ERR_MISALIGNED;
   return GPTQ_OK;
 }
@@ -44,110 +44,100 @@ int check_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, con
   return GPTQ_OK;
 }
 
-// ---- split-K workspace, one per (device, stream)
-struct Workspace {
-  float* partial = nullptr;
-  size_t partial_elems = 0;
-  int* counters = nullptr;
-  size_t counter_elems = 0;
-};
+// Decode launch shape.  Column tiles of 16 * cpl columns (widest that still
+// gives >= 256 workgroups), waves per workgroup so the grid holds ~4K waves,
+// and K phases sized to the LDS budget.
+constexpr size_t kDecodeLdsBudget = 150 * 1024;
+constexpr int kNoDecodePlan = 1;
 
-std::mutex g_ws_mutex;
-std::map<std::pair<int, void*>, Workspace> g_ws;
-
-int get_workspace(int device, hipStream_t stream, size_t partial_elems, size_t counter_elems, Workspace** out) {
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace& ws = g_ws[std::make_pair(device, (void*)stream)];
-  if (ws.partial_elems < partial_elems || ws.counter_elems < counter_elems) {
-    if (ws.partial || ws.counters) {
-      if (hipStreamSynchronize(stream) != hipSuccess) return GPTQ_ERR_DEVICE;
-      (void)hipFree(ws.partial);
-      (void)hipFree(ws.counters);
-      ws = Workspace{};
-    }
-    const size_t pe = partial_elems > 0 ? partial_elems : 1;
-    const size_t ce = counter_elems > 0 ? counter_elems : 1;
-    if (hipMalloc(&ws.partial, pe * sizeof(float)) != hipSuccess) {
-      ws = Workspace{};
-      return GPTQ_ERR_NO_MEM;
-    }
-    if (hipMalloc(&ws.counters, ce * sizeof(int)) != hipSuccess) {
-      (void)hipFree(ws.partial);
-      ws = Workspace{};
-      return GPTQ_ERR_NO_MEM;
-    }
-    // counters start at zero; every reducing workgroup puts its counter back to zero
-    if (hipMemset(ws.counters, 0, ce * sizeof(int)) != hipSuccess) return GPTQ_ERR_DEVICE;
-    ws.partial_elems = pe;
-    ws.counter_elems = ce;
+int decode_shape(int bits, int M, int N, int K, int G, int waves, bool* per_elem, gptq::GemmArgs* a) {
+  const int C = K / 32;
+  int cpl = 1;
+  for (int c : {4, 2}) {
+    if ((N + 16 * c - 1) / (16 * c) >= 256) { cpl = c; break; }
   }
-  *out = &ws;
-  return GPTQ_OK;
+  const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
+  int nw0 = waves > 0 ? waves : (tiles <= 512 ? 8 : 4);
+  if (nw0 > gptq::decode_max_waves(cpl)) nw0 = gptq::decode_max_waves(cpl);
+  const int U = gptq::decode_batch(cpl, bits, M);
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const int cpg = *per_elem ? 1 : (K / G) / 32;
+    const int unit = std::lcm(2 * U, cpg);           // cpw granularity: batch pairs, whole groups
+    for (int nw = nw0; nw >= 1; --nw) {
+      // chunks per phase: limited by the x (and g_idx) pieces each thread stages and by LDS
+      int pc_max = gptq::decode_max_x_pieces(M) * 64 * nw / (4 * M);
+      if (*per_elem) pc_max = std::min(pc_max, gptq::decode_max_g_pieces() * 64 * nw / 8);
+      auto fits = [&](int c) {
+        const int pc = nw * c;
+        return pc <= pc_max && gptq::decode_lds_bytes(M, pc, nw, cpl, *per_elem, G, cpg) <= kDecodeLdsBudget;
+      };
+      int cpw = (C + nw - 1) / nw;
+      cpw = (cpw + unit - 1) / unit * unit;
+      while (cpw > unit && !fits(cpw)) cpw -= unit;
+      if (!fits(cpw)) continue;
+      a->tiles = tiles;
+      a->cpl = cpl;
+      a->nw = nw;
+      a->cpw = cpw;
+      a->pc = nw * cpw;
+      a->phases = (C + a->pc - 1) / a->pc;
+      a->cpg = cpg;
+      return GPTQ_OK;
+    }
+    if (*per_elem) break;
+    *per_elem = true;                                // whole groups do not fit: per-row path
+  }
+  return kNoDecodePlan;                              // the scale/zero table does not fit LDS
 }
 
-// Decode launch shape: 64-column tiles x K slices; aim for ~1024 workgroups.
-void decode_shape(int M, int N, int K, int forced_split, bool per_elem, int* tiles, int* splits,
-                  int* wg_chunks) {
-  const int C = K / 32;
-  const int T = (N + 63) / 64;
-  constexpr int kTargetWorkgroups = 1024;
-  int S = forced_split > 0 ? forced_split : (kTargetWorkgroups + T / 2) / T;
-  if (S < 1) S = 1;
-  if (S > C) S = C;
-  int wc = (C + S - 1) / S;
-  wc = (wc + 3) & ~3;
-  while (wc > 4 && gptq::decode_lds_bytes(M, wc, per_elem) > 49152) wc -= 4;
-  *tiles = T;
-  *wg_chunks = wc;
-  *splits = (C + wc - 1) / wc;
+// Argument checks plus kernel choice and launch shape: pure host code.
+int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+              const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+              const void* out, int path, int decode_waves, gptq::GemmArgs* a, bool* use_decode, bool* per_elem) {
+  if (path < 0 || path > 2 || decode_waves < 0 || decode_waves > 16) return GPTQ_ERR_BAD_ARG;
+  int rc = check_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out);
+  if (rc != GPTQ_OK) return rc;
+  if (path == 1 && M > 16) return GPTQ_ERR_BAD_ARG;
+  *a = gptq::GemmArgs{};
+  a->x = static_cast<const _Float16*>(x);
+  a->qweight = qweight;
+  a->qzeros = qzeros;
+  a->scales = static_cast<const _Float16*>(scales);
+  a->g_idx = g_idx;
+  a->out = static_cast<_Float16*>(const_cast<void*>(out));
+  a->M = (int)M;
+  a->N = (int)N;
+  a->K = (int)K;
+  a->G = (int)(K / group_size);
+  a->group_size = group_size;
+  a->zero_offset = is_v2 ? 0 : 1;
+  a->chunks = (int)(K / 32);
+  a->zrow_words = N * bits / 32;
+  *use_decode = (path == 1) || (path == 0 && M <= 16);
+  if (M == 0) return GPTQ_OK;
+  if (*use_decode) {
+    *per_elem = (g_idx != nullptr) || (group_size % 32 != 0);
+    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, per_elem, a);
+    if (rc2 != kNoDecodePlan) return rc2;
+    if (path == 1) return GPTQ_ERR_BAD_ARG;         // forced decode, but no launch shape fits
+    *use_decode = false;                             // very many groups: the prefill kernel
+  }
+  *per_elem = (g_idx != nullptr) || (group_size % 64 != 0);
+  gptq::prefill_shape(a->M, a->N, &a->tiles_m, &a->tiles_n);
+  return GPTQ_OK;
 }
 
 int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-              void* out, void* stream_ptr, int path, int split_k) {
-  if (path < 0 || path > 2 || split_k < 0) return GPTQ_ERR_BAD_ARG;
-  int rc = check_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out);
-  if (rc != GPTQ_OK) return rc;
-  if (path == 1 && M > 16) return GPTQ_ERR_BAD_ARG;
-  if (M == 0) return GPTQ_OK;
+              void* out, void* stream_ptr, int path, int decode_waves) {
+  gptq::GemmArgs a;
+  bool use_decode = false, per_elem = false;
+  const int rc = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
+                           decode_waves, &a, &use_decode, &per_elem);
+  if (rc != GPTQ_OK || M == 0) return rc;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
-
-  gptq::GemmArgs a{};
-  a.x = static_cast<const _Float16*>(x);
-  a.qweight = qweight;
-  a.qzeros = qzeros;
-  a.scales = static_cast<const _Float16*>(scales);
-  a.g_idx = g_idx;
-  a.out = static_cast<_Float16*>(out);
-  a.M = (int)M;
-  a.N = (int)N;
-  a.K = (int)K;
-  a.G = (int)(K / group_size);
-  a.group_size = group_size;
-  a.zero_offset = is_v2 ? 0 : 1;
-  a.chunks = (int)(K / 32);
-  a.zrow_words = N * bits / 32;
-
-  const bool use_decode = (path == 1) || (path == 0 && M <= 16);
-  hipError_t err;
-  if (use_decode) {
-    const bool per_elem = (g_idx != nullptr) || (group_size % 32 != 0);
-    decode_shape(a.M, a.N, a.K, split_k, per_elem, &a.tiles, &a.splits, &a.wg_chunks);
-    if (a.splits > 1) {
-      int device = 0;
-      if (hipGetDevice(&device) != hipSuccess) return GPTQ_ERR_DEVICE;
-      Workspace* ws = nullptr;
-      rc = get_workspace(device, stream, (size_t)a.tiles * a.splits * a.M * 64, (size_t)a.tiles, &ws);
-      if (rc != GPTQ_OK) return rc;
-      a.partial = ws->partial;
-      a.counters = ws->counters;
-    }
-    err = gptq::launch_decode(bits, per_elem, a, stream);
-  } else {
-    const bool per_elem = (g_idx != nullptr) || (group_size % 64 != 0);
-    gptq::prefill_shape(a.M, a.N, &a.tiles_m, &a.tiles_n);
-    err = gptq::launch_prefill(bits, per_elem, a, stream);
-  }
+  const hipError_t err = use_decode ? gptq::launch_decode(bits, per_elem, a, stream)
+                                    : gptq::launch_prefill(bits, per_elem, a, stream);
   return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
 }
 
@@ -158,7 +148,19 @@ extern "C" {
 int gptq_gemm_check(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
                     const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
                     const void* out) {
-  return check_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out);
+  gptq::GemmArgs a;
+  bool use_decode = false, per_elem = false;
+  return plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, 0, 0, &a,
+                   &use_decode, &per_elem);
+}
+
+int gptq_gemm_ex_check(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                       const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                       const void* out, int path, int decode_waves) {
+  gptq::GemmArgs a;
+  bool use_decode = false, per_elem = false;
+  return plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path, decode_waves,
+                   &a, &use_decode, &per_elem);
 }
 
 int gptq_dequant_check(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,
@@ -172,10 +174,10 @@ int gptq_dequant_check(const int32_t* qweight, const int32_t* qzeros, const void
 
 int gptq_gemm_ex(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
                  const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-                 void* out, void* stream, int path, int split_k) {
+                 void* out, void* stream, int path, int decode_waves) {
   try {
     return gemm_impl(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, stream, path,
-                     split_k);
+                     decode_waves);
   } catch (const std::bad_alloc&) {
     return GPTQ_ERR_NO_MEM;
   } catch (...) {
@@ -234,23 +236,16 @@ const char* gptq_strerror(int code) {
     case GPTQ_ERR_BAD_BITS: return "bits must be 2, 3, 4 or 8";
     case GPTQ_ERR_BAD_SHAPE: return "bad shape: need M >= 0, N and K positive multiples of 32, within size limits";
     case GPTQ_ERR_BAD_GROUP: return "group_size must be positive and divide K";
-    case GPTQ_ERR_MISALIGNED: return "misaligned pointer (x, qweight, out: 16 B; scales: 8 B; qzeros, g_idx: 4 B)";
-    case GPTQ_ERR_NO_MEM: return "device memory allocation failed (workspace or temporary)";
+    case GPTQ_ERR_MISALIGNED: return "misaligned pointer (x, qweight, g_idx, out: 16 B; scales: 8 B; qzeros: 4 B)";
+    case GPTQ_ERR_NO_MEM: return "device memory allocation failed (quantizer temporary)";
     case GPTQ_ERR_LAUNCH: return "kernel launch failed";
     case GPTQ_ERR_DEVICE: return "HIP runtime call failed";
-    case GPTQ_ERR_BAD_ARG: return "option out of range (is_v2, sym, path or split_k)";
+    case GPTQ_ERR_BAD_ARG: return "option out of range (is_v2, sym, path or decode_waves)";
     default: return "unknown error";
   }
 }
 
-void gptq_release(void) {
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  for (auto& kv : g_ws) {
-    (void)hipFree(kv.second.partial);
-    (void)hipFree(kv.second.counters);
-  }
-  g_ws.clear();
-}
+void gptq_release(void) {}
 
 int gptq_abi_version(void) { return 1; }
 

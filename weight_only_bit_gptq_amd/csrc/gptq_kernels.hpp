@@ -26,17 +26,29 @@ struct GemmArgs {
   const _Float16* scales;
   const int32_t* g_idx;     // nullable
   _Float16* out;            // [M, N]
-  float* partial;           // decode split-K partial sums (nullable when splits == 1)
-  int* counters;            // decode per-tile arrival counters (nullable when splits == 1)
   int M, N, K, G, group_size, zero_offset;
   int chunks;               // K / 32
   int64_t zrow_words;       // N * bits / 32
-  // decode launch shape
-  int tiles;                // ceil(N / 64)
-  int splits;               // K slices reduced across workgroups
-  int wg_chunks;            // 32-row chunks per workgroup (multiple of 4)
+  // decode launch shape: tiles of 16*cpl columns, nw waves per workgroup,
+  // K in phases of pc chunks, cpw chunks per wave per phase (a multiple of
+  // cpg = group_size / 32 on the fast path, so wave ranges hold whole groups)
+  int tiles, cpl, nw, cpw, pc, phases, cpg;
   // prefill launch shape
   int tiles_m, tiles_n;
+};
+
+// LDS carve-up of the decode kernel: two phase buffers (x fragments, per-chunk
+// correction sums or the phase's g_idx slice), then the scale/zero table; the
+// cross-wave reduction buffer aliases everything after the main loop.
+struct DecodeLayout {
+  size_t buf_stride;        // bytes of one phase buffer
+  size_t corr_off;          // correction sums inside a buffer (fast path)
+  size_t gidx_off;          // uint16 g_idx slice inside a buffer (per-element path)
+  size_t ptab_off;          // the phase's scale/zero rows inside a buffer (fast path)
+  int ptab_rows;            // groups a phase covers (fast path)
+  size_t tab_off;           // whole scale/zero table (per-element path)
+  bool fits_staging;        // the table quads fit the staging registers
+  size_t total;
 };
 
 // Group of row k: g_idx[k] (clamped into [0, G) so a bad entry cannot read out
@@ -52,8 +64,13 @@ __device__ __forceinline__ int group_of(const int32_t* __restrict__ g_idx, int k
 hipError_t launch_dequant(int bits, const DequantArgs& a, hipStream_t stream);
 
 // Decode (M <= 16).  `per_elem` selects the per-element scale/zero path (act
-// order or group_size % 32 != 0).  LDS bytes needed for a launch shape:
-size_t decode_lds_bytes(int M, int wg_chunks, bool per_elem);
+// order or group_size % 32 != 0).
+// LDS bytes of a launch shape (SIZE_MAX if its table cannot be staged)
+size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg);
+int decode_max_x_pieces(int M);   // 16-byte x pieces each thread may stage per phase
+int decode_max_g_pieces();   // 16-byte g_idx pieces each thread may stage per phase
+int decode_batch(int cpl, int bits, int M);   // chunks per weight-load batch (cpw must be a multiple)
+int decode_max_waves(int cpl);
 hipError_t launch_decode(int bits, bool per_elem, const GemmArgs& a, hipStream_t stream);
 
 // Prefill (any M, used for M > 16).

@@ -95,7 +95,8 @@ GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qze
  *                 M <= 16), 2 = prefill kernel (any M).
  *   decode_waves  0 = automatic; 1..16 = waves per decode workgroup (each
  *                 workgroup owns a column tile for all of K; its waves split K;
- *                 values above 8 are clamped to 8).
+ *                 values above the kernel's limit, 16 for M = 1 with 16-column
+ *                 tiles and 8 otherwise, are clamped to it).
  * Other values give GPTQ_ERR_BAD_ARG.
  */
 GPTQ_API int gptq_gemm_ex(const void* x, const int32_t* qweight, const int32_t* qzeros,

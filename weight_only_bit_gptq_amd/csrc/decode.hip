@@ -3,48 +3,51 @@
 // section 1.1: decode reads every weight once per token).
 //
 // Work split.  A workgroup owns a column tile of TN = 16 * CPL columns for the
-// whole of K, so no partial sum ever leaves the workgroup: its NW waves split
-// K, each wave streams its share of the packed words (lane = one 8-row block
-// of CPL adjacent columns, CPL = 1, 2 or 4 words per load), and the waves
-// reduce through LDS at the end.  Tile width and wave count are chosen per
-// shape so the grid covers all 256 CUs; consecutive tiles are placed on the
-// same XCD so neighbouring row pieces share that XCD's L2 lines.
+// whole of K, so no partial sum ever leaves the workgroup: its waves split K,
+// each wave takes CPW consecutive 32-row chunks per phase (lane = one 8-row
+// block of CPL adjacent columns, CPL = 1, 2 or 4 words per load), and the
+// waves reduce through LDS at the end.  Tile width, wave count and CPW are
+// chosen per shape so the grid covers all 256 CUs with little padding;
+// consecutive tiles are placed on the same XCD so neighbouring row pieces
+// share that XCD's L2 lines.
 //
-// Latency.  Everything a workgroup needs besides its weights is small and is
-// staged in LDS by a prologue: x (permuted into the unpack's field order, in
-// K-phases when M * K does not fit), the tile's scale/zero table (G x TN), and
-// for act order the phase's g_idx slice.  Those loads go out first, then each
-// wave fills a ring of two batches of packed words; afterwards every batch
-// that is consumed is refilled two batches ahead, so a wave keeps 4-8 KB of
-// weights in flight and never waits on a scale or a zero point.
+// Memory-level parallelism.  CPW is a compile-time constant and the chunk loop
+// is straight-line and branch-free: a wave issues the loads of its small
+// operands (x, the scale/zero rows, for act order the g_idx slice), then all
+// CPW of its weight loads back to back (buffer loads: one per-lane offset, the
+// chunk's offset in a scalar register), and each chunk waits only for its own
+// load.  For M = 1 every decode layer here takes a single phase, so a
+// workgroup's whole weight tile is in flight right after launch.  Larger
+// M * K runs in K-phases whose x is staged in alternating LDS buffers.
 //
 // Contraction: one v_mfma_f32_16x16x32_f16 per (32-row chunk, column slot):
 // A = 16 rows of x (rows >= M are zero), B = the block each lane unpacked.
 //
-// Fast path (group_size % 32 == 0, no g_idx): B holds the raw magic pairs
-// 1024 + MUL*q, x is pre-divided by MUL, and the zero point and the magic
-// offset are removed per group through the accumulator's initial value:
-//   acc_g = -(1024 * sum x' + z * sum x' MUL) + sum x' * B = sum x (q - z)
-//   y    += s * acc_g                    (s, z constant over a group)
-// i.e. the dequant formula with the scale factored out of the group's sum
+// Fast path (group_size % 32 == 0, no g_idx): a chunk lies in one group, so
+// its scale s and zero z are constant over it.  B holds the raw magic pairs
+// 1024 + MUL*q, x is pre-divided by MUL (x' = x / MUL), and the zero point
+// and the magic offset enter through the MFMA's accumulator input:
+//   D = -(1024 * sum x' + z * sum x' MUL) + sum x' B = sum x (q - z)
+//   y += s * D
+// i.e. the dequant formula with the scale factored out of the chunk's sum
 // (page "Enhancing vLLM's support for the GPTQv2 format", section "Weight
-// quantization of LLMs").  Per-element path (act order or small groups): B is
+// quantization of LLMs").  Per-element path (act order or other groups): B is
 // the exact fp16 dequantized weight, built with each row's own scale and zero.
 #include "gptq_kernels.hpp"
 
 namespace gptq {
 
-// chunks per load batch: 16-column tiles load one word per chunk, so they use
-// longer batches to keep the same bytes in flight
-// (and 64-column tiles of two-word blocks use shorter ones to fit registers;
-// 8 * batch * M <= 64 * x pieces keeps a phase's x within the staging registers)
-__host__ __device__ constexpr int decode_batch_of(int cpl, int loads, int mv) {
-  return cpl == 1 ? (mv <= 2 ? 8 : 4) : (cpl == 4 && loads == 2 ? 2 : 4);
+// 16-byte x pieces a thread stages per phase: a phase holds nw * CPW chunks of
+// M rows, so CPW * M <= 16 * XP must hold (the host checks it).
+__host__ __device__ constexpr int decode_x_pieces_of(int mv) { return mv == 1 ? 2 : 8; }
+constexpr int kDecodeTQuads = 4;   // scale/zero table quads (4 columns of a group) per thread per round
+
+// CPW values compiled for a (CPL, words per block, MV) triple: weight words
+// per lane in flight, at most 64 where that leaves room for the rest (M = 1,
+// 32- and 64-column tiles) and 32 otherwise, so that nothing spills.
+__host__ __device__ constexpr bool decode_cpw_ok(int cpl, int loads, int cpw, int mv) {
+  return (cpw == 8 || cpw == 16 || cpw == 32) && cpw * cpl * loads <= ((mv == 1 && cpl > 1) ? 64 : 32);
 }
-// 16-byte x pieces a thread stages per phase (more rows of x -> more pieces)
-__host__ __device__ constexpr int decode_x_pieces_of(int mv) { return mv <= 2 ? 4 : 8; }
-constexpr int kDecodeGPieces = 4;  // 16-byte g_idx pieces (4 rows) a thread stages per phase
-constexpr int kDecodeTQuads = 4;   // scale/zero table quads (4 columns of a group) per thread
 
 template <int CPL> struct WordVec;
 template <> struct WordVec<1> { typedef uint32_t T; };
@@ -56,39 +59,32 @@ template <int CPL> __device__ __forceinline__ uint32_t word_of(const typename Wo
   else return v[j];
 }
 
-// Zero points of the CPL adjacent columns n .. n+CPL-1 (n % CPL == 0) of group
-// row g, as CPL b-bit fields in the low CPL*b bits.
-template <int BITS, int CPL>
-__device__ __forceinline__ uint32_t load_zeros(const int32_t* __restrict__ qzeros, int64_t row_words, int g, int n) {
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(qzeros) + (int64_t)g * row_words;
-  constexpr uint32_t mask = (CPL * BITS >= 32) ? 0xFFFFFFFFu : ((1u << (CPL * BITS)) - 1u);
-  if constexpr (BITS == 3) {
-    const int base = 3 * (n >> 5);
-    const int bit = 3 * (n & 31);
-    const int w = bit >> 5;
-    const uint32_t lo = row[base + w];
-    const uint32_t hi = row[base + (w < 2 ? w + 1 : 2)];
-    return __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(bit & 31)) & mask;
-  } else {
-    const int bit = n * BITS;
-    return (row[bit >> 5] >> (bit & 31)) & mask;
-  }
+template <int CPL>
+__device__ __forceinline__ typename WordVec<CPL>::T buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (CPL == 1) return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+  else if constexpr (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
 }
 
 __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
-__host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg) {
+// rows of x a chunk's correction sums are laid out for (multiple of 4 for M > 1)
+__host__ __device__ inline int decode_corr_rows(int M) { return M == 1 ? 1 : (M + 3) & ~3; }
+
+__host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg,
+                                                      int phases) {
   DecodeLayout L;
   const size_t tn = (size_t)16 * cpl;
   const size_t frag = (size_t)pc * 4 * M * 16;
   L.corr_off = frag;
-  const size_t corr = per_elem ? 0 : (size_t)pc * M * 8;
+  const size_t corr = per_elem ? 0 : (size_t)pc * decode_corr_rows(M) * 8;
   L.gidx_off = align16(frag + corr);
   const size_t gidx = per_elem ? (size_t)pc * 32 * 2 : 0;
   L.ptab_off = align16(L.gidx_off + gidx);
-  L.ptab_rows = per_elem ? 0 : (pc + cpg - 1) / cpg;    // groups a phase covers (fast path)
-  L.buf_stride = align16(L.ptab_off + (size_t)L.ptab_rows * tn * 4);
-  L.tab_off = 2 * L.buf_stride;                          // whole table (per-element path)
+  // groups a window of pc chunks can touch (fast path)
+  L.ptab_rows = per_elem ? 0 : (pc - 1) / cpg + 2;
+  L.buf_stride = align16(L.ptab_off + (size_t)L.ptab_rows * tn * 8);
+  L.tab_off = (phases > 1 ? 2 : 1) * L.buf_stride;       // whole table (per-element path)
   const size_t tab = per_elem ? (size_t)G * tn * 4 : 0;
   // the phase table is staged in one round; the whole table (per-element path) loops
   L.fits_staging = per_elem || (size_t)L.ptab_rows * tn / 4 <= (size_t)kDecodeTQuads * 64 * nw;
@@ -98,33 +94,33 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   return L;
 }
 
-size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg) {
-  const DecodeLayout L = decode_layout(M, pc, nw, cpl, per_elem, G, cpg);
+size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg, int phases) {
+  const DecodeLayout L = decode_layout(M, pc, nw, cpl, per_elem, G, cpg, phases);
   return L.fits_staging ? L.total : ~(size_t)0;
 }
 
-int decode_max_x_pieces(int M) { return decode_x_pieces_of(M <= 2 ? M : 4); }
-int decode_max_g_pieces() { return kDecodeGPieces; }
-int decode_max_waves(int) { return 8; }
-int decode_batch(int cpl, int bits, int M) {
-  return decode_batch_of(cpl, (bits == 3 || bits == 8) ? 2 : 1, M <= 2 ? M : 4);
+int decode_max_x_pieces(int M) { return decode_x_pieces_of(M == 1 ? 1 : 4); }
+int decode_max_waves(int cpl, int M) { return (cpl == 1 && M == 1) ? 16 : 8; }
+bool decode_cpw_allowed(int cpl, int bits, int cpw, int M) {
+  return decode_cpw_ok(cpl, (bits == 3 || bits == 8) ? 2 : 1, cpw, M == 1 ? 1 : 4);
 }
 
-// At most 8 waves per workgroup, so every lane has 256 registers for the
-// weight ring, the staging registers and the accumulators.
-template <int BITS, bool PER_ELEM, int MV, int CPL>
-__global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
+// 16 waves for 16-column tiles at M = 1 (128 registers per lane), 8 otherwise.
+template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
+__global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  constexpr int U = decode_batch_of(CPL, Block<BITS>::LOADS, MV);
   constexpr int XP = decode_x_pieces_of(MV);
-  constexpr int GP = kDecodeGPieces;
+  constexpr int GP = (CPW + 7) / 8;                  // g_idx pieces: 8 * CPW rows <= 64 * GP pieces of 4
   constexpr int TQ = kDecodeTQuads;
   constexpr int TN = 16 * CPL;
+  constexpr int L = Block<BITS>::LOADS;
   typedef typename WordVec<CPL>::T wvec;
+  typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-  const int M = a.M;
+  const int M = MV == 1 ? 1 : a.M;
   const int nthreads = (int)blockDim.x;
-  const int nw = nthreads >> 6;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -134,31 +130,35 @@ __global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
   if ((a.tiles & 7) == 0) t = (blockIdx.x & 7) * (a.tiles >> 3) + (blockIdx.x >> 3);
   const int n0 = t * TN;
   const int n = n0 + CPL * q;
-  const bool col_ok = n < a.N;
+  const int nc = n < a.N ? n : 0;                    // lanes past N read column 0 (result unused)
   const int C = a.chunks;
-  const int pc = a.pc, cpw = a.cpw, phases = a.phases;
-  const DecodeLayout lay = decode_layout(M, pc, nw, CPL, PER_ELEM, a.G, a.cpg);
-
-  const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.qweight);
+  const int pc = a.pc, phases = a.phases, cpg = a.cpg;
+  const DecodeLayout lay = decode_layout(M, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases);
+  const int Mp = decode_corr_rows(M);
   const uint32_t sel = block_sel<BITS>(kb);
 
-  // ---- prologue loads: x (phase 0), g_idx slice (phase 0), scale/zero table
+  // ---- small operands of a phase: x, g_idx slice, scale/zero rows.  The loads
+  // are unconditional (out-of-range indices are clamped, the value replaced by
+  // zero when it is stored) and keep raw words, so they issue as one burst.
   half8_t xr[XP];
   const int xpieces = pc * M * 4;
+  auto x_piece = [&](int p, int i, int& m, int& cl, int& kbe) {
+    const int e = tid + i * nthreads;
+    kbe = e & 3;
+    const int rest = e >> 2;
+    m = rest % M;
+    cl = rest / M;
+    return e < xpieces && p * pc + cl < C;
+  };
   auto load_x = [&](int p) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      const int e = tid + i * nthreads;
-      xr[i] = half8_t{};
-      if (e < xpieces) {
-        const int kbe = e & 3, rest = e >> 2;
-        const int m = rest % M, cl = rest / M;
-        const int c = p * pc + cl;
-        if (c < C) xr[i] = *reinterpret_cast<const half8_t*>(a.x + (int64_t)m * a.K + 32 * c + 8 * kbe);
-      }
+      int m, cl, kbe;
+      const bool ok = x_piece(p, i, m, cl, kbe);
+      const int c = ok ? p * pc + cl : 0;
+      xr[i] = *reinterpret_cast<const half8_t*>(a.x + (int64_t)(ok ? m : 0) * a.K + 32 * c + 8 * kbe);
     }
   };
-  typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
   i32x4_t gr[PER_ELEM ? GP : 1];
   const int gpieces = pc * 8;                        // 4 rows per piece
   auto load_g = [&](int p) {
@@ -166,33 +166,28 @@ __global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < GP; ++i) {
         const int e = tid + i * nthreads;
-        gr[i] = i32x4_t{0, 0, 0, 0};
-        if (e < gpieces) {
-          const int k = 32 * p * pc + 4 * e;
-          if (k < a.K) {
-            if (a.g_idx) gr[i] = *reinterpret_cast<const i32x4_t*>(a.g_idx + k);
-            else gr[i] = i32x4_t{k / a.group_size, (k + 1) / a.group_size, (k + 2) / a.group_size,
-                                 (k + 3) / a.group_size};
-          }
-        }
+        const int k = 32 * p * pc + 4 * e;
+        const int kk = (e < gpieces && k < a.K) ? k : 0;
+        if (a.g_idx) gr[i] = *reinterpret_cast<const i32x4_t*>(a.g_idx + kk);
+        else gr[i] = i32x4_t{kk / a.group_size, (kk + 1) / a.group_size, (kk + 2) / a.group_size,
+                             (kk + 3) / a.group_size};
       }
     }
   };
-  auto store_xg = [&](int buf) {
-    unsigned char* base = lds + (size_t)buf * lay.buf_stride;
+  auto store_xg = [&](int p) {
+    unsigned char* base = lds + (size_t)(p & 1) * lay.buf_stride;
     _Float16* frag = reinterpret_cast<_Float16*>(base);
     float* corr = reinterpret_cast<float*>(base + lay.corr_off);
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      const int e = tid + i * nthreads;
-      if (e >= xpieces) continue;                    // xpieces % 4 == 0: groups of four stay together
-      const int kbe = e & 3, rest = e >> 2;
-      const int m = rest % M, cl = rest / M;
+      int m, cl, kbe;
+      const bool ok = x_piece(p, i, m, cl, kbe);
+      if (tid + i * nthreads >= xpieces) continue;   // xpieces % 4 == 0: groups of four stay together
       half8_t av;
       float o = 0.f, xs = 0.f;
 #pragma unroll
       for (int h = 0; h < 8; ++h) {
-        const _Float16 xf = xr[i][Block<BITS>::F[h]];
+        const _Float16 xf = ok ? xr[i][Block<BITS>::F[h]] : (_Float16)0.f;
         if constexpr (PER_ELEM) {
           av[h] = xf;
         } else {
@@ -209,10 +204,7 @@ __global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
         xs += __shfl_xor(xs, 1);
         o += __shfl_xor(o, 2);
         xs += __shfl_xor(xs, 2);
-        if (kbe == 0) {
-          corr[(cl * M + m) * 2] = kMagic * o;
-          corr[(cl * M + m) * 2 + 1] = xs;
-        }
+        if (kbe == 0) *reinterpret_cast<f32x2_t*>(corr + (cl * Mp + m) * 2) = f32x2_t{-kMagic * o, -xs};
       }
     }
     if constexpr (PER_ELEM) {
@@ -221,9 +213,10 @@ __global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
       for (int i = 0; i < GP; ++i) {
         const int e = tid + i * nthreads;
         if (e < gpieces) {
+          const bool ok = 32 * p * pc + 4 * e < a.K;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            int g = gr[i][r];
+            int g = ok ? gr[i][r] : 0;
             g = g < 0 ? 0 : (g >= a.G ? a.G - 1 : g);
             gl[4 * e + r] = (uint16_t)g;
           }
@@ -232,95 +225,150 @@ __global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
     }
   };
 
-  // scale/zero table rows [g0, g0 + rows): entry (g, col) = (zero + offset) << 16 |
-  // fp16 scale bits, four columns per quad; staged like x (loads, then stores)
+  // scale/zero table rows [g0, g0 + rows), four columns per quad: raw scale
+  // and zero words in registers, unpacked when stored.  Rows past G and
+  // columns past N are stored as zero.
   u32x2_t tsr[TQ];
-  uint32_t tzr[TQ];
-  int tg0 = 0, trows = 0;
+  uint32_t tz0[TQ], tz1[TQ];
+  const uint32_t* qz = reinterpret_cast<const uint32_t*>(a.qzeros);
+  auto table_quad = [&](int rows, int e0, int i, int& r, int& c4) {
+    const int e = e0 + tid + i * nthreads;
+    r = e / (TN / 4);
+    c4 = e - r * (TN / 4);
+    return e < rows * (TN / 4);
+  };
   auto load_table = [&](int g0, int rows, int e0) {
-    tg0 = g0;
-    trows = max(0, min(rows, a.G - g0));
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
-      const int e = e0 + tid + i * nthreads;
-      tsr[i] = u32x2_t{0u, 0u};
-      tzr[i] = 0;
-      if (e < trows * (TN / 4)) {
-        const int gr_ = e / (TN / 4), c4 = e - gr_ * (TN / 4);
-        const int nn = n0 + 4 * c4;
-        if (nn < a.N) {
-          tsr[i] = *reinterpret_cast<const u32x2_t*>(a.scales + (int64_t)(g0 + gr_) * a.N + nn);
-          tzr[i] = load_zeros<BITS, 4>(a.qzeros, a.zrow_words, g0 + gr_, nn);
-        }
+      int r, c4;
+      const bool in = table_quad(rows, e0, i, r, c4);
+      const int nn = n0 + 4 * c4;
+      const bool ok = in && g0 + r < a.G && nn < a.N;
+      const int g = ok ? g0 + r : 0, nq = ok ? nn : 0;
+      tsr[i] = *reinterpret_cast<const u32x2_t*>(a.scales + (int64_t)g * a.N + nq);
+      const uint32_t* row = qz + (int64_t)g * a.zrow_words;
+      if constexpr (BITS == 3) {                     // 12 bits, possibly across two words
+        const int w = 3 * (nq >> 5) + ((3 * (nq & 31)) >> 5);
+        tz0[i] = row[w];
+        tz1[i] = row[((3 * (nq & 31)) >> 5) < 2 ? w + 1 : w];
+      } else {
+        tz0[i] = row[(nq * BITS) >> 5];
       }
     }
   };
-  auto store_table = [&](uint32_t* tw, int rows, int e0) {  // rows past G are written as zero
+  // four columns' (zero + offset) of quad i
+  auto quad_zeros = [&](int i, int c4) {
+    const int nq = n0 + 4 * c4;
+    if constexpr (BITS == 3) return __builtin_amdgcn_alignbit(tz1[i], tz0[i], (uint32_t)((3 * (nq & 31)) & 31));
+    else return tz0[i] >> ((nq * BITS) & 31);
+  };
+  auto store_table = [&](unsigned char* tw, int g0, int rows, int e0) {
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
-      const int e = e0 + tid + i * nthreads;
-      if (e < rows * (TN / 4)) {
-        const int gr_ = e / (TN / 4), c4 = e - gr_ * (TN / 4);
+      int r, c4;
+      if (!table_quad(rows, e0, i, r, c4)) continue;
+      const bool real = g0 + r < a.G && n0 + 4 * c4 < a.N;
+      const uint32_t zw = quad_zeros(i, c4);
+      uint32_t sb[4], z[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sb[j] = (j & 1) ? (tsr[i][j >> 1] >> 16) : (tsr[i][j >> 1] & 0xFFFFu);
+        z[j] = ((zw >> (BITS * j)) & ((1u << BITS) - 1u)) + (uint32_t)a.zero_offset;
+      }
+      if constexpr (PER_ELEM) {                      // (zero + offset) << 16 | fp16 scale bits
         u32x4_t v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t sb = (j & 1) ? (tsr[i][j >> 1] >> 16) : (tsr[i][j >> 1] & 0xFFFFu);
-          const uint32_t z = ((tzr[i] >> (BITS * j)) & ((1u << BITS) - 1u)) + (uint32_t)a.zero_offset;
-          v[j] = (z << 16) | sb;
-        }
-        *reinterpret_cast<u32x4_t*>(tw + gr_ * TN + 4 * c4) = v;
-      }
-    }
-  };
-
-  // ---- packed words: block kb of chunk c lives in rows BITS * c + row0(kb) (+ row1),
-  // so a chunk advances every lane's pointer by BITS rows.  Lanes past N read
-  // column 0 and slots past K re-read the last chunk: loads stay in bounds
-  // without branches and those results are never used.
-  const int nc = col_ok ? n : 0;
-  const uint32_t* p0 = qw + (int64_t)block_row0<BITS>(0, kb) * a.N + nc;
-  const uint32_t* p1 = qw + (int64_t)block_row1<BITS>(0, kb) * a.N + nc;
-  const int64_t cstride = (int64_t)BITS * a.N;      // words per chunk
-  int lp = 0, li = 0;                                // next chunk to load: phase, index in range
-  auto load_batch = [&](wvec* w0, wvec* w1) {
+        for (int j = 0; j < 4; ++j) v[j] = real ? ((z[j] << 16) | sb[j]) : 0u;
+        *reinterpret_cast<u32x4_t*>(tw + (r * TN + 4 * c4) * 4) = v;
+      } else {                                       // (scale, zero + offset) as fp32
+        f32x4_t v0, v1;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = min(lp * pc + wave * cpw + li, C - 1);
-      w0[u] = *reinterpret_cast<const wvec*>(p0 + c * cstride);
-      if constexpr (Block<BITS>::LOADS == 2) w1[u] = *reinterpret_cast<const wvec*>(p1 + c * cstride);
-      if (++li == cpw) {
-        li = 0;
-        ++lp;
+        for (int j = 0; j < 2; ++j) {
+          v0[2 * j] = real ? (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]) : 0.f;
+          v0[2 * j + 1] = real ? (float)z[j] : 0.f;
+          v1[2 * j] = real ? (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j + 2]) : 0.f;
+          v1[2 * j + 1] = real ? (float)z[j + 2] : 0.f;
+        }
+        *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8) = v0;
+        *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8 + 16) = v1;
       }
     }
   };
-
-  // (scale, zero + offset) of column slot j of table row r
-  auto group_param = [&](const uint32_t* tab, int r, int j, float& s, int& z) {
-    const uint32_t v = tab[r * TN + CPL * q + j];
-    s = (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
-    z = (int)(v >> 16);
+  auto stage_next = [&](int p) {                    // loads for phase p (registers)
+    load_x(p);
+    load_g(p);
+    if constexpr (!PER_ELEM) load_table(p * pc / cpg, lay.ptab_rows, 0);
+  };
+  auto store_stage = [&](int p) {                    // ... and their LDS stores
+    store_xg(p);
+    if constexpr (!PER_ELEM)
+      store_table(lds + (size_t)(p & 1) * lay.buf_stride + lay.ptab_off, p * pc / cpg, lay.ptab_rows, 0);
   };
 
-  floatx4_t accg[CPL];
-  float acc[CPL][MV];
+  // ---- packed words: block kb of chunk c lives in rows BITS * c + row0(kb)
+  // (+ row1), i.e. at the lane's offset in chunk 0 plus the wave-uniform
+  // c * BITS * N * 4 bytes.  Chunks past K re-read the last chunk: they meet
+  // zero x (and a zero table row) and add exactly nothing.
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.qweight), (short)0, (int)((int64_t)C * BITS * a.N * 4), 0x00020000);
+  const uint32_t off0 = (uint32_t)(block_row0<BITS>(0, kb) * a.N + nc) * 4u;
+  const uint32_t off1 = (uint32_t)(block_row1<BITS>(0, kb) * a.N + nc) * 4u;
+  const uint32_t cbytes = (uint32_t)BITS * (uint32_t)a.N * 4u;
+  wvec w0[CPW], w1[L == 2 ? CPW : 1];
+  auto load_w = [&](int p) {
+    const int cb = p * pc + wave * CPW;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const uint32_t so = (uint32_t)min(cb + u, C - 1) * cbytes;
+      w0[u] = buffer_words<CPL>(wrsrc, off0, so);
+      if constexpr (L == 2) w1[u] = buffer_words<CPL>(wrsrc, off1, so);
+      // issue in chunk order, so chunk u waits only for loads 0..u
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  floatx4_t accg[CPL];                               // per-element path: MFMA accumulators
+  float acc[CPL][MV];                                // fast path: scaled sums
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     accg[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < MV; ++v) acc[j][v] = 0.f;
   }
-  float s_cur[CPL];
+  // fast path: the previous chunk's MFMA results and scales, folded one chunk
+  // later; the empty asm pins each fold in place (otherwise the whole chain is
+  // sunk past the loop and every chunk's results stay live)
+  floatx4_t d_prev[CPL];
+  float s_prev[CPL];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) s_cur[j] = 0.f;
-
-  // one chunk: c is the chunk, cl its index inside the phase buffer, gi its
-  // index inside its group (wave ranges hold whole groups on the fast path)
+  for (int j = 0; j < CPL; ++j) {
+    d_prev[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    s_prev[j] = 0.f;
+  }
+  auto fold_prev = [&]() {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        acc[j][v] = __builtin_fmaf(s_prev[j], d_prev[j][v], acc[j][v]);
+        asm volatile("" : "+v"(acc[j][v]));
+      }
+    }
+  };
   const uint32_t* full_tab = reinterpret_cast<const uint32_t*>(lds + lay.tab_off);
-  auto compute_chunk = [&](int c, int cl, int gi, const unsigned char* base, uint32_t w0j[CPL], uint32_t w1j[CPL]) {
+  const int kbc = MV == 1 ? 0 : min(kb, Mp / 4 - 1);  // rows 4 kbc + v of the correction sums
+
+  // chunk u of this wave in phase p (cl = its index in the phase buffer,
+  // row = its group's row in the phase table)
+  auto compute_chunk = [&](int p, int u, int row) {
+    const unsigned char* base = lds + (size_t)(p & 1) * lay.buf_stride;
+    const int cl = wave * CPW + u;
     const _Float16* frag = reinterpret_cast<const _Float16*>(base);
     half8_t A = {};
     if (q < M) A = *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + q) << 3));
+    uint32_t w1j[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) w1j[j] = L == 2 ? word_of<CPL>(w1[L == 2 ? u : 0], j) : 0u;
 
     if constexpr (PER_ELEM) {
       // per-row scale and zero: the block's 8 rows each carry their own group
@@ -329,128 +377,97 @@ __global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
       const u16x8_t gv = *reinterpret_cast<const u16x8_t*>(gl + 32 * cl + 8 * kb);
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        uint32_t p[4];
-        unpack_block<BITS>(w0j[j], w1j[j], sel, p);
+        uint32_t pr[4];
+        unpack_block<BITS>(word_of<CPL>(w0[u], j), w1j[j], sel, pr);
         u32x4_t bw;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int fa = Block<BITS>::F[2 * v], fb = Block<BITS>::F[2 * v + 1];
-          float sa, sb;
-          int za, zb;
-          group_param(full_tab, (int)gv[fa], j, sa, za);
-          group_param(full_tab, (int)gv[fb], j, sb, zb);
-          const half2_t neg = {neg_offset<BITS>(v, za), neg_offset<BITS>(v, zb)};
-          const half2_t d = pair_minus_zero<BITS>(p[v], v, neg);
-          bw[v] = as_u32(d * half2_t{(_Float16)sa, (_Float16)sb});
+          const uint32_t ea = full_tab[(int)gv[Block<BITS>::F[2 * v]] * TN + CPL * q + j];
+          const uint32_t eb = full_tab[(int)gv[Block<BITS>::F[2 * v + 1]] * TN + CPL * q + j];
+          const half2_t neg = {neg_offset<BITS>(v, (int)(ea >> 16)), neg_offset<BITS>(v, (int)(eb >> 16))};
+          const half2_t d = pair_minus_zero<BITS>(pr[v], v, neg);
+          const half2_t s = {__builtin_bit_cast(_Float16, (uint16_t)(ea & 0xFFFFu)),
+                             __builtin_bit_cast(_Float16, (uint16_t)(eb & 0xFFFFu))};
+          bw[v] = as_u32(d * s);
         }
         accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), accg[j], 0, 0, 0);
       }
     } else {
-      if (gi == 0) {                                 // a group starts: its scale/zero from the
-        const float* corr = reinterpret_cast<const float*>(base + lay.corr_off);   // phase table,
-        const uint32_t* ptab = reinterpret_cast<const uint32_t*>(base + lay.ptab_off);  // and the
-        const int r = cl / a.cpg;                    // accumulators start at -(correction)
-        int z[CPL];
+      const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + (cl * Mp + 4 * kbc) * 2;
+      float O[MV], X[MV];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) group_param(ptab, r, j, s_cur[j], z[j]);
-        float O[MV], X[MV];
-#pragma unroll
-        for (int v = 0; v < MV; ++v) {
-          O[v] = 0.f;
-          X[v] = 0.f;
-          const int m = 4 * kb + v;
-          if (m < M) {
-            for (int i = 0; i < a.cpg; ++i) {
-              O[v] += corr[((cl + i) * M + m) * 2];
-              X[v] += corr[((cl + i) * M + m) * 2 + 1];
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const float zj = (float)z[j];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) accg[j][v] = (v < MV) ? -(O[v < MV ? v : 0] + zj * X[v < MV ? v : 0]) : 0.f;
-        }
+      for (int v = 0; v < MV; ++v) {
+        O[v] = corr[2 * v];
+        X[v] = corr[2 * v + 1];
       }
+      const float* te = reinterpret_cast<const float*>(base + lay.ptab_off) + (row * TN + CPL * q) * 2;
+      floatx4_t d[CPL];
+      float s[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        uint32_t p[4];
-        unpack_block<BITS>(w0j[j], w1j[j], sel, p);
-        const u32x4_t bw = {p[0], p[1], p[2], p[3]};
-        accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), accg[j], 0, 0, 0);
+        s[j] = te[2 * j];
+        const float z = te[2 * j + 1];
+        uint32_t pr[4];
+        unpack_block<BITS>(word_of<CPL>(w0[u], j), w1j[j], sel, pr);
+        const u32x4_t bw = {pr[0], pr[1], pr[2], pr[3]};
+        floatx4_t c0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c0[v] = v < MV ? __builtin_fmaf(z, X[v < MV ? v : 0], O[v < MV ? v : 0]) : 0.f;
+        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), c0, 0, 0, 0);
       }
-      if (gi == a.cpg - 1) {                         // group ends: fold in its scale
+      // the previous chunk's products are folded in while this chunk's MFMAs run
+      fold_prev();
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-#pragma unroll
-          for (int v = 0; v < MV; ++v) acc[j][v] += s_cur[j] * accg[j][v];
-        }
+      for (int j = 0; j < CPL; ++j) {
+        d_prev[j] = d[j];
+        s_prev[j] = s[j];
       }
     }
   };
 
-  auto stage_next = [&](int p) {                    // loads for phase p (registers)
-    load_x(p);
-    load_g(p);
-    if constexpr (!PER_ELEM) load_table(p * pc / a.cpg, lay.ptab_rows, 0);
-  };
-  auto store_stage = [&](int p) {                    // ... and their LDS stores
-    store_xg(p & 1);
-    if constexpr (!PER_ELEM)
-      store_table(reinterpret_cast<uint32_t*>(lds + (size_t)(p & 1) * lay.buf_stride + lay.ptab_off),
-                  lay.ptab_rows, 0);
-  };
-  // One batch: chunks [ci, ci + U) of this wave's range in phase p.  Chunks
-  // past K hold zero x and a zero table row, so they add exactly nothing and
-  // need no branch.
-  auto consume_batch = [&](int p, int ci, const wvec* w0, const wvec* w1) {
-    const unsigned char* base = lds + (size_t)(p & 1) * lay.buf_stride;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int cl = wave * cpw + ci + u;
-      uint32_t w0j[CPL], w1j[CPL];
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        w0j[j] = word_of<CPL>(w0[u], j);
-        w1j[j] = word_of<CPL>(w1[u], j);
-      }
-      int gi = 0;
-      if constexpr (!PER_ELEM) gi = (ci + u) % a.cpg;   // ranges hold whole groups
-      compute_chunk(p * pc + cl, cl, gi, base, w0j, w1j);
-    }
-  };
-
-  // ---- prologue: small operands first, then two batches of weights in flight
-  wvec wA0[U], wA1[U], wB0[U], wB1[U];
-  if constexpr (PER_ELEM) {                         // whole table, in rounds, before the first barrier
+  // ---- prologue: the first table round (per-element path), then phase 0's
+  // small operands, then all of phase 0's weight loads
+  if constexpr (PER_ELEM) load_table(0, a.G, 0);
+  stage_next(0);
+  __builtin_amdgcn_sched_barrier(0);               // small operands strictly before the weights
+  load_w(0);
+  if constexpr (PER_ELEM) {                         // whole table, before the first barrier
+    unsigned char* tw = lds + lay.tab_off;
+    store_table(tw, 0, a.G, 0);
     const int quads = a.G * (TN / 4);
-    for (int e0 = 0; e0 < quads; e0 += TQ * nthreads) {
+    for (int e0 = TQ * nthreads; e0 < quads; e0 += TQ * nthreads) {   // rare: very many groups
       load_table(0, a.G, e0);
-      store_table(const_cast<uint32_t*>(full_tab), a.G, e0);
+      store_table(tw, 0, a.G, e0);
     }
   }
-  stage_next(0);
-  load_batch(wA0, wA1);
-  load_batch(wB0, wB1);
 
-  // ---- per phase: stage (one barrier), then pairs of batches; every consumed
-  // batch is refilled two batches ahead (addresses past K are clamped)
+  // ---- per phase: stage (one barrier), compute the CPW chunks in load order,
+  // then issue the next phase's small operands and weights
   for (int p = 0; p < phases; ++p) {
     store_stage(p);
     __syncthreads();
-    if (p + 1 < phases) stage_next(p + 1);
-    for (int ci = 0; ci < cpw; ci += 2 * U) {
-      consume_batch(p, ci, wA0, wA1);
+    const int cb = p * pc + wave * CPW;              // this wave's first chunk
+    int row = cb / cpg - p * pc / cpg, rem = cb % cpg;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      compute_chunk(p, u, row);
+      // keep each chunk's LDS reads next to their use: hoisting all of them
+      // ahead of the weight waits would cost ~10 registers per chunk
       __builtin_amdgcn_sched_barrier(0);
-      load_batch(wA0, wA1);
+      if constexpr (!PER_ELEM) {
+        ++rem;
+        const bool next = rem == cpg;
+        row += next ? 1 : 0;
+        rem = next ? 0 : rem;
+      }
+    }
+    if (p + 1 < phases) {
+      stage_next(p + 1);
       __builtin_amdgcn_sched_barrier(0);
-      consume_batch(p, ci + U, wB0, wB1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_batch(wB0, wB1);
-      __builtin_amdgcn_sched_barrier(0);
+      load_w(p + 1);
     }
   }
+  if constexpr (!PER_ELEM) fold_prev();
 
   // ---- reduce the waves through LDS (rows < M), write fp16
   __syncthreads();
@@ -464,6 +481,7 @@ __global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
+  const int nw = nthreads >> 6;
   for (int e = tid; e < M * TN; e += nthreads) {
     const int m = e / TN, col = e - m * TN;
     if (n0 + col < a.N) {
@@ -474,33 +492,45 @@ __global__ __launch_bounds__(512) void decode_kernel(GemmArgs a) {
   }
 }
 
-template <int BITS, bool PER_ELEM, int MV, int CPL>
+template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
 static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
-  const size_t lds = decode_lds_bytes(a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg);
-  auto kern = decode_kernel<BITS, PER_ELEM, MV, CPL>;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  if constexpr (!decode_cpw_ok(CPL, Block<BITS>::LOADS, CPW, MV)) {
+    return hipErrorInvalidValue;
+  } else {
+    const size_t lds = decode_lds_bytes(a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg, a.phases);
+    auto kern = decode_kernel<BITS, PER_ELEM, MV, CPL, CPW>;
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(a.tiles), dim3(64 * a.nw), lds, stream, a);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(kern, dim3(a.tiles), dim3(64 * a.nw), lds, stream, a);
-  return hipGetLastError();
+}
+
+template <int BITS, bool PER_ELEM, int MV, int CPL>
+static hipError_t launch_decode_cpw(const GemmArgs& a, hipStream_t stream) {
+  switch (a.cpw) {
+    case 8: return launch_decode_k<BITS, PER_ELEM, MV, CPL, 8>(a, stream);
+    case 16: return launch_decode_k<BITS, PER_ELEM, MV, CPL, 16>(a, stream);
+    case 32: return launch_decode_k<BITS, PER_ELEM, MV, CPL, 32>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int BITS, bool PER_ELEM, int MV>
 static hipError_t launch_decode_cpl(const GemmArgs& a, hipStream_t stream) {
   switch (a.cpl) {
-    case 1: return launch_decode_k<BITS, PER_ELEM, MV, 1>(a, stream);
-    case 2: return launch_decode_k<BITS, PER_ELEM, MV, 2>(a, stream);
-    default: return launch_decode_k<BITS, PER_ELEM, MV, 4>(a, stream);
+    case 1: return launch_decode_cpw<BITS, PER_ELEM, MV, 1>(a, stream);
+    case 2: return launch_decode_cpw<BITS, PER_ELEM, MV, 2>(a, stream);
+    default: return launch_decode_cpw<BITS, PER_ELEM, MV, 4>(a, stream);
   }
 }
 
 template <int BITS, bool PER_ELEM>
 static hipError_t launch_decode_pe(const GemmArgs& a, hipStream_t stream) {
-  if (a.M == 1) return launch_decode_cpl<BITS, PER_ELEM, 1>(a, stream);
-  if (a.M == 2) return launch_decode_cpl<BITS, PER_ELEM, 2>(a, stream);
-  return launch_decode_cpl<BITS, PER_ELEM, 4>(a, stream);
+  return a.M == 1 ? launch_decode_cpl<BITS, PER_ELEM, 1>(a, stream) : launch_decode_cpl<BITS, PER_ELEM, 4>(a, stream);
 }
 
 template <int BITS>

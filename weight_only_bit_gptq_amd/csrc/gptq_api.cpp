@@ -5,7 +5,6 @@
 
 #include <algorithm>
 #include <cstdint>
-#include <numeric>
 #include <cstdlib>
 #include <new>
 #include <utility>
@@ -44,48 +43,65 @@ int check_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, con
   return GPTQ_OK;
 }
 
-// Decode launch shape.  Column tiles of 16 * cpl columns (widest that still
-// gives >= 256 workgroups), waves per workgroup so the grid holds ~4K waves,
-// and K phases sized to the LDS budget.
-constexpr size_t kDecodeLdsBudget = 150 * 1024;
+// Decode launch shape.  Column tiles of 16 * cpl columns: the widest that
+// still gives >= 256 workgroups and has a compiled chunks-per-wave value for
+// this M (narrower ones otherwise).  Then (waves, chunks per wave) so that K
+// takes as few phases as possible, with the least padding past K and the most
+// waves, within the LDS budget and the x staging limit (cpw * M <= 16 * x
+// pieces).  The fast path needs group_size % 32 == 0 (a chunk inside one
+// group); otherwise, or when its phase table does not fit, the per-element
+// path is used.
+constexpr size_t kDecodeLdsBudget = 160 * 1024;
 constexpr int kNoDecodePlan = 1;
 
-int decode_shape(int bits, int M, int N, int K, int G, int waves, bool* per_elem, gptq::GemmArgs* a) {
+bool decode_plan_for(int bits, int M, int K, int G, int waves, int cpl, bool per_elem, gptq::GemmArgs* a) {
   const int C = K / 32;
-  int cpl = 1;
-  for (int c : {4, 2}) {
-    if ((N + 16 * c - 1) / (16 * c) >= 256) { cpl = c; break; }
-  }
-  const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
-  int nw0 = waves > 0 ? waves : (tiles <= 512 ? 8 : 4);
-  if (nw0 > gptq::decode_max_waves(cpl)) nw0 = gptq::decode_max_waves(cpl);
-  const int U = gptq::decode_batch(cpl, bits, M);
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    const int cpg = *per_elem ? 1 : (K / G) / 32;
-    const int unit = std::lcm(2 * U, cpg);           // cpw granularity: batch pairs, whole groups
-    for (int nw = nw0; nw >= 1; --nw) {
-      // chunks per phase: limited by the x (and g_idx) pieces each thread stages and by LDS
-      int pc_max = gptq::decode_max_x_pieces(M) * 64 * nw / (4 * M);
-      if (*per_elem) pc_max = std::min(pc_max, gptq::decode_max_g_pieces() * 64 * nw / 8);
-      auto fits = [&](int c) {
-        const int pc = nw * c;
-        return pc <= pc_max && gptq::decode_lds_bytes(M, pc, nw, cpl, *per_elem, G, cpg) <= kDecodeLdsBudget;
-      };
-      int cpw = (C + nw - 1) / nw;
-      cpw = (cpw + unit - 1) / unit * unit;
-      while (cpw > unit && !fits(cpw)) cpw -= unit;
-      if (!fits(cpw)) continue;
-      a->tiles = tiles;
-      a->cpl = cpl;
-      a->nw = nw;
-      a->cpw = cpw;
-      a->pc = nw * cpw;
-      a->phases = (C + a->pc - 1) / a->pc;
-      a->cpg = cpg;
-      return GPTQ_OK;
+  const int maxw = gptq::decode_max_waves(cpl, M);
+  const int cpg = per_elem ? 1 : (K / G) / 32;
+  bool found = false;
+  int best_nw = 0, best_cpw = 0, best_phases = 0, best_waste = 0;
+  for (int cpw : {8, 16, 32}) {
+    if (!gptq::decode_cpw_allowed(cpl, bits, cpw, M)) continue;
+    if (cpw * M > 16 * gptq::decode_max_x_pieces(M)) continue;
+    const int lo = waves > 0 ? std::min(waves, maxw) : 1, hi = waves > 0 ? lo : maxw;
+    for (int nw = lo; nw <= hi; ++nw) {
+      const int pc = nw * cpw;
+      const int phases = (C + pc - 1) / pc;
+      if (gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases) > kDecodeLdsBudget) continue;
+      const int waste = phases * pc - C;
+      const bool better = !found || phases < best_phases ||
+                          (phases == best_phases && (waste < best_waste || (waste == best_waste && nw > best_nw)));
+      if (better) {
+        found = true;
+        best_nw = nw;
+        best_cpw = cpw;
+        best_phases = phases;
+        best_waste = waste;
+      }
     }
-    if (*per_elem) break;
-    *per_elem = true;                                // whole groups do not fit: per-row path
+  }
+  if (!found) return false;
+  a->cpl = cpl;
+  a->nw = best_nw;
+  a->cpw = best_cpw;
+  a->pc = best_nw * best_cpw;
+  a->phases = best_phases;
+  a->cpg = cpg;
+  return true;
+}
+
+int decode_shape(int bits, int M, int N, int K, int G, int waves, bool* per_elem, gptq::GemmArgs* a) {
+  if ((K / G) % 32 != 0) *per_elem = true;
+  for (int pe = *per_elem ? 1 : 0; pe < 2; ++pe) {
+    for (int cpl : {4, 2, 1}) {
+      const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
+      if (cpl > 1 && tiles < 256) continue;
+      if (decode_plan_for(bits, M, K, G, waves, cpl, pe == 1, a)) {
+        a->tiles = tiles;
+        *per_elem = pe == 1;
+        return GPTQ_OK;
+      }
+    }
   }
   return kNoDecodePlan;                              // the scale/zero table does not fit LDS
 }

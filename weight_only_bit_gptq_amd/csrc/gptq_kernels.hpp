@@ -30,16 +30,18 @@ struct GemmArgs {
   int chunks;               // K / 32
   int64_t zrow_words;       // N * bits / 32
   // decode launch shape: tiles of 16*cpl columns, nw waves per workgroup,
-  // K in phases of pc chunks, cpw chunks per wave per phase (a multiple of
-  // cpg = group_size / 32 on the fast path, so wave ranges hold whole groups)
+  // K in phases of pc = nw * cpw chunks, cpw chunks per wave per phase,
+  // cpg = group_size / 32 chunks per group on the fast path (else 1)
   int tiles, cpl, nw, cpw, pc, phases, cpg;
   // prefill launch shape
   int tiles_m, tiles_n;
 };
 
-// LDS carve-up of the decode kernel: two phase buffers (x fragments, per-chunk
-// correction sums or the phase's g_idx slice), then the scale/zero table; the
-// cross-wave reduction buffer aliases everything after the main loop.
+// LDS carve-up of the decode kernel: one phase buffer (two when K takes
+// several phases) holding x fragments and either per-chunk correction sums and
+// the phase's scale/zero rows (fast path) or the phase's g_idx slice, then the
+// whole scale/zero table (per-element path); the cross-wave reduction buffer
+// aliases everything after the main loop.
 struct DecodeLayout {
   size_t buf_stride;        // bytes of one phase buffer
   size_t corr_off;          // correction sums inside a buffer (fast path)
@@ -66,11 +68,10 @@ hipError_t launch_dequant(int bits, const DequantArgs& a, hipStream_t stream);
 // Decode (M <= 16).  `per_elem` selects the per-element scale/zero path (act
 // order or group_size % 32 != 0).
 // LDS bytes of a launch shape (SIZE_MAX if its table cannot be staged)
-size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg);
+size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg, int phases);
 int decode_max_x_pieces(int M);   // 16-byte x pieces each thread may stage per phase
-int decode_max_g_pieces();   // 16-byte g_idx pieces each thread may stage per phase
-int decode_batch(int cpl, int bits, int M);   // chunks per weight-load batch (cpw must be a multiple)
-int decode_max_waves(int cpl);
+int decode_max_waves(int cpl, int M);
+bool decode_cpw_allowed(int cpl, int bits, int cpw, int M);   // chunks per wave per phase compiled for this tile
 hipError_t launch_decode(int bits, bool per_elem, const GemmArgs& a, hipStream_t stream);
 
 // Prefill (any M, used for M > 16).

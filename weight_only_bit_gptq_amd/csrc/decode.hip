@@ -24,15 +24,16 @@
 // A = 16 rows of x (rows >= M are zero), B = the block each lane unpacked.
 //
 // Fast path (group_size % 32 == 0, no g_idx): a chunk lies in one group, so
-// its scale s and zero z are constant over it.  B holds the raw magic pairs
-// 1024 + MUL*q, x is pre-divided by MUL (x' = x / MUL), and the zero point
-// and the magic offset enter through the MFMA's accumulator input:
-//   D = -(1024 * sum x' + z * sum x' MUL) + sum x' B = sum x (q - z)
-//   y += s * D
-// i.e. the dequant formula with the scale factored out of the chunk's sum
-// (page "Enhancing vLLM's support for the GPTQv2 format", section "Weight
-// quantization of LLMs").  Per-element path (act order or other groups): B is
-// the exact fp16 dequantized weight, built with each row's own scale and zero.
+// its scale s and zero z are constant over it.  B holds each field as the fp16
+// subnormal MUL*q*2^-24 (a plain mask of the packed word; the MFMA keeps
+// subnormal inputs exactly) and x is pre-divided by MUL, so
+//   D = sum x' B = 2^-24 sum x q
+//   y += (s 2^24) D + (-s z) sum x = s sum x (q - z)
+// i.e. the dequant formula with the scale and the zero point factored out of
+// the chunk's sum (page "Enhancing vLLM's support for the GPTQv2 format",
+// section "Weight quantization of LLMs").  Per-element path (act order or
+// other groups): B is the exact fp16 dequantized weight, built with each
+// row's own scale and zero.
 #include "gptq_kernels.hpp"
 
 namespace gptq {
@@ -47,6 +48,19 @@ constexpr int kDecodeTQuads = 4;   // scale/zero table quads (4 columns of a gro
 // 32- and 64-column tiles) and 32 otherwise, so that nothing spills.
 __host__ __device__ constexpr bool decode_cpw_ok(int cpl, int loads, int cpw, int mv) {
   return (cpw == 8 || cpw == 16 || cpw == 32) && cpw * cpl * loads <= ((mv == 1 && cpl > 1) ? 64 : 32);
+}
+
+__host__ __device__ constexpr int decode_max_threads(int cpl, int mv) { return (cpl == 1 && mv == 1) ? 1024 : 512; }
+
+// Waves per SIMD each instantiation is compiled for (a register budget of
+// 512 / W per lane, met without spills): M = 1 runs 4 while a lane holds at
+// most 32 weight words and 3 above that (3-bit 32-column tiles, whose funnel
+// shifts need more registers, one less); M > 1 runs 2.
+__host__ __device__ constexpr int decode_waves_per_simd(int bits, int cpl, int cpw, int mv) {
+  const int words = cpw * cpl * ((bits == 3 || bits == 8) ? 2 : 1);
+  if (mv != 1) return 2;
+  if (words <= 32) return (bits == 3 && cpl == 2 && words == 32) ? 3 : 4;
+  return (bits == 3 && cpl == 2) ? 2 : 3;
 }
 
 template <int CPL> struct WordVec;
@@ -68,7 +82,7 @@ __device__ __forceinline__ typename WordVec<CPL>::T buffer_words(__amdgpu_buffer
 
 __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
-// rows of x a chunk's correction sums are laid out for (multiple of 4 for M > 1)
+// rows of x a chunk's sums are laid out for (multiple of 4 for M > 1)
 __host__ __device__ inline int decode_corr_rows(int M) { return M == 1 ? 1 : (M + 3) & ~3; }
 
 __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg,
@@ -77,7 +91,7 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   const size_t tn = (size_t)16 * cpl;
   const size_t frag = (size_t)pc * 4 * M * 16;
   L.corr_off = frag;
-  const size_t corr = per_elem ? 0 : (size_t)pc * decode_corr_rows(M) * 8;
+  const size_t corr = per_elem ? 0 : (size_t)pc * decode_corr_rows(M) * 4;
   L.gidx_off = align16(frag + corr);
   const size_t gidx = per_elem ? (size_t)pc * 32 * 2 : 0;
   L.ptab_off = align16(L.gidx_off + gidx);
@@ -100,14 +114,21 @@ size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, in
 }
 
 int decode_max_x_pieces(int M) { return decode_x_pieces_of(M == 1 ? 1 : 4); }
-int decode_max_waves(int cpl, int M) { return (cpl == 1 && M == 1) ? 16 : 8; }
+int decode_waves_per_simd_for(int bits, int cpl, int cpw, int M) {
+  return decode_waves_per_simd(bits, cpl, cpw, M == 1 ? 1 : 4);
+}
+int decode_max_threads_for(int cpl, int M) { return decode_max_threads(cpl, M == 1 ? 1 : 4); }
 bool decode_cpw_allowed(int cpl, int bits, int cpw, int M) {
   return decode_cpw_ok(cpl, (bits == 3 || bits == 8) ? 2 : 1, cpw, M == 1 ? 1 : 4);
 }
 
-// 16 waves for 16-column tiles at M = 1 (128 registers per lane), 8 otherwise.
+// Up to 16 waves for 16-column tiles at M = 1, 8 otherwise; each instantiation
+// is compiled for a fixed number of waves per SIMD, which the host uses to
+// size the grid so that every workgroup is resident at once.
 template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
-__global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_kernel(GemmArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(CPL, MV))))
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, CPL, CPW, MV))))
+void decode_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int XP = decode_x_pieces_of(MV);
   constexpr int GP = (CPW + 7) / 8;                  // g_idx pieces: 8 * CPW rows <= 64 * GP pieces of 4
@@ -117,7 +138,6 @@ __global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_ker
   typedef typename WordVec<CPL>::T wvec;
   typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
   const int M = MV == 1 ? 1 : a.M;
   const int nthreads = (int)blockDim.x;
@@ -184,7 +204,7 @@ __global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_ker
       const bool ok = x_piece(p, i, m, cl, kbe);
       if (tid + i * nthreads >= xpieces) continue;   // xpieces % 4 == 0: groups of four stay together
       half8_t av;
-      float o = 0.f, xs = 0.f;
+      float xs = 0.f;                                // sum of x' MUL over the piece
 #pragma unroll
       for (int h = 0; h < 8; ++h) {
         const _Float16 xf = ok ? xr[i][Block<BITS>::F[h]] : (_Float16)0.f;
@@ -194,17 +214,14 @@ __global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_ker
           const float mul = (float)Block<BITS>::MUL[h >> 1];
           const _Float16 xp = (_Float16)((float)xf / mul);
           av[h] = xp;
-          o += (float)xp;
           xs += (float)xp * mul;
         }
       }
       *reinterpret_cast<half8_t*>(frag + (((cl * 4 + kbe) * M + m) << 3)) = av;
       if constexpr (!PER_ELEM) {
-        o += __shfl_xor(o, 1);
         xs += __shfl_xor(xs, 1);
-        o += __shfl_xor(o, 2);
         xs += __shfl_xor(xs, 2);
-        if (kbe == 0) *reinterpret_cast<f32x2_t*>(corr + (cl * Mp + m) * 2) = f32x2_t{-kMagic * o, -xs};
+        if (kbe == 0) corr[cl * Mp + m] = xs;
       }
     }
     if constexpr (PER_ELEM) {
@@ -280,14 +297,14 @@ __global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_ker
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = real ? ((z[j] << 16) | sb[j]) : 0u;
         *reinterpret_cast<u32x4_t*>(tw + (r * TN + 4 * c4) * 4) = v;
-      } else {                                       // (scale, zero + offset) as fp32
+      } else {                                       // (s 2^24, -s (zero + offset)) as fp32, exact
         f32x4_t v0, v1;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          v0[2 * j] = real ? (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]) : 0.f;
-          v0[2 * j + 1] = real ? (float)z[j] : 0.f;
-          v1[2 * j] = real ? (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j + 2]) : 0.f;
-          v1[2 * j + 1] = real ? (float)z[j + 2] : 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const float sc = real ? (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]) : 0.f;
+          f32x4_t& v = j < 2 ? v0 : v1;
+          v[2 * (j & 1)] = sc * 16777216.0f;
+          v[2 * (j & 1) + 1] = -sc * (float)z[j];
         }
         *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8) = v0;
         *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8 + 16) = v1;
@@ -338,6 +355,7 @@ __global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_ker
   // fast path: the previous chunk's MFMA results and scales, folded one chunk
   // later; the empty asm pins each fold in place (otherwise the whole chain is
   // sunk past the loop and every chunk's results stay live)
+  constexpr bool kDeferFold = CPL < 4;
   floatx4_t d_prev[CPL];
   float s_prev[CPL];
 #pragma unroll
@@ -364,8 +382,8 @@ __global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_ker
     const unsigned char* base = lds + (size_t)(p & 1) * lay.buf_stride;
     const int cl = wave * CPW + u;
     const _Float16* frag = reinterpret_cast<const _Float16*>(base);
-    half8_t A = {};
-    if (q < M) A = *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + q) << 3));
+    // rows >= M of A only feed rows >= M of D, which are never used
+    const half8_t A = *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + min(q, M - 1)) << 3));
     uint32_t w1j[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) w1j[j] = L == 2 ? word_of<CPL>(w1[L == 2 ? u : 0], j) : 0u;
@@ -393,35 +411,34 @@ __global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_ker
         accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), accg[j], 0, 0, 0);
       }
     } else {
-      const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + (cl * Mp + 4 * kbc) * 2;
-      float O[MV], X[MV];
+      const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + cl * Mp + 4 * kbc;
+      float X[MV];
 #pragma unroll
-      for (int v = 0; v < MV; ++v) {
-        O[v] = corr[2 * v];
-        X[v] = corr[2 * v + 1];
-      }
+      for (int v = 0; v < MV; ++v) X[v] = corr[v];
       const float* te = reinterpret_cast<const float*>(base + lay.ptab_off) + (row * TN + CPL * q) * 2;
       floatx4_t d[CPL];
-      float s[CPL];
+      float s1[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        s[j] = te[2 * j];
-        const float z = te[2 * j + 1];
+        s1[j] = te[2 * j];
+        const float s2 = te[2 * j + 1];
         uint32_t pr[4];
-        unpack_block<BITS>(word_of<CPL>(w0[u], j), w1j[j], sel, pr);
+        unpack_block<BITS>(word_of<CPL>(w0[u], j), w1j[j], sel, pr, 0u);
         const u32x4_t bw = {pr[0], pr[1], pr[2], pr[3]};
-        floatx4_t c0;
+        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), floatx4_t{0.f, 0.f, 0.f, 0.f},
+                                                      0, 0, 0);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) c0[v] = v < MV ? __builtin_fmaf(z, X[v < MV ? v : 0], O[v < MV ? v : 0]) : 0.f;
-        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), c0, 0, 0, 0);
+        for (int v = 0; v < MV; ++v) acc[j][v] = __builtin_fmaf(s2, X[v], acc[j][v]);
       }
-      // the previous chunk's products are folded in while this chunk's MFMAs run
-      fold_prev();
+      // with one or two MFMAs per chunk the previous chunk's products are
+      // folded in while this chunk's MFMAs run; four cover their own latency
+      if constexpr (kDeferFold) fold_prev();
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         d_prev[j] = d[j];
-        s_prev[j] = s[j];
+        s_prev[j] = s1[j];
       }
+      if constexpr (!kDeferFold) fold_prev();
     }
   };
 
@@ -467,7 +484,7 @@ __global__ __launch_bounds__((CPL == 1 && MV == 1) ? 1024 : 512) void decode_ker
       load_w(p + 1);
     }
   }
-  if constexpr (!PER_ELEM) fold_prev();
+  if constexpr (!PER_ELEM && kDeferFold) fold_prev();
 
   // ---- reduce the waves through LDS (rows < M), write fp16
   __syncthreads();

@@ -43,49 +43,69 @@ int check_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, con
   return GPTQ_OK;
 }
 
-// Decode launch shape.  Column tiles of 16 * cpl columns: the widest that
-// still gives >= 256 workgroups and has a compiled chunks-per-wave value for
-// this M (narrower ones otherwise).  Then (waves, chunks per wave) so that K
-// takes as few phases as possible, with the least padding past K and the most
-// waves, within the LDS budget and the x staging limit (cpw * M <= 16 * x
-// pieces).  The fast path needs group_size % 32 == 0 (a chunk inside one
-// group); otherwise, or when its phase table does not fit, the per-element
-// path is used.
+// Decode launch shape: column tiles of 16 * cpl columns (cpl = 4 or 2 only
+// while that still gives >= 256 workgroups), waves per workgroup and chunks
+// per wave.  Every instantiation is compiled for a fixed number of waves per
+// SIMD, so the number of workgroups a CU holds at once is known here.  The
+// choice minimises, in order: rounds of workgroups (tiles / resident
+// workgroups, so that the whole grid is in flight at once), K phases, padding
+// chunks past K; then prefers more waves and wider tiles.  Limits: the LDS
+// budget and the x staging registers (cpw * M <= 16 * x pieces).  The fast
+// path needs group_size % 32 == 0 (a chunk inside one group); otherwise, or
+// when no fast-path shape fits, the per-element path is used.
 constexpr size_t kDecodeLdsBudget = 160 * 1024;
+constexpr int kCUs = 256;
 constexpr int kNoDecodePlan = 1;
 
-bool decode_plan_for(int bits, int M, int K, int G, int waves, int cpl, bool per_elem, gptq::GemmArgs* a) {
+struct DecodeChoice {
+  int rounds, phases, waste, nw, cpl, cpw, tiles;
+};
+
+bool better_choice(const DecodeChoice& a, const DecodeChoice& b) {
+  if (a.rounds != b.rounds) return a.rounds < b.rounds;
+  if (a.phases != b.phases) return a.phases < b.phases;
+  if (a.waste != b.waste) return a.waste < b.waste;
+  if (a.nw != b.nw) return a.nw > b.nw;
+  return a.cpl > b.cpl;
+}
+
+bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_elem, gptq::GemmArgs* a) {
   const int C = K / 32;
-  const int maxw = gptq::decode_max_waves(cpl, M);
   const int cpg = per_elem ? 1 : (K / G) / 32;
   bool found = false;
-  int best_nw = 0, best_cpw = 0, best_phases = 0, best_waste = 0;
-  for (int cpw : {8, 16, 32}) {
-    if (!gptq::decode_cpw_allowed(cpl, bits, cpw, M)) continue;
-    if (cpw * M > 16 * gptq::decode_max_x_pieces(M)) continue;
-    const int lo = waves > 0 ? std::min(waves, maxw) : 1, hi = waves > 0 ? lo : maxw;
-    for (int nw = lo; nw <= hi; ++nw) {
-      const int pc = nw * cpw;
-      const int phases = (C + pc - 1) / pc;
-      if (gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases) > kDecodeLdsBudget) continue;
-      const int waste = phases * pc - C;
-      const bool better = !found || phases < best_phases ||
-                          (phases == best_phases && (waste < best_waste || (waste == best_waste && nw > best_nw)));
-      if (better) {
-        found = true;
-        best_nw = nw;
-        best_cpw = cpw;
-        best_phases = phases;
-        best_waste = waste;
+  DecodeChoice best{};
+  for (int cpl : {4, 2, 1}) {
+    const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
+    if (cpl > 1 && tiles < kCUs) continue;
+    const int maxw = gptq::decode_max_threads_for(cpl, M) / 64;
+    for (int cpw : {8, 16, 32}) {
+      if (!gptq::decode_cpw_allowed(cpl, bits, cpw, M)) continue;
+      if (cpw * M > 16 * gptq::decode_max_x_pieces(M)) continue;
+      const int simd_waves = gptq::decode_waves_per_simd_for(bits, cpl, cpw, M);
+      const int lo = waves > 0 ? std::min(waves, maxw) : 1, hi = waves > 0 ? lo : maxw;
+      for (int nw = lo; nw <= hi; ++nw) {
+        const int pc = nw * cpw;
+        const int phases = (C + pc - 1) / pc;
+        const size_t lds = gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases);
+        if (lds > kDecodeLdsBudget) continue;
+        const int by_waves = simd_waves / ((nw + 3) / 4);
+        const int by_lds = (int)(kDecodeLdsBudget / std::max<size_t>(lds, 1));
+        const int resident = std::max(1, std::min({by_waves, by_lds, 16})) * kCUs;
+        const DecodeChoice c{(tiles + resident - 1) / resident, phases, phases * pc - C, nw, cpl, cpw, tiles};
+        if (!found || better_choice(c, best)) {
+          best = c;
+          found = true;
+        }
       }
     }
   }
   if (!found) return false;
-  a->cpl = cpl;
-  a->nw = best_nw;
-  a->cpw = best_cpw;
-  a->pc = best_nw * best_cpw;
-  a->phases = best_phases;
+  a->tiles = best.tiles;
+  a->cpl = best.cpl;
+  a->nw = best.nw;
+  a->cpw = best.cpw;
+  a->pc = best.nw * best.cpw;
+  a->phases = best.phases;
   a->cpg = cpg;
   return true;
 }
@@ -93,14 +113,9 @@ bool decode_plan_for(int bits, int M, int K, int G, int waves, int cpl, bool per
 int decode_shape(int bits, int M, int N, int K, int G, int waves, bool* per_elem, gptq::GemmArgs* a) {
   if ((K / G) % 32 != 0) *per_elem = true;
   for (int pe = *per_elem ? 1 : 0; pe < 2; ++pe) {
-    for (int cpl : {4, 2, 1}) {
-      const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
-      if (cpl > 1 && tiles < 256) continue;
-      if (decode_plan_for(bits, M, K, G, waves, cpl, pe == 1, a)) {
-        a->tiles = tiles;
-        *per_elem = pe == 1;
-        return GPTQ_OK;
-      }
+    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, a)) {
+      *per_elem = pe == 1;
+      return GPTQ_OK;
     }
   }
   return kNoDecodePlan;                              // the scale/zero table does not fit LDS

@@ -84,36 +84,40 @@ template <int BITS> __device__ __forceinline__ uint32_t block_sel(int kb) {
 }
 
 // Eight fields of one column's block -> four magic pairs (see file comment).
-// w0 / w1 are the column's words from block_row0 / block_row1.
+// w0 / w1 are the column's words from block_row0 / block_row1.  With
+// magic = 0 the pairs are instead the fp16 subnormals MUL * q * 2^-24 (every
+// shifted field stays inside the 10 mantissa bits), exact inputs for the
+// MFMA, which keeps fp16 subnormals.
 template <int BITS>
-__device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, uint32_t sel, uint32_t p[4]) {
+__device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, uint32_t sel, uint32_t p[4],
+                                             uint32_t magic = kMagicPair) {
   if constexpr (BITS == 4) {
     const uint32_t t = w0 >> 8;
-    p[0] = (w0 & 0x000F000Fu) | kMagicPair;   // f0, f4
-    p[1] = (w0 & 0x00F000F0u) | kMagicPair;   // 16 f1, 16 f5
-    p[2] = (t & 0x000F000Fu) | kMagicPair;    // f2, f6
-    p[3] = (t & 0x00F000F0u) | kMagicPair;    // 16 f3, 16 f7
+    p[0] = (w0 & 0x000F000Fu) | magic;   // f0, f4
+    p[1] = (w0 & 0x00F000F0u) | magic;   // 16 f1, 16 f5
+    p[2] = (t & 0x000F000Fu) | magic;    // f2, f6
+    p[3] = (t & 0x00F000F0u) | magic;    // 16 f3, 16 f7
   } else if constexpr (BITS == 2) {
     // spread the block's two bytes to bytes 0 and 2 (f0..f3 low, f4..f7 high)
     const uint32_t t = __builtin_amdgcn_perm(0u, w0, sel);
-    p[0] = (t & 0x00030003u) | kMagicPair;    // f0, f4
-    p[1] = (t & 0x000C000Cu) | kMagicPair;    // 4 f1, 4 f5
-    p[2] = (t & 0x00300030u) | kMagicPair;    // 16 f2, 16 f6
-    p[3] = (t & 0x00C000C0u) | kMagicPair;    // 64 f3, 64 f7
+    p[0] = (t & 0x00030003u) | magic;    // f0, f4
+    p[1] = (t & 0x000C000Cu) | magic;    // 4 f1, 4 f5
+    p[2] = (t & 0x00300030u) | magic;    // 16 f2, 16 f6
+    p[3] = (t & 0x00C000C0u) | magic;    // 64 f3, 64 f7
   } else if constexpr (BITS == 3) {
     // 24-bit block: f0..f3 in bits 0..11 stay, f4..f7 (bits 12..23) move to 16..27
     const uint32_t s = __builtin_amdgcn_alignbit(w1, w0, sel);
     const uint32_t t = (s & 0x0000FFFFu) | ((s << 4) & 0xFFFF0000u);
     const uint32_t t6 = t >> 6;
-    p[0] = (t & 0x00070007u) | kMagicPair;    // f0, f4
-    p[1] = (t & 0x00380038u) | kMagicPair;    // 8 f1, 8 f5
-    p[2] = (t & 0x01C001C0u) | kMagicPair;    // 64 f2, 64 f6
-    p[3] = (t6 & 0x00380038u) | kMagicPair;   // 8 f3, 8 f7
+    p[0] = (t & 0x00070007u) | magic;    // f0, f4
+    p[1] = (t & 0x00380038u) | magic;    // 8 f1, 8 f5
+    p[2] = (t & 0x01C001C0u) | magic;    // 64 f2, 64 f6
+    p[3] = (t6 & 0x00380038u) | magic;   // 8 f3, 8 f7
   } else {
-    p[0] = (w0 & 0x00FF00FFu) | kMagicPair;          // f0, f2
-    p[1] = ((w0 >> 8) & 0x00FF00FFu) | kMagicPair;   // f1, f3
-    p[2] = (w1 & 0x00FF00FFu) | kMagicPair;          // f4, f6
-    p[3] = ((w1 >> 8) & 0x00FF00FFu) | kMagicPair;   // f5, f7
+    p[0] = (w0 & 0x00FF00FFu) | magic;          // f0, f2
+    p[1] = ((w0 >> 8) & 0x00FF00FFu) | magic;   // f1, f3
+    p[2] = (w1 & 0x00FF00FFu) | magic;          // f4, f6
+    p[3] = ((w1 >> 8) & 0x00FF00FFu) | magic;   // f5, f7
   }
 }
 

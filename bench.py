@@ -20,10 +20,19 @@ The JSON line also carries:
                 qkv layer, same unit.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+
+Counter passes (HBM traffic of the decode kernel, see `--pmc-driver`):
+  rocprofv3 --pmc FETCH_SIZE -d D/fetch -o run -f csv -- python3 bench.py --pmc-driver
+  rocprofv3 --pmc WRITE_SIZE -d D/write -o run -f csv -- python3 bench.py --pmc-driver
+  python3 bench.py --summarize-pmc D/fetch/run_counter_collection.csv D/write/run_counter_collection.csv
+The summary goes to profiles/; `roofline.traffic` is read from it while the
+decode sources still hash to the value recorded there (null otherwise).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +42,12 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama7b_w4g128_hbm_traffic.txt")
+# sources that decide the decode kernel's code and launch shapes
+DECODE_SOURCES = ["weight_only_bit_gptq_amd/csrc/decode.hip", "weight_only_bit_gptq_amd/csrc/gptq_device.hpp",
+                  "weight_only_bit_gptq_amd/csrc/gptq_kernels.hpp", "weight_only_bit_gptq_amd/csrc/gptq_api.cpp"]
+PMC_COPY_BYTES = 256 << 20      # plain copy of known size that calibrates FETCH_SIZE / WRITE_SIZE
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
@@ -47,9 +62,35 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-cols", type=int, default=2048,
-                   help="columns of the qkv layer the CPU oracle processes")
+    p.add_argument("--cpu-sample-cols", type=int, default=12288,
+                   help="columns of the qkv layer the CPU oracle processes (default: all)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="repeat the oracle on the sample until this much CPU time has passed")
+    p.add_argument("--pmc-driver", action="store_true",
+                   help="only launch each decode layer 3 times and a plain copy, for a rocprofv3 --pmc pass")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the HBM traffic summary from two counter passes (no GPU needed)")
     return p.parse_args()
+
+
+def decode_sources_hash():
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Per-layer HBM bytes per launch from the committed counter summary, or
+    None when it is missing or was taken on other decode sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = [l for l in f if l.startswith("json: ")]
+        rec = json.loads(lines[-1][len("json: "):])
+    except (OSError, IndexError, ValueError):
+        return None
+    return rec if rec.get("sources_sha256") == decode_sources_hash() else None
 
 
 def layer_bytes(K, N, bits, gs):
@@ -129,8 +170,11 @@ def bench_decode(torch, gq, args, dev):
     alg = [layer_bytes(L["K"], L["N"], wl.bits, wl.group_size) + 2 * L["K"] + 2 * L["N"] for L in base]
     mean_launch_ms = float(np.mean(per_layer_ms))
     achieved = (sum(alg) / len(alg)) / (mean_launch_ms * 1e-3) / 1e9
-    layers = [{"layer": l.name, "K": l.K, "N": l.N, "alg_bytes": a, "us": round(t * 1e3, 2),
-               "GBps": round(a / (t * 1e-3) / 1e9, 1)} for l, a, t in zip(wl.layers, alg, per_layer_ms)]
+    kernels = [gq.describe(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits, wl.group_size, wl.is_v2,
+                           out=o) for L, o in zip(base, outs)]
+    layers = [{"layer": l.name, "K": l.K, "N": l.N, "kernel": kn, "alg_bytes": a, "us": round(t * 1e3, 2),
+               "GBps": round(a / (t * 1e-3) / 1e9, 1)}
+              for l, kn, a, t in zip(wl.layers, kernels, alg, per_layer_ms)]
     del g_all, g_layer
     return dict(wl=wl, wbytes=wbytes, copies=copies, ms_per_step=ms_per_step, achieved=achieved, steps=steps,
                 mean_launch_us=mean_launch_ms * 1e3, layers=layers, base=base)
@@ -204,7 +248,7 @@ def cpu_baseline(args):
                              layer.K, ncols)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= 10.0 or reps >= 20:
+        if el >= args.cpu_seconds or reps >= 200:
             break
     sec = el / reps
     gbps = layer_bytes(layer.K, ncols, wl.bits, wl.group_size) / sec / 1e9
@@ -220,8 +264,98 @@ def cpu_baseline(args):
                       f"single-threaded, BLAS up to {threads} threads)"}
 
 
+def pmc_driver(torch, gq, dev):
+    """Each decode layer 3 times (distinct weight copies, so no launch finds its
+    weights in L2), then a plain copy of PMC_COPY_BYTES; no timing."""
+    from workload import WORKLOADS
+    wl = WORKLOADS["llama7b_decode_w4g128"]
+    for layer in wl.layers:
+        L = make_layer(torch, gq, wl, layer, 1, dev)
+        out = torch.empty((1, layer.N), dtype=torch.float16, device=dev)
+        copies = [(L["qweight"].clone(), L["qzeros"].clone(), L["scales"].clone()) for _ in range(3)]
+        torch.cuda.synchronize()
+        for qw, qz, sc in copies:
+            gq.gemm(L["x"], qw, qz, sc, None, wl.bits, wl.group_size, wl.is_v2, out=out)
+        torch.cuda.synchronize()
+        print(f"{layer.name}: {gq.describe(L['x'], qw, qz, sc, None, wl.bits, wl.group_size, wl.is_v2, out=out)}",
+              flush=True)
+        del L, copies
+    a = torch.ones(PMC_COPY_BYTES // 2, dtype=torch.float16, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("pmc driver done", flush=True)
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode launches, scaled
+    by what the same counters read for the plain copy of PMC_COPY_BYTES."""
+    from workload import WORKLOADS
+    wl = WORKLOADS["llama7b_decode_w4g128"]
+
+    def rows(path, counter):
+        out = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+        out.sort()
+        return out
+
+    res = {}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rs = rows(path, counter)
+        dec = [r for r in rs if "decode_kernel" in r[1]]
+        cop = [r for r in rs if "copyBuffer" in r[1] or "copy" in r[1].lower()]
+        if len(dec) != 3 * len(wl.layers) or not cop:
+            raise SystemExit(f"{path}: expected {3 * len(wl.layers)} decode dispatches and a copy, "
+                             f"got {len(dec)} and {len(cop)}")
+        copy_kib = float(np.median([r[3] for r in cop[-3:]]))
+        scale = PMC_COPY_BYTES / (copy_kib * 1024.0)
+        res[name] = dict(dec=dec, copy_kib=copy_kib, scale=scale)
+    layers = []
+    for i, layer in enumerate(wl.layers):
+        f = res["fetch"]["dec"][3 * i:3 * i + 3]
+        w = res["write"]["dec"][3 * i:3 * i + 3]
+        fetch = float(np.mean([r[3] for r in f])) * 1024.0 * res["fetch"]["scale"]
+        write = float(np.mean([r[3] for r in w])) * 1024.0 * res["write"]["scale"]
+        alg = layer_bytes(layer.K, layer.N, wl.bits, wl.group_size) + 2 * layer.K + 2 * layer.N
+        layers.append({"layer": layer.name, "kernel": f[0][1], "grid": f[0][2],
+                       "fetch_bytes": int(fetch), "write_bytes": int(write), "traffic_bytes": int(fetch + write),
+                       "alg_bytes": alg, "traffic_over_alg": round((fetch + write) / alg, 4)})
+    rec = {"sources_sha256": decode_sources_hash(), "copy_bytes": PMC_COPY_BYTES,
+           "fetch_scale": round(res["fetch"]["scale"], 5), "write_scale": round(res["write"]["scale"], 5),
+           "layers": layers}
+    lines = [
+        "# HBM traffic per launch of the decode kernel, Llama-7B-shaped decode layers",
+        "# (M=1, 4-bit, group 128, symmetric, GPTQv1), one MI355X.",
+        "# Commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
+        "#   rocprofv3 --pmc FETCH_SIZE -d D/fetch -o run -f csv -- python3 R/bench.py --pmc-driver",
+        "#   rocprofv3 --pmc WRITE_SIZE -d D/write -o run -f csv -- python3 R/bench.py --pmc-driver",
+        "#   python3 R/bench.py --summarize-pmc D/fetch/run_counter_collection.csv D/write/run_counter_collection.csv",
+        f"# Calibration: a plain copy of {PMC_COPY_BYTES} bytes read FETCH_SIZE {res['fetch']['copy_kib']:.1f} KiB "
+        f"and WRITE_SIZE {res['write']['copy_kib']:.1f} KiB;",
+        f"# scale factors fetch {rec['fetch_scale']}, write {rec['write_scale']} (bytes per counted byte).",
+        "# Per layer: mean over 3 launches on distinct weight copies.",
+    ]
+    for l in layers:
+        lines.append(f"{l['layer']:8s} {l['kernel']}  grid {l['grid']}: fetch {l['fetch_bytes']} B, write "
+                     f"{l['write_bytes']} B, traffic {l['traffic_bytes']} B, algorithmic {l['alg_bytes']} B, "
+                     f"ratio {l['traffic_over_alg']}")
+    lines.append("json: " + json.dumps(rec))
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(run with --gpus 1)", file=sys.stderr)
@@ -233,6 +367,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     gq.library()
+    if args.pmc_driver:
+        pmc_driver(torch, gq, dev)
+        return
 
     dec = bench_decode(torch, gq, args, dev)
     print(f"# decode: {dec['ms_per_step'] * 1e3:.2f} us/step, layers: {dec['layers']}", file=sys.stderr, flush=True)
@@ -246,6 +383,14 @@ def main():
 
     wl = dec["wl"]
     value = dec["wbytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
+    traffic = read_traffic()
+    traffic_bytes = None
+    if traffic is not None:
+        by_layer = {t["layer"]: t for t in traffic["layers"]}
+        if all(l["layer"] in by_layer for l in dec["layers"]):
+            for l in dec["layers"]:
+                l["traffic_bytes"] = by_layer[l["layer"]]["traffic_bytes"]
+            traffic_bytes = int(np.mean([l["traffic_bytes"] for l in dec["layers"]]))
     line = {
         "metric": "GPTQ W4A16 GEMM: weight GB/s at M=1 and TFLOP/s at M=2048, % of roofline",
         "value": round(value, 1),
@@ -263,9 +408,11 @@ def main():
                    "bits": wl.bits, "group_size": wl.group_size, "sym": wl.sym, "format": "v2" if wl.is_v2 else "v1",
                    "weight_bytes_per_step": dec["wbytes"], "rotated_copies": dec["copies"]},
         "roofline": {"bound": "hbm", "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec["achieved"] / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "decode_kernel<4,false,1,8>", "mean_launch_us": round(dec["mean_launch_us"], 3),
-                     "per_layer": dec["layers"]},
+                     "frac": round(dec["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes,
+                     "kernel": "gptq::decode_kernel, one instantiation per layer (per_layer[].kernel); achieved = "
+                               "mean algorithmic bytes per launch / mean launch time over the 4 layers; traffic = "
+                               "mean HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "mean_launch_us": round(dec["mean_launch_us"], 3), "per_layer": dec["layers"]},
         "copy_GBps": round(ceiling, 1),
         "prefill": prefill,
         "cpu_baseline": cpu,

@@ -127,6 +127,17 @@ GPTQ_API int gptq_gemm_ex_check(const void* x, const int32_t* qweight, const int
                        const void* scales, const int32_t* g_idx, int bits, int group_size,
                        int is_v2, int64_t M, int64_t N, int64_t K, const void* out,
                        int path, int decode_waves);
+/*
+ * Names the kernel instantiation and launch shape gptq_gemm_ex would use for
+ * these arguments, as a NUL-terminated string in buf (at most buflen bytes,
+ * truncated if longer), e.g. for profiles.  Pure host code like the checks
+ * above; returns the same code they do (GPTQ_ERR_NULL_PTR also for a NULL buf
+ * or buflen <= 0).
+ */
+GPTQ_API int gptq_gemm_describe(const void* x, const int32_t* qweight, const int32_t* qzeros,
+                       const void* scales, const int32_t* g_idx, int bits, int group_size,
+                       int is_v2, int64_t M, int64_t N, int64_t K, const void* out,
+                       int path, int decode_waves, char* buf, int64_t buflen);
 GPTQ_API int gptq_dequant_check(const int32_t* qweight, const int32_t* qzeros, const void* scales,
                        const int32_t* g_idx, int bits, int group_size, int is_v2,
                        int64_t N, int64_t K, const void* w_out);

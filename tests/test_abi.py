@@ -29,7 +29,7 @@ def declared_status():
 def test_header_declares_api():
     names = declared_functions()
     for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check", "gptq_gemm_ex_check",
-              "gptq_dequant_check", "gptq_strerror", "gptq_release", "gptq_abi_version"):
+              "gptq_gemm_describe", "gptq_dequant_check", "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
     assert declared_status() == gq.STATUS
 
@@ -165,3 +165,20 @@ def test_forced_decode_always_has_a_launch_plan():
                     for waves in (0, 1, 2, 3, 4, 8, 16):
                         rc = lib.gptq_gemm_ex_check(X, QW, QZ, SC, gi, bits, gs, 1, M, N, K, OUT, 1, waves)
                         assert rc == 0, (bits, K, N, gs, gi, M, waves, rc)
+
+
+@needs_lib
+def test_describe_names_the_kernel():
+    lib = gq.library()
+    buf = ctypes.create_string_buffer(256)
+    assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 4, 128, 0, 1, 12288, 4096, OUT, 0, 0, buf, 256) == 0
+    assert buf.value.decode().startswith("gptq::decode_kernel<4, false, 1, ")
+    assert lib.gptq_gemm_describe(X, QW, QZ, SC, GI, 3, 128, 1, 16, 5120, 13824, OUT, 0, 0, buf, 256) == 0
+    assert buf.value.decode().startswith("gptq::decode_kernel<3, true, 4, ")
+    assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 8, 128, 1, 2048, 28672, 8192, OUT, 0, 0, buf, 256) == 0
+    assert buf.value.decode().startswith("gptq::prefill_kernel<8, false, 2>")
+    assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 5, 128, 1, 1, 4096, 4096, OUT, 0, 0, buf, 256) == -2
+    assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, 0, 0, None, 256) == -1
+    small = ctypes.create_string_buffer(8)
+    assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, 0, 0, small, 8) == 0
+    assert len(small.value) == 7

@@ -15,7 +15,7 @@ import os
 import threading
 from typing import Optional
 
-__all__ = ["gemm", "dequant", "quantize", "release", "library", "library_path", "GptqError",
+__all__ = ["gemm", "describe", "dequant", "quantize", "release", "library", "library_path", "GptqError",
            "STATUS", "PATH_AUTO", "PATH_DECODE", "PATH_PREFILL"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +64,9 @@ def library() -> ctypes.CDLL:
         lib.gptq_gemm_check.restype = i32
         lib.gptq_gemm_ex_check.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, i32, i32]
         lib.gptq_gemm_ex_check.restype = i32
+        lib.gptq_gemm_describe.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, i32, i32,
+                                           ctypes.c_char_p, i64]
+        lib.gptq_gemm_describe.restype = i32
         lib.gptq_dequant_check.argtypes = [i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, vp]
         lib.gptq_dequant_check.restype = i32
         lib.gptq_quantize.argtypes = [vp, i32p, i32, i32, i32, i32, i64, i64, i32p, i32p, vp, vp]
@@ -156,6 +159,22 @@ def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_s
                                 int(bool(is_v2)), M, N, K, out.data_ptr(), stream, int(path), int(decode_waves))
     _raise(code)
     return out
+
+
+def describe(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,
+             is_v2: bool, *, out=None, path: int = PATH_AUTO, decode_waves: int = 0) -> str:
+    """Kernel instantiation and launch shape `gemm` with these arguments uses."""
+    import torch
+    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
+    _check_tensor("x", x, torch.float16, dev)
+    M = x.shape[0]
+    out_ptr = out.data_ptr() if out is not None else x.data_ptr()
+    buf = ctypes.create_string_buffer(256)
+    code = library().gptq_gemm_describe(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                                        None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
+                                        int(bool(is_v2)), M, N, K, out_ptr, int(path), int(decode_waves), buf, 256)
+    _raise(code)
+    return buf.value.decode()
 
 
 def dequant(qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,

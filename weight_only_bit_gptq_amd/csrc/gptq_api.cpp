@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <new>
 #include <utility>
@@ -192,6 +193,30 @@ int gptq_gemm_ex_check(const void* x, const int32_t* qweight, const int32_t* qze
   bool use_decode = false, per_elem = false;
   return plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path, decode_waves,
                    &a, &use_decode, &per_elem);
+}
+
+int gptq_gemm_describe(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                       const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                       const void* out, int path, int decode_waves, char* buf, int64_t buflen) {
+  if (!buf || buflen <= 0) return GPTQ_ERR_NULL_PTR;
+  buf[0] = '\0';
+  gptq::GemmArgs a;
+  bool use_decode = false, per_elem = false;
+  const int rc = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
+                           decode_waves, &a, &use_decode, &per_elem);
+  if (rc != GPTQ_OK) return rc;
+  const char* pe = per_elem ? "true" : "false";
+  if (M == 0) {
+    std::snprintf(buf, (size_t)buflen, "none (M = 0)");
+  } else if (use_decode) {
+    std::snprintf(buf, (size_t)buflen,
+                  "gptq::decode_kernel<%d, %s, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d", bits, pe,
+                  M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles, 64 * a.nw, a.phases, a.pc);
+  } else {
+    std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s, 2> grid=%dx%d block=256", bits, pe, a.tiles_n,
+                  a.tiles_m);
+  }
+  return GPTQ_OK;
 }
 
 int gptq_dequant_check(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,

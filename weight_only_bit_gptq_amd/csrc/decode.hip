@@ -34,6 +34,8 @@
 // section "Weight quantization of LLMs").  Per-element path (act order or
 // other groups): B is the exact fp16 dequantized weight, built with each
 // row's own scale and zero.
+#include <type_traits>
+
 #include "gptq_kernels.hpp"
 
 namespace gptq {
@@ -43,24 +45,28 @@ namespace gptq {
 __host__ __device__ constexpr int decode_x_pieces_of(int mv) { return mv == 1 ? 2 : 8; }
 constexpr int kDecodeTQuads = 4;   // scale/zero table quads (4 columns of a group) per thread per round
 
-// CPW values compiled for a (CPL, words per block, MV) triple: weight words
-// per lane in flight, at most 64 where that leaves room for the rest (M = 1,
-// 32- and 64-column tiles) and 32 otherwise, so that nothing spills.
-__host__ __device__ constexpr bool decode_cpw_ok(int cpl, int loads, int cpw, int mv) {
-  return (cpw == 8 || cpw == 16 || cpw == 32) && cpw * cpl * loads <= ((mv == 1 && cpl > 1) ? 64 : 32);
+__host__ __device__ constexpr int decode_words(int bits, bool per_elem, int cpl, int cpw, int mv) {
+  return cpw * cpl * ((bits == 3 || bits == 8) ? 2 : 1);
 }
-
-__host__ __device__ constexpr int decode_max_threads(int cpl, int mv) { return (cpl == 1 && mv == 1) ? 1024 : 512; }
 
 // Waves per SIMD each instantiation is compiled for (a register budget of
 // 512 / W per lane, met without spills): M = 1 runs 4 while a lane holds at
-// most 32 weight words and 3 above that (3-bit 32-column tiles, whose funnel
-// shifts need more registers, one less); M > 1 runs 2.
-__host__ __device__ constexpr int decode_waves_per_simd(int bits, int cpl, int cpw, int mv) {
-  const int words = cpw * cpl * ((bits == 3 || bits == 8) ? 2 : 1);
-  if (mv != 1) return 2;
-  if (words <= 32) return (bits == 3 && cpl == 2 && words == 32) ? 3 : 4;
-  return (bits == 3 && cpl == 2) ? 2 : 3;
+// most 32 weight words and 3 above; M > 1 runs 2.
+__host__ __device__ constexpr int decode_waves_per_simd(int bits, bool per_elem, int cpl, int cpw, int mv) {
+  return mv != 1 ? 2 : (decode_words(bits, per_elem, cpl, cpw, mv) <= 32 ? 4 : 3);
+}
+
+// A workgroup's waves spread over the CU's 4 SIMDs, so at most 4 W of them.
+__host__ __device__ constexpr int decode_max_threads(int bits, bool per_elem, int cpl, int cpw, int mv) {
+  return 256 * decode_waves_per_simd(bits, per_elem, cpl, cpw, mv) < 1024
+             ? 256 * decode_waves_per_simd(bits, per_elem, cpl, cpw, mv) : 1024;
+}
+
+// CPW values compiled: at most 64 weight words per lane in flight where that
+// leaves room for the rest (M = 1, 32- and 64-column tiles), 32 otherwise.
+__host__ __device__ constexpr bool decode_cpw_ok(int bits, bool per_elem, int cpl, int cpw, int mv) {
+  return (cpw == 8 || cpw == 16 || cpw == 32) &&
+         decode_words(bits, per_elem, cpl, cpw, mv) <= ((mv == 1 && cpl > 1) ? 64 : 32);
 }
 
 template <int CPL> struct WordVec;
@@ -85,23 +91,32 @@ __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t
 // rows of x a chunk's sums are laid out for (multiple of 4 for M > 1)
 __host__ __device__ inline int decode_corr_rows(int M) { return M == 1 ? 1 : (M + 3) & ~3; }
 
+// LDS carve-up.  Fast path: one region per wave holding only that wave's
+// chunks of a phase (x fragments, per-chunk sums of x, the scale/zero rows of
+// the groups they touch), so a wave stages and reads its own data and never
+// waits for the others before the final reduction.  Per-element path: a phase buffer shared
+// by the workgroup (two when K takes several phases: x fragments and the
+// phase's g_idx slice) plus the whole scale/zero table, behind a barrier.
 __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg,
                                                       int phases) {
   DecodeLayout L;
   const size_t tn = (size_t)16 * cpl;
-  const size_t frag = (size_t)pc * 4 * M * 16;
+  const int cpw = pc / nw;
+  const int chunks = per_elem ? pc : cpw;                // chunks one staging region holds
+  const size_t frag = align16((size_t)chunks * 4 * M * 16);
   L.corr_off = frag;
-  const size_t corr = per_elem ? 0 : (size_t)pc * decode_corr_rows(M) * 4;
-  L.gidx_off = align16(frag + corr);
-  const size_t gidx = per_elem ? (size_t)pc * 32 * 2 : 0;
-  L.ptab_off = align16(L.gidx_off + gidx);
-  // groups a window of pc chunks can touch (fast path)
-  L.ptab_rows = per_elem ? 0 : (pc - 1) / cpg + 2;
+  const size_t corr = per_elem ? 0 : align16((size_t)chunks * decode_corr_rows(M) * 4);
+  L.gidx_off = frag + corr;
+  const size_t gidx = per_elem ? align16((size_t)chunks * 32 * 2) : 0;
+  L.ptab_off = L.gidx_off + gidx;
+  // fast path: the groups a run of cpw consecutive chunks can touch
+  L.ptab_rows = per_elem ? 0 : (cpw - 1) / cpg + 2;
   L.buf_stride = align16(L.ptab_off + (size_t)L.ptab_rows * tn * 8);
-  L.tab_off = (phases > 1 ? 2 : 1) * L.buf_stride;       // whole table (per-element path)
+  const int regions = per_elem ? (phases > 1 ? 2 : 1) : nw;
+  L.tab_off = (size_t)regions * L.buf_stride;            // whole table (per-element path)
   const size_t tab = per_elem ? (size_t)G * tn * 4 : 0;
-  // the phase table is staged in one round; the whole table (per-element path) loops
-  L.fits_staging = per_elem || (size_t)L.ptab_rows * tn / 4 <= (size_t)kDecodeTQuads * 64 * nw;
+  // a wave stages its rows in one round; the whole table (per-element path) loops
+  L.fits_staging = per_elem || (size_t)L.ptab_rows * tn / 4 <= (size_t)kDecodeTQuads * 64;
   const size_t data = L.tab_off + tab;
   const size_t red = (size_t)nw * M * tn * 4;
   L.total = data > red ? data : red;
@@ -114,20 +129,21 @@ size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, in
 }
 
 int decode_max_x_pieces(int M) { return decode_x_pieces_of(M == 1 ? 1 : 4); }
-int decode_waves_per_simd_for(int bits, int cpl, int cpw, int M) {
-  return decode_waves_per_simd(bits, cpl, cpw, M == 1 ? 1 : 4);
+int decode_waves_per_simd_for(int bits, bool per_elem, int cpl, int cpw, int M) {
+  return decode_waves_per_simd(bits, per_elem, cpl, cpw, M == 1 ? 1 : 4);
 }
-int decode_max_threads_for(int cpl, int M) { return decode_max_threads(cpl, M == 1 ? 1 : 4); }
-bool decode_cpw_allowed(int cpl, int bits, int cpw, int M) {
-  return decode_cpw_ok(cpl, (bits == 3 || bits == 8) ? 2 : 1, cpw, M == 1 ? 1 : 4);
+int decode_max_threads_for(int bits, bool per_elem, int cpl, int cpw, int M) {
+  return decode_max_threads(bits, per_elem, cpl, cpw, M == 1 ? 1 : 4);
+}
+bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M) {
+  return decode_cpw_ok(bits, per_elem, cpl, cpw, M == 1 ? 1 : 4);
 }
 
-// Up to 16 waves for 16-column tiles at M = 1, 8 otherwise; each instantiation
-// is compiled for a fixed number of waves per SIMD, which the host uses to
-// size the grid so that every workgroup is resident at once.
+// Each instantiation is compiled for a fixed number of waves per SIMD, which
+// the host uses to size the grid and to know how many workgroups a CU holds.
 template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(CPL, MV))))
-__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, CPL, CPW, MV))))
+__global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(BITS, PER_ELEM, CPL, CPW, MV))))
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, PER_ELEM, CPL, CPW, MV))))
 void decode_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int XP = decode_x_pieces_of(MV);
@@ -157,31 +173,44 @@ void decode_kernel(GemmArgs a) {
   const int Mp = decode_corr_rows(M);
   const uint32_t sel = block_sel<BITS>(kb);
 
+  // ---- staging scope: the fast path stages per wave (its own CPW chunks, in
+  // its own LDS region), the per-element path per workgroup (the phase's pc
+  // chunks, shared).  st / sn: this thread's index and the staging threads.
+  const int st = PER_ELEM ? tid : lane;
+  const int sn = PER_ELEM ? nthreads : 64;
+  const int sc = PER_ELEM ? pc : CPW;                // chunks one staging region holds
+  // Chunk u of wave w in phase p is p*pc + w*CPW + u: each wave reads a run of
+  // consecutive packed rows.
+  auto stage_chunk = [&](int p, int cl) __attribute__((always_inline)) { return PER_ELEM ? p * pc + cl : p * pc + wave * CPW + cl; };
+  auto stage_base = [&](int p) __attribute__((always_inline)) {
+    return lds + (size_t)(PER_ELEM ? (phases > 1 ? (p & 1) : 0) : wave) * lay.buf_stride;
+  };
+
   // ---- small operands of a phase: x, g_idx slice, scale/zero rows.  The loads
   // are unconditional (out-of-range indices are clamped, the value replaced by
   // zero when it is stored) and keep raw words, so they issue as one burst.
   half8_t xr[XP];
-  const int xpieces = pc * M * 4;
-  auto x_piece = [&](int p, int i, int& m, int& cl, int& kbe) {
-    const int e = tid + i * nthreads;
+  const int xpieces = sc * M * 4;
+  auto x_piece = [&](int p, int i, int& m, int& cl, int& kbe) __attribute__((always_inline)) {
+    const int e = st + i * sn;
     kbe = e & 3;
     const int rest = e >> 2;
     m = rest % M;
     cl = rest / M;
-    return e < xpieces && p * pc + cl < C;
+    return e < xpieces && stage_chunk(p, cl) < C;
   };
-  auto load_x = [&](int p) {
+  auto load_x = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       int m, cl, kbe;
       const bool ok = x_piece(p, i, m, cl, kbe);
-      const int c = ok ? p * pc + cl : 0;
+      const int c = ok ? stage_chunk(p, cl) : 0;
       xr[i] = *reinterpret_cast<const half8_t*>(a.x + (int64_t)(ok ? m : 0) * a.K + 32 * c + 8 * kbe);
     }
   };
   i32x4_t gr[PER_ELEM ? GP : 1];
   const int gpieces = pc * 8;                        // 4 rows per piece
-  auto load_g = [&](int p) {
+  auto load_g = [&](int p) __attribute__((always_inline)) {
     if constexpr (PER_ELEM) {
 #pragma unroll
       for (int i = 0; i < GP; ++i) {
@@ -194,15 +223,15 @@ void decode_kernel(GemmArgs a) {
       }
     }
   };
-  auto store_xg = [&](int p) {
-    unsigned char* base = lds + (size_t)(p & 1) * lay.buf_stride;
+  auto store_xg = [&](int p) __attribute__((always_inline)) {
+    unsigned char* base = stage_base(p);
     _Float16* frag = reinterpret_cast<_Float16*>(base);
     float* corr = reinterpret_cast<float*>(base + lay.corr_off);
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       int m, cl, kbe;
       const bool ok = x_piece(p, i, m, cl, kbe);
-      if (tid + i * nthreads >= xpieces) continue;   // xpieces % 4 == 0: groups of four stay together
+      if (st + i * sn >= xpieces) continue;          // xpieces % 4 == 0: groups of four stay together
       half8_t av;
       float xs = 0.f;                                // sum of x' MUL over the piece
 #pragma unroll
@@ -242,26 +271,27 @@ void decode_kernel(GemmArgs a) {
     }
   };
 
-  // scale/zero table rows [g0, g0 + rows), four columns per quad: raw scale
-  // and zero words in registers, unpacked when stored.  Rows past G and
-  // columns past N are stored as zero.
+  // scale/zero table rows r < rows holding group group_of_row(r), four columns
+  // per quad: raw scale and zero words in registers, unpacked when stored.
+  // Groups past G and columns past N are stored as zero.
   u32x2_t tsr[TQ];
   uint32_t tz0[TQ], tz1[TQ];
   const uint32_t* qz = reinterpret_cast<const uint32_t*>(a.qzeros);
-  auto table_quad = [&](int rows, int e0, int i, int& r, int& c4) {
-    const int e = e0 + tid + i * nthreads;
+  auto table_quad = [&](int rows, int e0, int i, int& r, int& c4) __attribute__((always_inline)) {
+    const int e = e0 + st + i * sn;
     r = e / (TN / 4);
     c4 = e - r * (TN / 4);
     return e < rows * (TN / 4);
   };
-  auto load_table = [&](int g0, int rows, int e0) {
+  auto load_table = [&](auto group_of_row, int rows, int e0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
       int r, c4;
       const bool in = table_quad(rows, e0, i, r, c4);
       const int nn = n0 + 4 * c4;
-      const bool ok = in && g0 + r < a.G && nn < a.N;
-      const int g = ok ? g0 + r : 0, nq = ok ? nn : 0;
+      const int gr = group_of_row(r);
+      const bool ok = in && gr < a.G && nn < a.N;
+      const int g = ok ? gr : 0, nq = ok ? nn : 0;
       tsr[i] = *reinterpret_cast<const u32x2_t*>(a.scales + (int64_t)g * a.N + nq);
       const uint32_t* row = qz + (int64_t)g * a.zrow_words;
       if constexpr (BITS == 3) {                     // 12 bits, possibly across two words
@@ -274,17 +304,17 @@ void decode_kernel(GemmArgs a) {
     }
   };
   // four columns' (zero + offset) of quad i
-  auto quad_zeros = [&](int i, int c4) {
+  auto quad_zeros = [&](int i, int c4) __attribute__((always_inline)) {
     const int nq = n0 + 4 * c4;
     if constexpr (BITS == 3) return __builtin_amdgcn_alignbit(tz1[i], tz0[i], (uint32_t)((3 * (nq & 31)) & 31));
     else return tz0[i] >> ((nq * BITS) & 31);
   };
-  auto store_table = [&](unsigned char* tw, int g0, int rows, int e0) {
+  auto store_table = [&](unsigned char* tw, auto group_of_row, int rows, int e0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
       int r, c4;
       if (!table_quad(rows, e0, i, r, c4)) continue;
-      const bool real = g0 + r < a.G && n0 + 4 * c4 < a.N;
+      const bool real = group_of_row(r) < a.G && n0 + 4 * c4 < a.N;
       const uint32_t zw = quad_zeros(i, c4);
       uint32_t sb[4], z[4];
 #pragma unroll
@@ -311,15 +341,20 @@ void decode_kernel(GemmArgs a) {
       }
     }
   };
-  auto stage_next = [&](int p) {                    // loads for phase p (registers)
+  // fast path: row r of a wave's table holds group stage_chunk(p, 0) / cpg + r
+  auto chunk_group = [&](int p) __attribute__((always_inline)) {
+    const int g0 = stage_chunk(p, 0) / cpg;
+    return [g0](int r) __attribute__((always_inline)) { return g0 + r; };
+  };
+  auto whole_table = [](int r) { return r; };
+  auto stage_next = [&](int p) __attribute__((always_inline)) {                    // loads for phase p (registers)
     load_x(p);
     load_g(p);
-    if constexpr (!PER_ELEM) load_table(p * pc / cpg, lay.ptab_rows, 0);
+    if constexpr (!PER_ELEM) load_table(chunk_group(p), lay.ptab_rows, 0);
   };
-  auto store_stage = [&](int p) {                    // ... and their LDS stores
+  auto store_stage = [&](int p) __attribute__((always_inline)) {                    // ... and their LDS stores
     store_xg(p);
-    if constexpr (!PER_ELEM)
-      store_table(lds + (size_t)(p & 1) * lay.buf_stride + lay.ptab_off, p * pc / cpg, lay.ptab_rows, 0);
+    if constexpr (!PER_ELEM) store_table(stage_base(p) + lay.ptab_off, chunk_group(p), lay.ptab_rows, 0);
   };
 
   // ---- packed words: block kb of chunk c lives in rows BITS * c + row0(kb)
@@ -331,14 +366,14 @@ void decode_kernel(GemmArgs a) {
   const uint32_t off0 = (uint32_t)(block_row0<BITS>(0, kb) * a.N + nc) * 4u;
   const uint32_t off1 = (uint32_t)(block_row1<BITS>(0, kb) * a.N + nc) * 4u;
   const uint32_t cbytes = (uint32_t)BITS * (uint32_t)a.N * 4u;
-  wvec w0[CPW], w1[L == 2 ? CPW : 1];
-  auto load_w = [&](int p) {
-    const int cb = p * pc + wave * CPW;
+  wvec w0[1][CPW], w1[1][L == 2 ? CPW : 1];
+  auto load_w = [&](int p, auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
-      const uint32_t so = (uint32_t)min(cb + u, C - 1) * cbytes;
-      w0[u] = buffer_words<CPL>(wrsrc, off0, so);
-      if constexpr (L == 2) w1[u] = buffer_words<CPL>(wrsrc, off1, so);
+      const uint32_t so = (uint32_t)min(p * pc + wave * CPW + u, C - 1) * cbytes;
+      w0[set][u] = buffer_words<CPL>(wrsrc, off0, so);
+      if constexpr (L == 2) w1[set][u] = buffer_words<CPL>(wrsrc, off1, so);
       // issue in chunk order, so chunk u waits only for loads 0..u
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -363,7 +398,7 @@ void decode_kernel(GemmArgs a) {
     d_prev[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     s_prev[j] = 0.f;
   }
-  auto fold_prev = [&]() {
+  auto fold_prev = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
 #pragma unroll
@@ -376,17 +411,18 @@ void decode_kernel(GemmArgs a) {
   const uint32_t* full_tab = reinterpret_cast<const uint32_t*>(lds + lay.tab_off);
   const int kbc = MV == 1 ? 0 : min(kb, Mp / 4 - 1);  // rows 4 kbc + v of the correction sums
 
-  // chunk u of this wave in phase p (cl = its index in the phase buffer,
-  // row = its group's row in the phase table)
-  auto compute_chunk = [&](int p, int u, int row) {
-    const unsigned char* base = lds + (size_t)(p & 1) * lay.buf_stride;
-    const int cl = wave * CPW + u;
+  // chunk u of this wave in phase p (cl = its index in the staging region,
+  // row = its group's row in the wave's table), words from register set `set`
+  auto compute_chunk = [&](int p, int u, int row, auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    const unsigned char* base = stage_base(p);
+    const int cl = PER_ELEM ? wave * CPW + u : u;
     const _Float16* frag = reinterpret_cast<const _Float16*>(base);
     // rows >= M of A only feed rows >= M of D, which are never used
     const half8_t A = *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + min(q, M - 1)) << 3));
     uint32_t w1j[CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) w1j[j] = L == 2 ? word_of<CPL>(w1[L == 2 ? u : 0], j) : 0u;
+    for (int j = 0; j < CPL; ++j) w1j[j] = L == 2 ? word_of<CPL>(w1[set][L == 2 ? u : 0], j) : 0u;
 
     if constexpr (PER_ELEM) {
       // per-row scale and zero: the block's 8 rows each carry their own group
@@ -396,7 +432,7 @@ void decode_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         uint32_t pr[4];
-        unpack_block<BITS>(word_of<CPL>(w0[u], j), w1j[j], sel, pr);
+        unpack_block<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], sel, pr);
         u32x4_t bw;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -423,7 +459,7 @@ void decode_kernel(GemmArgs a) {
         s1[j] = te[2 * j];
         const float s2 = te[2 * j + 1];
         uint32_t pr[4];
-        unpack_block<BITS>(word_of<CPL>(w0[u], j), w1j[j], sel, pr, 0u);
+        unpack_block<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], sel, pr, 0u);
         const u32x4_t bw = {pr[0], pr[1], pr[2], pr[3]};
         d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), floatx4_t{0.f, 0.f, 0.f, 0.f},
                                                       0, 0, 0);
@@ -442,46 +478,67 @@ void decode_kernel(GemmArgs a) {
     }
   };
 
-  // ---- prologue: the first table round (per-element path), then phase 0's
-  // small operands, then all of phase 0's weight loads
-  if constexpr (PER_ELEM) load_table(0, a.G, 0);
-  stage_next(0);
-  __builtin_amdgcn_sched_barrier(0);               // small operands strictly before the weights
-  load_w(0);
-  if constexpr (PER_ELEM) {                         // whole table, before the first barrier
-    unsigned char* tw = lds + lay.tab_off;
-    store_table(tw, 0, a.G, 0);
-    const int quads = a.G * (TN / 4);
-    for (int e0 = TQ * nthreads; e0 < quads; e0 += TQ * nthreads) {   // rare: very many groups
-      load_table(0, a.G, e0);
-      store_table(tw, 0, a.G, e0);
-    }
-  }
-
-  // ---- per phase: stage (one barrier), compute the CPW chunks in load order,
-  // then issue the next phase's small operands and weights
-  for (int p = 0; p < phases; ++p) {
-    store_stage(p);
-    __syncthreads();
-    const int cb = p * pc + wave * CPW;              // this wave's first chunk
-    int row = cb / cpg - p * pc / cpg, rem = cb % cpg;
+  using S0 = std::integral_constant<int, 0>;       // register set index, compile-time
+  auto wave_fence = [&]() __attribute__((always_inline)) {
+    // the wave reads back only what its own lanes wrote: LDS operations of one
+    // wave complete in order, the fences keep the compiler's order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto compute_phase = [&](int p, auto set_c) __attribute__((always_inline)) {
+    int row = 0, rem = stage_chunk(p, 0) % cpg;      // group row of chunk u, tracked incrementally
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
-      compute_chunk(p, u, row);
+      compute_chunk(p, u, row, set_c);
       // keep each chunk's LDS reads next to their use: hoisting all of them
       // ahead of the weight waits would cost ~10 registers per chunk
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (!PER_ELEM) {
-        ++rem;
-        const bool next = rem == cpg;
+        const bool next = ++rem == cpg;
         row += next ? 1 : 0;
         rem = next ? 0 : rem;
       }
     }
-    if (p + 1 < phases) {
-      stage_next(p + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(p + 1);
+  };
+  // issue phase p's loads: small operands strictly before the weights, so
+  // waiting for the former never waits for the latter
+  auto issue = [&](int p, auto set_c) __attribute__((always_inline)) {
+    stage_next(p);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(p, set_c);
+  };
+
+  if constexpr (PER_ELEM) {
+    // ---- prologue: the first table round, phase 0's small operands and
+    // weights, then the rest of the whole table before the first barrier
+    load_table(whole_table, a.G, 0);
+    issue(0, S0{});
+    unsigned char* tw = lds + lay.tab_off;
+    store_table(tw, whole_table, a.G, 0);
+    const int quads = a.G * (TN / 4);
+    for (int e0 = TQ * nthreads; e0 < quads; e0 += TQ * nthreads) {   // rare: very many groups
+      load_table(whole_table, a.G, e0);
+      store_table(tw, whole_table, a.G, e0);
+    }
+    // ---- per phase: stage (one barrier), compute, issue the next phase
+    for (int p = 0; p < phases; ++p) {
+      store_stage(p);
+      __syncthreads();
+      compute_phase(p, S0{});
+      if (p + 1 < phases) issue(p + 1, S0{});
+    }
+  } else {
+    // ---- per phase: stage (wave-local), compute, issue the next phase.  One
+    // register set: a second one, keeping the next phase's words in flight
+    // during compute, measured slower on MI355X (more bytes in flight per CU
+    // than the memory system serves efficiently).
+    issue(0, S0{});
+    for (int p = 0; p < phases; ++p) {
+      store_stage(p);
+      wave_fence();
+      compute_phase(p, S0{});
+      if (p + 1 < phases) issue(p + 1, S0{});
     }
   }
   if constexpr (!PER_ELEM && kDeferFold) fold_prev();
@@ -511,7 +568,7 @@ void decode_kernel(GemmArgs a) {
 
 template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
 static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
-  if constexpr (!decode_cpw_ok(CPL, Block<BITS>::LOADS, CPW, MV)) {
+  if constexpr (!decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV)) {
     return hipErrorInvalidValue;
   } else {
     const size_t lds = decode_lds_bytes(a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg, a.phases);

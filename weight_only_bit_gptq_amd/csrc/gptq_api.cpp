@@ -45,29 +45,38 @@ int check_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, con
 }
 
 // Decode launch shape: column tiles of 16 * cpl columns (cpl = 4 or 2 only
-// while that still gives >= 256 workgroups), waves per workgroup and chunks
+// while that still gives >= 192 workgroups), waves per workgroup and chunks
 // per wave.  Every instantiation is compiled for a fixed number of waves per
-// SIMD, so the number of workgroups a CU holds at once is known here.  The
-// choice minimises, in order: rounds of workgroups (tiles / resident
-// workgroups, so that the whole grid is in flight at once), K phases, padding
-// chunks past K; then prefers more waves and wider tiles.  Limits: the LDS
-// budget and the x staging registers (cpw * M <= 16 * x pieces).  The fast
-// path needs group_size % 32 == 0 (a chunk inside one group); otherwise, or
-// when no fast-path shape fits, the per-element path is used.
+// SIMD, so the number of workgroups a CU holds at once is known here.
+// Measured on MI355X, a decode GEMV streams fastest with ~8-13 MB of weights
+// in flight across the chip (more only queues; the rows of a whole matrix
+// requested at once run slower) and every workgroup resident.  The choice
+// therefore minimises, in order: rounds of workgroups; whether the bytes in
+// flight exceed kInflightCap; their distance below it; the distance of the
+// wave count from 8; then prefers wider tiles, fewer K phases and less padding.
+// Limits: the LDS budget and the x staging registers (cpw * M <= 16 * x
+// pieces).  The fast path needs group_size % 32 == 0 (a chunk inside one
+// group); otherwise, or when no fast-path shape fits, the per-element path.
 constexpr size_t kDecodeLdsBudget = 160 * 1024;
 constexpr int kCUs = 256;
+constexpr int64_t kInflightCap = 13ll << 20;
 constexpr int kNoDecodePlan = 1;
 
 struct DecodeChoice {
-  int rounds, phases, waste, nw, cpl, cpw, tiles;
+  int rounds;
+  bool over;          // bytes in flight above kInflightCap
+  int64_t inflight;
+  int nw, cpl, cpw, tiles, phases, waste;
 };
 
 bool better_choice(const DecodeChoice& a, const DecodeChoice& b) {
   if (a.rounds != b.rounds) return a.rounds < b.rounds;
+  if (a.over != b.over) return !a.over;
+  if (a.inflight != b.inflight) return a.over ? a.inflight < b.inflight : a.inflight > b.inflight;
+  if (std::abs(a.nw - 8) != std::abs(b.nw - 8)) return std::abs(a.nw - 8) < std::abs(b.nw - 8);
+  if (a.cpl != b.cpl) return a.cpl > b.cpl;
   if (a.phases != b.phases) return a.phases < b.phases;
-  if (a.waste != b.waste) return a.waste < b.waste;
-  if (a.nw != b.nw) return a.nw > b.nw;
-  return a.cpl > b.cpl;
+  return a.waste < b.waste;
 }
 
 bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_elem, gptq::GemmArgs* a) {
@@ -75,16 +84,18 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
   const int cpg = per_elem ? 1 : (K / G) / 32;
   bool found = false;
   DecodeChoice best{};
+  const int64_t loads = (bits == 3 || bits == 8) ? 2 : 1;
   for (int cpl : {4, 2, 1}) {
     const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
-    if (cpl > 1 && tiles < kCUs) continue;
-    const int maxw = gptq::decode_max_threads_for(cpl, M) / 64;
+    if (cpl > 1 && tiles < 192) continue;
     for (int cpw : {8, 16, 32}) {
-      if (!gptq::decode_cpw_allowed(cpl, bits, cpw, M)) continue;
+      if (!gptq::decode_cpw_allowed(bits, per_elem, cpl, cpw, M)) continue;
       if (cpw * M > 16 * gptq::decode_max_x_pieces(M)) continue;
-      const int simd_waves = gptq::decode_waves_per_simd_for(bits, cpl, cpw, M);
+      const int maxw = gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M) / 64;
+      const int simd_waves = gptq::decode_waves_per_simd_for(bits, per_elem, cpl, cpw, M);
       const int lo = waves > 0 ? std::min(waves, maxw) : 1, hi = waves > 0 ? lo : maxw;
       for (int nw = lo; nw <= hi; ++nw) {
+        if (waves == 0 && (nw & (nw - 1)) != 0) continue;   // automatic: 1, 2, 4, 8, 16 waves
         const int pc = nw * cpw;
         const int phases = (C + pc - 1) / pc;
         const size_t lds = gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases);
@@ -92,7 +103,10 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
         const int by_waves = simd_waves / ((nw + 3) / 4);
         const int by_lds = (int)(kDecodeLdsBudget / std::max<size_t>(lds, 1));
         const int resident = std::max(1, std::min({by_waves, by_lds, 16})) * kCUs;
-        const DecodeChoice c{(tiles + resident - 1) / resident, phases, phases * pc - C, nw, cpl, cpw, tiles};
+        // weight bytes one phase of the resident workgroups has in flight
+        const int64_t inflight = (int64_t)std::min(tiles, resident) * std::min(pc, C) * 64 * cpl * loads * 4;
+        const DecodeChoice c{(tiles + resident - 1) / resident, inflight > kInflightCap, inflight, nw, cpl, cpw,
+                             tiles, phases, phases * pc - C};
         if (!found || better_choice(c, best)) {
           best = c;
           found = true;

@@ -70,9 +70,11 @@ hipError_t launch_dequant(int bits, const DequantArgs& a, hipStream_t stream);
 // LDS bytes of a launch shape (SIZE_MAX if its table cannot be staged)
 size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg, int phases);
 int decode_max_x_pieces(int M);   // 16-byte x pieces each thread may stage per phase
-int decode_max_threads_for(int cpl, int M);   // workgroup size limit of the instantiation
-int decode_waves_per_simd_for(int bits, int cpl, int cpw, int M);   // occupancy it is compiled for
-bool decode_cpw_allowed(int cpl, int bits, int cpw, int M);   // chunks per wave per phase compiled for this tile
+// per instantiation: workgroup size limit, waves per SIMD it is compiled for,
+// and whether that chunks-per-wave value is compiled at all
+int decode_max_threads_for(int bits, bool per_elem, int cpl, int cpw, int M);
+int decode_waves_per_simd_for(int bits, bool per_elem, int cpl, int cpw, int M);
+bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M);
 hipError_t launch_decode(int bits, bool per_elem, const GemmArgs& a, hipStream_t stream);
 
 // Prefill (any M, used for M > 16).

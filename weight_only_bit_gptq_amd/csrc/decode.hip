@@ -43,7 +43,15 @@ namespace gptq {
 // 16-byte x pieces a thread stages per phase: a phase holds nw * CPW chunks of
 // M rows, so CPW * M <= 16 * XP must hold (the host checks it).
 __host__ __device__ constexpr int decode_x_pieces_of(int mv) { return mv == 1 ? 2 : 8; }
-constexpr int kDecodeTQuads = 4;   // scale/zero table quads (4 columns of a group) per thread per round
+constexpr int kDecodeTQuads = 4;   // at most this many scale/zero quads (4 columns of a group) per thread per round
+
+// Table quads a thread stages per round: enough for the rows a wave's run of
+// cpw chunks touches with 32-row groups, at most kDecodeTQuads (the host
+// rejects shapes whose rows do not fit).
+__host__ __device__ constexpr int decode_table_quads(bool per_elem, int cpl, int cpw) {
+  return per_elem ? kDecodeTQuads
+                  : ((cpw + 1) * 4 * cpl + 63) / 64 < kDecodeTQuads ? ((cpw + 1) * 4 * cpl + 63) / 64 : kDecodeTQuads;
+}
 
 __host__ __device__ constexpr int decode_words(int bits, bool per_elem, int cpl, int cpw, int mv) {
   return cpw * cpl * ((bits == 3 || bits == 8) ? 2 : 1);
@@ -116,7 +124,7 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   L.tab_off = (size_t)regions * L.buf_stride;            // whole table (per-element path)
   const size_t tab = per_elem ? (size_t)G * tn * 4 : 0;
   // a wave stages its rows in one round; the whole table (per-element path) loops
-  L.fits_staging = per_elem || (size_t)L.ptab_rows * tn / 4 <= (size_t)kDecodeTQuads * 64;
+  L.fits_staging = per_elem || (size_t)L.ptab_rows * tn / 4 <= (size_t)decode_table_quads(per_elem, cpl, cpw) * 64;
   const size_t data = L.tab_off + tab;
   const size_t red = (size_t)nw * M * tn * 4;
   L.total = data > red ? data : red;
@@ -148,7 +156,7 @@ void decode_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int XP = decode_x_pieces_of(MV);
   constexpr int GP = (CPW + 7) / 8;                  // g_idx pieces: 8 * CPW rows <= 64 * GP pieces of 4
-  constexpr int TQ = kDecodeTQuads;
+  constexpr int TQ = decode_table_quads(PER_ELEM, CPL, CPW);
   constexpr int TN = 16 * CPL;
   constexpr int L = Block<BITS>::LOADS;
   typedef typename WordVec<CPL>::T wvec;
@@ -234,17 +242,20 @@ void decode_kernel(GemmArgs a) {
       if (st + i * sn >= xpieces) continue;          // xpieces % 4 == 0: groups of four stay together
       half8_t av;
       float xs = 0.f;                                // sum of x' MUL over the piece
+      const half8_t xv = ok ? xr[i] : half8_t{};
 #pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        const _Float16 xf = ok ? xr[i][Block<BITS>::F[h]] : (_Float16)0.f;
-        if constexpr (PER_ELEM) {
-          av[h] = xf;
-        } else {
-          const float mul = (float)Block<BITS>::MUL[h >> 1];
-          const _Float16 xp = (_Float16)((float)xf / mul);
-          av[h] = xp;
-          xs += (float)xp * mul;
+      for (int v = 0; v < 4; ++v) {
+        // the pair of register v in field order; x' = x / MUL is exact in fp16
+        // (a power-of-two scaling) up to subnormal rounding, like the scalar form
+        half2_t pr = {xv[Block<BITS>::F[2 * v]], xv[Block<BITS>::F[2 * v + 1]]};
+        if constexpr (!PER_ELEM) {
+          const _Float16 inv = (_Float16)(1.0f / (float)Block<BITS>::MUL[v]);
+          const _Float16 mul = (_Float16)Block<BITS>::MUL[v];
+          pr = pr * half2_t{inv, inv};
+          xs = __builtin_amdgcn_fdot2(pr, half2_t{mul, mul}, xs, false);
         }
+        av[2 * v] = pr[0];
+        av[2 * v + 1] = pr[1];
       }
       *reinterpret_cast<half8_t*>(frag + (((cl * 4 + kbe) * M + m) << 3)) = av;
       if constexpr (!PER_ELEM) {
@@ -271,6 +282,15 @@ void decode_kernel(GemmArgs a) {
     }
   };
 
+  // Fast-path table row: entry (s 2^24, -s z) of column col at float offset
+  // tab_pos(col).  64-column tiles split a row into two planes (columns 4q,
+  // 4q+1 | 4q+2, 4q+3) so that the 16 lanes of a read fetch consecutive
+  // 16-byte pieces (no LDS bank conflicts); narrower tiles are contiguous.
+  auto tab_pos = [](int col) __attribute__((always_inline)) {
+    if constexpr (CPL == 4) return (((col & 3) >> 1) * 16 + (col >> 2)) * 4 + (col & 1) * 2;
+    else return col * 2;
+  };
+
   // scale/zero table rows r < rows holding group group_of_row(r), four columns
   // per quad: raw scale and zero words in registers, unpacked when stored.
   // Groups past G and columns past N are stored as zero.
@@ -286,6 +306,7 @@ void decode_kernel(GemmArgs a) {
   auto load_table = [&](auto group_of_row, int rows, int e0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
+      if (i > 0 && e0 + i * sn >= rows * (TN / 4)) break;   // wave-uniform: no quad of this round left
       int r, c4;
       const bool in = table_quad(rows, e0, i, r, c4);
       const int nn = n0 + 4 * c4;
@@ -312,6 +333,7 @@ void decode_kernel(GemmArgs a) {
   auto store_table = [&](unsigned char* tw, auto group_of_row, int rows, int e0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
+      if (i > 0 && e0 + i * sn >= rows * (TN / 4)) break;
       int r, c4;
       if (!table_quad(rows, e0, i, r, c4)) continue;
       const bool real = group_of_row(r) < a.G && n0 + 4 * c4 < a.N;
@@ -336,8 +358,8 @@ void decode_kernel(GemmArgs a) {
           v[2 * (j & 1)] = sc * 16777216.0f;
           v[2 * (j & 1) + 1] = -sc * (float)z[j];
         }
-        *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8) = v0;
-        *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8 + 16) = v1;
+        *reinterpret_cast<f32x4_t*>(tw + r * TN * 8 + tab_pos(4 * c4) * 4) = v0;
+        *reinterpret_cast<f32x4_t*>(tw + r * TN * 8 + tab_pos(4 * c4 + 2) * 4) = v1;
       }
     }
   };
@@ -367,10 +389,11 @@ void decode_kernel(GemmArgs a) {
   const uint32_t off1 = (uint32_t)(block_row1<BITS>(0, kb) * a.N + nc) * 4u;
   const uint32_t cbytes = (uint32_t)BITS * (uint32_t)a.N * 4u;
   wvec w0[1][CPW], w1[1][L == 2 ? CPW : 1];
-  auto load_w = [&](int p, auto set_c) __attribute__((always_inline)) {
+  // chunks [U0, U1) of this wave in phase p
+  auto load_w = [&](int p, auto set_c, auto u0_c, auto u1_c) __attribute__((always_inline)) {
     constexpr int set = decltype(set_c)::value;
 #pragma unroll
-    for (int u = 0; u < CPW; ++u) {
+    for (int u = decltype(u0_c)::value; u < decltype(u1_c)::value; ++u) {
       const uint32_t so = (uint32_t)min(p * pc + wave * CPW + u, C - 1) * cbytes;
       w0[set][u] = buffer_words<CPL>(wrsrc, off0, so);
       if constexpr (L == 2) w1[set][u] = buffer_words<CPL>(wrsrc, off1, so);
@@ -451,13 +474,13 @@ void decode_kernel(GemmArgs a) {
       float X[MV];
 #pragma unroll
       for (int v = 0; v < MV; ++v) X[v] = corr[v];
-      const float* te = reinterpret_cast<const float*>(base + lay.ptab_off) + (row * TN + CPL * q) * 2;
+      const float* te = reinterpret_cast<const float*>(base + lay.ptab_off) + row * TN * 2;
       floatx4_t d[CPL];
       float s1[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        s1[j] = te[2 * j];
-        const float s2 = te[2 * j + 1];
+        s1[j] = te[tab_pos(CPL * q + j)];
+        const float s2 = te[tab_pos(CPL * q + j) + 1];
         uint32_t pr[4];
         unpack_block<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], sel, pr, 0u);
         const u32x4_t bw = {pr[0], pr[1], pr[2], pr[3]};
@@ -479,6 +502,10 @@ void decode_kernel(GemmArgs a) {
   };
 
   using S0 = std::integral_constant<int, 0>;       // register set index, compile-time
+  constexpr int H = CPW / 2;                        // the two halves of a wave's run of a phase
+  using U0 = std::integral_constant<int, 0>;
+  using UH = std::integral_constant<int, H>;
+  using UE = std::integral_constant<int, CPW>;
   auto wave_fence = [&]() __attribute__((always_inline)) {
     // the wave reads back only what its own lanes wrote: LDS operations of one
     // wave complete in order, the fences keep the compiler's order
@@ -486,11 +513,11 @@ void decode_kernel(GemmArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  auto compute_phase = [&](int p, auto set_c) __attribute__((always_inline)) {
-    int row = 0, rem = stage_chunk(p, 0) % cpg;      // group row of chunk u, tracked incrementally
+  // chunks [U0, U1) of phase p; row / rem track the group row of the next chunk
+  auto compute_range = [&](int p, auto u0_c, auto u1_c, int& row, int& rem) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      compute_chunk(p, u, row, set_c);
+    for (int u = decltype(u0_c)::value; u < decltype(u1_c)::value; ++u) {
+      compute_chunk(p, u, row, S0{});
       // keep each chunk's LDS reads next to their use: hoisting all of them
       // ahead of the weight waits would cost ~10 registers per chunk
       __builtin_amdgcn_sched_barrier(0);
@@ -503,17 +530,17 @@ void decode_kernel(GemmArgs a) {
   };
   // issue phase p's loads: small operands strictly before the weights, so
   // waiting for the former never waits for the latter
-  auto issue = [&](int p, auto set_c) __attribute__((always_inline)) {
+  auto issue = [&](int p) __attribute__((always_inline)) {
     stage_next(p);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(p, set_c);
+    load_w(p, S0{}, U0{}, UE{});
   };
 
   if constexpr (PER_ELEM) {
     // ---- prologue: the first table round, phase 0's small operands and
     // weights, then the rest of the whole table before the first barrier
     load_table(whole_table, a.G, 0);
-    issue(0, S0{});
+    issue(0);
     unsigned char* tw = lds + lay.tab_off;
     store_table(tw, whole_table, a.G, 0);
     const int quads = a.G * (TN / 4);
@@ -525,21 +552,35 @@ void decode_kernel(GemmArgs a) {
     for (int p = 0; p < phases; ++p) {
       store_stage(p);
       __syncthreads();
-      compute_phase(p, S0{});
-      if (p + 1 < phases) issue(p + 1, S0{});
+      int row = 0, rem = 0;
+      compute_range(p, U0{}, UE{}, row, rem);
+      if (p + 1 < phases) issue(p + 1);
     }
   } else {
-    // ---- per phase: stage (wave-local), compute, issue the next phase.  One
-    // register set: a second one, keeping the next phase's words in flight
-    // during compute, measured slower on MI355X (more bytes in flight per CU
-    // than the memory system serves efficiently).
-    issue(0, S0{});
-    for (int p = 0; p < phases; ++p) {
-      store_stage(p);
+    // ---- per phase (staging wave-local): while the second half of phase p's
+    // run is computed, the next phase's small operands and first half of
+    // words are in flight; its second half is issued once the first half of
+    // the register set is free.  So the bytes a wave has in flight stay at
+    // about one run, and compute overlaps the memory stream.  The last phase
+    // is peeled off so that every issued load is consumed and every wait is
+    // exact (no branch between a load and its use).
+    issue(0);
+    store_stage(0);
+    wave_fence();
+    int p = 0;
+    for (; p + 1 < phases; ++p) {
+      int row = 0, rem = stage_chunk(p, 0) % cpg;
+      compute_range(p, U0{}, UH{}, row, rem);
+      stage_next(p + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(p + 1, S0{}, U0{}, UH{});
+      compute_range(p, UH{}, UE{}, row, rem);
+      store_stage(p + 1);
       wave_fence();
-      compute_phase(p, S0{});
-      if (p + 1 < phases) issue(p + 1, S0{});
+      load_w(p + 1, S0{}, UH{}, UE{});
     }
+    int row = 0, rem = stage_chunk(p, 0) % cpg;
+    compute_range(p, U0{}, UE{}, row, rem);
   }
   if constexpr (!PER_ELEM && kDeferFold) fold_prev();
 

@@ -227,7 +227,7 @@ int gptq_gemm_describe(const void* x, const int32_t* qweight, const int32_t* qze
                   "gptq::decode_kernel<%d, %s, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d", bits, pe,
                   M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles, 64 * a.nw, a.phases, a.pc);
   } else {
-    std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s, 2> grid=%dx%d block=256", bits, pe, a.tiles_n,
+    std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s> grid=%dx%d block=256", bits, pe, a.tiles_n,
                   a.tiles_m);
   }
   return GPTQ_OK;

@@ -121,6 +121,66 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, uint32_t 
   }
 }
 
+// Natural-order variant: the eight halves of a block come out as the pairs
+// (f0, f1), (f2, f3), (f4, f5), (f6, f7), each half of register v with its
+// own power-of-two multiplier MULN<BITS>::LO[v] / HI[v], so that the other
+// MFMA operand can be x in its natural k order.
+template <int BITS> struct MULN;
+template <> struct MULN<2> { static constexpr int LO[4] = {1, 16, 1, 16}, HI[4] = {4, 64, 4, 64}; };
+template <> struct MULN<3> { static constexpr int LO[4] = {1, 64, 1, 64}, HI[4] = {1, 64, 1, 64}; };
+template <> struct MULN<4> { static constexpr int LO[4] = {1, 1, 1, 1}, HI[4] = {16, 16, 16, 16}; };
+template <> struct MULN<8> { static constexpr int LO[4] = {1, 1, 1, 1}, HI[4] = {1, 1, 1, 1}; };
+
+// Byte selector copying byte b of the source into bytes 0 and 2 (zeros elsewhere).
+__device__ __forceinline__ uint32_t dup_byte_sel(int b) { return 0x0C000C00u | (uint32_t)b | ((uint32_t)b << 16); }
+
+template <int BITS>
+__device__ __forceinline__ void unpack_block_natural(uint32_t w0, uint32_t w1, int kb, uint32_t p[4]) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      p[v] = (__builtin_amdgcn_perm(0u, w0, dup_byte_sel(v)) & 0x00F0000Fu) | kMagicPair;
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t b = 2 * (v & 1);
+      p[v] = __builtin_amdgcn_perm(0u, v < 2 ? w0 : w1, 0x0C000C00u | b | ((b + 1) << 16)) | kMagicPair;
+    }
+  } else if constexpr (BITS == 2) {
+    const int b0 = 2 * (kb & 1);                 // the block's two bytes: f0..f3, f4..f7
+    const uint32_t t0 = __builtin_amdgcn_perm(0u, w0, dup_byte_sel(b0));
+    const uint32_t t1 = __builtin_amdgcn_perm(0u, w0, dup_byte_sel(b0 + 1));
+    p[0] = (t0 & 0x000C0003u) | kMagicPair;    // f0, 4 f1
+    p[1] = (t0 & 0x00C00030u) | kMagicPair;    // 16 f2, 64 f3
+    p[2] = (t1 & 0x000C0003u) | kMagicPair;    // f4, 4 f5
+    p[3] = (t1 & 0x00C00030u) | kMagicPair;    // 16 f6, 64 f7
+  } else {
+    // 24-bit block: fields 0..3 in bits 0..11, fields 4..7 in bits 12..23;
+    // u = lo12 | lo12 << 13 puts f1 at bits 16..18 and f3 at 22..24
+    const uint32_t t = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)((24 * kb) & 31));
+    const uint32_t lo = t & 0xFFFu, hi = (t >> 12) & 0xFFFu;
+    const uint32_t u0 = lo | (lo << 13), u1 = hi | (hi << 13);
+    p[0] = (u0 & 0x00070007u) | kMagicPair;    // f0, f1
+    p[1] = (u0 & 0x01C001C0u) | kMagicPair;    // 64 f2, 64 f3
+    p[2] = (u1 & 0x00070007u) | kMagicPair;    // f4, f5
+    p[3] = (u1 & 0x01C001C0u) | kMagicPair;    // 64 f6, 64 f7
+  }
+}
+
+// Natural-order magic pair of register v -> exact (q - z) in both halves.
+template <int BITS>
+__device__ __forceinline__ half2_t pair_minus_zero_natural(uint32_t p, int v, half2_t neg_off) {
+  const half2_t inv = {(_Float16)(1.0f / (float)MULN<BITS>::LO[v]), (_Float16)(1.0f / (float)MULN<BITS>::HI[v])};
+  return __builtin_bit_cast(half2_t, p) * inv + neg_off;
+}
+
+// -(1024 / MUL + z) for both halves of natural register v.
+template <int BITS>
+__device__ __forceinline__ half2_t neg_offset_natural(int v, int zlo, int zhi) {
+  return half2_t{(_Float16)(-(kMagic / (float)MULN<BITS>::LO[v] + (float)zlo)),
+                 (_Float16)(-(kMagic / (float)MULN<BITS>::HI[v] + (float)zhi))};
+}
+
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 

@@ -8,17 +8,24 @@
 // Tiling: workgroup tile 128 x 256, four waves splitting the 256 columns (no
 // two waves dequantize the same weights), wave tile 128 x 64 = four 32-row
 // by two 32-column v_mfma_f32_32x32x16_f16 tiles, so every dequantized B
-// fragment feeds four MFMAs.  K advances in 64-row tiles; the x tile goes
-// global -> registers -> LDS (double buffered, permuted into the unpack's
-// field order, XOR-swizzled 16-byte slots), while every lane loads its own
-// packed words (one 64-bit load = two adjacent columns) and turns them into
-// B operands: unpack_block -> exact (q - z) -> one fp16 multiply by the
-// scale, the same bits gptq_dequant produces.
+// fragment feeds four MFMAs.  K advances in 64-row tiles.
+//
+// Pipeline, two tiles deep: x tiles go from global memory straight into LDS
+// (buffer loads with the LDS destination, three stages, XOR-swizzled 16-byte
+// slots, no registers), the packed words of a tile into one of three
+// register sets (one 64-bit load = two adjacent columns); at the start of tile
+// kt the loads of tile kt + 2 are issued.  Every load is a buffer load:
+// offsets past the tensor read zero without touching memory, so the loop has
+// no branch around a load and every wait is exact.  B operands: the
+// natural-order unpack (x needs no permutation) -> exact (q - z) -> one fp16
+// multiply by the scale, the same bits gptq_dequant produces.
 //
 // Grid: one workgroup per output tile; when the tile count is a multiple of 8,
 // consecutive tiles of the column-major tile order go to the same XCD
 // (workgroup ids are dealt round-robin over the 8 XCDs), so an XCD's L2 holds
 // a few weight column tiles and the x row tiles they share.
+#include <type_traits>
+
 #include "gptq_kernels.hpp"
 
 namespace gptq {
@@ -27,6 +34,7 @@ constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 256;
 constexpr int kPrefillBK = 64;
 constexpr int kPrefillMS = kPrefillBM / 32;      // 32-row MFMA subtiles per wave
+constexpr int kPrefillStages = 3;                 // x tiles in LDS: current + two in flight
 
 void prefill_shape(int M, int N, int* tiles_m, int* tiles_n) {
   *tiles_m = (M + kPrefillBM - 1) / kPrefillBM;
@@ -34,18 +42,31 @@ void prefill_shape(int M, int N, int* tiles_m, int* tiles_n) {
 }
 
 // Two workgroups per CU: 256 registers per lane for the 128 accumulators, the
-// B and A fragments and the next tile's loads.
+// B and A fragments and three tiles of packed words.
 template <int BITS, bool PER_ELEM>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
   constexpr int BM = kPrefillBM;
   constexpr int BK = kPrefillBK;
   constexpr int MS = kPrefillMS;
-  constexpr int A_PER_THREAD = BM * (BK / 8) / 256;      // 16-byte x pieces per thread per tile
-  __shared__ __align__(16) _Float16 a_lds[2][BM * BK];
+  constexpr int NST = kPrefillStages;
+  constexpr int L = Block<BITS>::LOADS;
+  constexpr int XI = BM * (BK / 8) / 256;          // 16-byte x pieces per thread (per wave: XI loads of 1 KB)
+  // three separate arrays (not one indexed by a runtime stage), so that the
+  // compiler can tell the stages apart and does not wait for the x tiles in
+  // flight before reading the current one
+  __shared__ __align__(16) _Float16 a_lds0[BM * BK];
+  __shared__ __align__(16) _Float16 a_lds1[BM * BK];
+  __shared__ __align__(16) _Float16 a_lds2[BM * BK];
+  auto stage_lds = [&](auto st_c) __attribute__((always_inline)) -> _Float16* {
+    constexpr int st = decltype(st_c)::value % NST;
+    if constexpr (st == 0) return a_lds0;
+    else if constexpr (st == 1) return a_lds1;
+    else return a_lds2;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int t = blockIdx.x;
   const int ntiles = a.tiles_m * a.tiles_n;
@@ -56,61 +77,69 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
   const int kb2 = lane >> 5;         // 8-row block within a 16-row k step
   const int n = tn * kPrefillBN + wave * 64 + 2 * q;   // this lane's two columns n, n + 1
   const bool col_ok = n < a.N;
-
-  const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.qweight);
+  const int nc = col_ok ? n : 0;
   const int ktiles = (a.K + BK - 1) / BK;
 
-  // ---- x tile staging: global -> registers (permuted) -> LDS
-  half8_t xr[A_PER_THREAD];
-  auto load_x = [&](int kt) {
+  // ---- x tiles: slot s = m * 8 + (kblk ^ (m & 7)) of a stage holds x[m0 + m,
+  // 8 kblk .. 8 kblk + 8) of the tile.  Load i of wave w fills slots
+  // (4 w + i) * 64 + lane, so each lane fetches the piece that lands there.
+  // Rows past M read zero (past the end of x); k past K is never used.
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(a.x), (short)0, (int)((uint32_t)a.M * (uint32_t)a.K * 2u), 0x00020000);
+  uint32_t xoff[XI];
 #pragma unroll
-    for (int i = 0; i < A_PER_THREAD; ++i) {
-      const int e = tid + 256 * i;
-      const int m = e >> 3, kblk = e & 7;
-      const int row = m0 + m, kk = kt * BK + 8 * kblk;
-      half8_t v = {};
-      if (row < a.M && kk < a.K) {
-        const half8_t raw = *reinterpret_cast<const half8_t*>(a.x + (int64_t)row * a.K + kk);
+  for (int i = 0; i < XI; ++i) {
+    const int s = (4 * wave + i) * 64 + lane;
+    const int m = s >> 3, kblk = (s & 7) ^ (m & 7);
+    xoff[i] = ((uint32_t)(m0 + m) * (uint32_t)a.K + 8u * kblk) * 2u;
+    if (m0 + m >= a.M) xoff[i] = 0xFFFFFFF0u;      // past the end: reads zero
+  }
+  auto load_x = [&](int kt, auto st_c) __attribute__((always_inline)) {
+    _Float16* sl = stage_lds(st_c);
 #pragma unroll
-        for (int h = 0; h < 8; ++h) v[h] = raw[Block<BITS>::F[h]];
-      }
-      xr[i] = v;
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PER_THREAD; ++i) {
-      const int e = tid + 256 * i;
-      const int m = e >> 3, kblk = e & 7;
-      *reinterpret_cast<half8_t*>(&a_lds[buf][(m * 8 + (kblk ^ (m & 7))) * 8]) = xr[i];
+    for (int i = 0; i < XI; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrsrc, (__attribute__((address_space(3))) void*)(sl + (4 * wave + i) * 64 * 8), 16,
+          (xoff[i] == 0xFFFFFFF0u || kt >= ktiles) ? 0xFFFFFFF0u : xoff[i] + (uint32_t)kt * BK * 2u, 0, 0, 0);
     }
   };
 
-  // ---- packed weight words of one k tile (4 steps of 16 rows), two columns per load
-  u32x2_t w0[4], w1[4];
-  auto load_w = [&](int kt) {
+  // ---- packed words of a tile (4 steps of 16 rows), three register sets
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.qweight), (short)0, (int)((uint32_t)(a.K / 32 * BITS) * (uint32_t)a.N * 4u), 0x00020000);
+  // three register sets on the fast path (tiles kt, kt + 1, kt + 2); the
+  // per-element path, whose scale/zero lookups need the registers, keeps one
+  constexpr int NSR = PER_ELEM ? 1 : NST;
+  u32x2_t w0[NSR][4], w1[NSR][L == 2 ? 4 : 1];
+  // the tile's group parameters (fast path: one group per k tile) travel with
+  // its words, so waiting for a tile never waits for a newer load
+  uint32_t zw0[NSR], zw1[NSR];
+  half2_t sw[NSR];
+  const uint32_t* qzr = reinterpret_cast<const uint32_t*>(a.qzeros);
+  auto load_w = [&](int kt, auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value % NSR;
+    if constexpr (!PER_ELEM) {
+      const int g = min((kt * BK) / a.group_size, a.G - 1);
+      const uint32_t* zrow = qzr + (int64_t)g * a.zrow_words;
+      const int n4 = nc & ~3;
+      if constexpr (BITS == 3) {
+        const int w = 3 * (n4 >> 5) + ((3 * (n4 & 31)) >> 5);
+        zw0[set] = zrow[w];
+        zw1[set] = zrow[((3 * (n4 & 31)) >> 5) < 2 ? w + 1 : w];
+      } else {
+        zw0[set] = zrow[(n4 * BITS) >> 5];
+      }
+      sw[set] = *reinterpret_cast<const half2_t*>(a.scales + (int64_t)g * a.N + nc);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int k = kt * BK + 16 * s;
-      w0[s] = u32x2_t{0u, 0u};
-      w1[s] = w0[s];
-      if (col_ok && k < a.K) {
-        const int c = k >> 5, kb = 2 * (s & 1) + kb2;
-        w0[s] = *reinterpret_cast<const u32x2_t*>(qw + (int64_t)block_row0<BITS>(c, kb) * a.N + n);
-        if constexpr (Block<BITS>::LOADS == 2)
-          w1[s] = *reinterpret_cast<const u32x2_t*>(qw + (int64_t)block_row1<BITS>(c, kb) * a.N + n);
-      }
-    }
-  };
-
-  // ---- group parameters (fast path: one group per k tile, group_size % 64 == 0)
-  uint32_t zg = 0, zg_next = 0;
-  half2_t sg = {}, sg_next = {};
-  auto load_group = [&](int kt, uint32_t& z2, half2_t& s2) {
-    if (col_ok && kt * BK < a.K) {
-      const int g = (kt * BK) / a.group_size;
-      z2 = load_zero4<BITS>(a.qzeros, a.zrow_words, g, n & ~3) >> (BITS * (n & 3));
-      s2 = *reinterpret_cast<const half2_t*>(a.scales + (int64_t)g * a.N + n);
+      const int c = (kt * BK + 16 * s) >> 5, kb = 2 * (s & 1) + kb2;
+      // rows past K lie past the end of qweight and read zero
+      w0[set][s] = __builtin_amdgcn_raw_buffer_load_b64(
+          wrsrc, (int)(((uint32_t)block_row0<BITS>(c, kb) * (uint32_t)a.N + (uint32_t)nc) * 4u), 0, 0);
+      if constexpr (L == 2)
+        w1[set][s] = __builtin_amdgcn_raw_buffer_load_b64(
+            wrsrc, (int)(((uint32_t)block_row1<BITS>(c, kb) * (uint32_t)a.N + (uint32_t)nc) * 4u), 0, 0);
     }
   };
 
@@ -122,102 +151,117 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  load_x(0);
-  load_w(0);
-  if constexpr (!PER_ELEM) load_group(0, zg, sg);
-  store_x(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int buf = kt & 1;
-    u32x2_t cw0[4], cw1[4];
+  // scale/zero of the lane's two columns for the tile's group (fast path),
+  // from register set `set`
+  auto group_consts = [&](int set, half2_t negp[2][4], half2_t sp[2]) __attribute__((always_inline)) {
+    const int n4 = nc & ~3;
+    uint32_t z4;
+    if constexpr (BITS == 3) z4 = __builtin_amdgcn_alignbit(zw1[set], zw0[set], (uint32_t)((3 * (n4 & 31)) & 31));
+    else z4 = zw0[set] >> ((n4 * BITS) & 31);
+    const uint32_t z2 = z4 >> (BITS * (nc & 3));
+    const half2_t s2 = sw[set];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) { cw0[s] = w0[s]; cw1[s] = w1[s]; }
-    if (kt + 1 < ktiles) {
-      load_x(kt + 1);
-      load_w(kt + 1);
-      if constexpr (!PER_ELEM) load_group(kt + 1, zg_next, sg_next);
+    for (int j = 0; j < 2; ++j) {
+      const int z = field_of4(z2, j, BITS) + a.zero_offset;
+      sp[j] = half2_t{s2[j], s2[j]};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) negp[j][v] = neg_offset_natural<BITS>(v, z, z);
     }
+  };
 
-    // B operand constants of this tile's group (fast path)
+  // one k tile from LDS stage `stage` and register set `set`
+  auto compute_tile = [&](int kt, auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value % NSR;
+    const _Float16* sl = stage_lds(set_c);
     half2_t negp[2][4], sp[2];
-    if constexpr (!PER_ELEM) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int z = field_of4(zg, j, BITS) + a.zero_offset;
-        sp[j] = half2_t{sg[j], sg[j]};
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const _Float16 o = neg_offset<BITS>(v, z);
-          negp[j][v] = half2_t{o, o};
-        }
-      }
-    }
-
+    if constexpr (!PER_ELEM) group_consts(set, negp, sp);
     const int ksteps = min(4, (a.K - kt * BK) >> 4);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s >= ksteps) break;
       const int kb = 2 * (s & 1) + kb2;
-      const uint32_t sel = block_sel<BITS>(kb);
-
       half8_t B[2];
-      if constexpr (PER_ELEM) {
-        const int k0 = kt * BK + 16 * s + 8 * kb2;
-        uint32_t z2h[8];
-        half2_t s2h[8];
 #pragma unroll
-        for (int h = 0; h < 8; ++h) {
-          z2h[h] = 0;
-          s2h[h] = half2_t{};
-          if (col_ok) {
-            const int g = group_of(a.g_idx, k0 + h, a.group_size, a.G);
-            z2h[h] = load_zero4<BITS>(a.qzeros, a.zrow_words, g, n & ~3) >> (BITS * (n & 3));
-            s2h[h] = *reinterpret_cast<const half2_t*>(a.scales + (int64_t)g * a.N + n);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint32_t p[4];
-          unpack_block<BITS>(cw0[s][j], cw1[s][j], sel, p);
-          u32x4_t bw;
+      for (int j = 0; j < 2; ++j) {
+        uint32_t p[4];
+        unpack_block_natural<BITS>(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p);
+        u32x4_t bw;
+        if constexpr (PER_ELEM) {
+          const int k0 = kt * BK + 16 * s + 8 * kb2;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int fa = Block<BITS>::F[2 * v], fb = Block<BITS>::F[2 * v + 1];
-            const half2_t neg = {neg_offset<BITS>(v, field_of4(z2h[fa], j, BITS) + a.zero_offset),
-                                 neg_offset<BITS>(v, field_of4(z2h[fb], j, BITS) + a.zero_offset)};
-            bw[v] = as_u32(pair_minus_zero<BITS>(p[v], v, neg) * half2_t{s2h[fa][j], s2h[fb][j]});
+            const int ga = group_of(a.g_idx, k0 + 2 * v, a.group_size, a.G);
+            const int gb = group_of(a.g_idx, k0 + 2 * v + 1, a.group_size, a.G);
+            const uint32_t za = load_zero4<BITS>(a.qzeros, a.zrow_words, ga, nc & ~3) >> (BITS * ((nc & 3) + j));
+            const uint32_t zb = load_zero4<BITS>(a.qzeros, a.zrow_words, gb, nc & ~3) >> (BITS * ((nc & 3) + j));
+            const half2_t neg = neg_offset_natural<BITS>(v, (int)(za & ((1u << BITS) - 1u)) + a.zero_offset,
+                                                         (int)(zb & ((1u << BITS) - 1u)) + a.zero_offset);
+            const half2_t sc = {a.scales[(int64_t)ga * a.N + nc + j], a.scales[(int64_t)gb * a.N + nc + j]};
+            bw[v] = as_u32(pair_minus_zero_natural<BITS>(p[v], v, neg) * sc);
           }
-          B[j] = __builtin_bit_cast(half8_t, bw);
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint32_t p[4];
-          unpack_block<BITS>(cw0[s][j], cw1[s][j], sel, p);
-          u32x4_t bw;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) bw[v] = as_u32(pair_minus_zero<BITS>(p[v], v, negp[j][v]) * sp[j]);
-          B[j] = __builtin_bit_cast(half8_t, bw);
+          for (int v = 0; v < 4; ++v) bw[v] = as_u32(pair_minus_zero_natural<BITS>(p[v], v, negp[j][v]) * sp[j]);
         }
+        B[j] = __builtin_bit_cast(half8_t, bw);
       }
-
 #pragma unroll
       for (int i = 0; i < MS; ++i) {
         const int m = 32 * i + q;
         const int kblk = 2 * s + kb2;
-        const half8_t A = *reinterpret_cast<const half8_t*>(&a_lds[buf][(m * 8 + (kblk ^ (m & 7))) * 8]);
+        const half8_t A = *reinterpret_cast<const half8_t*>(sl + (m * 8 + (kblk ^ (m & 7))) * 8);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[j], acc[i][j], 0, 0, 0);
       }
     }
+  };
 
-    if (kt + 1 < ktiles) {
-      store_x(buf ^ 1);
-      if constexpr (!PER_ELEM) { zg = zg_next; sg = sg_next; }
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  constexpr int LOADS_PER_TILE = XI + 4 * L + (BITS == 3 ? 3 : 2);
+  // s_waitcnt immediate: vmcnt <= n, no wait on the other counters
+  constexpr int kWaitOneTile = (LOADS_PER_TILE & 15) | ((LOADS_PER_TILE >> 4) << 14) | 0x70 | 0xF00;
+  // tile kt: wait until its loads (issued two tiles earlier) are done while
+  // the next tile's stay in flight, barrier (every wave's x pieces are in LDS
+  // and the stage of tile kt - 1 is free), issue tile kt + 2, compute tile kt
+  auto step = [&](int kt, auto set_c, auto next_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    if constexpr (PER_ELEM) {
+      // one register set: the words of tile kt were the last loads issued
+      __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+      __syncthreads();
+      load_x(kt + 2, next_c);
+      compute_tile(kt, set_c);
+      load_w(kt + 1, S0{});
+    } else {
+      // a plain s_barrier: __syncthreads() would also wait for the x tiles
+      // still in flight (its fence covers every LDS write, DMA included); the
+      // compiler-only fences keep LDS reads and loads on their side of it
+      __builtin_amdgcn_s_waitcnt(kWaitOneTile);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      load_x(kt + 2, next_c);
+      load_w(kt + 2, next_c);
+      compute_tile(kt, set_c);
     }
-    __syncthreads();
+  };
+
+  load_x(0, S0{});
+  if constexpr (PER_ELEM) {
+    load_x(1, S1{});
+    load_w(0, S0{});
+  } else {
+    load_w(0, S0{});
+    load_x(1, S1{});
+    load_w(1, S1{});
+  }
+  for (int kt = 0; kt < ktiles; kt += 3) {
+    step(kt, S0{}, S2{});
+    step(kt + 1, S1{}, S0{});
+    step(kt + 2, S2{}, S1{});
   }
 
   // ---- epilogue: fp32 -> fp16, two adjacent columns per store

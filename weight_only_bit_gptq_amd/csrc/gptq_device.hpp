@@ -134,8 +134,12 @@ template <> struct MULN<8> { static constexpr int LO[4] = {1, 1, 1, 1}, HI[4] = 
 // Byte selector copying byte b of the source into bytes 0 and 2 (zeros elsewhere).
 __device__ __forceinline__ uint32_t dup_byte_sel(int b) { return 0x0C000C00u | (uint32_t)b | ((uint32_t)b << 16); }
 
+// `magic` is kMagicPair held in a register the compiler cannot see through,
+// so that mask-and-or is one v_and_or_b32 (the mask from a scalar register;
+// these VOP3 forms take no literal).
 template <int BITS>
-__device__ __forceinline__ void unpack_block_natural(uint32_t w0, uint32_t w1, int kb, uint32_t p[4]) {
+__device__ __forceinline__ void unpack_block_natural(uint32_t w0, uint32_t w1, int kb, uint32_t p[4],
+                                                     uint32_t kMagicPair) {
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int v = 0; v < 4; ++v)

@@ -92,7 +92,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
     const int s = (4 * wave + i) * 64 + lane;
     const int m = s >> 3, kblk = (s & 7) ^ (m & 7);
     xoff[i] = ((uint32_t)(m0 + m) * (uint32_t)a.K + 8u * kblk) * 2u;
-    if (m0 + m >= a.M) xoff[i] = 0xFFFFFFF0u;      // past the end: reads zero
+    // rows past M: an offset past the end of x (plus at most the K bytes of
+    // a tile offset it stays past it, or wraps to valid data of row 0); such
+    // rows only feed output rows that are never stored
+    if (m0 + m >= a.M) xoff[i] = 0xF0000000u;
   }
   auto load_x = [&](int kt, auto st_c) __attribute__((always_inline)) {
     _Float16* sl = stage_lds(st_c);
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
     for (int i = 0; i < XI; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xrsrc, (__attribute__((address_space(3))) void*)(sl + (4 * wave + i) * 64 * 8), 16,
-          (xoff[i] == 0xFFFFFFF0u || kt >= ktiles) ? 0xFFFFFFF0u : xoff[i] + (uint32_t)kt * BK * 2u, 0, 0, 0);
+          xoff[i] + (uint32_t)min(kt, ktiles - 1) * BK * 2u, 0, 0, 0);
     }
   };
 
@@ -111,6 +114,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
   // per-element path, whose scale/zero lookups need the registers, keeps one
   constexpr int NSR = PER_ELEM ? 1 : NST;
   u32x2_t w0[NSR][4], w1[NSR][L == 2 ? 4 : 1];
+  // byte offsets of the lane's words for the 4 steps of tile 0; a tile is
+  // BK * BITS / 32 packed rows further on
+  const uint32_t tile_bytes = (uint32_t)(BK / 32 * BITS) * (uint32_t)a.N * 4u;
+  uint32_t woff0[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = (16 * s) >> 5, kb = 2 * (s & 1) + kb2;
+    woff0[s] = ((uint32_t)block_row0<BITS>(c, kb) * (uint32_t)a.N + (uint32_t)nc) * 4u;
+  }
+  // second word of a two-word block: (row1 - row0) rows further on
+  auto woff1 = [&](int s) __attribute__((always_inline)) {
+    const int c = (16 * s) >> 5, kb = 2 * (s & 1) + kb2;
+    return woff0[s] + (uint32_t)(block_row1<BITS>(c, kb) - block_row0<BITS>(c, kb)) * (uint32_t)a.N * 4u;
+  };
   // the tile's group parameters (fast path: one group per k tile) travel with
   // its words, so waiting for a tile never waits for a newer load
   uint32_t zw0[NSR], zw1[NSR];
@@ -131,17 +148,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
       }
       sw[set] = *reinterpret_cast<const half2_t*>(a.scales + (int64_t)g * a.N + nc);
     }
+    // rows past K lie past the end of qweight and read zero
+    const uint32_t tile_off = (uint32_t)kt * tile_bytes;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int c = (kt * BK + 16 * s) >> 5, kb = 2 * (s & 1) + kb2;
-      // rows past K lie past the end of qweight and read zero
-      w0[set][s] = __builtin_amdgcn_raw_buffer_load_b64(
-          wrsrc, (int)(((uint32_t)block_row0<BITS>(c, kb) * (uint32_t)a.N + (uint32_t)nc) * 4u), 0, 0);
-      if constexpr (L == 2)
-        w1[set][s] = __builtin_amdgcn_raw_buffer_load_b64(
-            wrsrc, (int)(((uint32_t)block_row1<BITS>(c, kb) * (uint32_t)a.N + (uint32_t)nc) * 4u), 0, 0);
+      w0[set][s] = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, (int)(woff0[s] + tile_off), 0, 0);
+      if constexpr (L == 2) w1[set][s] = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, (int)(woff1(s) + tile_off), 0, 0);
     }
   };
+
+  uint32_t magic;                                    // kMagicPair in a register (see unpack_block_natural)
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
   floatx16_t acc[MS][2];
 #pragma unroll
@@ -184,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         uint32_t p[4];
-        unpack_block_natural<BITS>(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p);
+        unpack_block_natural<BITS>(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p, magic);
         u32x4_t bw;
         if constexpr (PER_ELEM) {
           const int k0 = kt * BK + 16 * s + 8 * kb2;

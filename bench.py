@@ -203,9 +203,23 @@ def bench_prefill(torch, gq, args, dev):
             ms = a.elapsed_time(b) / args.prefill_steps
             flops = 2.0 * 2048 * layer.K * layer.N
             tf = flops / (ms * 1e-3) / 1e12
-            res.append({"workload": name, "layer": layer.name, "M": 2048, "K": layer.K, "N": layer.N,
-                        "bits": wl.bits, "ms": round(ms, 4), "TFLOPs": round(tf, 1),
-                        "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+            row = {"workload": name, "layer": layer.name, "M": 2048, "K": layer.K, "N": layer.N,
+                   "bits": wl.bits, "ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                   "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+            if name == "mlp70b_prefill_w4g128":
+                # context: the vendor dense fp16 GEMM (torch.matmul) on the same shape, unquantized W
+                W = torch.randn((layer.K, layer.N), dtype=torch.float16, device=dev)
+                for _ in range(2):
+                    torch.matmul(L["x"], W, out=out)
+                torch.cuda.synchronize()
+                a.record()
+                for _ in range(args.prefill_steps):
+                    torch.matmul(L["x"], W, out=out)
+                b.record()
+                torch.cuda.synchronize()
+                row["dense_fp16_matmul_TFLOPs"] = round(flops / (a.elapsed_time(b) / args.prefill_steps * 1e-3) / 1e12, 1)
+                del W
+            res.append(row)
             del L, out
             torch.cuda.empty_cache()
     return res

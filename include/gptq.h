@@ -67,7 +67,8 @@ typedef enum gptq_status {
   GPTQ_ERR_NO_MEM = -6,      /* the quantizer's temporary could not be allocated */
   GPTQ_ERR_LAUNCH = -7,      /* a kernel launch failed */
   GPTQ_ERR_DEVICE = -8,      /* no current HIP device or a HIP runtime call failed */
-  GPTQ_ERR_BAD_ARG = -9      /* is_v2 / sym not 0 or 1, or a gptq_gemm_ex option out of range */
+  GPTQ_ERR_BAD_ARG = -9      /* is_v2 / sym / to_v2 not 0 or 1, a gptq_gemm_ex option out of range,
+                                or partially overlapping conversion buffers */
 } gptq_status;
 
 /* Size limits (GPTQ_ERR_BAD_SHAPE beyond them): M <= 2^24, N and K <= 2^20,
@@ -161,6 +162,27 @@ GPTQ_API int gptq_dequant_check(const int32_t* qweight, const int32_t* qzeros, c
 GPTQ_API int gptq_quantize(const float* w, const int32_t* g_idx, int bits, int group_size,
                            int sym, int is_v2, int64_t N, int64_t K, int32_t* qweight,
                            int32_t* qzeros, void* scales, void* stream);
+
+/*
+ * GPTQv1 <-> GPTQv2 conversion of packed zero points, qzeros [G, N*bits/32]
+ * int32 (layout as for gptq_gemm), device memory (page "Enhancing vLLM's
+ * support for the GPTQv2 format", section "From GPTQv1 to GPTQv2": v1 stores
+ * clamp(zero - 1) and adds 1 at run time, v2 stores zero).
+ *   to_v2 = 1: every stored b-bit field f becomes f + 1; a field of 2^b - 1
+ *              (zero 2^b, never written by a v1 quantizer) saturates at 2^b - 1.
+ *   to_v2 = 0: f becomes max(f - 1, 0); a v2 zero of 0 is stored as 0 and
+ *              reads back as zero 1 (the format's documented loss).
+ * Saturated (to_v2 = 1) or clamped (to_v2 = 0) fields are lossy: when
+ * lossy_count (device int32, nullable) is given, their number is added to it
+ * (the caller zeroes it first).  qzeros_out may equal qzeros_in (in place);
+ * any other overlap is GPTQ_ERR_BAD_ARG.  N % 32 == 0, G >= 1; pointers 4-byte
+ * aligned.  Enqueues one kernel on `stream`; allocates nothing.
+ */
+GPTQ_API int gptq_convert_zeros(const int32_t* qzeros_in, int32_t* qzeros_out, int bits, int64_t G, int64_t N,
+                                int to_v2, int32_t* lossy_count, void* stream);
+/* Argument checks of gptq_convert_zeros only (pure host, no launch). */
+GPTQ_API int gptq_convert_zeros_check(const int32_t* qzeros_in, const int32_t* qzeros_out, int bits, int64_t G,
+                                      int64_t N, int to_v2, const int32_t* lossy_count);
 
 /* Static text for a gptq_status code ("unknown error" for other values). */
 GPTQ_API const char* gptq_strerror(int code);

@@ -20,6 +20,7 @@ from .gptq_ref import (  # noqa: F401
     store_zeros,
     convert_zeros_v1_to_v2,
     convert_zeros_v2_to_v1,
+    convert_zeros_packed,
     pack_fields,
     unpack_fields,
     pack_along_k,

@@ -125,12 +125,15 @@ def store_zeros(zero: np.ndarray, bits: int, is_v2: bool) -> np.ndarray:
     return np.clip(zero - 1, 0, max_q(bits))
 
 
-def convert_zeros_v1_to_v2(stored_v1: np.ndarray, bits: int) -> np.ndarray:
+def convert_zeros_v1_to_v2(stored_v1: np.ndarray, bits: int, saturate: bool = False) -> np.ndarray:
     """v1 -> v2: the runtime +1 becomes part of the stored value [P1-V2].  Exact
-    for every v1 value a quantizer writes (those are <= 2^b - 2)."""
+    for every v1 value a quantizer writes (those are <= 2^b - 2).  A v1 field
+    of 2^b - 1 has no v2 encoding: an error, or 2^b - 1 with saturate=True."""
     out = np.asarray(stored_v1, dtype=np.int64) + 1
     if out.size and out.max() > max_q(bits):
-        raise ValueError("a v1 zero of 2^b - 1 has no v2 encoding")
+        if not saturate:
+            raise ValueError("a v1 zero of 2^b - 1 has no v2 encoding")
+        out = np.minimum(out, max_q(bits))
     return out
 
 
@@ -193,6 +196,20 @@ def unpack_along_k(qweight: np.ndarray, bits: int, K: int) -> np.ndarray:
 
 def unpack_along_n(qzeros: np.ndarray, bits: int, N: int) -> np.ndarray:
     return np.ascontiguousarray(unpack_fields(np.ascontiguousarray(np.asarray(qzeros).T), bits, N).T)
+
+
+def convert_zeros_packed(qzeros: np.ndarray, bits: int, N: int, to_v2: bool):
+    """Packed qzeros [G, N*b/32] in one format -> the other [P1-V2], plus the
+    number of fields the target cannot hold exactly (v1 fields of 2^b - 1,
+    saturated; v2 zeros of 0, stored as 0 = run-time zero 1)."""
+    stored = unpack_along_n(qzeros, bits, N)
+    if to_v2:
+        lossy = int(np.count_nonzero(stored == max_q(bits)))
+        conv = convert_zeros_v1_to_v2(stored, bits, saturate=True)
+    else:
+        lossy = int(np.count_nonzero(stored == 0))
+        conv = convert_zeros_v2_to_v1(stored, bits)
+    return pack_along_n(conv, bits), lossy
 
 
 def dequant_ref(qweight: np.ndarray, qzeros: np.ndarray, scales: np.ndarray,

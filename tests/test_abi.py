@@ -29,7 +29,8 @@ def declared_status():
 def test_header_declares_api():
     names = declared_functions()
     for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check", "gptq_gemm_ex_check",
-              "gptq_gemm_describe", "gptq_dequant_check", "gptq_strerror", "gptq_release", "gptq_abi_version"):
+              "gptq_gemm_describe", "gptq_dequant_check", "gptq_convert_zeros", "gptq_convert_zeros_check",
+              "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
     assert declared_status() == gq.STATUS
 
@@ -107,6 +108,22 @@ def test_dequant_check_codes():
 
 
 @needs_lib
+def test_convert_zeros_check_codes():
+    lib = gq.library()
+    ck = lambda i=QZ, o=OUT, b=4, G=8, N=4096, v=1, c=None: lib.gptq_convert_zeros_check(i, o, b, G, N, v, c)
+    assert ck() == 0
+    assert ck(o=QZ) == 0                          # in place
+    assert ck(c=GI) == 0
+    assert ck(i=None) == -1 and ck(o=None) == -1
+    for b in (1, 5, 16):
+        assert ck(b=b) == -2
+    assert ck(G=0) == -3 and ck(N=0) == -3 and ck(N=48) == -3 and ck(N=1 << 21) == -3
+    assert ck(v=2) == -9
+    assert ck(o=QZ + 4) == -9                     # partial overlap
+    assert ck(i=QZ + 2) == -5 and ck(c=GI + 2) == -5
+    assert ck(b=3, N=32, G=1) == 0
+
+
 def test_invalid_calls_return_before_any_launch():
     """gptq_gemm / gptq_dequant with bad arguments fail in the host checks, so
     they are safe to call without a GPU."""

@@ -233,6 +233,39 @@ def test_workload_full_size(dev, wname, lname, M):
     assert np.array_equal(w.cpu().numpy().view(np.uint16), w_ref.view(np.uint16))
 
 
+# ------------------------------------------------------------------ v1 <-> v2 zero conversion, bit-exact
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("to_v2", [True, False])
+def test_convert_zeros_bit_exact(dev, bits, to_v2):
+    """gptq_convert_zeros matches the oracle's packed conversion word for word,
+    counts the lossy fields, and converts in place."""
+    for G, N in ((3, 32), (7, 4128), (1, 96), (200, 1056)):
+        qz = random_words(np.random.default_rng(G * 31 + bits), (G, N * bits // 32))
+        qz[0, 0], qz[-1, -1] = -1, 0                  # all-max fields, all-zero fields
+        want, lossy = oracle.convert_zeros_packed(qz, bits, N, to_v2)
+        t = torch.from_numpy(qz).to(dev)
+        cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+        got = gq.convert_zeros(t, bits, N, to_v2, lossy_count=cnt)
+        assert np.array_equal(got.cpu().numpy(), want), (G, N)
+        assert int(cnt.item()) == lossy, (G, N)
+        assert np.array_equal(t.cpu().numpy(), qz)    # input untouched
+        gq.convert_zeros(t, bits, N, to_v2, out=t)    # in place, no counter
+        assert np.array_equal(t.cpu().numpy(), want), (G, N, "in place")
+
+
+def test_convert_zeros_then_gemm_matches_v1(dev):
+    """A v1 layer converted to v2 on the GPU gives the same GEMM result as the
+    v1 layer read with is_v2 = 0 (dequant compared bit for bit)."""
+    K, N, gs, bits = 512, 256, 128, 4
+    d = draw_layer(K, N, 1, sigma=0.02, group_size=gs, seed=3)
+    L = oracle.quantize_layer(d.W, bits, gs, False, False)
+    qw, qz, sc, _ = upload(L, dev)
+    qz2 = gq.convert_zeros(qz, bits, N, True)
+    w1 = gq.dequant(qw, qz, sc, None, bits, gs, False)
+    w2 = gq.dequant(qw, qz2, sc, None, bits, gs, True)
+    assert torch.equal(w1.view(torch.int16), w2.view(torch.int16))
+
+
 # ------------------------------------------------------------------ quantize + pack, bit-exact
 QZ_GRID = list(itertools.product(BITS, (False, True), (False, True), (False, True)))
 

@@ -240,6 +240,44 @@ def test_int2_v1_zero_range_shrinks():
         oracle.convert_zeros_v1_to_v2(np.array([[3]]), 2)
 
 
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("to_v2", [True, False])
+def test_convert_zeros_packed_bruteforce(bits, to_v2):
+    """Packed conversion against per-field big-integer arithmetic: +1 saturating
+    at 2^b - 1 (v1 -> v2) or -1 clamped at 0 (v2 -> v1), every field alone."""
+    G, N = 5, 64
+    qz = random_words(np.random.default_rng(bits + 10 * to_v2), (G, N * bits // 32))
+    qz[0, 0], qz[1, -1] = -1, 0          # a word of all-max fields, a word of zero fields
+    out, lossy = oracle.convert_zeros_packed(qz, bits, N, to_v2)
+    top = (1 << bits) - 1
+    want_lossy = 0
+    for g in range(G):
+        f = bigint_fields(qz[g], bits, N)
+        if to_v2:
+            conv = [min(v + 1, top) for v in f]
+            want_lossy += sum(v == top for v in f)
+        else:
+            conv = [max(v - 1, 0) for v in f]
+            want_lossy += sum(v == 0 for v in f)
+        assert [int(w) & 0xFFFFFFFF for w in out[g]] == bigint_pack(conv, bits)
+    assert lossy == want_lossy > 0
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_convert_zeros_packed_keeps_dequant(bits):
+    """A quantizer's v1 zeros converted to v2 dequantize to the same fp16 bits
+    when read as v2, and converting back restores the v1 words."""
+    d = draw_layer(128, 64, 1, sigma=0.02, group_size=32, outlier_rate=0.02, seed=5)
+    lay = oracle.quantize_layer(d.W, bits, 32, sym=False, is_v2=False)
+    qz2, lossy = oracle.convert_zeros_packed(lay.qzeros, bits, 64, True)
+    assert lossy == 0
+    w1 = oracle.dequant_ref(lay.qweight, lay.qzeros, lay.scales, None, bits, 32, False, 128, 64)
+    w2 = oracle.dequant_ref(lay.qweight, qz2, lay.scales, None, bits, 32, True, 128, 64)
+    assert np.array_equal(w1.view(np.uint16), w2.view(np.uint16))
+    back, _ = oracle.convert_zeros_packed(qz2, bits, 64, False)
+    assert np.array_equal(back, lay.qzeros)
+
+
 # ---------------------------------------------------------------- dequant, brute force
 def dequant_bruteforce(qweight, qzeros, scales, g_idx, bits, gs, is_v2, K, N):
     cols = [bigint_fields(qweight[:, n], bits, K) for n in range(N)]

@@ -15,7 +15,7 @@ import os
 import threading
 from typing import Optional
 
-__all__ = ["gemm", "describe", "dequant", "quantize", "release", "library", "library_path", "GptqError",
+__all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "release", "library", "library_path", "GptqError",
            "STATUS", "PATH_AUTO", "PATH_DECODE", "PATH_PREFILL"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,10 @@ def library() -> ctypes.CDLL:
         lib.gptq_dequant_check.restype = i32
         lib.gptq_quantize.argtypes = [vp, i32p, i32, i32, i32, i32, i64, i64, i32p, i32p, vp, vp]
         lib.gptq_quantize.restype = i32
+        lib.gptq_convert_zeros.argtypes = [i32p, i32p, i32, i64, i64, i32, i32p, vp]
+        lib.gptq_convert_zeros.restype = i32
+        lib.gptq_convert_zeros_check.argtypes = [i32p, i32p, i32, i64, i64, i32, i32p]
+        lib.gptq_convert_zeros_check.restype = i32
         lib.gptq_strerror.argtypes = [i32]
         lib.gptq_strerror.restype = ctypes.c_char_p
         lib.gptq_release.argtypes = []
@@ -227,6 +231,39 @@ def quantize(w, g_idx: Optional[object], bits: int, group_size: int, sym: bool, 
                                  qzeros.data_ptr(), scales.data_ptr(), stream)
     _raise(code)
     return qweight, qzeros, scales
+
+
+def convert_zeros(qzeros, bits: int, N: int, to_v2: bool, out=None, lossy_count=None):
+    """GPTQv1 <-> GPTQv2 conversion of packed zeros qzeros [G, N*b/32] (int32, GPU).
+
+    Returns ``out`` (a new tensor unless given; may be ``qzeros`` itself for an
+    in-place conversion).  ``lossy_count``, an int32 tensor of one element on
+    the same device, if given, is incremented by the number of fields that the
+    target format cannot hold exactly."""
+    import torch
+    if bits not in (2, 3, 4, 8):
+        raise ValueError("bits must be 2, 3, 4 or 8")
+    dev = qzeros.device if isinstance(qzeros, torch.Tensor) else None
+    _check_tensor("qzeros", qzeros, torch.int32, dev)
+    if N <= 0 or N % 32 or qzeros.dim() != 2 or qzeros.shape[1] != N * bits // 32 or qzeros.shape[0] < 1:
+        raise ValueError(f"qzeros must be [G >= 1, {N * bits // 32}] with N % 32 == 0")
+    G = qzeros.shape[0]
+    if out is None:
+        out = torch.empty_like(qzeros)
+    _check_tensor("out", out, torch.int32, dev)
+    if tuple(out.shape) != tuple(qzeros.shape):
+        raise ValueError("out must have the shape of qzeros")
+    if lossy_count is not None:
+        _check_tensor("lossy_count", lossy_count, torch.int32, dev)
+        if lossy_count.numel() != 1:
+            raise ValueError("lossy_count must hold one element")
+    lib = library()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        code = lib.gptq_convert_zeros(qzeros.data_ptr(), out.data_ptr(), int(bits), G, int(N), int(bool(to_v2)),
+                                      None if lossy_count is None else lossy_count.data_ptr(), stream)
+    _raise(code)
+    return out
 
 
 def release():

@@ -299,6 +299,31 @@ int gptq_quantize(const float* w, const int32_t* g_idx, int bits, int group_size
   return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
 }
 
+int gptq_convert_zeros_check(const int32_t* qzeros_in, const int32_t* qzeros_out, int bits, int64_t G, int64_t N,
+                             int to_v2, const int32_t* lossy_count) {
+  if (!qzeros_in || !qzeros_out) return GPTQ_ERR_NULL_PTR;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_BAD_BITS;
+  if (G <= 0 || N <= 0 || N % 32 != 0 || N > ((int64_t)1 << 20) || G > ((int64_t)1 << 20) ||
+      G * (N * bits / 32) >= kMaxElems)
+    return GPTQ_ERR_BAD_SHAPE;
+  if (to_v2 != 0 && to_v2 != 1) return GPTQ_ERR_BAD_ARG;
+  if (!aligned(qzeros_in, 4) || !aligned(qzeros_out, 4) || (lossy_count && !aligned(lossy_count, 4)))
+    return GPTQ_ERR_MISALIGNED;
+  const int64_t bytes = G * (N * bits / 32) * 4;
+  const uintptr_t a = (uintptr_t)qzeros_in, b = (uintptr_t)qzeros_out;
+  if (a != b && a < b + bytes && b < a + bytes) return GPTQ_ERR_BAD_ARG;  // partial overlap
+  return GPTQ_OK;
+}
+
+int gptq_convert_zeros(const int32_t* qzeros_in, int32_t* qzeros_out, int bits, int64_t G, int64_t N, int to_v2,
+                       int32_t* lossy_count, void* stream) {
+  const int rc = gptq_convert_zeros_check(qzeros_in, qzeros_out, bits, G, N, to_v2, lossy_count);
+  if (rc != GPTQ_OK) return rc;
+  const hipError_t err = gptq::launch_convert_zeros(qzeros_in, qzeros_out, bits, G, N, to_v2, lossy_count,
+                                                    reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
+}
+
 const char* gptq_strerror(int code) {
   switch (code) {
     case GPTQ_OK: return "ok";
@@ -310,7 +335,7 @@ const char* gptq_strerror(int code) {
     case GPTQ_ERR_NO_MEM: return "device memory allocation failed (quantizer temporary)";
     case GPTQ_ERR_LAUNCH: return "kernel launch failed";
     case GPTQ_ERR_DEVICE: return "HIP runtime call failed";
-    case GPTQ_ERR_BAD_ARG: return "option out of range (is_v2, sym, path or decode_waves)";
+    case GPTQ_ERR_BAD_ARG: return "option out of range (is_v2, sym, to_v2, path or decode_waves) or overlapping buffers";
     default: return "unknown error";
   }
 }

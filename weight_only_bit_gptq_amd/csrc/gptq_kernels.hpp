@@ -85,4 +85,8 @@ hipError_t launch_prefill(int bits, bool per_elem, const GemmArgs& a, hipStream_
 hipError_t launch_quantize(const float* w, const int32_t* g_idx, int bits, int group_size, int sym, int is_v2,
                            int N, int K, int32_t* qweight, int32_t* qzeros, void* scales, hipStream_t stream);
 
+// GPTQv1 <-> GPTQv2 stored zero conversion of a packed qzeros [G, N*b/32].
+hipError_t launch_convert_zeros(const int32_t* in, int32_t* out, int bits, int64_t G, int64_t N, int to_v2,
+                                int32_t* lossy_count, hipStream_t stream);
+
 }  // namespace gptq

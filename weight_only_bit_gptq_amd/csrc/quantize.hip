@@ -187,4 +187,87 @@ hipError_t launch_quantize(const float* w, const int32_t* g_idx, int bits, int g
   return err != hipSuccess ? err : ferr;
 }
 
+// ---------------------------------------------------------------------------
+// Zero-point format conversion (page "Enhancing vLLM's support for the GPTQv2
+// format", section "From GPTQv1 to GPTQv2"): GPTQv1 stores clamp(zero - 1) and
+// adds 1 at run time, GPTQv2 stores the zero itself.  v1 -> v2 adds 1 to every
+// stored field, v2 -> v1 subtracts 1 clamped at 0.  A v1 field of 2^b - 1 (a
+// zero of 2^b, which no v1 writer produces) has no v2 encoding and saturates to
+// 2^b - 1; a v2 zero of 0 becomes the v1 field 0 (run-time zero 1).  Both are
+// counted as lossy.
+//
+// One thread per unit of whole fields: one word for b in {2, 4, 8}, the three
+// words of a 32-field chunk for b = 3 (fields 10 and 21 straddle words).  Rows
+// hold N*b/32 words with N % 32 == 0, so units never cross a row and the
+// tensor is converted as one flat array.  A thread reads all of its words
+// before writing them, so in == out is allowed.
+
+template <int BITS>
+__device__ __forceinline__ uint32_t convert_field(uint32_t f, int to_v2, int* lossy) {
+  constexpr uint32_t kMax = (1u << BITS) - 1u;
+  if (to_v2) {
+    *lossy += (f == kMax);
+    return f == kMax ? kMax : f + 1u;
+  }
+  *lossy += (f == 0u);
+  return f == 0u ? 0u : f - 1u;
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(256) convert_zeros_kernel(const int32_t* __restrict__ in, int32_t* out,
+                                                            int64_t units, int to_v2, int32_t* lossy_count) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int lossy = 0;
+  if (u < units) {
+    if constexpr (BITS == 3) {
+      const uint32_t w0 = (uint32_t)in[3 * u], w1 = (uint32_t)in[3 * u + 1], w2 = (uint32_t)in[3 * u + 2];
+      const uint64_t lo = (uint64_t)w0 | ((uint64_t)w1 << 32);
+      uint64_t olo = 0;
+      uint32_t ohi = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int p = 3 * i;  // bit position in the 96-bit chunk
+        uint32_t f;
+        if (p + 3 <= 64) f = (uint32_t)(lo >> p) & 7u;
+        else if (p >= 64) f = (w2 >> (p - 64)) & 7u;
+        else f = (uint32_t)(lo >> p) | ((w2 << (64 - p)) & 7u);
+        const uint32_t g = convert_field<3>(f, to_v2, &lossy);
+        if (p + 3 <= 64) olo |= (uint64_t)g << p;
+        else if (p >= 64) ohi |= g << (p - 64);
+        else { olo |= (uint64_t)g << p; ohi |= g >> (64 - p); }
+      }
+      out[3 * u] = (int32_t)(uint32_t)olo;
+      out[3 * u + 1] = (int32_t)(uint32_t)(olo >> 32);
+      out[3 * u + 2] = (int32_t)ohi;
+    } else {
+      const uint32_t w = (uint32_t)in[u];
+      uint32_t o = 0;
+#pragma unroll
+      for (int i = 0; i < 32 / BITS; ++i)
+        o |= convert_field<BITS>((w >> (BITS * i)) & ((1u << BITS) - 1u), to_v2, &lossy) << (BITS * i);
+      out[u] = (int32_t)o;
+    }
+  }
+  if (lossy_count) {
+    // wave sum, then one vector atomic per wave
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lossy += __shfl_xor(lossy, off, 64);
+    if ((threadIdx.x & 63) == 0 && lossy) atomicAdd(lossy_count, lossy);
+  }
+}
+
+hipError_t launch_convert_zeros(const int32_t* in, int32_t* out, int bits, int64_t G, int64_t N, int to_v2,
+                                int32_t* lossy_count, hipStream_t stream) {
+  const int64_t words = G * (N * bits / 32);
+  const int64_t units = bits == 3 ? words / 3 : words;
+  const dim3 grid((unsigned)((units + 255) / 256)), block(256);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(convert_zeros_kernel<2>, grid, block, 0, stream, in, out, units, to_v2, lossy_count); break;
+    case 3: hipLaunchKernelGGL(convert_zeros_kernel<3>, grid, block, 0, stream, in, out, units, to_v2, lossy_count); break;
+    case 4: hipLaunchKernelGGL(convert_zeros_kernel<4>, grid, block, 0, stream, in, out, units, to_v2, lossy_count); break;
+    default: hipLaunchKernelGGL(convert_zeros_kernel<8>, grid, block, 0, stream, in, out, units, to_v2, lossy_count); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace gptq

@@ -165,6 +165,78 @@ def test_decode_multi_phase_k(dev, bits, M):
         assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, f"N={N}")
 
 
+SPLIT_CASES = [(4, 128, 1, 8192, 512, False), (4, 128, 3, 8192, 96, False), (8, 128, 7, 8192, 512, True),
+               (2, 64, 4, 12288, 1024, False), (3, 128, 16, 13824, 640, True), (4, 128, 1, 11008, 1024, False),
+               (3, 32, 2, 9216, 352, False), (4, 128, 16, 8192, 1536, False)]
+
+
+@pytest.mark.parametrize("bits,gs,M,K,N,act", SPLIT_CASES)
+def test_decode_split_k(dev, bits, gs, M, K, N, act):
+    """Shapes whose launch splits K over several workgroups per column tile:
+    oracle parity on sampled columns, bit-identical repeated calls (fixed
+    split order), and a second call that rewrites every output (the arrival
+    counters are re-armed by the first)."""
+    d, L = quantized(K, N, M, bits, gs, False, True, act, seed=K + N + M)
+    qw, qz, sc, gi = upload(L, dev)
+    x = torch.from_numpy(d.x).to(dev)
+    desc = gq.describe(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_DECODE)
+    assert "k_splits=1" not in desc, desc
+    cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 80)), [N - 1]]))
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, True, K, N, cols=cols)
+    y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_DECODE)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_DECODE, out=out)
+    assert_close(y1[:, torch.from_numpy(cols).to(dev)], ref, desc)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), desc
+
+
+def test_decode_split_k_alternating_shapes(dev):
+    """Split-K calls of different shapes (different partial-sum sizes and tile
+    counts) alternate on one stream and share its workspace; every call must
+    find its tiles' arrival counters at zero and leave them so."""
+    layers = []
+    for (bits, gs, M, K, N) in ((4, 128, 1, 8192, 1024), (4, 128, 4, 8192, 96), (2, 64, 1, 8192, 1024)):
+        d, L = quantized(K, N, M, bits, gs, False, True, False, seed=N + M)
+        qw, qz, sc, gi = upload(L, dev)
+        x = torch.from_numpy(d.x).to(dev)
+        assert "k_splits=1" not in gq.describe(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_DECODE)
+        cols = np.arange(0, N, max(1, N // 64))
+        ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N, cols=cols)
+        layers.append((x, qw, qz, sc, bits, gs, M, N, cols, ref))
+    for rep in range(3):
+        for i in (2, 0, 1, 0, 2, 1):
+            x, qw, qz, sc, bits, gs, M, N, cols, ref = layers[i]
+            out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+            gq.gemm(x, qw, qz, sc, None, bits, gs, True, path=gq.PATH_DECODE, out=out)
+            assert_close(out[:, torch.from_numpy(cols).to(dev)], ref, f"rep {rep} layer {i}")
+
+
+def test_decode_split_k_other_stream_and_graph(dev):
+    """A split-K call on a new stream (its own workspace) and inside a captured
+    graph on a stream that never ran eagerly (no workspace yet: the call falls
+    back to one split) both match the default-stream result."""
+    bits, gs, M, K, N = 4, 128, 1, 8192, 512
+    d, L = quantized(K, N, M, bits, gs, True, False, False, seed=77)
+    qw, qz, sc, gi = upload(L, dev)
+    x = torch.from_numpy(d.x).to(dev)
+    y0 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False)
+    s.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    s2 = torch.cuda.Stream()
+    out = torch.zeros((M, N), dtype=torch.float16, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s2):
+        gq.gemm(x, qw, qz, sc, gi, bits, gs, False, out=out)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_close(out, y0.float().cpu().numpy().astype(np.float64), "graph replay")
+
+
 def test_gemm_closed_forms(dev):
     """One-hot rows of x pick rows of W^ (exact up to fp16 output rounding,
     which is the identity for fp16 inputs); x = 0 gives 0."""

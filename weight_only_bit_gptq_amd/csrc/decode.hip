@@ -170,12 +170,17 @@ void decode_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int kb = lane >> 4;          // 8-row block of the chunk (A and B operands)
   const int q = lane & 15;           // column slot (B) and x row (A)
-  int t = blockIdx.x;
-  if ((a.tiles & 7) == 0) t = (blockIdx.x & 7) * (a.tiles >> 3) + (blockIdx.x >> 3);
+  // workgroup -> (column tile t, K split sk); consecutive units share an XCD
+  int unit = blockIdx.x;
+  const int units = a.tiles * a.ks;
+  if ((units & 7) == 0) unit = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
+  const int t = unit / a.ks;
+  const int sk = unit - t * a.ks;
+  const int c0 = sk * a.cks;                         // first chunk of this split
   const int n0 = t * TN;
   const int n = n0 + CPL * q;
   const int nc = n < a.N ? n : 0;                    // lanes past N read column 0 (result unused)
-  const int C = a.chunks;
+  const int C = min(a.chunks - c0, a.cks);          // chunks of this split (>= 1)
   const int pc = a.pc, phases = a.phases, cpg = a.cpg;
   const DecodeLayout lay = decode_layout(M, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases);
   const int Mp = decode_corr_rows(M);
@@ -213,7 +218,7 @@ void decode_kernel(GemmArgs a) {
       int m, cl, kbe;
       const bool ok = x_piece(p, i, m, cl, kbe);
       const int c = ok ? stage_chunk(p, cl) : 0;
-      xr[i] = *reinterpret_cast<const half8_t*>(a.x + (int64_t)(ok ? m : 0) * a.K + 32 * c + 8 * kbe);
+      xr[i] = *reinterpret_cast<const half8_t*>(a.x + (int64_t)(ok ? m : 0) * a.K + 32 * (c0 + c) + 8 * kbe);
     }
   };
   i32x4_t gr[PER_ELEM ? GP : 1];
@@ -223,8 +228,8 @@ void decode_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < GP; ++i) {
         const int e = tid + i * nthreads;
-        const int k = 32 * p * pc + 4 * e;
-        const int kk = (e < gpieces && k < a.K) ? k : 0;
+        const int k = 32 * p * pc + 4 * e;           // row within the split
+        const int kk = (e < gpieces && k < 32 * C) ? 32 * c0 + k : 0;
         if (a.g_idx) gr[i] = *reinterpret_cast<const i32x4_t*>(a.g_idx + kk);
         else gr[i] = i32x4_t{kk / a.group_size, (kk + 1) / a.group_size, (kk + 2) / a.group_size,
                              (kk + 3) / a.group_size};
@@ -270,7 +275,7 @@ void decode_kernel(GemmArgs a) {
       for (int i = 0; i < GP; ++i) {
         const int e = tid + i * nthreads;
         if (e < gpieces) {
-          const bool ok = 32 * p * pc + 4 * e < a.K;
+          const bool ok = 32 * p * pc + 4 * e < 32 * C;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             int g = ok ? gr[i][r] : 0;
@@ -365,7 +370,7 @@ void decode_kernel(GemmArgs a) {
   };
   // fast path: row r of a wave's table holds group stage_chunk(p, 0) / cpg + r
   auto chunk_group = [&](int p) __attribute__((always_inline)) {
-    const int g0 = stage_chunk(p, 0) / cpg;
+    const int g0 = (c0 + stage_chunk(p, 0)) / cpg;
     return [g0](int r) __attribute__((always_inline)) { return g0 + r; };
   };
   auto whole_table = [](int r) { return r; };
@@ -384,7 +389,7 @@ void decode_kernel(GemmArgs a) {
   // c * BITS * N * 4 bytes.  Chunks past K re-read the last chunk: they meet
   // zero x (and a zero table row) and add exactly nothing.
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(a.qweight), (short)0, (int)((int64_t)C * BITS * a.N * 4), 0x00020000);
+      const_cast<int32_t*>(a.qweight), (short)0, (int)((int64_t)a.chunks * BITS * a.N * 4), 0x00020000);
   const uint32_t off0 = (uint32_t)(block_row0<BITS>(0, kb) * a.N + nc) * 4u;
   const uint32_t off1 = (uint32_t)(block_row1<BITS>(0, kb) * a.N + nc) * 4u;
   const uint32_t cbytes = (uint32_t)BITS * (uint32_t)a.N * 4u;
@@ -394,7 +399,7 @@ void decode_kernel(GemmArgs a) {
     constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int u = decltype(u0_c)::value; u < decltype(u1_c)::value; ++u) {
-      const uint32_t so = (uint32_t)min(p * pc + wave * CPW + u, C - 1) * cbytes;
+      const uint32_t so = (uint32_t)(c0 + min(p * pc + wave * CPW + u, C - 1)) * cbytes;
       w0[set][u] = buffer_words<CPL>(wrsrc, off0, so);
       if constexpr (L == 2) w1[set][u] = buffer_words<CPL>(wrsrc, off1, so);
       // issue in chunk order, so chunk u waits only for loads 0..u
@@ -569,7 +574,7 @@ void decode_kernel(GemmArgs a) {
     wave_fence();
     int p = 0;
     for (; p + 1 < phases; ++p) {
-      int row = 0, rem = stage_chunk(p, 0) % cpg;
+      int row = 0, rem = (c0 + stage_chunk(p, 0)) % cpg;
       compute_range(p, U0{}, UH{}, row, rem);
       stage_next(p + 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -579,7 +584,7 @@ void decode_kernel(GemmArgs a) {
       wave_fence();
       load_w(p + 1, S0{}, UH{}, UE{});
     }
-    int row = 0, rem = stage_chunk(p, 0) % cpg;
+    int row = 0, rem = (c0 + stage_chunk(p, 0)) % cpg;
     compute_range(p, U0{}, UE{}, row, rem);
   }
   if constexpr (!PER_ELEM && kDeferFold) fold_prev();
@@ -597,14 +602,56 @@ void decode_kernel(GemmArgs a) {
   }
   __syncthreads();
   const int nw = nthreads >> 6;
+  if (a.ks == 1) {
+    for (int e = tid; e < M * TN; e += nthreads) {
+      const int m = e / TN, col = e - m * TN;
+      if (n0 + col < a.N) {
+        float s = 0.f;
+        for (int w = 0; w < nw; ++w) s += red[(w * M + m) * TN + col];
+        a.out[(int64_t)m * a.N + n0 + col] = (_Float16)s;
+      }
+    }
+    return;
+  }
+  // ---- split K: publish this split's sums, count the tile's arrivals; the
+  // last split to arrive adds all of them in split order (deterministic) and
+  // re-arms the counter.  The partial sums move only through agent-scope
+  // atomic stores and loads, which are coherent across the XCDs' L2s by
+  // themselves; the one ordering needed, every store of the workgroup
+  // complete before its arrival is counted, comes from each wave waiting for
+  // its stores (vmcnt 0) before the barrier.  (A full release/acquire fence
+  // would also write back and invalidate the whole L2, which only plain
+  // accesses need and which stalls every workgroup on that XCD.)
   for (int e = tid; e < M * TN; e += nthreads) {
     const int m = e / TN, col = e - m * TN;
     if (n0 + col < a.N) {
       float s = 0.f;
       for (int w = 0; w < nw; ++w) s += red[(w * M + m) * TN + col];
+      __hip_atomic_store(a.ws + ((int64_t)sk * M + m) * a.N + n0 + col, s, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this wave's stores are complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __shared__ int last_split;
+  __syncthreads();
+  if (tid == 0)
+    last_split = __hip_atomic_fetch_add(a.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(a.ks - 1);
+  __syncthreads();
+  if (!last_split) return;
+  for (int e = tid; e < M * TN; e += nthreads) {
+    const int m = e / TN, col = e - m * TN;
+    if (n0 + col < a.N) {
+      float s = 0.f;
+      for (int k = 0; k < a.ks; ++k)
+        s += __hip_atomic_load(a.ws + ((int64_t)k * M + m) * a.N + n0 + col, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
       a.out[(int64_t)m * a.N + n0 + col] = (_Float16)s;
     }
   }
+  if (tid == 0) __hip_atomic_store(a.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
@@ -619,7 +666,7 @@ static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(a.tiles), dim3(64 * a.nw), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.tiles * a.ks), dim3(64 * a.nw), lds, stream, a);
     return hipGetLastError();
   }
 }

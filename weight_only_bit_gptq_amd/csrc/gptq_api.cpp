@@ -7,8 +7,10 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <utility>
+#include <vector>
 
 #include "gptq.h"
 #include "gptq_kernels.hpp"
@@ -57,16 +59,21 @@ int check_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, con
 // Limits: the LDS budget and the x staging registers (cpw * M <= 16 * x
 // pieces).  The fast path needs group_size % 32 == 0 (a chunk inside one
 // group); otherwise, or when no fast-path shape fits, the per-element path.
-constexpr size_t kDecodeLdsBudget = 160 * 1024;
+// dynamic LDS per workgroup (the kernel adds a few bytes of static LDS)
+constexpr size_t kDecodeLdsBudget = 160 * 1024 - 256;
 constexpr int kCUs = 256;
 constexpr int64_t kInflightCap = 13ll << 20;
 constexpr int kNoDecodePlan = 1;
+constexpr int kMinSplitChunks = 32;                  // a K split covers at least 1024 rows
+constexpr int kMinSplitK = 8192;                     // ... of a K this long (shorter: not worth the reduction)
+constexpr int64_t kSplitWsCap = 16ll << 20;          // fp32 partial sums of all splits, bytes
 
 struct DecodeChoice {
   int rounds;
   bool over;          // bytes in flight above kInflightCap
   int64_t inflight;
-  int nw, cpl, cpw, tiles, phases, waste;
+  int nw, cpl, cpw, ks, tiles, phases, waste;
+  int busy;           // CUs with at least one workgroup
 };
 
 bool better_choice(const DecodeChoice& a, const DecodeChoice& b) {
@@ -75,60 +82,96 @@ bool better_choice(const DecodeChoice& a, const DecodeChoice& b) {
   if (a.inflight != b.inflight) return a.over ? a.inflight < b.inflight : a.inflight > b.inflight;
   if (std::abs(a.nw - 8) != std::abs(b.nw - 8)) return std::abs(a.nw - 8) < std::abs(b.nw - 8);
   if (a.cpl != b.cpl) return a.cpl > b.cpl;
+  if (a.busy != b.busy) return a.busy > b.busy;
+  if (a.ks != b.ks) return a.ks < b.ks;
   if (a.phases != b.phases) return a.phases < b.phases;
   return a.waste < b.waste;
 }
 
-bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_elem, gptq::GemmArgs* a) {
+// Launch shape of one (cpl, nw, cpw, ks) candidate, or false when it does not
+// fit (registers, LDS, x staging, split sizes).
+bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int cpl, int nw, int cpw, int ks,
+                      DecodeChoice* c, size_t* lds_out) {
   const int C = K / 32;
   const int cpg = per_elem ? 1 : (K / G) / 32;
+  if (!gptq::decode_cpw_allowed(bits, per_elem, cpl, cpw, M)) return false;
+  if (cpw * M > 16 * gptq::decode_max_x_pieces(M)) return false;
+  if (nw < 1 || 64 * nw > gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M)) return false;
+  const int cks = (C + ks - 1) / ks;
+  if (ks < 1 || (ks - 1) * cks >= C || (ks > 1 && cks < kMinSplitChunks)) return false;
+  if (ks > 1 && (int64_t)ks * M * N * 4 > kSplitWsCap) return false;
+  const int pc = nw * cpw;
+  const int phases = (cks + pc - 1) / pc;
+  const size_t lds = gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases);
+  if (lds > kDecodeLdsBudget) return false;
+  const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
+  const int units = tiles * ks;
+  const int simd_waves = gptq::decode_waves_per_simd_for(bits, per_elem, cpl, cpw, M);
+  const int by_waves = simd_waves / ((nw + 3) / 4);
+  const int by_lds = (int)(kDecodeLdsBudget / std::max<size_t>(lds, 1));
+  const int resident = std::max(1, std::min({by_waves, by_lds, 16})) * kCUs;
+  // weight bytes one phase of the resident workgroups has in flight
+  const int64_t loads = (bits == 3 || bits == 8) ? 2 : 1;
+  const int64_t inflight = (int64_t)std::min(units, resident) * std::min(pc, cks) * 64 * cpl * loads * 4;
+  *c = DecodeChoice{(units + resident - 1) / resident, inflight > kInflightCap, inflight,
+                    nw, cpl, cpw, ks, tiles, phases, phases * pc - cks, std::min(units, kCUs)};
+  *lds_out = lds;
+  return true;
+}
+
+void apply_choice(const DecodeChoice& c, int K, int G, bool per_elem, gptq::GemmArgs* a) {
+  const int C = K / 32;
+  a->tiles = c.tiles;
+  a->cpl = c.cpl;
+  a->nw = c.nw;
+  a->cpw = c.cpw;
+  a->pc = c.nw * c.cpw;
+  a->phases = c.phases;
+  a->cpg = per_elem ? 1 : (K / G) / 32;
+  a->ks = c.ks;
+  a->cks = (C + c.ks - 1) / c.ks;
+}
+
+bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_elem, bool allow_split,
+                     gptq::GemmArgs* a) {
   bool found = false;
   DecodeChoice best{};
-  const int64_t loads = (bits == 3 || bits == 8) ? 2 : 1;
   for (int cpl : {4, 2, 1}) {
     const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
-    if (cpl > 1 && tiles < 192) continue;
-    for (int cpw : {8, 16, 32}) {
-      if (!gptq::decode_cpw_allowed(bits, per_elem, cpl, cpw, M)) continue;
-      if (cpw * M > 16 * gptq::decode_max_x_pieces(M)) continue;
-      const int maxw = gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M) / 64;
-      const int simd_waves = gptq::decode_waves_per_simd_for(bits, per_elem, cpl, cpw, M);
-      const int lo = waves > 0 ? std::min(waves, maxw) : 1, hi = waves > 0 ? lo : maxw;
-      for (int nw = lo; nw <= hi; ++nw) {
-        if (waves == 0 && (nw & (nw - 1)) != 0) continue;   // automatic: 1, 2, 4, 8, 16 waves
-        const int pc = nw * cpw;
-        const int phases = (C + pc - 1) / pc;
-        const size_t lds = gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases);
-        if (lds > kDecodeLdsBudget) continue;
-        const int by_waves = simd_waves / ((nw + 3) / 4);
-        const int by_lds = (int)(kDecodeLdsBudget / std::max<size_t>(lds, 1));
-        const int resident = std::max(1, std::min({by_waves, by_lds, 16})) * kCUs;
-        // weight bytes one phase of the resident workgroups has in flight
-        const int64_t inflight = (int64_t)std::min(tiles, resident) * std::min(pc, C) * 64 * cpl * loads * 4;
-        const DecodeChoice c{(tiles + resident - 1) / resident, inflight > kInflightCap, inflight, nw, cpl, cpw,
-                             tiles, phases, phases * pc - C};
-        if (!found || better_choice(c, best)) {
-          best = c;
-          found = true;
+    for (int ks : {1, 2, 3, 4, 6, 8}) {
+      // K splits pay for their cross-workgroup reduction (about 2 us) only
+      // when the narrowest column tiles leave most CUs idle and K is long
+      // (measured on MI355X: at N >= 4096, or K = 4096, every split shape was
+      // slower than the best unsplit one; at N <= 1536 with K >= 8192 they
+      // were 10-25% faster)
+      if (ks > 1 && (!allow_split || N / 16 >= kCUs / 2 || K < kMinSplitK)) continue;
+      if (cpl > 1 && tiles * ks < 192) continue;
+      for (int cpw : {8, 16, 32}) {
+        const int maxw = gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M) / 64;
+        const int lo = waves > 0 ? std::min(waves, maxw) : 1, hi = waves > 0 ? lo : maxw;
+        for (int nw = lo; nw <= hi; ++nw) {
+          if (waves == 0 && (nw & (nw - 1)) != 0) continue;   // automatic: 1, 2, 4, 8, 16 waves
+          DecodeChoice c;
+          size_t lds;
+          if (!decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, cpw, ks, &c, &lds)) continue;
+          if (!found || better_choice(c, best)) {
+            best = c;
+            found = true;
+          }
         }
       }
     }
   }
   if (!found) return false;
-  a->tiles = best.tiles;
-  a->cpl = best.cpl;
-  a->nw = best.nw;
-  a->cpw = best.cpw;
-  a->pc = best.nw * best.cpw;
-  a->phases = best.phases;
-  a->cpg = cpg;
+  apply_choice(best, K, G, per_elem, a);
   return true;
 }
 
-int decode_shape(int bits, int M, int N, int K, int G, int waves, bool* per_elem, gptq::GemmArgs* a) {
+int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_split, bool* per_elem,
+                 gptq::GemmArgs* a) {
   if ((K / G) % 32 != 0) *per_elem = true;
   for (int pe = *per_elem ? 1 : 0; pe < 2; ++pe) {
-    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, a)) {
+    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, allow_split, a)) {
       *per_elem = pe == 1;
       return GPTQ_OK;
     }
@@ -139,7 +182,8 @@ int decode_shape(int bits, int M, int N, int K, int G, int waves, bool* per_elem
 // Argument checks plus kernel choice and launch shape: pure host code.
 int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-              const void* out, int path, int decode_waves, gptq::GemmArgs* a, bool* use_decode, bool* per_elem) {
+              const void* out, int path, int decode_waves, gptq::GemmArgs* a, bool* use_decode, bool* per_elem,
+              bool allow_split = true) {
   if (path < 0 || path > 2 || decode_waves < 0 || decode_waves > 16) return GPTQ_ERR_BAD_ARG;
   int rc = check_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out);
   if (rc != GPTQ_OK) return rc;
@@ -163,7 +207,7 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
   if (M == 0) return GPTQ_OK;
   if (*use_decode) {
     *per_elem = (g_idx != nullptr) || (group_size % 32 != 0);
-    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, per_elem, a);
+    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, allow_split, per_elem, a);
     if (rc2 != kNoDecodePlan) return rc2;
     if (path == 1) return GPTQ_ERR_BAD_ARG;         // forced decode, but no launch shape fits
     *use_decode = false;                             // very many groups: the prefill kernel
@@ -171,6 +215,63 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
   *per_elem = (g_idx != nullptr) || (group_size % 64 != 0);
   gptq::prefill_shape(a->M, a->N, &a->tiles_m, &a->tiles_n);
   return GPTQ_OK;
+}
+
+// Split-K workspace, one per (device, stream): the per-tile arrival counters
+// at a fixed place (the first kCounterBytes, enough for every tile count),
+// then the fp32 partial sums.  Counters are zeroed once at allocation and
+// every kernel leaves them at zero, so calls of any shape can share them.
+// Grown (after draining the stream) when a call needs more; never allocated
+// while the stream is being captured.
+constexpr size_t kCounterBytes = (size_t)4 << 16;   // N <= 2^20 columns: at most 2^16 tiles
+struct SplitWorkspace {
+  int device;
+  hipStream_t stream;
+  char* base;
+  size_t bytes;
+};
+std::mutex g_ws_mu;
+std::vector<SplitWorkspace> g_ws;
+
+bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, float** ws, uint32_t** cnt) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || cnt_bytes > kCounterBytes) return false;
+  const size_t need = kCounterBytes + ws_bytes;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  SplitWorkspace* e = nullptr;
+  for (auto& w : g_ws)
+    if (w.device == dev && w.stream == stream) e = &w;
+  if (e == nullptr || e->bytes < need) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return false;
+    size_t bytes = std::max(need, (size_t)1 << 20);
+    if (e != nullptr) {
+      bytes = std::max(bytes, 2 * e->bytes);
+      if (hipStreamSynchronize(stream) != hipSuccess) return false;   // queued kernels may use the old one
+      (void)hipFree(e->base);
+      e->base = nullptr;
+      e->bytes = 0;
+    }
+    char* base = nullptr;
+    if (hipMalloc(reinterpret_cast<void**>(&base), bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    if (hipMemsetAsync(base, 0, bytes, stream) != hipSuccess) {
+      (void)hipFree(base);
+      return false;
+    }
+    if (e == nullptr) {
+      g_ws.push_back(SplitWorkspace{dev, stream, base, bytes});
+      e = &g_ws.back();
+    } else {
+      e->base = base;
+      e->bytes = bytes;
+    }
+  }
+  *cnt = reinterpret_cast<uint32_t*>(e->base);
+  *ws = reinterpret_cast<float*>(e->base + kCounterBytes);
+  return true;
 }
 
 int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
@@ -182,6 +283,13 @@ int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
                            decode_waves, &a, &use_decode, &per_elem);
   if (rc != GPTQ_OK || M == 0) return rc;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  if (use_decode && a.ks > 1 &&
+      !split_workspace(stream, (size_t)a.ks * a.M * a.N * 4, (size_t)a.tiles * 4, &a.ws, &a.cnt)) {
+    // no workspace (first use under stream capture, or out of memory): one split
+    const int rc2 = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
+                              decode_waves, &a, &use_decode, &per_elem, false);
+    if (rc2 != GPTQ_OK) return rc2;
+  }
   const hipError_t err = use_decode ? gptq::launch_decode(bits, per_elem, a, stream)
                                     : gptq::launch_prefill(bits, per_elem, a, stream);
   return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
@@ -224,8 +332,8 @@ int gptq_gemm_describe(const void* x, const int32_t* qweight, const int32_t* qze
     std::snprintf(buf, (size_t)buflen, "none (M = 0)");
   } else if (use_decode) {
     std::snprintf(buf, (size_t)buflen,
-                  "gptq::decode_kernel<%d, %s, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d", bits, pe,
-                  M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles, 64 * a.nw, a.phases, a.pc);
+                  "gptq::decode_kernel<%d, %s, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d k_splits=%d",
+                  bits, pe, M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles * a.ks, 64 * a.nw, a.phases, a.pc, a.ks);
   } else {
     std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s> grid=%dx%d block=256", bits, pe, a.tiles_n,
                   a.tiles_m);
@@ -340,7 +448,19 @@ const char* gptq_strerror(int code) {
   }
 }
 
-void gptq_release(void) {}
+void gptq_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  for (auto& w : g_ws) {
+    if (hipSetDevice(w.device) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(w.base);
+    }
+  }
+  g_ws.clear();
+  if (have) (void)hipSetDevice(cur);
+}
 
 int gptq_abi_version(void) { return 1; }
 

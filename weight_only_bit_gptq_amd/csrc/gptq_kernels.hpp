@@ -33,6 +33,13 @@ struct GemmArgs {
   // K in phases of pc = nw * cpw chunks, cpw chunks per wave per phase,
   // cpg = group_size / 32 chunks per group on the fast path (else 1)
   int tiles, cpl, nw, cpw, pc, phases, cpg;
+  // split K: ks workgroups per column tile, each over cks consecutive chunks
+  // (the last one over the rest); with ks > 1 every workgroup stores its fp32
+  // partial sums to ws [ks, M, N] and the last of a tile to arrive (counted in
+  // cnt[tile], reset to 0 by that workgroup) adds them in split order
+  int ks, cks;
+  float* ws;
+  uint32_t* cnt;
   // prefill launch shape
   int tiles_m, tiles_n;
 };

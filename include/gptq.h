@@ -25,14 +25,21 @@
  *   out      fp16  [M, N]          written, never accumulated into.
  * with G = K / group_size.  The int32 words are bit containers (no sign).
  *
- * Ownership and streams: the library keeps no pointer after a call returns
- * and owns no device memory between calls (gptq_quantize alone uses a
- * stream-ordered temporary that is freed on the same stream).  Work is
- * enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
- * asynchronous: buffers must stay valid until that work completes, and a
- * device-side fault surfaces at the caller's next synchronisation.  The GEMM
- * and dequant entry points allocate nothing, so they may be captured in a HIP
- * graph.
+ * Ownership and streams: the library keeps no caller pointer after a call
+ * returns.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and is asynchronous: buffers must stay valid until that work
+ * completes, and a device-side fault surfaces at the caller's next
+ * synchronisation.  The library's own device memory: a split-K workspace per
+ * (device, stream), allocated (hipMalloc, zeroed on the stream) by the first
+ * decode call on that stream whose launch splits K, grown when a later call
+ * needs more (after synchronising that stream), and freed by gptq_release;
+ * gptq_quantize uses a stream-ordered temporary freed on the same stream.
+ * Calls on one stream may be captured in a HIP graph: a capture never
+ * allocates (a split-K call captured before its stream has a workspace runs
+ * unsplit instead), and the graph keeps using the workspace that existed at
+ * capture time, so gptq_release must not run while such a graph may replay.
+ * Concurrent calls on different streams are safe; two host threads enqueuing
+ * on the same stream at once are not.
  *
  * Errors: every function returns GPTQ_OK (0) or a negative gptq_status code;
  * nothing is launched when an argument check fails, and no C++ exception
@@ -83,8 +90,11 @@ typedef enum gptq_status {
  *               Mandatory: there is no default and no format detection.
  *   M, N, K     x is [M,K], out is [M,N]; N % 32 == 0 and K % 32 == 0.
  *   stream      hipStream_t as void*.
- * M <= 16 runs the decode kernel (workgroups own full-K column tiles, MFMA
- * with M padded to 16); larger M runs the MFMA prefill kernel.
+ * M <= 16 runs the decode kernel (workgroups own column tiles, MFMA with M
+ * padded to 16; for narrow N with K >= 8192 the workgroups of a tile split K
+ * and the last to finish adds the fp32 partial sums, in a fixed order, so
+ * results are deterministic either way); larger M runs the MFMA prefill
+ * kernel.
  */
 GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros,
               const void* scales, const int32_t* g_idx, int bits, int group_size,
@@ -187,8 +197,10 @@ GPTQ_API int gptq_convert_zeros_check(const int32_t* qzeros_in, const int32_t* q
 /* Static text for a gptq_status code ("unknown error" for other values). */
 GPTQ_API const char* gptq_strerror(int code);
 
-/* Releases library-owned device memory.  The library keeps none between calls,
- * so this is a no-op kept for callers that pair it with their teardown. */
+/* Releases library-owned device memory (the split-K workspaces of every device
+ * and stream), after synchronising those devices.  Later calls allocate again
+ * as needed.  Not to be called while another thread is calling the library or
+ * while a captured graph that used a workspace may still replay. */
 GPTQ_API void gptq_release(void);
 
 /* Library ABI version: 1. */

@@ -267,5 +267,5 @@ def convert_zeros(qzeros, bits: int, N: int, to_v2: bool, out=None, lossy_count=
 
 
 def release():
-    """Release library-owned device memory (none is kept between calls)."""
+    """Release library-owned device memory (the split-K workspaces), after synchronising the devices."""
     library().gptq_release()

@@ -21,6 +21,9 @@ from .gptq_ref import (  # noqa: F401
     convert_zeros_v1_to_v2,
     convert_zeros_v2_to_v1,
     convert_zeros_packed,
+    repack_tiled,
+    unrepack_tiled,
+    TILE_COLS,
     pack_fields,
     unpack_fields,
     pack_along_k,

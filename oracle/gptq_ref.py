@@ -212,6 +212,32 @@ def convert_zeros_packed(qzeros: np.ndarray, bits: int, N: int, to_v2: bool):
     return pack_along_n(conv, bits), lossy
 
 
+TILE_COLS = 16   # columns of one tile of the tiled qweight layout
+
+
+def repack_tiled(qweight: np.ndarray, bits: int) -> np.ndarray:
+    """Checkpoint qweight [K*b/32, N] -> the tiled layout, int32 [N/16, K/32, b, 16].
+
+    Word (t, c, r, j) is packed row c*b + r of column 16*t + j: each 16-column
+    tile holds, chunk after chunk (32 rows of K), the b packed rows of that
+    chunk, 16 words each.  A pure permutation of words: the bits inside a word
+    are untouched.  (An offline re-layout in the spirit of the page "Weight-only
+    INT4 quantization: GPTQ, AWQ and the Marlin kernel", section 6.1; the
+    concrete order is this library's own, so the pages fix no expected value.)"""
+    w = np.ascontiguousarray(qweight)
+    R, N = w.shape
+    if R % bits != 0 or N % TILE_COLS != 0:
+        raise ValueError("qweight must be [K*b/32, N] with N % 16 == 0")
+    C = R // bits
+    return np.ascontiguousarray(w.reshape(C, bits, N // TILE_COLS, TILE_COLS).transpose(2, 0, 1, 3))
+
+
+def unrepack_tiled(tiled: np.ndarray, bits: int, K: int, N: int) -> np.ndarray:
+    """Inverse of repack_tiled: the tiled layout -> checkpoint qweight [K*b/32, N]."""
+    t = np.asarray(tiled).reshape(N // TILE_COLS, K // 32, bits, TILE_COLS)
+    return np.ascontiguousarray(t.transpose(1, 2, 0, 3).reshape(K // 32 * bits, N))
+
+
 def dequant_ref(qweight: np.ndarray, qzeros: np.ndarray, scales: np.ndarray,
                 g_idx: Optional[np.ndarray], bits: int, group_size: int, is_v2: bool,
                 K: int, N: int, cols: Optional[np.ndarray] = None) -> np.ndarray:

@@ -278,6 +278,22 @@ def test_convert_zeros_packed_keeps_dequant(bits):
     assert np.array_equal(back, lay.qzeros)
 
 
+@pytest.mark.parametrize("bits", BITS)
+def test_repack_tiled_index_map(bits):
+    """Tiled layout against its element-wise definition, written as loops:
+    word (t, c, r, j) = qweight[c*b + r, 16 t + j]; and the inverse."""
+    K, N = 96, 48
+    qw = random_words(np.random.default_rng(bits), (K * bits // 32, N))
+    tiled = oracle.repack_tiled(qw, bits)
+    assert tiled.shape == (N // 16, K // 32, bits, 16) and tiled.dtype == np.int32
+    for t in range(N // 16):
+        for c in range(K // 32):
+            for r in range(bits):
+                for j in range(16):
+                    assert tiled[t, c, r, j] == qw[c * bits + r, 16 * t + j]
+    assert np.array_equal(oracle.unrepack_tiled(tiled.ravel(), bits, K, N), qw)
+
+
 # ---------------------------------------------------------------- dequant, brute force
 def dequant_bruteforce(qweight, qzeros, scales, g_idx, bits, gs, is_v2, K, N):
     cols = [bigint_fields(qweight[:, n], bits, K) for n in range(N)]

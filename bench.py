@@ -5,9 +5,11 @@ Metric: "GPTQ W4A16 GEMM: weight GB/s at M=1 and TFLOP/s at M=2048, % of
 roofline".  A step is one decode pass over the four Llama-7B-shaped layers
 (qkv 4096->12288, o_proj 4096->4096, gate_up 4096->22016, down 11008->4096) at
 M=1, 4-bit g128 symmetric GPTQv1, synthetic seeded weights quantized on the
-GPU by the library's own quantizer.  `value` = packed weight bytes (qweight +
-qzeros + scales) per step / step time.  Distinct weight copies (>= 1 GB in
-total) are rotated so the 256 MB Infinity Cache cannot serve them.
+GPU by the library's own quantizer, qweight then re-laid out once into the
+tiled layout (gptq_repack_tiled, untimed).  `value` = packed weight bytes
+(qweight + qzeros + scales) per step / step time.  Distinct weight copies
+(>= 1 GB in total) are rotated so the 256 MB Infinity Cache cannot serve them.
+The same step on the checkpoint qweight layout is reported beside it.
 
 The JSON line also carries:
   roofline      the decode kernel: algorithmic bytes per launch (weights + x +
@@ -61,6 +63,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-checkpoint-layout", action="store_true",
+                   help="skip the decode step on the checkpoint qweight layout (reported beside the tiled one)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-cols", type=int, default=12288,
                    help="columns of the qkv layer the CPU oracle processes (default: all)")
@@ -98,25 +102,28 @@ def layer_bytes(K, N, bits, gs):
     return K * bits // 8 * N + G * N * bits // 8 + G * N * 2   # qweight + qzeros + scales
 
 
-def make_layer(torch, gq, wl, layer, M, dev):
+def make_layer(torch, gq, wl, layer, M, dev, tiled=False):
     from workload import draw_workload_layer
     d = draw_workload_layer(wl, layer, M, seed=0)
     w = torch.from_numpy(d.W).to(dev)
     gi = None if d.g_idx is None else torch.from_numpy(d.g_idx).to(dev)
     qw, qz, sc = gq.quantize(w, gi, wl.bits, wl.group_size, wl.sym, wl.is_v2)
     del w
+    if tiled:                      # one-time re-layout at load (not timed)
+        qw = gq.repack_tiled(qw, wl.bits)
     x = torch.from_numpy(d.x).to(dev)
     return dict(qweight=qw, qzeros=qz, scales=sc, g_idx=gi, x=x, K=layer.K, N=layer.N)
 
 
-def bench_decode(torch, gq, args, dev):
+def bench_decode(torch, gq, args, dev, tiled):
     """Decode step timing.  Launches are captured in HIP graphs so the Python
     binding's per-call overhead stays out of the timed region: one graph holds
     R steps (R rotated weight copies x 4 layers); per-layer graphs hold R launches
-    of one layer and give the kernel's mean launch time."""
+    of one layer and give the kernel's mean launch time.  `tiled`: qweight in
+    the tiled layout (repacked once at load), else the checkpoint layout."""
     from workload import WORKLOADS
     wl = WORKLOADS["llama7b_decode_w4g128"]
-    base = [make_layer(torch, gq, wl, l, 1, dev) for l in wl.layers]
+    base = [make_layer(torch, gq, wl, l, 1, dev, tiled) for l in wl.layers]
     wbytes = sum(layer_bytes(L["K"], L["N"], wl.bits, wl.group_size) for L in base)
     copies = max(1, -(-ROTATE_BYTES // wbytes))
     sets = [base] + [[{**L, "qweight": L["qweight"].clone(), "qzeros": L["qzeros"].clone(),
@@ -284,7 +291,7 @@ def pmc_driver(torch, gq, dev):
     from workload import WORKLOADS
     wl = WORKLOADS["llama7b_decode_w4g128"]
     for layer in wl.layers:
-        L = make_layer(torch, gq, wl, layer, 1, dev)
+        L = make_layer(torch, gq, wl, layer, 1, dev, tiled=True)
         out = torch.empty((1, layer.N), dtype=torch.float16, device=dev)
         copies = [(L["qweight"].clone(), L["qzeros"].clone(), L["scales"].clone()) for _ in range(3)]
         torch.cuda.synchronize()
@@ -344,7 +351,7 @@ def summarize_pmc(fetch_csv, write_csv):
            "layers": layers}
     lines = [
         "# HBM traffic per launch of the decode kernel, Llama-7B-shaped decode layers",
-        "# (M=1, 4-bit, group 128, symmetric, GPTQv1), one MI355X.",
+        "# (M=1, 4-bit, group 128, symmetric, GPTQv1, qweight in the tiled layout), one MI355X.",
         "# Commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
         "#   rocprofv3 --pmc FETCH_SIZE -d D/fetch -o run -f csv -- python3 R/bench.py --pmc-driver",
         "#   rocprofv3 --pmc WRITE_SIZE -d D/write -o run -f csv -- python3 R/bench.py --pmc-driver",
@@ -385,9 +392,17 @@ def main():
         pmc_driver(torch, gq, dev)
         return
 
-    dec = bench_decode(torch, gq, args, dev)
-    print(f"# decode: {dec['ms_per_step'] * 1e3:.2f} us/step, layers: {dec['layers']}", file=sys.stderr, flush=True)
+    dec = bench_decode(torch, gq, args, dev, tiled=True)
+    print(f"# decode (tiled): {dec['ms_per_step'] * 1e3:.2f} us/step, layers: {dec['layers']}", file=sys.stderr,
+          flush=True)
     del dec["base"]
+    torch.cuda.empty_cache()
+    dec_ck = None
+    if not args.no_checkpoint_layout:
+        dec_ck = bench_decode(torch, gq, args, dev, tiled=False)
+        print(f"# decode (checkpoint layout): {dec_ck['ms_per_step'] * 1e3:.2f} us/step, layers: {dec_ck['layers']}",
+              file=sys.stderr, flush=True)
+        del dec_ck["base"]
     torch.cuda.empty_cache()
     ceiling = copy_ceiling(torch, dev)
     prefill = None if args.no_prefill else bench_prefill(torch, gq, args, dev)
@@ -420,13 +435,19 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, min/max quantized on the GPU; N(0,1) fp16 x)",
         "config": {"workload": wl.name, "layers": [f"{l.name} {l.K}->{l.N}" for l in wl.layers], "M": 1,
                    "bits": wl.bits, "group_size": wl.group_size, "sym": wl.sym, "format": "v2" if wl.is_v2 else "v1",
-                   "weight_bytes_per_step": dec["wbytes"], "rotated_copies": dec["copies"]},
+                   "weight_bytes_per_step": dec["wbytes"], "rotated_copies": dec["copies"],
+                   "qweight_layout": "tiled [N/16][K/32][bits][16], made once at load by gptq_repack_tiled (untimed)"},
         "roofline": {"bound": "hbm", "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes,
                      "kernel": "gptq::decode_kernel, one instantiation per layer (per_layer[].kernel); achieved = "
                                "mean algorithmic bytes per launch / mean launch time over the 4 layers; traffic = "
                                "mean HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "mean_launch_us": round(dec["mean_launch_us"], 3), "per_layer": dec["layers"]},
+        "checkpoint_layout": None if dec_ck is None else {
+            "value": round(dec_ck["wbytes"] / (dec_ck["ms_per_step"] * 1e-3) / 1e9, 1),
+            "ms_per_step": round(dec_ck["ms_per_step"], 5), "achieved": round(dec_ck["achieved"], 1),
+            "frac": round(dec_ck["achieved"] / HBM_PEAK_GBPS, 4), "mean_launch_us": round(dec_ck["mean_launch_us"], 3),
+            "per_layer": dec_ck["layers"]},
         "copy_GBps": round(ceiling, 1),
         "prefill": prefill,
         "cpu_baseline": cpu,

@@ -194,6 +194,43 @@ GPTQ_API int gptq_convert_zeros(const int32_t* qzeros_in, int32_t* qzeros_out, i
 GPTQ_API int gptq_convert_zeros_check(const int32_t* qzeros_in, const int32_t* qzeros_out, int bits, int64_t G,
                                       int64_t N, int to_v2, const int32_t* lossy_count);
 
+/*
+ * Tiled qweight layout: the same words as the checkpoint layout, reordered so
+ * that each 16-column tile is one contiguous run (an offline re-layout in the
+ * spirit of the page "Weight-only INT4 quantization: GPTQ, AWQ and the Marlin
+ * kernel", section 6.1; the order is this library's own):
+ *   qweight_tiled int32 [N/16][K/32][bits][16],
+ *   qweight_tiled[t][c][r][j] = qweight[c*bits + r][16*t + j].
+ * The decode kernel then streams each workgroup's weights from one contiguous
+ * region instead of 64-256-byte pieces of rows N*4 bytes apart (measured on
+ * MI355X: 5-11% less time per Llama-7B-shaped decode layer at M = 1).
+ * qzeros, scales and g_idx are unchanged.
+ *
+ * gptq_repack_tiled / gptq_unrepack_tiled convert between the layouts on
+ * `stream` (one kernel, a pure word permutation).  Same N, K, bits rules as
+ * gptq_gemm; both buffers 16-byte aligned, K*bits/32*N int32 words each,
+ * and they must not overlap (GPTQ_ERR_BAD_ARG, also for in == out).
+ */
+GPTQ_API int gptq_repack_tiled(const int32_t* qweight, int32_t* qweight_tiled, int bits, int64_t N, int64_t K,
+                               void* stream);
+GPTQ_API int gptq_unrepack_tiled(const int32_t* qweight_tiled, int32_t* qweight, int bits, int64_t N, int64_t K,
+                                 void* stream);
+
+/* gptq_gemm / gptq_gemm_ex / gptq_gemm_describe with qweight in the tiled
+ * layout: same arguments, results and error codes (decode workgroups then
+ * own 16-column tiles). */
+GPTQ_API int gptq_gemm_tiled(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros,
+                             const void* scales, const int32_t* g_idx, int bits, int group_size, int is_v2,
+                             int64_t M, int64_t N, int64_t K, void* out, void* stream);
+GPTQ_API int gptq_gemm_tiled_ex(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros,
+                                const void* scales, const int32_t* g_idx, int bits, int group_size, int is_v2,
+                                int64_t M, int64_t N, int64_t K, void* out, void* stream, int path,
+                                int decode_waves);
+GPTQ_API int gptq_gemm_tiled_describe(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros,
+                                      const void* scales, const int32_t* g_idx, int bits, int group_size,
+                                      int is_v2, int64_t M, int64_t N, int64_t K, const void* out, int path,
+                                      int decode_waves, char* buf, int64_t buflen);
+
 /* Static text for a gptq_status code ("unknown error" for other values). */
 GPTQ_API const char* gptq_strerror(int code);
 

@@ -30,6 +30,8 @@ def test_header_declares_api():
     names = declared_functions()
     for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check", "gptq_gemm_ex_check",
               "gptq_gemm_describe", "gptq_dequant_check", "gptq_convert_zeros", "gptq_convert_zeros_check",
+              "gptq_repack_tiled", "gptq_unrepack_tiled", "gptq_gemm_tiled", "gptq_gemm_tiled_ex",
+              "gptq_gemm_tiled_describe",
               "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
     assert declared_status() == gq.STATUS
@@ -122,6 +124,31 @@ def test_convert_zeros_check_codes():
     assert ck(o=QZ + 4) == -9                     # partial overlap
     assert ck(i=QZ + 2) == -5 and ck(c=GI + 2) == -5
     assert ck(b=3, N=32, G=1) == 0
+
+
+def test_repack_argument_codes():
+    """Bad repack arguments return before any launch (safe without a GPU)."""
+    lib = gq.library()
+    for fn in (lib.gptq_repack_tiled, lib.gptq_unrepack_tiled):
+        assert fn(None, OUT, 4, 4096, 4096, None) == -1
+        assert fn(QW, None, 4, 4096, 4096, None) == -1
+        assert fn(QW, OUT, 5, 4096, 4096, None) == -2
+        assert fn(QW, OUT, 4, 48, 4096, None) == -3
+        assert fn(QW, OUT, 4, 4096, 4112, None) == -3
+        assert fn(QW + 4, OUT, 4, 4096, 4096, None) == -5
+        assert fn(QW, QW, 4, 4096, 4096, None) == -9          # in place
+        assert fn(QW, QW + 16, 4, 64, 64, None) == -9         # overlap
+
+
+def test_tiled_describe_uses_16_column_tiles():
+    lib = gq.library()
+    buf = ctypes.create_string_buffer(256)
+    for (bits, gs, M, K, N) in ((4, 128, 1, 4096, 12288), (4, 128, 1, 4096, 22016), (2, 64, 16, 4096, 12288),
+                                (3, 128, 16, 5120, 13824), (8, 128, 4, 4096, 4096)):
+        assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, bits, gs, 1, M, N, K, OUT, 0, 0, buf, 256) == 0
+        assert buf.value.decode().startswith(f"gptq::decode_kernel<{bits}, false, {1 if M == 1 else 4}, 1, "), buf.value
+    assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, 4, 128, 1, 2048, 8192, 8192, OUT, 0, 0, buf, 256) == 0
+    assert buf.value.decode().startswith("gptq::prefill_kernel<4, false>")
 
 
 def test_invalid_calls_return_before_any_launch():

@@ -237,6 +237,63 @@ def test_decode_split_k_other_stream_and_graph(dev):
         assert_close(out, y0.float().cpu().numpy().astype(np.float64), "graph replay")
 
 
+# ------------------------------------------------------------------ tiled qweight layout
+@pytest.mark.parametrize("bits", BITS)
+def test_repack_tiled_bit_exact(dev, bits):
+    """gptq_repack_tiled reproduces the oracle's word permutation exactly and
+    gptq_unrepack_tiled inverts it."""
+    for K, N in ((96, 32), (4096, 544), (11008, 64)):
+        qw = random_words(np.random.default_rng(K + N + bits), (K * bits // 32, N))
+        t = torch.from_numpy(qw).to(dev)
+        tiled = gq.repack_tiled(t, bits)
+        assert np.array_equal(tiled.cpu().numpy(), oracle.repack_tiled(qw, bits)), (K, N)
+        assert torch.equal(gq.unrepack_tiled(tiled, bits), t), (K, N)
+
+
+def upload_tiled(L, dev):
+    """The layer with qweight in the tiled layout, permuted by the oracle."""
+    qw, qz, sc, gi = upload(L, dev)
+    return torch.from_numpy(oracle.repack_tiled(L.qweight, L.bits)).to(dev), qz, sc, gi
+
+
+@pytest.mark.parametrize("bits,act,gs", list(itertools.product(BITS, (False, True), (32, 128))))
+def test_gemm_tiled_small_grid(dev, bits, act, gs):
+    """GEMM on the tiled layout: oracle parity on every path; the prefill
+    result equals the checkpoint layout's bit for bit (same kernel, same
+    order, only the weight addresses differ)."""
+    K, N = 512, 160
+    d, L = quantized(K, N, 40, bits, gs, False, True, act, seed=bits * 7 + gs)
+    qw, qz, sc, gi = upload(L, dev)
+    qt = upload_tiled(L, dev)[0]
+    xt = torch.from_numpy(d.x).to(dev)
+    for M in (1, 3, 16, 17, 40):
+        ref = oracle.gptq_gemm_ref(d.x[:M], L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, True, K, N)
+        x = xt[:M].contiguous()
+        for p in [gq.PATH_AUTO, gq.PATH_PREFILL] + ([gq.PATH_DECODE] if M <= 16 else []):
+            y = gq.gemm(x, qt, qz, sc, gi, bits, gs, True, path=p)
+            assert_close(y, ref, f"tiled M={M} path={p}")
+        yt = gq.gemm(x, qt, qz, sc, gi, bits, gs, True, path=gq.PATH_PREFILL)
+        yc = gq.gemm(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_PREFILL)
+        assert torch.equal(yt.view(torch.int16), yc.view(torch.int16)), f"M={M}"
+
+
+@pytest.mark.parametrize("bits,gs,M,K,N,act", [(4, 32, 7, 96, 32, False), (3, 96, 5, 288, 224, False),
+                                               (2, 16, 2, 256, 64, False), (4, 128, 1, 8192, 512, False),
+                                               (8, 128, 7, 11008, 1024, True), (4, 128, 1, 4096, 4096, False),
+                                               (2, 64, 16, 4096, 2048, False), (3, 128, 16, 5120, 1024, True)])
+def test_gemm_tiled_shapes(dev, bits, gs, M, K, N, act):
+    """Tiled layout at ragged, per-element, split-K and full-width shapes
+    (sampled columns against the oracle)."""
+    d, L = quantized(K, N, M, bits, gs, False, True, act, seed=K + N + gs)
+    qt, qz, sc, gi = upload_tiled(L, dev)
+    x = torch.from_numpy(d.x).to(dev)
+    cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 96)), [N - 1]]))
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, True, K, N, cols=cols)
+    desc = gq.describe(x, qt, qz, sc, gi, bits, gs, True, path=gq.PATH_DECODE)
+    y = gq.gemm(x, qt, qz, sc, gi, bits, gs, True, path=gq.PATH_DECODE)
+    assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, desc)
+
+
 def test_gemm_closed_forms(dev):
     """One-hot rows of x pick rows of W^ (exact up to fp16 output rounding,
     which is the identity for fp16 inputs); x = 0 gives 0."""

@@ -15,7 +15,7 @@ import os
 import threading
 from typing import Optional
 
-__all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "release", "library", "library_path", "GptqError",
+__all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "repack_tiled", "unrepack_tiled", "release", "library", "library_path", "GptqError",
            "STATUS", "PATH_AUTO", "PATH_DECODE", "PATH_PREFILL"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,17 @@ def library() -> ctypes.CDLL:
         lib.gptq_dequant_check.restype = i32
         lib.gptq_quantize.argtypes = [vp, i32p, i32, i32, i32, i32, i64, i64, i32p, i32p, vp, vp]
         lib.gptq_quantize.restype = i32
+        lib.gptq_gemm_tiled_ex.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, vp, i32, i32]
+        lib.gptq_gemm_tiled_ex.restype = i32
+        lib.gptq_gemm_tiled.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, vp]
+        lib.gptq_gemm_tiled.restype = i32
+        lib.gptq_gemm_tiled_describe.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, i32,
+                                                 i32, ctypes.c_char_p, i64]
+        lib.gptq_gemm_tiled_describe.restype = i32
+        lib.gptq_repack_tiled.argtypes = [i32p, i32p, i32, i64, i64, vp]
+        lib.gptq_repack_tiled.restype = i32
+        lib.gptq_unrepack_tiled.argtypes = [i32p, i32p, i32, i64, i64, vp]
+        lib.gptq_unrepack_tiled.restype = i32
         lib.gptq_convert_zeros.argtypes = [i32p, i32p, i32, i64, i64, i32, i32p, vp]
         lib.gptq_convert_zeros.restype = i32
         lib.gptq_convert_zeros_check.argtypes = [i32p, i32p, i32, i64, i64, i32, i32p]
@@ -119,13 +130,24 @@ def _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K=None):
     _check_tensor("scales", scales, torch.float16, dev)
     if g_idx is not None:
         _check_tensor("g_idx", g_idx, torch.int32, dev)
-    if qweight.dim() != 2 or qzeros.dim() != 2 or scales.dim() != 2:
-        raise ValueError("qweight, qzeros and scales must be 2-D")
-    N = qweight.shape[1]
-    if K is None:
-        K = qweight.shape[0] * 32 // bits
-    if qweight.shape[0] * 32 != K * bits:
-        raise ValueError(f"qweight has {qweight.shape[0]} rows, expected K*bits/32 = {K * bits / 32}")
+    if qzeros.dim() != 2 or scales.dim() != 2:
+        raise ValueError("qzeros and scales must be 2-D")
+    if qweight.dim() == 4:                 # tiled layout [N/16, K/32, bits, 16]
+        if qweight.shape[2] != bits or qweight.shape[3] != 16:
+            raise ValueError(f"tiled qweight must be [N/16, K/32, {bits}, 16], got {tuple(qweight.shape)}")
+        N = qweight.shape[0] * 16
+        if K is None:
+            K = qweight.shape[1] * 32
+        if qweight.shape[1] * 32 != K:
+            raise ValueError(f"tiled qweight covers K = {qweight.shape[1] * 32}, expected {K}")
+    elif qweight.dim() == 2:               # checkpoint layout [K*bits/32, N]
+        N = qweight.shape[1]
+        if K is None:
+            K = qweight.shape[0] * 32 // bits
+        if qweight.shape[0] * 32 != K * bits:
+            raise ValueError(f"qweight has {qweight.shape[0]} rows, expected K*bits/32 = {K * bits / 32}")
+    else:
+        raise ValueError("qweight must be 2-D (checkpoint layout) or 4-D (tiled layout)")
     if group_size <= 0 or K % group_size:
         raise ValueError("group_size must divide K")
     G = K // group_size
@@ -142,7 +164,9 @@ def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_s
          is_v2: bool, *, out=None, path: int = PATH_AUTO, decode_waves: int = 0):
     """out[M, N] (fp16) = x[M, K] (fp16) . dequant(qweight, qzeros, scales, g_idx).
 
-    Enqueued on the current HIP stream of x's device (asynchronous)."""
+    qweight is the checkpoint layout [K*bits/32, N] or, 4-D, the tiled layout
+    made by `repack_tiled`.  Enqueued on the current HIP stream of x's device
+    (asynchronous)."""
     import torch
     dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
     _check_tensor("x", x, torch.float16, dev)
@@ -158,9 +182,10 @@ def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_s
     lib = library()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        code = lib.gptq_gemm_ex(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
-                                None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
-                                int(bool(is_v2)), M, N, K, out.data_ptr(), stream, int(path), int(decode_waves))
+        fn = lib.gptq_gemm_tiled_ex if qweight.dim() == 4 else lib.gptq_gemm_ex
+        code = fn(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                  None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
+                  int(bool(is_v2)), M, N, K, out.data_ptr(), stream, int(path), int(decode_waves))
     _raise(code)
     return out
 
@@ -174,17 +199,21 @@ def describe(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, gro
     M = x.shape[0]
     out_ptr = out.data_ptr() if out is not None else x.data_ptr()
     buf = ctypes.create_string_buffer(256)
-    code = library().gptq_gemm_describe(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
-                                        None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
-                                        int(bool(is_v2)), M, N, K, out_ptr, int(path), int(decode_waves), buf, 256)
+    lib = library()
+    fn = lib.gptq_gemm_tiled_describe if qweight.dim() == 4 else lib.gptq_gemm_describe
+    code = fn(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+              None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
+              int(bool(is_v2)), M, N, K, out_ptr, int(path), int(decode_waves), buf, 256)
     _raise(code)
     return buf.value.decode()
 
 
 def dequant(qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,
             is_v2: bool, *, out=None):
-    """W^ [K, N] fp16, bit-exact dequantization of the packed weights."""
+    """W^ [K, N] fp16, bit-exact dequantization of the packed weights (checkpoint layout)."""
     import torch
+    if isinstance(qweight, torch.Tensor) and qweight.dim() == 4:
+        raise ValueError("dequant takes the checkpoint qweight layout (unrepack_tiled the tiled one)")
     dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
     if out is None:
         out = torch.empty((K, N), dtype=torch.float16, device=dev)
@@ -263,6 +292,42 @@ def convert_zeros(qzeros, bits: int, N: int, to_v2: bool, out=None, lossy_count=
         code = lib.gptq_convert_zeros(qzeros.data_ptr(), out.data_ptr(), int(bits), G, int(N), int(bool(to_v2)),
                                       None if lossy_count is None else lossy_count.data_ptr(), stream)
     _raise(code)
+    return out
+
+
+def repack_tiled(qweight, bits: int):
+    """Checkpoint qweight [K*bits/32, N] (int32, GPU) -> tiled layout [N/16, K/32, bits, 16]."""
+    import torch
+    if bits not in (2, 3, 4, 8):
+        raise ValueError("bits must be 2, 3, 4 or 8")
+    dev = qweight.device if isinstance(qweight, torch.Tensor) else None
+    _check_tensor("qweight", qweight, torch.int32, dev)
+    if qweight.dim() != 2 or (qweight.shape[0] * 32) % bits:
+        raise ValueError("qweight must be [K*bits/32, N]")
+    N, K = qweight.shape[1], qweight.shape[0] * 32 // bits
+    if N % 32 or K % 32:
+        raise ValueError("need N % 32 == 0 and K % 32 == 0")
+    out = torch.empty((N // 16, K // 32, bits, 16), dtype=torch.int32, device=dev)
+    lib = library()
+    with torch.cuda.device(dev):
+        _raise(lib.gptq_repack_tiled(qweight.data_ptr(), out.data_ptr(), int(bits), N, K,
+                                     torch.cuda.current_stream(dev).cuda_stream))
+    return out
+
+
+def unrepack_tiled(qweight_tiled, bits: int):
+    """Tiled layout [N/16, K/32, bits, 16] -> checkpoint qweight [K*bits/32, N]."""
+    import torch
+    dev = qweight_tiled.device if isinstance(qweight_tiled, torch.Tensor) else None
+    _check_tensor("qweight_tiled", qweight_tiled, torch.int32, dev)
+    if qweight_tiled.dim() != 4 or qweight_tiled.shape[2] != bits or qweight_tiled.shape[3] != 16:
+        raise ValueError(f"qweight_tiled must be [N/16, K/32, {bits}, 16]")
+    N, K = qweight_tiled.shape[0] * 16, qweight_tiled.shape[1] * 32
+    out = torch.empty((K * bits // 32, N), dtype=torch.int32, device=dev)
+    lib = library()
+    with torch.cuda.device(dev):
+        _raise(lib.gptq_unrepack_tiled(qweight_tiled.data_ptr(), out.data_ptr(), int(bits), N, K,
+                                       torch.cuda.current_stream(dev).cuda_stream))
     return out
 
 

@@ -133,10 +133,22 @@ void apply_choice(const DecodeChoice& c, int K, int G, bool per_elem, gptq::Gemm
 }
 
 bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_elem, bool allow_split,
-                     gptq::GemmArgs* a) {
+                     bool tiled, gptq::GemmArgs* a) {
   bool found = false;
   DecodeChoice best{};
+  // tiled layout, M = 1, full-width: 8 waves of 16 chunks each was within 3%
+  // of the fastest shape on every Llama-7B decode layer (MI355X sweeps), where
+  // the general rules below pick 4 waves (one round of workgroups) and lose
+  // up to 10%
+  if (tiled && M == 1 && !per_elem && waves == 0 && N / 16 >= kCUs / 2) {
+    size_t lds;
+    if (decode_candidate(bits, M, N, K, G, per_elem, 1, 8, 16, 1, &best, &lds)) {
+      apply_choice(best, K, G, per_elem, a);
+      return true;
+    }
+  }
   for (int cpl : {4, 2, 1}) {
+    if (tiled && cpl != 1) continue;                 // the tiled layout's tiles are 16 columns
     const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
     for (int ks : {1, 2, 3, 4, 6, 8}) {
       // K splits pay for their cross-workgroup reduction (about 2 us) only
@@ -167,11 +179,11 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
   return true;
 }
 
-int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_split, bool* per_elem,
+int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_split, bool tiled, bool* per_elem,
                  gptq::GemmArgs* a) {
   if ((K / G) % 32 != 0) *per_elem = true;
   for (int pe = *per_elem ? 1 : 0; pe < 2; ++pe) {
-    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, allow_split, a)) {
+    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, allow_split, tiled, a)) {
       *per_elem = pe == 1;
       return GPTQ_OK;
     }
@@ -182,8 +194,8 @@ int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_spl
 // Argument checks plus kernel choice and launch shape: pure host code.
 int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-              const void* out, int path, int decode_waves, gptq::GemmArgs* a, bool* use_decode, bool* per_elem,
-              bool allow_split = true) {
+              const void* out, int path, int decode_waves, bool tiled, gptq::GemmArgs* a, bool* use_decode,
+              bool* per_elem, bool allow_split = true) {
   if (path < 0 || path > 2 || decode_waves < 0 || decode_waves > 16) return GPTQ_ERR_BAD_ARG;
   int rc = check_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out);
   if (rc != GPTQ_OK) return rc;
@@ -203,11 +215,12 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
   a->zero_offset = is_v2 ? 0 : 1;
   a->chunks = (int)(K / 32);
   a->zrow_words = N * bits / 32;
+  a->wtiled = tiled ? 1 : 0;
   *use_decode = (path == 1) || (path == 0 && M <= 16);
   if (M == 0) return GPTQ_OK;
   if (*use_decode) {
     *per_elem = (g_idx != nullptr) || (group_size % 32 != 0);
-    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, allow_split, per_elem, a);
+    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, allow_split, tiled, per_elem, a);
     if (rc2 != kNoDecodePlan) return rc2;
     if (path == 1) return GPTQ_ERR_BAD_ARG;         // forced decode, but no launch shape fits
     *use_decode = false;                             // very many groups: the prefill kernel
@@ -276,18 +289,18 @@ bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, floa
 
 int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-              void* out, void* stream_ptr, int path, int decode_waves) {
+              void* out, void* stream_ptr, int path, int decode_waves, bool tiled) {
   gptq::GemmArgs a;
   bool use_decode = false, per_elem = false;
   const int rc = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
-                           decode_waves, &a, &use_decode, &per_elem);
+                           decode_waves, tiled, &a, &use_decode, &per_elem);
   if (rc != GPTQ_OK || M == 0) return rc;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   if (use_decode && a.ks > 1 &&
       !split_workspace(stream, (size_t)a.ks * a.M * a.N * 4, (size_t)a.tiles * 4, &a.ws, &a.cnt)) {
     // no workspace (first use under stream capture, or out of memory): one split
     const int rc2 = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
-                              decode_waves, &a, &use_decode, &per_elem, false);
+                              decode_waves, tiled, &a, &use_decode, &per_elem, false);
     if (rc2 != GPTQ_OK) return rc2;
   }
   const hipError_t err = use_decode ? gptq::launch_decode(bits, per_elem, a, stream)
@@ -304,7 +317,7 @@ int gptq_gemm_check(const void* x, const int32_t* qweight, const int32_t* qzeros
                     const void* out) {
   gptq::GemmArgs a;
   bool use_decode = false, per_elem = false;
-  return plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, 0, 0, &a,
+  return plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, 0, 0, false, &a,
                    &use_decode, &per_elem);
 }
 
@@ -314,18 +327,21 @@ int gptq_gemm_ex_check(const void* x, const int32_t* qweight, const int32_t* qze
   gptq::GemmArgs a;
   bool use_decode = false, per_elem = false;
   return plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path, decode_waves,
-                   &a, &use_decode, &per_elem);
+                   false, &a, &use_decode, &per_elem);
 }
 
-int gptq_gemm_describe(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
-                       const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-                       const void* out, int path, int decode_waves, char* buf, int64_t buflen) {
+}  // extern "C"
+
+namespace {
+int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                  const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                  const void* out, int path, int decode_waves, bool tiled, char* buf, int64_t buflen) {
   if (!buf || buflen <= 0) return GPTQ_ERR_NULL_PTR;
   buf[0] = '\0';
   gptq::GemmArgs a;
   bool use_decode = false, per_elem = false;
   const int rc = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
-                           decode_waves, &a, &use_decode, &per_elem);
+                           decode_waves, tiled, &a, &use_decode, &per_elem);
   if (rc != GPTQ_OK) return rc;
   const char* pe = per_elem ? "true" : "false";
   if (M == 0) {
@@ -339,6 +355,24 @@ int gptq_gemm_describe(const void* x, const int32_t* qweight, const int32_t* qze
                   a.tiles_m);
   }
   return GPTQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int gptq_gemm_describe(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                       const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                       const void* out, int path, int decode_waves, char* buf, int64_t buflen) {
+  return describe_impl(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
+                       decode_waves, false, buf, buflen);
+}
+
+int gptq_gemm_tiled_describe(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros,
+                             const void* scales, const int32_t* g_idx, int bits, int group_size, int is_v2,
+                             int64_t M, int64_t N, int64_t K, const void* out, int path, int decode_waves, char* buf,
+                             int64_t buflen) {
+  return describe_impl(x, qweight_tiled, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
+                       decode_waves, true, buf, buflen);
 }
 
 int gptq_dequant_check(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,
@@ -355,12 +389,57 @@ int gptq_gemm_ex(const void* x, const int32_t* qweight, const int32_t* qzeros, c
                  void* out, void* stream, int path, int decode_waves) {
   try {
     return gemm_impl(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, stream, path,
-                     decode_waves);
+                     decode_waves, false);
   } catch (const std::bad_alloc&) {
     return GPTQ_ERR_NO_MEM;
   } catch (...) {
     return GPTQ_ERR_DEVICE;
   }
+}
+
+int gptq_gemm_tiled_ex(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros, const void* scales,
+                       const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                       void* out, void* stream, int path, int decode_waves) {
+  try {
+    return gemm_impl(x, qweight_tiled, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, stream, path,
+                     decode_waves, true);
+  } catch (const std::bad_alloc&) {
+    return GPTQ_ERR_NO_MEM;
+  } catch (...) {
+    return GPTQ_ERR_DEVICE;
+  }
+}
+
+int gptq_gemm_tiled(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros, const void* scales,
+                    const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                    void* out, void* stream) {
+  return gptq_gemm_tiled_ex(x, qweight_tiled, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, stream,
+                            0, 0);
+}
+
+namespace {
+int repack_impl(const int32_t* in, int32_t* out, int bits, int64_t N, int64_t K, int to_tiled, void* stream) {
+  if (!in || !out) return GPTQ_ERR_NULL_PTR;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_BAD_BITS;
+  if (N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return GPTQ_ERR_BAD_SHAPE;
+  if (N > ((int64_t)1 << 20) || K > ((int64_t)1 << 20) || N * K >= kMaxElems) return GPTQ_ERR_BAD_SHAPE;
+  if (!aligned(in, 16) || !aligned(out, 16)) return GPTQ_ERR_MISALIGNED;
+  const int64_t bytes = K / 32 * bits * N * 4;
+  const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out;
+  if (a < b + bytes && b < a + bytes) return GPTQ_ERR_BAD_ARG;          // no overlap, not even in place
+  const hipError_t err = gptq::launch_repack(in, out, bits, N, K, to_tiled, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
+}
+}  // namespace
+
+int gptq_repack_tiled(const int32_t* qweight, int32_t* qweight_tiled, int bits, int64_t N, int64_t K,
+                      void* stream) {
+  return repack_impl(qweight, qweight_tiled, bits, N, K, 1, stream);
+}
+
+int gptq_unrepack_tiled(const int32_t* qweight_tiled, int32_t* qweight, int bits, int64_t N, int64_t K,
+                        void* stream) {
+  return repack_impl(qweight_tiled, qweight, bits, N, K, 0, stream);
 }
 
 int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,

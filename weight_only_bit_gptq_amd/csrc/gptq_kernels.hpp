@@ -40,6 +40,10 @@ struct GemmArgs {
   int ks, cks;
   float* ws;
   uint32_t* cnt;
+  // qweight layout: 0 = checkpoint [K*b/32, N]; 1 = tiled [N/16][K/32][b][16]
+  // (16-column tiles, each chunk's b packed rows contiguous; decode then uses
+  // 16-column workgroup tiles)
+  int wtiled;
   // prefill launch shape
   int tiles_m, tiles_n;
 };
@@ -91,6 +95,10 @@ hipError_t launch_prefill(int bits, bool per_elem, const GemmArgs& a, hipStream_
 // Min/max quantize + pack (fp32 W -> qweight, qzeros, scales).
 hipError_t launch_quantize(const float* w, const int32_t* g_idx, int bits, int group_size, int sym, int is_v2,
                            int N, int K, int32_t* qweight, int32_t* qzeros, void* scales, hipStream_t stream);
+
+// qweight checkpoint layout <-> tiled layout (to_tiled = 1: forward).
+hipError_t launch_repack(const int32_t* in, int32_t* out, int bits, int64_t N, int64_t K, int to_tiled,
+                         hipStream_t stream);
 
 // GPTQv1 <-> GPTQv2 stored zero conversion of a packed qzeros [G, N*b/32].
 hipError_t launch_convert_zeros(const int32_t* in, int32_t* out, int bits, int64_t G, int64_t N, int to_v2,

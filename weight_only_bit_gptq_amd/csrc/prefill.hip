@@ -115,18 +115,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
   constexpr int NSR = PER_ELEM ? 1 : NST;
   u32x2_t w0[NSR][4], w1[NSR][L == 2 ? 4 : 1];
   // byte offsets of the lane's words for the 4 steps of tile 0; a tile is
-  // BK * BITS / 32 packed rows further on
-  const uint32_t tile_bytes = (uint32_t)(BK / 32 * BITS) * (uint32_t)a.N * 4u;
+  // BK * BITS / 32 packed rows further on.  A packed row is N * 4 bytes in
+  // the checkpoint layout; in the tiled one it is 64 bytes (16 columns) and
+  // column n sits in tile n / 16, which starts at (n / 16) * chunks * BITS * 64.
+  const uint32_t wrow = a.wtiled ? 64u : (uint32_t)a.N * 4u;
+  const uint32_t wcol = a.wtiled ? (uint32_t)(nc >> 4) * (uint32_t)a.chunks * (uint32_t)BITS * 64u +
+                                       (uint32_t)(nc & 15) * 4u
+                                 : (uint32_t)nc * 4u;
+  const uint32_t tile_bytes = (uint32_t)(BK / 32 * BITS) * wrow;
   uint32_t woff0[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int c = (16 * s) >> 5, kb = 2 * (s & 1) + kb2;
-    woff0[s] = ((uint32_t)block_row0<BITS>(c, kb) * (uint32_t)a.N + (uint32_t)nc) * 4u;
+    woff0[s] = (uint32_t)block_row0<BITS>(c, kb) * wrow + wcol;
   }
   // second word of a two-word block: (row1 - row0) rows further on
   auto woff1 = [&](int s) __attribute__((always_inline)) {
     const int c = (16 * s) >> 5, kb = 2 * (s & 1) + kb2;
-    return woff0[s] + (uint32_t)(block_row1<BITS>(c, kb) - block_row0<BITS>(c, kb)) * (uint32_t)a.N * 4u;
+    return woff0[s] + (uint32_t)(block_row1<BITS>(c, kb) - block_row0<BITS>(c, kb)) * wrow;
   };
   // the tile's group parameters (fast path: one group per k tile) travel with
   // its words, so waiting for a tile never waits for a newer load

@@ -270,4 +270,33 @@ hipError_t launch_convert_zeros(const int32_t* in, int32_t* out, int bits, int64
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// qweight re-layout.  Checkpoint layout: int32 [K*b/32, N] (packed row r,
+// column n).  Tiled layout: int32 [N/16][K/32][b][16]: word (t, c, r, j) is
+// packed row c*b + r of column 16 t + j, so a 16-column tile's words are one
+// contiguous run, chunk (32 rows of K) after chunk.  Words move unchanged.
+// One thread per word of the tiled array (its writes coalesce; its reads are
+// 64-byte pieces of checkpoint rows).
+__global__ void __launch_bounds__(256) repack_kernel(const int32_t* __restrict__ in, int32_t* __restrict__ out,
+                                                     int bits, int64_t N, int64_t K, int to_tiled) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;     // tiled index
+  const int64_t rows = K / 32 * bits;
+  if (i >= rows * N) return;
+  const int64_t j = i & 15;
+  const int64_t rest = i >> 4;                     // (t * (K/32) + c) * bits + r
+  const int64_t cr = rest % rows;                  // c * bits + r: the packed row
+  const int64_t t = rest / rows;
+  const int64_t src = cr * N + 16 * t + j;         // checkpoint index
+  if (to_tiled) out[i] = in[src];
+  else out[src] = in[i];
+}
+
+hipError_t launch_repack(const int32_t* in, int32_t* out, int bits, int64_t N, int64_t K, int to_tiled,
+                         hipStream_t stream) {
+  const int64_t words = K / 32 * bits * N;
+  hipLaunchKernelGGL(repack_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream, in, out, bits, N, K,
+                     to_tiled);
+  return hipGetLastError();
+}
+
 }  // namespace gptq

@@ -140,13 +140,18 @@ def test_repack_argument_codes():
         assert fn(QW, QW + 16, 4, 64, 64, None) == -9         # overlap
 
 
-def test_tiled_describe_uses_16_column_tiles():
+def test_tiled_describe_shapes():
+    """Tiled-layout plans: the M = 1 shapes picked from the layer sweeps, the
+    general rules elsewhere, the prefill kernel for large M."""
     lib = gq.library()
     buf = ctypes.create_string_buffer(256)
-    for (bits, gs, M, K, N) in ((4, 128, 1, 4096, 12288), (4, 128, 1, 4096, 22016), (2, 64, 16, 4096, 12288),
-                                (3, 128, 16, 5120, 13824), (8, 128, 4, 4096, 4096)):
+    for (bits, gs, M, K, N, want) in ((4, 128, 1, 4096, 12288, "<4, false, 1, 1, 16> grid=768 block=512"),
+                                      (4, 128, 1, 4096, 22016, "<4, false, 1, 2, 8> grid=688 block=512"),
+                                      (4, 128, 1, 11008, 4096, "<4, false, 1, 1, 16> grid=256 block=512"),
+                                      (2, 64, 16, 4096, 12288, "<2, false, 4, "),
+                                      (3, 128, 16, 5120, 13824, "<3, false, 4, ")):
         assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, bits, gs, 1, M, N, K, OUT, 0, 0, buf, 256) == 0
-        assert buf.value.decode().startswith(f"gptq::decode_kernel<{bits}, false, {1 if M == 1 else 4}, 1, "), buf.value
+        assert buf.value.decode().startswith("gptq::decode_kernel" + want), buf.value
     assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, 4, 128, 1, 2048, 8192, 8192, OUT, 0, 0, buf, 256) == 0
     assert buf.value.decode().startswith("gptq::prefill_kernel<4, false>")
 

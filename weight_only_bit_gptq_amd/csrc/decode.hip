@@ -386,15 +386,17 @@ void decode_kernel(GemmArgs a) {
 
   // ---- packed words: block kb of chunk c lives in packed rows BITS * c +
   // row0(kb) (+ row1), i.e. at the lane's offset in chunk 0 plus the
-  // wave-uniform c * BITS row strides.  A packed row of the tile is N * 4
-  // bytes apart in the checkpoint layout and 64 bytes apart in the tiled one
-  // (whose tile t starts at t * chunks * BITS * 64 bytes; 16-column tiles
-  // only).  Chunks past K re-read the last chunk: they meet zero x (and a
-  // zero table row) and add exactly nothing.
+  // wave-uniform c * BITS row strides.  A packed row is N * 4 bytes apart in
+  // the checkpoint layout and 64 bytes apart in the tiled one, where column n
+  // lies in 16-column tile n / 16 (starting at (n / 16) * chunks * BITS * 64
+  // bytes); a lane's CPL adjacent columns never cross a 16-column tile.
+  // Chunks past K re-read the last chunk: they meet zero x (and a zero table
+  // row) and add exactly nothing.
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(a.qweight), (short)0, (int)((int64_t)a.chunks * BITS * a.N * 4), 0x00020000);
   const uint32_t wrow = a.wtiled ? 64u : (uint32_t)a.N * 4u;
-  const uint32_t wcol = a.wtiled ? (uint32_t)t * (uint32_t)a.chunks * (uint32_t)BITS * 64u + (uint32_t)q * 4u
+  const uint32_t wcol = a.wtiled ? (uint32_t)(nc >> 4) * (uint32_t)a.chunks * (uint32_t)BITS * 64u +
+                                       (uint32_t)(nc & 15) * 4u
                                  : (uint32_t)nc * 4u;
   const uint32_t off0 = (uint32_t)block_row0<BITS>(0, kb) * wrow + wcol;
   const uint32_t off1 = (uint32_t)block_row1<BITS>(0, kb) * wrow + wcol;

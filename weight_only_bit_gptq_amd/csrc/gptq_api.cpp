@@ -136,19 +136,19 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
                      bool tiled, gptq::GemmArgs* a) {
   bool found = false;
   DecodeChoice best{};
-  // tiled layout, M = 1, full-width: 8 waves of 16 chunks each was within 3%
-  // of the fastest shape on every Llama-7B decode layer (MI355X sweeps), where
-  // the general rules below pick 4 waves (one round of workgroups) and lose
-  // up to 10%
+  // tiled layout, M = 1, full-width: 16-column tiles with 8 waves of 16
+  // chunks (32-column tiles with 8 waves of 8 chunks from N = 16384 on) were
+  // within 3% of the fastest shape on every Llama-7B decode layer in MI355X
+  // sweeps, where the general rules below lose up to 10%
   if (tiled && M == 1 && !per_elem && waves == 0 && N / 16 >= kCUs / 2) {
     size_t lds;
-    if (decode_candidate(bits, M, N, K, G, per_elem, 1, 8, 16, 1, &best, &lds)) {
+    const bool wide = N >= 16384;
+    if (decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, 8, wide ? 8 : 16, 1, &best, &lds)) {
       apply_choice(best, K, G, per_elem, a);
       return true;
     }
   }
   for (int cpl : {4, 2, 1}) {
-    if (tiled && cpl != 1) continue;                 // the tiled layout's tiles are 16 columns
     const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
     for (int ks : {1, 2, 3, 4, 6, 8}) {
       // K splits pay for their cross-workgroup reduction (about 2 us) only

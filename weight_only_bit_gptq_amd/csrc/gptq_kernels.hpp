@@ -41,8 +41,7 @@ struct GemmArgs {
   float* ws;
   uint32_t* cnt;
   // qweight layout: 0 = checkpoint [K*b/32, N]; 1 = tiled [N/16][K/32][b][16]
-  // (16-column tiles, each chunk's b packed rows contiguous; decode then uses
-  // 16-column workgroup tiles)
+  // (16-column tiles, each chunk's b packed rows contiguous)
   int wtiled;
   // prefill launch shape
   int tiles_m, tiles_n;

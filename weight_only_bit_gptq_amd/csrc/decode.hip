@@ -447,20 +447,47 @@ void decode_kernel(GemmArgs a) {
   const uint32_t* full_tab = reinterpret_cast<const uint32_t*>(lds + lay.tab_off);
   const int kbc = MV == 1 ? 0 : min(kb, Mp / 4 - 1);  // rows 4 kbc + v of the correction sums
 
-  // chunk u of this wave in phase p (cl = its index in the staging region,
-  // row = its group's row in the wave's table), words from register set `set`
-  auto compute_chunk = [&](int p, int u, int row, auto set_c) __attribute__((always_inline)) {
-    constexpr int set = decltype(set_c)::value;
+  // fast path: a chunk's LDS operands (A fragment, sum of x, the group row's
+  // table entries), read one chunk ahead of their use so that LDS latency
+  // overlaps the previous chunk's work
+  struct FastOps {
+    half8_t A;
+    float X[MV];
+    float s1[CPL], s2[CPL];
+  };
+  auto fast_ops = [&](int p, int u, int row) __attribute__((always_inline)) {
+    FastOps o;
     const unsigned char* base = stage_base(p);
-    const int cl = PER_ELEM ? wave * CPW + u : u;
     const _Float16* frag = reinterpret_cast<const _Float16*>(base);
     // rows >= M of A only feed rows >= M of D, which are never used
-    const half8_t A = *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + min(q, M - 1)) << 3));
+    o.A = *reinterpret_cast<const half8_t*>(frag + (((u * 4 + kb) * M + min(q, M - 1)) << 3));
+    const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + u * Mp + 4 * kbc;
+#pragma unroll
+    for (int v = 0; v < MV; ++v) o.X[v] = corr[v];
+    const float* te = reinterpret_cast<const float*>(base + lay.ptab_off) + row * TN * 2;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      o.s1[j] = te[tab_pos(CPL * q + j)];
+      o.s2[j] = te[tab_pos(CPL * q + j) + 1];
+    }
+    return o;
+  };
+
+  // chunk u of this wave in phase p (cl = its index in the staging region,
+  // row = its group's row in the wave's table), words from register set `set`;
+  // the fast path takes its LDS operands from `fo`
+  auto compute_chunk = [&](int p, int u, int row, auto set_c, const FastOps& fo) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    const unsigned char* base = stage_base(p);
     uint32_t w1j[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) w1j[j] = L == 2 ? word_of<CPL>(w1[set][L == 2 ? u : 0], j) : 0u;
 
     if constexpr (PER_ELEM) {
+      const int cl = wave * CPW + u;
+      const _Float16* frag = reinterpret_cast<const _Float16*>(base);
+      // rows >= M of A only feed rows >= M of D, which are never used
+      const half8_t A = *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + min(q, M - 1)) << 3));
       // per-row scale and zero: the block's 8 rows each carry their own group
       const uint16_t* gl = reinterpret_cast<const uint16_t*>(base + lay.gidx_off);
       typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
@@ -483,24 +510,18 @@ void decode_kernel(GemmArgs a) {
         accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), accg[j], 0, 0, 0);
       }
     } else {
-      const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + cl * Mp + 4 * kbc;
-      float X[MV];
-#pragma unroll
-      for (int v = 0; v < MV; ++v) X[v] = corr[v];
-      const float* te = reinterpret_cast<const float*>(base + lay.ptab_off) + row * TN * 2;
       floatx4_t d[CPL];
       float s1[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        s1[j] = te[tab_pos(CPL * q + j)];
-        const float s2 = te[tab_pos(CPL * q + j) + 1];
+        s1[j] = fo.s1[j];
         uint32_t pr[4];
         unpack_block<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], sel, pr, 0u);
         const u32x4_t bw = {pr[0], pr[1], pr[2], pr[3]};
-        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), floatx4_t{0.f, 0.f, 0.f, 0.f},
-                                                      0, 0, 0);
+        d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fo.A, __builtin_bit_cast(half8_t, bw),
+                                                      floatx4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int v = 0; v < MV; ++v) acc[j][v] = __builtin_fmaf(s2, X[v], acc[j][v]);
+        for (int v = 0; v < MV; ++v) acc[j][v] = __builtin_fmaf(fo.s2[j], fo.X[v], acc[j][v]);
       }
       // with one or two MFMAs per chunk the previous chunk's products are
       // folded in while this chunk's MFMAs run; four cover their own latency
@@ -528,16 +549,28 @@ void decode_kernel(GemmArgs a) {
   };
   // chunks [U0, U1) of phase p; row / rem track the group row of the next chunk
   auto compute_range = [&](int p, auto u0_c, auto u1_c, int& row, int& rem) __attribute__((always_inline)) {
+    constexpr int u0 = decltype(u0_c)::value, u1 = decltype(u1_c)::value;
+    if constexpr (PER_ELEM) {
 #pragma unroll
-    for (int u = decltype(u0_c)::value; u < decltype(u1_c)::value; ++u) {
-      compute_chunk(p, u, row, S0{});
-      // keep each chunk's LDS reads next to their use: hoisting all of them
-      // ahead of the weight waits would cost ~10 registers per chunk
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!PER_ELEM) {
+      for (int u = u0; u < u1; ++u) {
+        compute_chunk(p, u, row, S0{}, FastOps{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // the LDS operands of chunk u + 1 are read before chunk u is computed
+      // (one chunk ahead only: hoisting all of them ahead of the weight waits
+      // would cost ~10 registers per chunk)
+      FastOps cur = fast_ops(p, u0, row);
+#pragma unroll
+      for (int u = u0; u < u1; ++u) {
         const bool next = ++rem == cpg;
         row += next ? 1 : 0;
         rem = next ? 0 : rem;
+        FastOps nxt = cur;
+        if (u + 1 < u1) nxt = fast_ops(p, u + 1, row);
+        compute_chunk(p, u, row, S0{}, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        cur = nxt;
       }
     }
   };

@@ -137,13 +137,13 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
   bool found = false;
   DecodeChoice best{};
   // tiled layout, M = 1, full-width: 16-column tiles with 8 waves of 16
-  // chunks (32-column tiles with 8 waves of 8 chunks from N = 16384 on) were
-  // within 3% of the fastest shape on every Llama-7B decode layer in MI355X
+  // chunks (32-column tiles with 4 waves of 8 chunks from N = 16384 on) were
+  // the fastest or within 3% of it on every Llama-7B decode layer in MI355X
   // sweeps, where the general rules below lose up to 10%
   if (tiled && M == 1 && !per_elem && waves == 0 && N / 16 >= kCUs / 2) {
     size_t lds;
     const bool wide = N >= 16384;
-    if (decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, 8, wide ? 8 : 16, 1, &best, &lds)) {
+    if (decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, wide ? 4 : 8, wide ? 8 : 16, 1, &best, &lds)) {
       apply_choice(best, K, G, per_elem, a);
       return true;
     }

@@ -464,7 +464,9 @@ void decode_kernel(GemmArgs a) {
     const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + u * Mp + 4 * kbc;
 #pragma unroll
     for (int v = 0; v < MV; ++v) o.X[v] = corr[v];
-    const float* te = reinterpret_cast<const float*>(base + lay.ptab_off) + row * TN * 2;
+    // the group row is wave-uniform: keep its offset in a scalar register
+    const int row_bytes = __builtin_amdgcn_readfirstlane(row * TN * 8);
+    const float* te = reinterpret_cast<const float*>(base + lay.ptab_off + row_bytes);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       o.s1[j] = te[tab_pos(CPL * q + j)];
@@ -559,13 +561,17 @@ void decode_kernel(GemmArgs a) {
     } else {
       // the LDS operands of chunk u + 1 are read before chunk u is computed
       // (one chunk ahead only: hoisting all of them ahead of the weight waits
-      // would cost ~10 registers per chunk)
+      // would cost ~10 registers per chunk).  row / rem are wave-uniform.
+      row = __builtin_amdgcn_readfirstlane(row);
+      rem = __builtin_amdgcn_readfirstlane(rem);
       FastOps cur = fast_ops(p, u0, row);
 #pragma unroll
       for (int u = u0; u < u1; ++u) {
-        const bool next = ++rem == cpg;
-        row += next ? 1 : 0;
-        rem = next ? 0 : rem;
+        // inc = (rem + 1 == cpg), in integer arithmetic so that it stays in
+        // scalar registers (a compare would go through a vector select)
+        const int inc = 1 - (int)min(1u, (uint32_t)((rem + 1) ^ cpg));
+        row = __builtin_amdgcn_readfirstlane(row + inc);
+        rem = __builtin_amdgcn_readfirstlane((rem + 1) * (1 - inc));
         FastOps nxt = cur;
         if (u + 1 < u1) nxt = fast_ops(p, u + 1, row);
         compute_chunk(p, u, row, S0{}, cur);

@@ -33,6 +33,7 @@ from .gptq_ref import (  # noqa: F401
     dequant_ref,
     gemm_ref,
     gptq_gemm_ref,
+    moe_gemm_ref,
     quantize_layer,
     QuantizedLayer,
 )

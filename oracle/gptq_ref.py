@@ -274,6 +274,23 @@ def gptq_gemm_ref(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K,
                                    is_v2, K, N, cols=cols))
 
 
+def moe_gemm_ref(x, experts, offsets, bits, group_size, is_v2, K, N, cols=None) -> np.ndarray:
+    """Grouped GEMM over routed tokens: rows [offsets[e], offsets[e+1]) of x use
+    expert e's packed weights; each expert's rows go through gptq_gemm_ref.
+    `experts` is a list of (qweight, qzeros, scales, g_idx).  Rows of no expert
+    are NaN (the GPU leaves them untouched).  (MoE models quantize their
+    expert weights like dense layers: page "Weight-only INT4 quantization:
+    GPTQ, AWQ and the Marlin kernel", section 7.)"""
+    x = np.asarray(x)
+    ncols = N if cols is None else len(cols)
+    y = np.full((x.shape[0], ncols), np.nan)
+    for e, (qw, qz, sc, gi) in enumerate(experts):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            y[r0:r1] = gptq_gemm_ref(x[r0:r1], qw, qz, sc, gi, bits, group_size, is_v2, K, N, cols=cols)
+    return y
+
+
 @dataclass
 class QuantizedLayer:
     qweight: np.ndarray   # int32 [K*b/32, N]

@@ -294,6 +294,27 @@ def test_repack_tiled_index_map(bits):
     assert np.array_equal(oracle.unrepack_tiled(tiled.ravel(), bits, K, N), qw)
 
 
+def test_moe_gemm_ref_rows_match_their_expert():
+    """Each routed row equals that single row through its own expert's layer,
+    computed from the dequantized weights with an explicit per-row loop; rows
+    of no expert stay NaN."""
+    K, N, gs, bits = 64, 32, 32, 4
+    experts = []
+    for e in range(3):
+        d = draw_layer(K, N, 1, sigma=0.02, group_size=gs, seed=40 + e)
+        L = oracle.quantize_layer(d.W, bits, gs, False, True)
+        experts.append((L.qweight, L.qzeros, L.scales, None))
+    x = draw_layer(K, N, 9, sigma=0.02, group_size=gs, seed=50).x
+    offsets = [0, 4, 4, 8]                      # expert 1 has no rows; row 8 has no expert
+    y = oracle.moe_gemm_ref(x, experts, offsets, bits, gs, True, K, N)
+    for e in range(3):
+        W = oracle.dequant_ref(*experts[e][:3], None, bits, gs, True, K, N).astype(np.float64)
+        for r in range(offsets[e], offsets[e + 1]):
+            want = [sum(float(x[r, k]) * W[k, n] for k in range(K)) for n in range(N)]
+            assert np.allclose(y[r], want, rtol=0, atol=1e-12)
+    assert np.isnan(y[8]).all()
+
+
 # ---------------------------------------------------------------- dequant, brute force
 def dequant_bruteforce(qweight, qzeros, scales, g_idx, bits, gs, is_v2, K, N):
     cols = [bigint_fields(qweight[:, n], bits, K) for n in range(N)]

@@ -231,6 +231,34 @@ GPTQ_API int gptq_gemm_tiled_describe(const void* x, const int32_t* qweight_tile
                                       int is_v2, int64_t M, int64_t N, int64_t K, const void* out, int path,
                                       int decode_waves, char* buf, int64_t buflen);
 
+/*
+ * Grouped (mixture-of-experts) decode GEMM: for every expert e,
+ *   out[r, :] = x[r, :] . dequant(expert e's weights)   for r in [off[e], off[e+1])
+ * i.e. one gptq_gemm per expert over the tokens routed to it, in one launch
+ * (page "Weight-only INT4 quantization: GPTQ, AWQ and the Marlin kernel",
+ * section 7: GPTQ quantizes the expert weights of MoE models too).
+ *   x               fp16 [T, K], tokens sorted by expert (device)
+ *   qweight         int32 [E][K*bits/32][N]  (checkpoint layout per expert)
+ *   qzeros          int32 [E][G][N*bits/32],  scales fp16 [E][G][N]
+ *   g_idx           int32 [E][K] or NULL
+ *   expert_offsets  int32 [E+1] device: expert e's rows are [off[e], off[e+1]),
+ *                   nondecreasing, off[0] = 0, off[E] <= T (values are clamped
+ *                   to [0, T], so bad offsets never reach outside x / out)
+ *   max_tokens_per_expert  host bound on off[e+1] - off[e]: the launch covers
+ *                   that many rows per expert in blocks of 16; rows beyond it
+ *                   are not computed (their out rows are left as they were)
+ *   out             fp16 [T, N]; rows of no expert are left as they were.
+ * Same bits / group_size / is_v2 / N / K rules and alignment as gptq_gemm.
+ * Uses the decode kernel (blocks of up to 16 rows, MFMA with rows padded to
+ * 16), so it suits per-expert token counts of decode batches; allocates
+ * nothing; deterministic.  T == 0 or max_tokens_per_expert == 0 launches
+ * nothing.
+ */
+GPTQ_API int gptq_moe_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                           const int32_t* g_idx, const int32_t* expert_offsets, int n_experts,
+                           int max_tokens_per_expert, int bits, int group_size, int is_v2, int64_t T, int64_t N,
+                           int64_t K, void* out, void* stream);
+
 /* Static text for a gptq_status code ("unknown error" for other values). */
 GPTQ_API const char* gptq_strerror(int code);
 

@@ -31,7 +31,7 @@ def test_header_declares_api():
     for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check", "gptq_gemm_ex_check",
               "gptq_gemm_describe", "gptq_dequant_check", "gptq_convert_zeros", "gptq_convert_zeros_check",
               "gptq_repack_tiled", "gptq_unrepack_tiled", "gptq_gemm_tiled", "gptq_gemm_tiled_ex",
-              "gptq_gemm_tiled_describe",
+              "gptq_gemm_tiled_describe", "gptq_moe_gemm",
               "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
     assert declared_status() == gq.STATUS
@@ -154,6 +154,26 @@ def test_tiled_describe_shapes():
         assert buf.value.decode().startswith("gptq::decode_kernel" + want), buf.value
     assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, 4, 128, 1, 2048, 8192, 8192, OUT, 0, 0, buf, 256) == 0
     assert buf.value.decode().startswith("gptq::prefill_kernel<4, false>")
+
+
+def test_moe_argument_codes():
+    """Bad grouped-GEMM arguments return before any launch (safe without a GPU)."""
+    lib = gq.library()
+    OFF = 0x70000
+    mo = lambda x=X, qw=QW, qz=QZ, sc=SC, gi=None, off=OFF, E=8, mt=16, b=4, gs=128, v2=1, T=32, N=4096, K=4096, o=OUT: \
+        lib.gptq_moe_gemm(x, qw, qz, sc, gi, off, E, mt, b, gs, v2, T, N, K, o, None)
+    assert mo(off=None) == -1
+    assert mo(qw=None) == -1
+    assert mo(b=5) == -2
+    assert mo(N=48) == -3
+    assert mo(T=-1) == -3
+    assert mo(gs=100) == -4
+    assert mo(E=0) == -9
+    assert mo(mt=-1) == -9
+    assert mo(x=X + 8) == -5
+    assert mo(off=OFF + 2) == -5
+    assert mo(T=0, x=None, o=None) == 0               # nothing to do, nothing launched
+    assert mo(mt=0) == 0
 
 
 def test_invalid_calls_return_before_any_launch():

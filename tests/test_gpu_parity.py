@@ -294,6 +294,82 @@ def test_gemm_tiled_shapes(dev, bits, gs, M, K, N, act):
     assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, desc)
 
 
+# ------------------------------------------------------------------ grouped (MoE) decode
+def moe_problem(E, K, N, counts, bits, gs, act, seed, sym=False, is_v2=True):
+    """E experts quantized by the oracle; tokens sorted by expert, `counts[e]` rows each."""
+    experts = []
+    for e in range(E):
+        d = draw_layer(K, N, 1, sigma=0.02, group_size=gs, act_order=act, seed=seed + e)
+        experts.append(oracle.quantize_layer(d.W, bits, gs, sym, is_v2, d.g_idx))
+    T = int(sum(counts))
+    x = draw_layer(K, N, max(T, 1), sigma=0.02, group_size=gs, seed=seed + 1000).x[:T]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return experts, x, offsets
+
+
+def moe_upload(experts, x, offsets, act, dev):
+    st = lambda name: torch.from_numpy(np.ascontiguousarray(np.stack([getattr(L, name) for L in experts]))).to(dev)
+    gi = st("g_idx") if act else None
+    return (torch.from_numpy(x).to(dev), st("qweight"), st("qzeros"), st("scales"), gi,
+            torch.from_numpy(offsets).to(dev))
+
+
+@pytest.mark.parametrize("bits,gs,act", [(4, 128, False), (4, 32, False), (2, 64, False), (3, 128, True),
+                                         (8, 128, False), (4, 96, False)])
+def test_moe_gemm_parity(dev, bits, gs, act):
+    """Routed rows match the oracle expert by expert; experts with no rows,
+    with more than 16 rows (several blocks) and rows after the last expert."""
+    E, K, N = 6, 384, 160
+    counts = [3, 0, 17, 1, 40, 5]
+    experts, x, offsets = moe_problem(E, K, N, counts, bits, gs, act, seed=bits * 31 + gs)
+    xt, qw, qz, sc, gi, off = moe_upload(experts, x, offsets, act, dev)
+    T = x.shape[0]
+    xt = torch.cat([xt, torch.ones((2, K), dtype=torch.float16, device=dev)])   # 2 rows of no expert
+    out = torch.full((T + 2, N), 7.0, dtype=torch.float16, device=dev)
+    gq.moe_gemm(xt, qw, qz, sc, gi, off, max(counts), bits, gs, True, out=out)
+    ref = oracle.moe_gemm_ref(x, [(L.qweight, L.qzeros, L.scales, L.g_idx) for L in experts], offsets, bits, gs,
+                              True, K, N)
+    assert_close(out[:T], ref)
+    assert bool((out[T:] == 7.0).all())
+
+
+def test_moe_gemm_bounds(dev):
+    """max_tokens_per_expert below an expert's count leaves its extra rows
+    untouched; offsets past T are clamped to T (nothing outside x / out)."""
+    E, K, N, bits, gs = 3, 256, 96, 4, 128
+    counts = [20, 5, 9]
+    experts, x, offsets = moe_problem(E, K, N, counts, bits, gs, False, seed=9)
+    xt, qw, qz, sc, gi, off = moe_upload(experts, x, offsets, False, dev)
+    ref = oracle.moe_gemm_ref(x, [(L.qweight, L.qzeros, L.scales, None) for L in experts], offsets, bits, gs,
+                              True, K, N)
+    out = torch.full((x.shape[0], N), 7.0, dtype=torch.float16, device=dev)
+    gq.moe_gemm(xt, qw, qz, sc, None, off, 16, bits, gs, True, out=out)
+    assert_close(out[:16], ref[:16])                 # expert 0: its first 16 rows only
+    assert bool((out[16:20] == 7.0).all())
+    assert_close(out[20:], ref[20:])
+    # offsets running past T: expert 2's rows are clamped to [25, 34)
+    off2 = torch.tensor([0, 20, 25, 1000], dtype=torch.int32, device=dev)
+    out2 = torch.full((x.shape[0], N), 7.0, dtype=torch.float16, device=dev)
+    gq.moe_gemm(xt, qw, qz, sc, None, off2, 1000, bits, gs, True, out=out2)
+    assert_close(out2, ref)
+
+
+def test_moe_gemm_full_size_mixtral(dev):
+    """Mixtral-class expert FFN shape (4096 -> 14336, 8 experts, 16 tokens x
+    top-2 routing), 4-bit g128: sampled columns against the oracle."""
+    E, K, N, bits, gs = 8, 4096, 14336, 4, 128
+    rng = np.random.default_rng(5)
+    picks = np.array([rng.choice(E, size=2, replace=False) for _ in range(16)]).ravel()
+    counts = np.bincount(picks, minlength=E)
+    experts, x, offsets = moe_problem(E, K, N, counts, bits, gs, False, seed=11, sym=True, is_v2=False)
+    xt, qw, qz, sc, gi, off = moe_upload(experts, x, offsets, False, dev)
+    out = gq.moe_gemm(xt, qw, qz, sc, None, off, int(counts.max()), bits, gs, False)
+    cols = np.arange(0, N, 149)
+    ref = oracle.moe_gemm_ref(x, [(L.qweight, L.qzeros, L.scales, None) for L in experts], offsets, bits, gs,
+                              False, K, N, cols=cols)
+    assert_close(out[:, torch.from_numpy(cols).to(dev)], ref)
+
+
 def test_gemm_closed_forms(dev):
     """One-hot rows of x pick rows of W^ (exact up to fp16 output rounding,
     which is the identity for fp16 inputs); x = 0 gives 0."""

@@ -15,7 +15,7 @@ import os
 import threading
 from typing import Optional
 
-__all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "repack_tiled", "unrepack_tiled", "release", "library", "library_path", "GptqError",
+__all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "repack_tiled", "unrepack_tiled", "moe_gemm", "release", "library", "library_path", "GptqError",
            "STATUS", "PATH_AUTO", "PATH_DECODE", "PATH_PREFILL"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +78,8 @@ def library() -> ctypes.CDLL:
         lib.gptq_gemm_tiled_describe.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, i32,
                                                  i32, ctypes.c_char_p, i64]
         lib.gptq_gemm_tiled_describe.restype = i32
+        lib.gptq_moe_gemm.argtypes = [vp, i32p, i32p, vp, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, vp, vp]
+        lib.gptq_moe_gemm.restype = i32
         lib.gptq_repack_tiled.argtypes = [i32p, i32p, i32, i64, i64, vp]
         lib.gptq_repack_tiled.restype = i32
         lib.gptq_unrepack_tiled.argtypes = [i32p, i32p, i32, i64, i64, vp]
@@ -291,6 +293,46 @@ def convert_zeros(qzeros, bits: int, N: int, to_v2: bool, out=None, lossy_count=
         stream = torch.cuda.current_stream(dev).cuda_stream
         code = lib.gptq_convert_zeros(qzeros.data_ptr(), out.data_ptr(), int(bits), G, int(N), int(bool(to_v2)),
                                       None if lossy_count is None else lossy_count.data_ptr(), stream)
+    _raise(code)
+    return out
+
+
+def moe_gemm(x, qweight, qzeros, scales, g_idx: Optional[object], expert_offsets, max_tokens_per_expert: int,
+             bits: int, group_size: int, is_v2: bool, *, out=None):
+    """Grouped decode GEMM: rows [off[e], off[e+1]) of x (tokens sorted by
+    expert) times expert e's weights.  qweight [E, K*bits/32, N], qzeros
+    [E, G, N*bits/32], scales [E, G, N], g_idx [E, K] or None, expert_offsets
+    int32 [E+1] on the GPU.  Rows of no expert keep out's previous contents."""
+    import torch
+    if qweight.dim() != 3 or qzeros.dim() != 3 or scales.dim() != 3:
+        raise ValueError("qweight, qzeros, scales must be [E, ...] stacks")
+    E = qweight.shape[0]
+    dev, N, K = _weights(qweight[0], qzeros[0], scales[0], None if g_idx is None else g_idx[0], bits,
+                         group_size, is_v2)
+    for name, t in (("qweight", qweight), ("qzeros", qzeros), ("scales", scales)):
+        if t.shape[0] != E or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [E={E}, ...] stack")
+    if g_idx is not None and (tuple(g_idx.shape) != (E, K) or not g_idx.is_contiguous()):
+        raise ValueError(f"g_idx must be [{E}, {K}]")
+    _check_tensor("x", x, torch.float16, dev)
+    _check_tensor("expert_offsets", expert_offsets, torch.int32, dev)
+    if tuple(expert_offsets.shape) != (E + 1,):
+        raise ValueError(f"expert_offsets must be [{E + 1}]")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [T, {K}]")
+    T = x.shape[0]
+    if out is None:
+        out = torch.zeros((T, N), dtype=torch.float16, device=dev)
+    else:
+        _check_tensor("out", out, torch.float16, dev)
+        if tuple(out.shape) != (T, N):
+            raise ValueError(f"out must be [{T}, {N}]")
+    lib = library()
+    with torch.cuda.device(dev):
+        code = lib.gptq_moe_gemm(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                                 None if g_idx is None else g_idx.data_ptr(), expert_offsets.data_ptr(), E,
+                                 int(max_tokens_per_expert), int(bits), int(group_size), int(bool(is_v2)), T, N, K,
+                                 out.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
     _raise(code)
     return out
 

@@ -154,6 +154,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(BIT
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, PER_ELEM, CPL, CPW, MV))))
 void decode_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
+  // workgroup -> (column tile t, K split sk); consecutive units share an XCD
+  int unit = blockIdx.x;
+  if (a.n_experts > 0) {
+    // grouped decode: (expert, block of up to 16 of its rows, column tile);
+    // blocks without rows leave at once (the expert's rows are clamped to M)
+    const int per_expert = a.tiles * a.moe_blocks;
+    const int e = blockIdx.x / per_expert;
+    const int rest = blockIdx.x - e * per_expert;
+    const int b = rest / a.tiles;
+    unit = rest - b * a.tiles;
+    const int r_end = min(max(a.moe_off[e + 1], 0), a.M);
+    const int r0 = min(max(a.moe_off[e], 0), a.M) + 16 * b;
+    const int rows = min(16, r_end - r0);
+    if (rows <= 0) return;
+    a.M = rows;
+    a.x += (int64_t)r0 * a.K;
+    a.out += (int64_t)r0 * a.N;
+    a.qweight += e * a.qw_stride;
+    a.qzeros += e * a.qz_stride;
+    a.scales += e * a.sc_stride;
+    if (a.g_idx) a.g_idx += e * a.gi_stride;
+  } else {
+    const int units = a.tiles * a.ks;
+    if ((units & 7) == 0) unit = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
+  }
   constexpr int XP = decode_x_pieces_of(MV);
   constexpr int GP = (CPW + 7) / 8;                  // g_idx pieces: 8 * CPW rows <= 64 * GP pieces of 4
   constexpr int TQ = decode_table_quads(PER_ELEM, CPL, CPW);
@@ -170,10 +195,6 @@ void decode_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int kb = lane >> 4;          // 8-row block of the chunk (A and B operands)
   const int q = lane & 15;           // column slot (B) and x row (A)
-  // workgroup -> (column tile t, K split sk); consecutive units share an XCD
-  int unit = blockIdx.x;
-  const int units = a.tiles * a.ks;
-  if ((units & 7) == 0) unit = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
   const int t = unit / a.ks;
   const int sk = unit - t * a.ks;
   const int c0 = sk * a.cks;                         // first chunk of this split
@@ -182,8 +203,12 @@ void decode_kernel(GemmArgs a) {
   const int nc = n < a.N ? n : 0;                    // lanes past N read column 0 (result unused)
   const int C = min(a.chunks - c0, a.cks);          // chunks of this split (>= 1)
   const int pc = a.pc, phases = a.phases, cpg = a.cpg;
-  const DecodeLayout lay = decode_layout(M, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases);
-  const int Mp = decode_corr_rows(M);
+  // rows the LDS layout is sized for: the multi-row instantiation reads its
+  // per-chunk sums of x in groups of four rows, so it lays out at least two
+  // rows (four sums) even for a one-row block of a grouped launch
+  const int ML = MV == 1 ? 1 : max(M, 2);
+  const DecodeLayout lay = decode_layout(ML, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases);
+  const int Mp = decode_corr_rows(ML);
   const uint32_t sel = block_sel<BITS>(kb);
 
   // ---- staging scope: the fast path stages per wave (its own CPW chunks, in
@@ -706,14 +731,15 @@ static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
   if constexpr (!decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV)) {
     return hipErrorInvalidValue;
   } else {
-    const size_t lds = decode_lds_bytes(a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg, a.phases);
+    const size_t lds = decode_lds_bytes(a.n_experts > 0 ? 16 : a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg, a.phases);
     auto kern = decode_kernel<BITS, PER_ELEM, MV, CPL, CPW>;
     if (lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(a.tiles * a.ks), dim3(64 * a.nw), lds, stream, a);
+    const int grid = a.n_experts > 0 ? a.n_experts * a.moe_blocks * a.tiles : a.tiles * a.ks;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * a.nw), lds, stream, a);
     return hipGetLastError();
   }
 }
@@ -739,7 +765,9 @@ static hipError_t launch_decode_cpl(const GemmArgs& a, hipStream_t stream) {
 
 template <int BITS, bool PER_ELEM>
 static hipError_t launch_decode_pe(const GemmArgs& a, hipStream_t stream) {
-  return a.M == 1 ? launch_decode_cpl<BITS, PER_ELEM, 1>(a, stream) : launch_decode_cpl<BITS, PER_ELEM, 4>(a, stream);
+  // grouped decode: up to 16 rows per workgroup whatever the total
+  return a.M == 1 && a.n_experts == 0 ? launch_decode_cpl<BITS, PER_ELEM, 1>(a, stream)
+                                      : launch_decode_cpl<BITS, PER_ELEM, 4>(a, stream);
 }
 
 template <int BITS>

@@ -418,6 +418,49 @@ int gptq_gemm_tiled(const void* x, const int32_t* qweight_tiled, const int32_t* 
 }
 
 namespace {
+int moe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,
+             const int32_t* expert_offsets, int n_experts, int max_tokens_per_expert, int bits, int group_size,
+             int is_v2, int64_t T, int64_t N, int64_t K, void* out, void* stream) {
+  int rc = check_weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, N, K);
+  if (rc != GPTQ_OK) return rc;
+  if (!expert_offsets) return GPTQ_ERR_NULL_PTR;
+  if (n_experts < 1 || n_experts > (1 << 16) || max_tokens_per_expert < 0) return GPTQ_ERR_BAD_ARG;
+  if (T < 0 || T > ((int64_t)1 << 24) || T * K >= kMaxElems || T * N >= kMaxElems) return GPTQ_ERR_BAD_SHAPE;
+  if ((int64_t)n_experts * (K / 32 * bits) * N >= kMaxElems) return GPTQ_ERR_BAD_SHAPE;
+  if (T == 0 || max_tokens_per_expert == 0) return GPTQ_OK;
+  if (!x || !out) return GPTQ_ERR_NULL_PTR;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(expert_offsets, 4)) return GPTQ_ERR_MISALIGNED;
+  gptq::GemmArgs a{};
+  a.x = static_cast<const _Float16*>(x);
+  a.qweight = qweight;
+  a.qzeros = qzeros;
+  a.scales = static_cast<const _Float16*>(scales);
+  a.g_idx = g_idx;
+  a.out = static_cast<_Float16*>(out);
+  a.M = (int)T;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.G = (int)(K / group_size);
+  a.group_size = group_size;
+  a.zero_offset = is_v2 ? 0 : 1;
+  a.chunks = (int)(K / 32);
+  a.zrow_words = N * bits / 32;
+  bool per_elem = (g_idx != nullptr) || (group_size % 32 != 0);
+  // launch shape for blocks of up to 16 rows, no K split (one workgroup per
+  // expert block and column tile)
+  if (decode_shape(bits, 16, a.N, a.K, a.G, 0, false, false, &per_elem, &a) != GPTQ_OK) return GPTQ_ERR_BAD_SHAPE;
+  a.moe_off = expert_offsets;
+  a.n_experts = n_experts;
+  a.moe_blocks = (max_tokens_per_expert + 15) / 16;
+  a.qw_stride = K / 32 * bits * N;
+  a.qz_stride = a.G * a.zrow_words;
+  a.sc_stride = (int64_t)a.G * N;
+  a.gi_stride = K;
+  if ((int64_t)n_experts * a.moe_blocks * a.tiles >= ((int64_t)1 << 31)) return GPTQ_ERR_BAD_SHAPE;
+  const hipError_t err = gptq::launch_decode(bits, per_elem, a, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
+}
+
 int repack_impl(const int32_t* in, int32_t* out, int bits, int64_t N, int64_t K, int to_tiled, void* stream) {
   if (!in || !out) return GPTQ_ERR_NULL_PTR;
   if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_BAD_BITS;
@@ -431,6 +474,17 @@ int repack_impl(const int32_t* in, int32_t* out, int bits, int64_t N, int64_t K,
   return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
 }
 }  // namespace
+
+int gptq_moe_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                  const int32_t* g_idx, const int32_t* expert_offsets, int n_experts, int max_tokens_per_expert,
+                  int bits, int group_size, int is_v2, int64_t T, int64_t N, int64_t K, void* out, void* stream) {
+  try {
+    return moe_impl(x, qweight, qzeros, scales, g_idx, expert_offsets, n_experts, max_tokens_per_expert, bits,
+                    group_size, is_v2, T, N, K, out, stream);
+  } catch (...) {
+    return GPTQ_ERR_DEVICE;
+  }
+}
 
 int gptq_repack_tiled(const int32_t* qweight, int32_t* qweight_tiled, int bits, int64_t N, int64_t K,
                       void* stream) {

@@ -232,6 +232,62 @@ def bench_prefill(torch, gq, args, dev):
     return res
 
 
+def bench_moe(torch, gq, args, dev):
+    """Grouped decode (gptq_moe_gemm) on a Mixtral-class expert layer: 8 experts
+    4096 -> 14336, 4-bit g128 sym v1, 16 tokens routed top-2 (seeded), weight
+    copies rotated past the Infinity Cache.  Reports weight GB/s over the
+    experts that received tokens (all of them read once per launch)."""
+    E, K, N, bits, gs = 8, 4096, 14336, 4, 128
+    rng = np.random.default_rng(0)
+    picks = np.array([rng.choice(E, size=2, replace=False) for _ in range(16)]).ravel()
+    counts = np.bincount(picks, minlength=E)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=dev)
+    T = int(counts.sum())
+    gen = torch.Generator(device=dev).manual_seed(0)
+    qws, qzs, scs = [], [], []
+    for _ in range(E):
+        w = torch.randn((K, N), generator=gen, device=dev, dtype=torch.float32) * 0.02
+        qw, qz, sc = gq.quantize(w, None, bits, gs, True, False)
+        qws.append(qw), qzs.append(qz), scs.append(sc)
+        del w
+    base = (torch.stack(qws), torch.stack(qzs), torch.stack(scs))
+    del qws, qzs, scs
+    x = torch.randn((T, K), generator=gen, device=dev, dtype=torch.float32).half()
+    out = torch.empty((T, N), dtype=torch.float16, device=dev)
+    active = int((counts > 0).sum())
+    wbytes = active * layer_bytes(K, N, bits, gs)
+    copies = max(2, -(-ROTATE_BYTES // (E * layer_bytes(K, N, bits, gs))))
+    sets = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
+    mt = int(counts.max())
+    run = lambda st: gq.moe_gemm(x, st[0], st[1], st[2], None, offsets, mt, bits, gs, False, out=out)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for st in sets:
+            run(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for st in sets:
+            run(st)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    del g, sets, base
+    torch.cuda.empty_cache()
+    return {"workload": "mixtral_expert_w1_w4g128", "experts": E, "K": K, "N": N, "tokens": 16, "top_k": 2,
+            "active_experts": active, "us": round(us, 2), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
+            "frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def copy_ceiling(torch, dev):
     """Plain device copy of 1 GiB: read + write GB/s (context for the HBM roofline)."""
     a = torch.empty(1 << 29, dtype=torch.float16, device=dev)
@@ -404,6 +460,8 @@ def main():
               file=sys.stderr, flush=True)
         del dec_ck["base"]
     torch.cuda.empty_cache()
+    moe = bench_moe(torch, gq, args, dev)
+    print(f"# moe: {moe}", file=sys.stderr, flush=True)
     ceiling = copy_ceiling(torch, dev)
     prefill = None if args.no_prefill else bench_prefill(torch, gq, args, dev)
     if prefill:
@@ -448,6 +506,7 @@ def main():
             "ms_per_step": round(dec_ck["ms_per_step"], 5), "achieved": round(dec_ck["achieved"], 1),
             "frac": round(dec_ck["achieved"] / HBM_PEAK_GBPS, 4), "mean_launch_us": round(dec_ck["mean_launch_us"], 3),
             "per_layer": dec_ck["layers"]},
+        "moe": moe,
         "copy_GBps": round(ceiling, 1),
         "prefill": prefill,
         "cpu_baseline": cpu,

@@ -80,8 +80,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
   const int nc = col_ok ? n : 0;
   const int ktiles = (a.K + BK - 1) / BK;
 
-  // ---- x tiles: slot s = m * 8 + (kblk ^ (m & 7)) of a stage holds x[m0 + m,
-  // 8 kblk .. 8 kblk + 8) of the tile.  Load i of wave w fills slots
+  // ---- x tiles: slot s = m * 8 + (kblk ^ ((m >> 1) & 7)) of a stage holds
+  // x[m0 + m, 8 kblk .. 8 kblk + 8) of the tile.  The swizzle puts the 16
+  // rows one 128-bit LDS read serves per cycle (16 lanes) in 16 different
+  // 16-byte bank groups of gfx950's 64 banks (rows m and m + 1 sit 128 bytes
+  // apart, so only every other row needs a distinct column block).  Load i of wave w fills slots
   // (4 w + i) * 64 + lane, so each lane fetches the piece that lands there.
   // Rows past M read zero (past the end of x); k past K is never used.
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int s = (4 * wave + i) * 64 + lane;
-    const int m = s >> 3, kblk = (s & 7) ^ (m & 7);
+    const int m = s >> 3, kblk = (s & 7) ^ ((m >> 1) & 7);
     xoff[i] = ((uint32_t)(m0 + m) * (uint32_t)a.K + 8u * kblk) * 2u;
     // rows past M: an offset past the end of x (plus at most the K bytes of
     // a tile offset it stays past it, or wraps to valid data of row 0); such
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
       for (int i = 0; i < MS; ++i) {
         const int m = 32 * i + q;
         const int kblk = 2 * s + kb2;
-        const half8_t A = *reinterpret_cast<const half8_t*>(sl + (m * 8 + (kblk ^ (m & 7))) * 8);
+        const half8_t A = *reinterpret_cast<const half8_t*>(sl + (m * 8 + (kblk ^ ((m >> 1) & 7))) * 8);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[j], acc[i][j], 0, 0, 0);

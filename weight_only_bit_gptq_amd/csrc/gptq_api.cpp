@@ -351,8 +351,10 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
                   "gptq::decode_kernel<%d, %s, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d k_splits=%d",
                   bits, pe, M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles * a.ks, 64 * a.nw, a.phases, a.pc, a.ks);
   } else {
-    std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s> grid=%dx%d block=256", bits, pe, a.tiles_n,
-                  a.tiles_m);
+    // the pipelined full-tile body: fast path, K % 64 == 0, not 8-bit
+    const bool full = !per_elem && K % 64 == 0 && bits != 8;
+    std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s, %s> grid=%dx%d block=256", bits, pe,
+                  full ? "true" : "false", a.tiles_n, a.tiles_m);
   }
   return GPTQ_OK;
 }

@@ -43,7 +43,11 @@ void prefill_shape(int M, int N, int* tiles_m, int* tiles_n) {
 
 // Two workgroups per CU: 256 registers per lane for the 128 accumulators, the
 // B and A fragments and three tiles of packed words.
-template <int BITS, bool PER_ELEM>
+// FULL (fast path, K % 64 == 0): every k tile has its four 16-row steps and
+// runs the software-pipelined tile body; otherwise (act order, other group
+// sizes, a last half tile) the plain body with a step count per tile.  Two
+// separate instantiations: one body with both paths behind a branch spills.
+template <int BITS, bool PER_ELEM, bool FULL>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
   constexpr int BM = kPrefillBM;
   constexpr int BK = kPrefillBK;
@@ -195,13 +199,57 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
     }
   };
 
-  // one k tile from LDS stage `stage` and register set `set`
-  auto compute_tile = [&](int kt, auto set_c) __attribute__((always_inline)) {
+  // fast path, a whole k tile: the B operands of step s + 1 are made (VALU)
+  // while the MFMAs of step s run, in the same wave, so the two pipes overlap
+  // without relying on the other wave of the SIMD
+  auto compute_full_tile = [&](auto set_c) __attribute__((always_inline)) {
     constexpr int set = decltype(set_c)::value % NSR;
     const _Float16* sl = stage_lds(set_c);
     half2_t negp[2][4], sp[2];
-    if constexpr (!PER_ELEM) group_consts(set, negp, sp);
+    group_consts(set, negp, sp);
+    auto make_B = [&](int s, half8_t (&B)[2]) __attribute__((always_inline)) {
+      const int kb = 2 * (s & 1) + kb2;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t p[4];
+        unpack_block_natural<BITS>(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p, magic);
+        u32x4_t bw;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bw[v] = as_u32(pair_minus_zero_natural<BITS>(p[v], v, negp[j][v]) * sp[j]);
+        B[j] = __builtin_bit_cast(half8_t, bw);
+      }
+    };
+    half8_t Bc[2], Bn[2];
+    make_B(0, Bc);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) make_B(s + 1, Bn);
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+        const int m = 32 * i + q;
+        const int kblk = 2 * s + kb2;
+        const half8_t A = *reinterpret_cast<const half8_t*>(sl + (m * 8 + (kblk ^ ((m >> 1) & 7))) * 8);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bc[j], acc[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) Bc[j] = Bn[j];
+    }
+  };
+
+  // one k tile from LDS stage `stage` and register set `set`
+  auto compute_tile = [&](int kt, auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value % NSR;
+    if constexpr (FULL) {
+      // the loop runs tiles in threes: tiles past the end compute nothing
+      if (kt < ktiles) compute_full_tile(set_c);
+      return;
+    }
     const int ksteps = min(4, (a.K - kt * BK) >> 4);
+    const _Float16* sl = stage_lds(set_c);
+    half2_t negp[2][4], sp[2];
+    if constexpr (!PER_ELEM) group_consts(set, negp, sp);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s >= ksteps) break;
@@ -305,16 +353,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
   }
 }
 
-template <int BITS, bool PER_ELEM>
+template <int BITS, bool PER_ELEM, bool FULL>
 static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(a.tiles_m * a.tiles_n);
-  hipLaunchKernelGGL((prefill_kernel<BITS, PER_ELEM>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int BITS>
 static hipError_t launch_prefill_bits(bool per_elem, const GemmArgs& a, hipStream_t stream) {
-  return per_elem ? launch_prefill_pe<BITS, true>(a, stream) : launch_prefill_pe<BITS, false>(a, stream);
+  if (per_elem) return launch_prefill_pe<BITS, true, false>(a, stream);
+  // 8-bit: the pipelined body needs more registers than 2 workgroups per CU
+  // leave (it spills), so it keeps the plain body
+  if constexpr (BITS == 8) return launch_prefill_pe<BITS, false, false>(a, stream);
+  else
+    return a.K % 64 == 0 ? launch_prefill_pe<BITS, false, true>(a, stream)
+                         : launch_prefill_pe<BITS, false, false>(a, stream);
 }
 
 hipError_t launch_prefill(int bits, bool per_elem, const GemmArgs& a, hipStream_t stream) {

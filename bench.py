@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--prefill-steps", type=int, default=10)
+    p.add_argument("--warm-seconds", type=float, default=0.5,
+                   help="untimed GPU work before each timed region (MI355X raises its clocks over "
+                        "hundreds of milliseconds of load; measured without it, prefill reads ~15%% low)")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-checkpoint-layout", action="store_true",
                    help="skip the decode step on the checkpoint qweight layout (reported beside the tiled one)")
@@ -169,8 +172,17 @@ def bench_decode(torch, gq, args, dev, tiled):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
+    def warm(graph):
+        # untimed replays until the clocks have settled (see --warm-seconds)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.warm_seconds:
+            for _ in range(20):
+                graph.replay()
+            torch.cuda.synchronize()
+
     replays = max(1, -(-args.steps // copies))
     steps = replays * copies
+    warm(g_all)
     ms_per_step = timed(g_all, replays) / steps
     per_layer_ms = [timed(g, replays) / steps for g in g_layer]
 
@@ -197,9 +209,13 @@ def bench_prefill(torch, gq, args, dev):
             out = torch.empty((2048, layer.N), dtype=torch.float16, device=dev)
             run = lambda: gq.gemm(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits,
                                   wl.group_size, wl.is_v2, out=out)
-            for _ in range(2):
-                run()
-            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            while True:                       # untimed warm-up (see --warm-seconds)
+                for _ in range(5):
+                    run()
+                torch.cuda.synchronize()
+                if time.perf_counter() - t0 >= args.warm_seconds:
+                    break
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
@@ -216,9 +232,11 @@ def bench_prefill(torch, gq, args, dev):
             if name == "mlp70b_prefill_w4g128":
                 # context: the vendor dense fp16 GEMM (torch.matmul) on the same shape, unquantized W
                 W = torch.randn((layer.K, layer.N), dtype=torch.float16, device=dev)
-                for _ in range(2):
-                    torch.matmul(L["x"], W, out=out)
-                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                while time.perf_counter() - t0 < args.warm_seconds:
+                    for _ in range(5):
+                        torch.matmul(L["x"], W, out=out)
+                    torch.cuda.synchronize()
                 a.record()
                 for _ in range(args.prefill_steps):
                     torch.matmul(L["x"], W, out=out)
@@ -270,8 +288,11 @@ def bench_moe(torch, gq, args, dev):
     with torch.cuda.graph(g, stream=side):
         for st in sets:
             run(st)
-    g.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.warm_seconds:     # untimed warm-up
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     reps = 20

@@ -250,6 +250,61 @@ def bench_prefill(torch, gq, args, dev):
     return res
 
 
+def bench_decode_configs(torch, gq, args, dev):
+    """The other decode workloads (2-bit g64 asym v2 with outliers at M = 1, 4,
+    16; 3-bit g128 act-order at M = 16), tiled layout: per-layer launch time
+    from a graph of launches over rotated weight copies, and algorithmic
+    bytes (weights + g_idx + x + y) per launch against 8 TB/s."""
+    from workload import WORKLOADS
+    res = []
+    for name in ("lowbit_decode_w2g64", "actorder_decode_w3g128"):
+        wl = WORKLOADS[name]
+        for layer in wl.layers:
+            L = make_layer(torch, gq, wl, layer, max(wl.Ms), dev, tiled=True)
+            wb = layer_bytes(layer.K, layer.N, wl.bits, wl.group_size) + (4 * layer.K if wl.act_order else 0)
+            copies = max(2, -(-ROTATE_BYTES // wb))
+            sets = [L["qweight"]] + [L["qweight"].clone() for _ in range(copies - 1)]
+            for M in wl.Ms:
+                x = L["x"][:M].contiguous()
+                out = torch.empty((M, layer.N), dtype=torch.float16, device=dev)
+                run = lambda qw: gq.gemm(x, qw, L["qzeros"], L["scales"], L["g_idx"], wl.bits, wl.group_size,
+                                         wl.is_v2, out=out)
+                side = torch.cuda.Stream(dev)
+                side.wait_stream(torch.cuda.current_stream(dev))
+                with torch.cuda.stream(side):
+                    for qw in sets:
+                        run(qw)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for qw in sets:
+                        run(qw)
+                t0 = time.perf_counter()
+                while time.perf_counter() - t0 < args.warm_seconds / 4:
+                    for _ in range(10):
+                        g.replay()
+                    torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                reps = 20
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+                alg = wb + 2 * M * layer.K + 2 * M * layer.N
+                res.append({"workload": name, "layer": f"{layer.name} {layer.K}->{layer.N}", "M": M,
+                            "kernel": gq.describe(x, sets[0], L["qzeros"], L["scales"], L["g_idx"], wl.bits,
+                                                  wl.group_size, wl.is_v2, out=out),
+                            "us": round(us, 2), "GBps": round(alg / (us * 1e-6) / 1e9, 1),
+                            "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+                del g
+            del L, sets
+            torch.cuda.empty_cache()
+    return res
+
+
 def bench_moe(torch, gq, args, dev):
     """Grouped decode (gptq_moe_gemm) on a Mixtral-class expert layer: 8 experts
     4096 -> 14336, 4-bit g128 sym v1, 16 tokens routed top-2 (seeded), weight
@@ -481,6 +536,8 @@ def main():
               file=sys.stderr, flush=True)
         del dec_ck["base"]
     torch.cuda.empty_cache()
+    dec_other = bench_decode_configs(torch, gq, args, dev)
+    print(f"# other decode configs: {dec_other}", file=sys.stderr, flush=True)
     moe = bench_moe(torch, gq, args, dev)
     print(f"# moe: {moe}", file=sys.stderr, flush=True)
     ceiling = copy_ceiling(torch, dev)
@@ -527,6 +584,7 @@ def main():
             "ms_per_step": round(dec_ck["ms_per_step"], 5), "achieved": round(dec_ck["achieved"], 1),
             "frac": round(dec_ck["achieved"] / HBM_PEAK_GBPS, 4), "mean_launch_us": round(dec_ck["mean_launch_us"], 3),
             "per_layer": dec_ck["layers"]},
+        "decode_other": dec_other,
         "moe": moe,
         "copy_GBps": round(ceiling, 1),
         "prefill": prefill,

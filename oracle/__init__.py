@@ -34,6 +34,7 @@ from .gptq_ref import (  # noqa: F401
     gemm_ref,
     gptq_gemm_ref,
     moe_gemm_ref,
+    sort_act_order,
     quantize_layer,
     QuantizedLayer,
 )

@@ -274,6 +274,24 @@ def gptq_gemm_ref(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K,
                                    is_v2, K, N, cols=cols))
 
 
+def sort_act_order(qweight: np.ndarray, g_idx: np.ndarray, bits: int, group_size: int, K: int):
+    """Rows of an act-order layer sorted by group: perm = the stable order of
+    g_idx, packed row fields q_sorted[i, n] = q[perm[i], n].  When every group
+    has exactly group_size rows, row i of the sorted layer lies in group
+    i // group_size, so the layer is an ordinary grouped one for x[:, perm]:
+    sum_k x[m, k] W^[k, n] = sum_i x[m, perm[i]] W^[perm[i], n].  (Act order
+    assigns rows to groups out of order: page "GPTQ quantization principles
+    and engineering practice", section 3.4, desc_act; the row sort with a
+    gathered x is this library's reading of how to run such a layer.)
+    Returns (qweight_sorted [K*b/32, N], perm int32 [K])."""
+    g = group_of_rows(K, group_size, g_idx)
+    perm = np.argsort(g, kind="stable")
+    if not np.array_equal(g[perm], np.arange(K) // group_size):
+        raise ValueError("act-order groups are not all of group_size rows")
+    q = unpack_along_k(qweight, bits, K)
+    return pack_along_k(q[perm], bits), perm.astype(np.int32)
+
+
 def moe_gemm_ref(x, experts, offsets, bits, group_size, is_v2, K, N, cols=None) -> np.ndarray:
     """Grouped GEMM over routed tokens: rows [offsets[e], offsets[e+1]) of x use
     expert e's packed weights; each expert's rows go through gptq_gemm_ref.

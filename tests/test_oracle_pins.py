@@ -315,6 +315,30 @@ def test_moe_gemm_ref_rows_match_their_expert():
     assert np.isnan(y[8]).all()
 
 
+@pytest.mark.parametrize("bits", BITS)
+def test_sort_act_order(bits):
+    """Sorted rows: packed row fields follow perm (checked field by field with
+    big-integer extraction), perm sorts g_idx into i // gs, and the GEMM with
+    x[:, perm] on the sorted layer (no g_idx) equals the act-order GEMM."""
+    K, N, gs = 256, 64, 64
+    d = draw_layer(K, N, 3, sigma=0.02, group_size=gs, act_order=True, seed=bits + 60)
+    L = oracle.quantize_layer(d.W, bits, gs, False, True, d.g_idx)
+    qs, perm = oracle.sort_act_order(L.qweight, L.g_idx, bits, gs, K)
+    assert sorted(perm.tolist()) == list(range(K))
+    assert np.array_equal(L.g_idx[perm], np.arange(K) // gs)
+    for n in (0, 17, N - 1):
+        orig = bigint_fields(L.qweight[:, n], bits, K)
+        new = bigint_fields(qs[:, n], bits, K)
+        assert new == [orig[p] for p in perm]
+    y_act = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, True, K, N)
+    y_srt = oracle.gptq_gemm_ref(d.x[:, perm], qs, L.qzeros, L.scales, None, bits, gs, True, K, N)
+    assert np.allclose(y_act, y_srt, rtol=0, atol=1e-12)
+    bad = L.g_idx.copy()
+    bad[0] = (bad[0] + 1) % (K // gs)           # one group one row short, another one long
+    with pytest.raises(ValueError):
+        oracle.sort_act_order(L.qweight, bad, bits, gs, K)
+
+
 # ---------------------------------------------------------------- dequant, brute force
 def dequant_bruteforce(qweight, qzeros, scales, g_idx, bits, gs, is_v2, K, N):
     cols = [bigint_fields(qweight[:, n], bits, K) for n in range(N)]

@@ -252,7 +252,8 @@ def bench_prefill(torch, gq, args, dev):
 
 def bench_decode_configs(torch, gq, args, dev):
     """The other decode workloads (2-bit g64 asym v2 with outliers at M = 1, 4,
-    16; 3-bit g128 act-order at M = 16), tiled layout: per-layer launch time
+    16; 3-bit g128 act-order at M = 16, rows sorted by group once at load and
+    x gathered per call), tiled layout: per-layer launch time
     from a graph of launches over rotated weight copies, and algorithmic
     bytes (weights + g_idx + x + y) per launch against 8 TB/s."""
     from workload import WORKLOADS
@@ -260,15 +261,24 @@ def bench_decode_configs(torch, gq, args, dev):
     for name in ("lowbit_decode_w2g64", "actorder_decode_w3g128"):
         wl = WORKLOADS[name]
         for layer in wl.layers:
-            L = make_layer(torch, gq, wl, layer, max(wl.Ms), dev, tiled=True)
+            L = make_layer(torch, gq, wl, layer, max(wl.Ms), dev, tiled=not wl.act_order)
+            perm = None
+            if wl.act_order:               # rows sorted by group once at load, x gathered per call
+                qs, perm = gq.sort_act_order(L["qweight"], L["g_idx"], wl.bits, wl.group_size)
+                L["qweight"] = gq.repack_tiled(qs, wl.bits)
+                del qs
             wb = layer_bytes(layer.K, layer.N, wl.bits, wl.group_size) + (4 * layer.K if wl.act_order else 0)
             copies = max(2, -(-ROTATE_BYTES // wb))
             sets = [L["qweight"]] + [L["qweight"].clone() for _ in range(copies - 1)]
             for M in wl.Ms:
                 x = L["x"][:M].contiguous()
                 out = torch.empty((M, layer.N), dtype=torch.float16, device=dev)
-                run = lambda qw: gq.gemm(x, qw, L["qzeros"], L["scales"], L["g_idx"], wl.bits, wl.group_size,
-                                         wl.is_v2, out=out)
+                if perm is None:
+                    run = lambda qw: gq.gemm(x, qw, L["qzeros"], L["scales"], None, wl.bits, wl.group_size,
+                                             wl.is_v2, out=out)
+                else:
+                    run = lambda qw: gq.gemm_sorted(x, qw, L["qzeros"], L["scales"], perm, wl.bits, wl.group_size,
+                                                    wl.is_v2, out=out)
                 side = torch.cuda.Stream(dev)
                 side.wait_stream(torch.cuda.current_stream(dev))
                 with torch.cuda.stream(side):
@@ -295,7 +305,8 @@ def bench_decode_configs(torch, gq, args, dev):
                 us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
                 alg = wb + 2 * M * layer.K + 2 * M * layer.N
                 res.append({"workload": name, "layer": f"{layer.name} {layer.K}->{layer.N}", "M": M,
-                            "kernel": gq.describe(x, sets[0], L["qzeros"], L["scales"], L["g_idx"], wl.bits,
+                            "kernel": ("x gathered by perm, then " if perm is not None else "") +
+                                      gq.describe(x, sets[0], L["qzeros"], L["scales"], None, wl.bits,
                                                   wl.group_size, wl.is_v2, out=out),
                             "us": round(us, 2), "GBps": round(alg / (us * 1e-6) / 1e9, 1),
                             "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})

@@ -232,6 +232,37 @@ GPTQ_API int gptq_gemm_tiled_describe(const void* x, const int32_t* qweight_tile
                                       int decode_waves, char* buf, int64_t buflen);
 
 /*
+ * Act-order layers with their rows sorted by group (page "GPTQ quantization
+ * principles and engineering practice", section 3.4: act order quantizes
+ * rows out of order, so g_idx scatters each group's rows over K).  Sorting
+ * the rows by group makes every group contiguous again, and
+ *   y = x . W^ = x[:, perm] . W^[perm, :]
+ * so the layer runs on the grouped fast path with x gathered by perm.
+ *
+ * gptq_sort_act_order: perm[i] = original row of sorted row i (a stable sort
+ * of g_idx, decided on the host: g_idx is read back, so the call synchronizes
+ * `stream`), and qweight_sorted [K*bits/32, N] = qweight's packed rows in that
+ * order (bit-exact field moves).  Requires every group to hold exactly
+ * group_size rows and g_idx entries in [0, G) (else GPTQ_ERR_BAD_ARG: use
+ * gptq_gemm with g_idx instead); not during stream capture (GPTQ_ERR_BAD_ARG).
+ * qzeros and scales are unchanged.  qweight_sorted must not overlap qweight;
+ * qweight_sorted and perm 16-byte aligned.
+ *
+ * gptq_gemm_sorted: gptq_gemm for such a layer: x is gathered by perm into
+ * the stream's library workspace (M*K*2 bytes, allocated on first use outside
+ * stream capture, else GPTQ_ERR_NO_MEM) and the grouped GEMM runs on it.
+ * layout: 0 = qweight_sorted in the checkpoint layout, 1 = tiled (after
+ * gptq_repack_tiled).  path / decode_waves as for gptq_gemm_ex.
+ */
+GPTQ_API int gptq_sort_act_order(const int32_t* qweight, const int32_t* g_idx, int bits, int group_size, int64_t N,
+                                 int64_t K, int32_t* qweight_sorted, int32_t* perm, void* stream);
+GPTQ_API int gptq_gemm_sorted(const void* x, const int32_t* qweight_sorted, const int32_t* qzeros,
+                              const void* scales, const int32_t* perm, int bits, int group_size, int is_v2,
+                              int64_t M, int64_t N, int64_t K, void* out, void* stream, int layout, int path,
+                              int decode_waves);
+
+/*
+ * Grouped (mixture-of-experts) decode GEMM/*
  * Grouped (mixture-of-experts) decode GEMM: for every expert e,
  *   out[r, :] = x[r, :] . dequant(expert e's weights)   for r in [off[e], off[e+1])
  * i.e. one gptq_gemm per expert over the tokens routed to it, in one launch

@@ -31,7 +31,7 @@ def test_header_declares_api():
     for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check", "gptq_gemm_ex_check",
               "gptq_gemm_describe", "gptq_dequant_check", "gptq_convert_zeros", "gptq_convert_zeros_check",
               "gptq_repack_tiled", "gptq_unrepack_tiled", "gptq_gemm_tiled", "gptq_gemm_tiled_ex",
-              "gptq_gemm_tiled_describe", "gptq_moe_gemm",
+              "gptq_gemm_tiled_describe", "gptq_moe_gemm", "gptq_sort_act_order", "gptq_gemm_sorted",
               "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
     assert declared_status() == gq.STATUS
@@ -174,6 +174,23 @@ def test_moe_argument_codes():
     assert mo(off=OFF + 2) == -5
     assert mo(T=0, x=None, o=None) == 0               # nothing to do, nothing launched
     assert mo(mt=0) == 0
+
+
+def test_sorted_argument_codes():
+    """Bad act-order sort / sorted GEMM arguments return before touching the device."""
+    lib = gq.library()
+    PERM = 0x80000
+    assert lib.gptq_sort_act_order(QW, None, 4, 128, 4096, 4096, OUT, PERM, None) == -1
+    assert lib.gptq_sort_act_order(QW, GI, 5, 128, 4096, 4096, OUT, PERM, None) == -2
+    assert lib.gptq_sort_act_order(QW, GI, 4, 100, 4096, 4096, OUT, PERM, None) == -4
+    assert lib.gptq_sort_act_order(QW, GI, 4, 128, 4096, 4096, OUT + 4, PERM, None) == -5
+    assert lib.gptq_sort_act_order(QW, GI, 4, 128, 4096, 4096, QW, PERM, None) == -9     # in place
+    sg = lambda perm=PERM, layout=0, path=0, K=4096: lib.gptq_gemm_sorted(X, QW, QZ, SC, perm, 4, 128, 1, 1, 4096, K,
+                                                                          OUT, None, layout, path, 0)
+    assert sg(perm=None) == -1
+    assert sg(perm=PERM + 2) == -5
+    assert sg(layout=2) == -9
+    assert sg(path=3) == -9
 
 
 def test_invalid_calls_return_before_any_launch():

@@ -294,6 +294,65 @@ def test_gemm_tiled_shapes(dev, bits, gs, M, K, N, act):
     assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, desc)
 
 
+# ------------------------------------------------------------------ act-order rows sorted by group
+@pytest.mark.parametrize("bits", BITS)
+def test_sort_act_order_bit_exact(dev, bits):
+    """gptq_sort_act_order reproduces the oracle's perm and sorted packed rows."""
+    K, N, gs = 512, 96, 128
+    d, L = quantized(K, N, 1, bits, gs, False, True, True, seed=bits + 70)
+    qw, qz, sc, gi = upload(L, dev)
+    want_q, want_p = oracle.sort_act_order(L.qweight, L.g_idx, bits, gs, K)
+    qs, perm = gq.sort_act_order(qw, gi, bits, gs)
+    assert np.array_equal(perm.cpu().numpy(), want_p)
+    assert np.array_equal(qs.cpu().numpy(), want_q)
+
+
+def test_sort_act_order_rejects_unequal_groups(dev):
+    K, N, gs, bits = 256, 64, 64, 4
+    d, L = quantized(K, N, 1, bits, gs, False, True, True, seed=3)
+    qw, qz, sc, gi = upload(L, dev)
+    bad = gi.clone()
+    bad[0] = (int(bad[0]) + 1) % (K // gs)
+    with pytest.raises(gq.GptqError):
+        gq.sort_act_order(qw, bad, bits, gs)
+
+
+@pytest.mark.parametrize("bits,M,tiled", [(3, 16, False), (3, 16, True), (4, 1, False), (4, 1, True),
+                                          (2, 5, False), (8, 16, True), (4, 40, False), (3, 33, True)])
+def test_gemm_sorted_matches_act_order(dev, bits, M, tiled):
+    """The sorted act-order layer with x gathered by perm gives the act-order
+    GEMM of the original layer (oracle), on the decode and prefill paths."""
+    K, N, gs = 1024, 160, 128
+    d, L = quantized(K, N, M, bits, gs, False, True, True, seed=bits * 3 + M)
+    qw, qz, sc, gi = upload(L, dev)
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, True, K, N)
+    qs, perm = gq.sort_act_order(qw, gi, bits, gs)
+    if tiled:
+        qs = gq.repack_tiled(qs, bits)
+    x = torch.from_numpy(d.x).to(dev)
+    for p in [gq.PATH_AUTO, gq.PATH_PREFILL] + ([gq.PATH_DECODE] if M <= 16 else []):
+        y = gq.gemm_sorted(x, qs, qz, sc, perm, bits, gs, True, path=p)
+        assert_close(y, ref, f"path={p}")
+
+
+def test_gemm_sorted_full_size_actorder(dev):
+    """3-bit act-order decode layers at full size (5120 -> 13824 and
+    13824 -> 5120, M = 16), sorted and tiled: sampled columns."""
+    from workload import WORKLOADS
+    wl = WORKLOADS["actorder_decode_w3g128"]
+    for layer in wl.layers:
+        d = draw_workload_layer(wl, layer, 16, seed=0)
+        L = oracle.quantize_layer(d.W, wl.bits, wl.group_size, wl.sym, wl.is_v2, d.g_idx)
+        qw, qz, sc, gi = upload(L, dev)
+        qs, perm = gq.sort_act_order(qw, gi, wl.bits, wl.group_size)
+        qs = gq.repack_tiled(qs, wl.bits)
+        cols = np.arange(0, layer.N, 97)
+        ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, wl.bits, wl.group_size, wl.is_v2,
+                                   layer.K, layer.N, cols=cols)
+        y = gq.gemm_sorted(torch.from_numpy(d.x).to(dev), qs, qz, sc, perm, wl.bits, wl.group_size, wl.is_v2)
+        assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, layer.name)
+
+
 # ------------------------------------------------------------------ grouped (MoE) decode
 def moe_problem(E, K, N, counts, bits, gs, act, seed, sym=False, is_v2=True):
     """E experts quantized by the oracle; tokens sorted by expert, `counts[e]` rows each."""

@@ -15,7 +15,8 @@ import os
 import threading
 from typing import Optional
 
-__all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "repack_tiled", "unrepack_tiled", "moe_gemm", "release", "library", "library_path", "GptqError",
+__all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "repack_tiled", "unrepack_tiled", "moe_gemm",
+           "sort_act_order", "gemm_sorted", "release", "library", "library_path", "GptqError",
            "STATUS", "PATH_AUTO", "PATH_DECODE", "PATH_PREFILL"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +79,10 @@ def library() -> ctypes.CDLL:
         lib.gptq_gemm_tiled_describe.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, i32,
                                                  i32, ctypes.c_char_p, i64]
         lib.gptq_gemm_tiled_describe.restype = i32
+        lib.gptq_sort_act_order.argtypes = [i32p, i32p, i32, i32, i64, i64, i32p, i32p, vp]
+        lib.gptq_sort_act_order.restype = i32
+        lib.gptq_gemm_sorted.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, vp, i32, i32, i32]
+        lib.gptq_gemm_sorted.restype = i32
         lib.gptq_moe_gemm.argtypes = [vp, i32p, i32p, vp, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, vp, vp]
         lib.gptq_moe_gemm.restype = i32
         lib.gptq_repack_tiled.argtypes = [i32p, i32p, i32, i64, i64, vp]
@@ -293,6 +298,58 @@ def convert_zeros(qzeros, bits: int, N: int, to_v2: bool, out=None, lossy_count=
         stream = torch.cuda.current_stream(dev).cuda_stream
         code = lib.gptq_convert_zeros(qzeros.data_ptr(), out.data_ptr(), int(bits), G, int(N), int(bool(to_v2)),
                                       None if lossy_count is None else lossy_count.data_ptr(), stream)
+    _raise(code)
+    return out
+
+
+def sort_act_order(qweight, g_idx, bits: int, group_size: int):
+    """Act-order layer -> (qweight_sorted [K*bits/32, N], perm int32 [K]): rows
+    sorted by group (stable), for `gemm_sorted`.  Synchronizes the stream."""
+    import torch
+    if bits not in (2, 3, 4, 8):
+        raise ValueError("bits must be 2, 3, 4 or 8")
+    dev = qweight.device if isinstance(qweight, torch.Tensor) else None
+    _check_tensor("qweight", qweight, torch.int32, dev)
+    _check_tensor("g_idx", g_idx, torch.int32, dev)
+    if qweight.dim() != 2:
+        raise ValueError("qweight must be the checkpoint layout [K*bits/32, N]")
+    N, K = qweight.shape[1], qweight.shape[0] * 32 // bits
+    if tuple(g_idx.shape) != (K,):
+        raise ValueError(f"g_idx must be [{K}]")
+    qs = torch.empty_like(qweight)
+    perm = torch.empty((K,), dtype=torch.int32, device=dev)
+    lib = library()
+    with torch.cuda.device(dev):
+        _raise(lib.gptq_sort_act_order(qweight.data_ptr(), g_idx.data_ptr(), int(bits), int(group_size), N, K,
+                                       qs.data_ptr(), perm.data_ptr(), torch.cuda.current_stream(dev).cuda_stream))
+    return qs, perm
+
+
+def gemm_sorted(x, qweight_sorted, qzeros, scales, perm, bits: int, group_size: int, is_v2: bool, *, out=None,
+                path: int = PATH_AUTO, decode_waves: int = 0):
+    """gemm for an act-order layer whose rows were sorted by `sort_act_order`
+    (qweight_sorted in the checkpoint layout, or 4-D tiled by repack_tiled)."""
+    import torch
+    dev, N, K = _weights(qweight_sorted, qzeros, scales, None, bits, group_size, is_v2)
+    _check_tensor("x", x, torch.float16, dev)
+    _check_tensor("perm", perm, torch.int32, dev)
+    if tuple(perm.shape) != (K,):
+        raise ValueError(f"perm must be [{K}]")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M, {K}]")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    else:
+        _check_tensor("out", out, torch.float16, dev)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be [{M}, {N}]")
+    lib = library()
+    with torch.cuda.device(dev):
+        code = lib.gptq_gemm_sorted(x.data_ptr(), qweight_sorted.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                                    perm.data_ptr(), int(bits), int(group_size), int(bool(is_v2)), M, N, K,
+                                    out.data_ptr(), torch.cuda.current_stream(dev).cuda_stream,
+                                    1 if qweight_sorted.dim() == 4 else 0, int(path), int(decode_waves))
     _raise(code)
     return out
 

@@ -246,10 +246,14 @@ struct SplitWorkspace {
 std::mutex g_ws_mu;
 std::vector<SplitWorkspace> g_ws;
 
-bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, float** ws, uint32_t** cnt) {
+// x_bytes > 0 also reserves a buffer after the partial sums (the gathered x
+// of gptq_gemm_sorted), returned in *xbuf.
+bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, float** ws, uint32_t** cnt,
+                     size_t x_bytes = 0, void** xbuf = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || cnt_bytes > kCounterBytes) return false;
-  const size_t need = kCounterBytes + ws_bytes;
+  const size_t ws_al = (ws_bytes + 255) & ~(size_t)255;
+  const size_t need = kCounterBytes + ws_al + x_bytes;
   std::lock_guard<std::mutex> lock(g_ws_mu);
   SplitWorkspace* e = nullptr;
   for (auto& w : g_ws)
@@ -284,18 +288,41 @@ bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, floa
   }
   *cnt = reinterpret_cast<uint32_t*>(e->base);
   *ws = reinterpret_cast<float*>(e->base + kCounterBytes);
+  if (xbuf) *xbuf = e->base + kCounterBytes + ws_al;
   return true;
 }
 
+// x_perm (nullable): rows of qweight are sorted by act-order group and x is
+// gathered into that order first (x_perm[i] = original row of sorted row i).
 int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-              void* out, void* stream_ptr, int path, int decode_waves, bool tiled) {
+              void* out, void* stream_ptr, int path, int decode_waves, bool tiled, const int32_t* x_perm = nullptr) {
   gptq::GemmArgs a;
   bool use_decode = false, per_elem = false;
   const int rc = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
                            decode_waves, tiled, &a, &use_decode, &per_elem);
   if (rc != GPTQ_OK || M == 0) return rc;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  if (x_perm) {
+    // one workspace request for the gathered x and (if planned) the split sums
+    const size_t xb = (size_t)M * K * 2;
+    const bool split = use_decode && a.ks > 1;
+    void* xg = nullptr;
+    bool ok = split_workspace(stream, split ? (size_t)a.ks * a.M * a.N * 4 : 0, split ? (size_t)a.tiles * 4 : 0,
+                              &a.ws, &a.cnt, xb, &xg);
+    if (!ok && split) {
+      const int rc2 = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
+                                decode_waves, tiled, &a, &use_decode, &per_elem, false);
+      if (rc2 != GPTQ_OK) return rc2;
+      ok = split_workspace(stream, 0, 0, &a.ws, &a.cnt, xb, &xg);
+    }
+    if (!ok) return GPTQ_ERR_NO_MEM;
+    if (gptq::launch_gather_cols(x, x_perm, xg, M, K, stream) != hipSuccess) return GPTQ_ERR_LAUNCH;
+    a.x = static_cast<const _Float16*>(xg);
+    const hipError_t err = use_decode ? gptq::launch_decode(bits, per_elem, a, stream)
+                                      : gptq::launch_prefill(bits, per_elem, a, stream);
+    return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
+  }
   if (use_decode && a.ks > 1 &&
       !split_workspace(stream, (size_t)a.ks * a.M * a.N * 4, (size_t)a.tiles * 4, &a.ws, &a.cnt)) {
     // no workspace (first use under stream capture, or out of memory): one split
@@ -477,6 +504,65 @@ int repack_impl(const int32_t* in, int32_t* out, int bits, int64_t N, int64_t K,
 }
 }  // namespace
 
+int gptq_sort_act_order(const int32_t* qweight, const int32_t* g_idx, int bits, int group_size, int64_t N,
+                        int64_t K, int32_t* qweight_sorted, int32_t* perm, void* stream_ptr) {
+  try {
+    if (!g_idx || !qweight_sorted || !perm) return GPTQ_ERR_NULL_PTR;
+    // scales/qzeros are not read: pass qweight in their place for the checks
+    int rc = check_weights(qweight, qweight, qweight, nullptr, bits, group_size, 1, N, K);
+    if (rc != GPTQ_OK) return rc;
+    if (!aligned(qweight_sorted, 16) || !aligned(perm, 16) || !aligned(g_idx, 4)) return GPTQ_ERR_MISALIGNED;
+    const int64_t bytes = K / 32 * bits * N * 4;
+    const uintptr_t a0 = (uintptr_t)qweight, b0 = (uintptr_t)qweight_sorted;
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return GPTQ_ERR_BAD_ARG;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return GPTQ_ERR_BAD_ARG;
+    // the order is decided on the host: a stable sort of g_idx (read back)
+    std::vector<int32_t> g((size_t)K), p((size_t)K);
+    if (hipMemcpyAsync(g.data(), g_idx, (size_t)K * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return GPTQ_ERR_DEVICE;
+    const int64_t G = K / group_size;
+    std::vector<int64_t> count((size_t)G + 1, 0);
+    for (int64_t k = 0; k < K; ++k) {
+      if (g[k] < 0 || g[k] >= G) return GPTQ_ERR_BAD_ARG;
+      ++count[(size_t)g[k] + 1];
+    }
+    for (int64_t i = 0; i < G; ++i) {
+      if (count[(size_t)i + 1] != group_size) return GPTQ_ERR_BAD_ARG;   // every group exactly group_size rows
+      count[(size_t)i + 1] += count[(size_t)i];
+    }
+    for (int64_t k = 0; k < K; ++k) p[(size_t)count[(size_t)g[k]]++] = (int32_t)k;   // stable counting sort
+    if (hipMemcpyAsync(perm, p.data(), (size_t)K * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return GPTQ_ERR_DEVICE;
+    if (gptq::launch_sort_rows(qweight, perm, qweight_sorted, bits, N, K, stream) != hipSuccess) return GPTQ_ERR_LAUNCH;
+    // the host vector must outlive the copy
+    return hipStreamSynchronize(stream) == hipSuccess ? GPTQ_OK : GPTQ_ERR_DEVICE;
+  } catch (const std::bad_alloc&) {
+    return GPTQ_ERR_NO_MEM;
+  } catch (...) {
+    return GPTQ_ERR_DEVICE;
+  }
+}
+
+int gptq_gemm_sorted(const void* x, const int32_t* qweight_sorted, const int32_t* qzeros, const void* scales,
+                     const int32_t* perm, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                     void* out, void* stream, int layout, int path, int decode_waves) {
+  try {
+    if (!perm) return GPTQ_ERR_NULL_PTR;
+    if (!aligned(perm, 4)) return GPTQ_ERR_MISALIGNED;
+    if (layout != 0 && layout != 1) return GPTQ_ERR_BAD_ARG;
+    if (K % 8 != 0) return GPTQ_ERR_BAD_SHAPE;
+    return gemm_impl(x, qweight_sorted, qzeros, scales, nullptr, bits, group_size, is_v2, M, N, K, out, stream, path,
+                     decode_waves, layout == 1, perm);
+  } catch (const std::bad_alloc&) {
+    return GPTQ_ERR_NO_MEM;
+  } catch (...) {
+    return GPTQ_ERR_DEVICE;
+  }
+}
+
 int gptq_moe_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
                   const int32_t* g_idx, const int32_t* expert_offsets, int n_experts, int max_tokens_per_expert,
                   int bits, int group_size, int is_v2, int64_t T, int64_t N, int64_t K, void* out, void* stream) {
@@ -575,7 +661,7 @@ const char* gptq_strerror(int code) {
     case GPTQ_ERR_BAD_SHAPE: return "bad shape: need M >= 0, N and K positive multiples of 32, within size limits";
     case GPTQ_ERR_BAD_GROUP: return "group_size must be positive and divide K";
     case GPTQ_ERR_MISALIGNED: return "misaligned pointer (x, qweight, g_idx, out: 16 B; scales: 8 B; qzeros: 4 B)";
-    case GPTQ_ERR_NO_MEM: return "device memory allocation failed (quantizer temporary)";
+    case GPTQ_ERR_NO_MEM: return "device memory allocation failed (a temporary or workspace; none is allocated during stream capture)";
     case GPTQ_ERR_LAUNCH: return "kernel launch failed";
     case GPTQ_ERR_DEVICE: return "HIP runtime call failed";
     case GPTQ_ERR_BAD_ARG: return "option out of range (is_v2, sym, to_v2, path or decode_waves) or overlapping buffers";

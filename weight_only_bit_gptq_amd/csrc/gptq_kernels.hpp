@@ -107,6 +107,12 @@ hipError_t launch_quantize(const float* w, const int32_t* g_idx, int bits, int g
 hipError_t launch_repack(const int32_t* in, int32_t* out, int bits, int64_t N, int64_t K, int to_tiled,
                          hipStream_t stream);
 
+// Act-order rows sorted by group (qweight rows permuted bit-exactly) and x
+// gathered into the sorted row order.
+hipError_t launch_sort_rows(const int32_t* in, const int32_t* perm, int32_t* out, int bits, int64_t N, int64_t K,
+                            hipStream_t stream);
+hipError_t launch_gather_cols(const void* x, const int32_t* perm, void* xg, int64_t M, int64_t K, hipStream_t stream);
+
 // GPTQv1 <-> GPTQv2 stored zero conversion of a packed qzeros [G, N*b/32].
 hipError_t launch_convert_zeros(const int32_t* in, int32_t* out, int bits, int64_t G, int64_t N, int to_v2,
                                 int32_t* lossy_count, hipStream_t stream);

@@ -299,4 +299,80 @@ hipError_t launch_repack(const int32_t* in, int32_t* out, int bits, int64_t N, i
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Act-order row sort.  perm[i] is the original row of sorted row i (rows
+// ordered by group).  One thread per (32-row chunk of the sorted layer,
+// column): it gathers the 32 fields of rows perm[32c .. 32c + 32) of its
+// column from the packed checkpoint layout and packs them into the chunk's
+// BITS words.  Reads are scattered; this runs once per layer.
+template <int BITS>
+__device__ __forceinline__ uint32_t field_of_row(const uint32_t* __restrict__ q, int64_t N, int64_t n, int r) {
+  if constexpr (BITS == 3) {
+    const int c = r >> 5, f = r & 31;                      // chunk, field: bit 3f of the chunk's 96 bits
+    const int w = 3 * c + ((3 * f) >> 5), off = (3 * f) & 31;
+    uint32_t v = q[(int64_t)w * N + n] >> off;
+    if (off > 29) v |= q[(int64_t)(w + 1) * N + n] << (32 - off);
+    return v & 7u;
+  } else {
+    constexpr int PER = 32 / BITS;
+    return (q[(int64_t)(r / PER) * N + n] >> (BITS * (r % PER))) & ((1u << BITS) - 1u);
+  }
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(256) sort_rows_kernel(const int32_t* __restrict__ in, const int32_t* __restrict__ perm,
+                                                        int32_t* __restrict__ out, int64_t N, int chunks) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  if (n >= N || c >= chunks) return;
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(in);
+  uint32_t w[BITS];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) w[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t f = field_of_row<BITS>(q, N, n, perm[32 * c + i]);
+    const int bit = BITS * i;                              // LSB-first stream of the chunk
+    w[bit >> 5] |= f << (bit & 31);
+    if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
+  }
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) out[((int64_t)c * BITS + i) * N + n] = (int32_t)w[i];
+}
+
+hipError_t launch_sort_rows(const int32_t* in, const int32_t* perm, int32_t* out, int bits, int64_t N, int64_t K,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / 32)), block(256);
+  const int chunks = (int)(K / 32);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(sort_rows_kernel<2>, grid, block, 0, stream, in, perm, out, N, chunks); break;
+    case 3: hipLaunchKernelGGL(sort_rows_kernel<3>, grid, block, 0, stream, in, perm, out, N, chunks); break;
+    case 4: hipLaunchKernelGGL(sort_rows_kernel<4>, grid, block, 0, stream, in, perm, out, N, chunks); break;
+    default: hipLaunchKernelGGL(sort_rows_kernel<8>, grid, block, 0, stream, in, perm, out, N, chunks); break;
+  }
+  return hipGetLastError();
+}
+
+// x gathered into the sorted row order: xg[m, i] = x[m, perm[i]].  One thread
+// per 8 consecutive i (one 16-byte store).
+__global__ void __launch_bounds__(256) gather_cols_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+                                                          uint16_t* __restrict__ xg, int64_t M, int64_t K) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (m, i / 8)
+  const int64_t per_row = K / 8;
+  if (t >= M * per_row) return;
+  const int64_t m = t / per_row, i0 = (t - m * per_row) * 8;
+  typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+  u16x8_t v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = x[m * K + perm[i0 + j]];
+  *reinterpret_cast<u16x8_t*>(xg + m * K + i0) = v;
+}
+
+hipError_t launch_gather_cols(const void* x, const int32_t* perm, void* xg, int64_t M, int64_t K, hipStream_t stream) {
+  const int64_t threads = M * (K / 8);
+  hipLaunchKernelGGL(gather_cols_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), perm, static_cast<uint16_t*>(xg), M, K);
+  return hipGetLastError();
+}
+
 }  // namespace gptq

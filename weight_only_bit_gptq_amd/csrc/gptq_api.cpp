@@ -140,6 +140,24 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
   // chunks (32-column tiles with 4 waves of 8 chunks from N = 16384 on) were
   // the fastest or within 3% of it on every Llama-7B decode layer in MI355X
   // sweeps, where the general rules below lose up to 10%
+  // tiled layout, 2..16 rows, full-width: 8 chunks per wave, 64-column tiles
+  // for 2/4-bit layers from N = 8192 on (32-column otherwise), 8 or 4 waves,
+  // whichever pads K less (8 on a tie), two K splits for N <= 4096 with
+  // K >= 8192 -- the fastest shapes of MI355X sweeps at M = 4 and 16, where
+  // the general rules below are up to 40% slower
+  if (tiled && M > 1 && !per_elem && waves == 0 && N / 16 >= kCUs / 2) {
+    const int C = K / 32;
+    const int cpl = (bits == 2 || bits == 4) && N >= 8192 ? 4 : 2;
+    const int ks = (allow_split && N <= 4096 && K >= 8192) ? 2 : 1;
+    const int cks = (C + ks - 1) / ks;
+    const int waste8 = (cks + 63) / 64 * 64 - cks, waste4 = (cks + 31) / 32 * 32 - cks;
+    const int nw = waste4 < waste8 ? 4 : 8;
+    size_t lds;
+    if (decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, 8, ks, &best, &lds)) {
+      apply_choice(best, K, G, per_elem, a);
+      return true;
+    }
+  }
   if (tiled && M == 1 && !per_elem && waves == 0 && N / 16 >= kCUs / 2) {
     size_t lds;
     const bool wide = N >= 16384;

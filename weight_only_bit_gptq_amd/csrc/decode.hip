@@ -282,13 +282,15 @@ void decode_kernel(GemmArgs a) {
           const _Float16 inv = (_Float16)(1.0f / (float)Block<BITS>::MUL[v]);
           const _Float16 mul = (_Float16)Block<BITS>::MUL[v];
           pr = pr * half2_t{inv, inv};
-          xs = __builtin_amdgcn_fdot2(pr, half2_t{mul, mul}, xs, false);
+          if constexpr (MV == 1) xs = __builtin_amdgcn_fdot2(pr, half2_t{mul, mul}, xs, false);
         }
         av[2 * v] = pr[0];
         av[2 * v + 1] = pr[1];
       }
       *reinterpret_cast<half8_t*>(frag + (((cl * 4 + kbe) * M + m) << 3)) = av;
-      if constexpr (!PER_ELEM) {
+      // one-row instantiation: the chunk's sum of x (x' MUL) for the zero
+      // term; the multi-row one gets its sums from an MFMA at compute time
+      if constexpr (!PER_ELEM && MV == 1) {
         xs += __shfl_xor(xs, 1);
         xs += __shfl_xor(xs, 2);
         if (kbe == 0) corr[cl * Mp + m] = xs;
@@ -477,7 +479,7 @@ void decode_kernel(GemmArgs a) {
   // overlaps the previous chunk's work
   struct FastOps {
     half8_t A;
-    float X[MV];
+    float X[1];                                      // one-row instantiation only
     float s1[CPL], s2[CPL];
   };
   auto fast_ops = [&](int p, int u, int row) __attribute__((always_inline)) {
@@ -486,9 +488,10 @@ void decode_kernel(GemmArgs a) {
     const _Float16* frag = reinterpret_cast<const _Float16*>(base);
     // rows >= M of A only feed rows >= M of D, which are never used
     o.A = *reinterpret_cast<const half8_t*>(frag + (((u * 4 + kb) * M + min(q, M - 1)) << 3));
-    const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + u * Mp + 4 * kbc;
-#pragma unroll
-    for (int v = 0; v < MV; ++v) o.X[v] = corr[v];
+    if constexpr (MV == 1) {
+      const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + u * Mp + 4 * kbc;
+      o.X[0] = corr[0];
+    }
     // the group row is wave-uniform: keep its offset in a scalar register
     const int row_bytes = __builtin_amdgcn_readfirstlane(row * TN * 8);
     const float* te = reinterpret_cast<const float*>(base + lay.ptab_off + row_bytes);
@@ -537,6 +540,24 @@ void decode_kernel(GemmArgs a) {
         accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), accg[j], 0, 0, 0);
       }
     } else {
+      // sums of x over the chunk for every row: one MFMA against a B operand
+      // holding each register's MUL, i.e. sum x' MUL = what the one-row
+      // staging computes with dot products (D rows 4 kb + v = this lane's rows)
+      float X[MV];
+      if constexpr (MV == 1) {
+        X[0] = fo.X[0];
+      } else {
+        half8_t ones;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          ones[2 * v] = (_Float16)Block<BITS>::MUL[v];
+          ones[2 * v + 1] = (_Float16)Block<BITS>::MUL[v];
+        }
+        const floatx4_t dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(fo.A, ones, floatx4_t{0.f, 0.f, 0.f, 0.f},
+                                                                    0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < MV; ++v) X[v] = dx[v];
+      }
       floatx4_t d[CPL];
       float s1[CPL];
 #pragma unroll
@@ -548,7 +569,7 @@ void decode_kernel(GemmArgs a) {
         d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fo.A, __builtin_bit_cast(half8_t, bw),
                                                       floatx4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int v = 0; v < MV; ++v) acc[j][v] = __builtin_fmaf(fo.s2[j], fo.X[v], acc[j][v]);
+        for (int v = 0; v < MV; ++v) acc[j][v] = __builtin_fmaf(fo.s2[j], X[v], acc[j][v]);
       }
       // with one or two MFMAs per chunk the previous chunk's products are
       // folded in while this chunk's MFMAs run; four cover their own latency

@@ -180,6 +180,11 @@ void decode_kernel(GemmArgs a) {
     if ((units & 7) == 0) unit = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
   }
   constexpr int XP = decode_x_pieces_of(MV);
+  // the zero term's per-chunk sums of x: dot products at staging for one row,
+  // an extra MFMA per chunk for several rows (for one row the extra MFMA in
+  // every chunk's chain measured slower on MI355X; for 4 and 16 rows the
+  // staging work it removes made the layers 5-21% faster)
+  constexpr bool kSumsByMfma = MV != 1;
   constexpr int GP = (CPW + 7) / 8;                  // g_idx pieces: 8 * CPW rows <= 64 * GP pieces of 4
   constexpr int TQ = decode_table_quads(PER_ELEM, CPL, CPW);
   constexpr int TN = 16 * CPL;
@@ -282,7 +287,7 @@ void decode_kernel(GemmArgs a) {
           const _Float16 inv = (_Float16)(1.0f / (float)Block<BITS>::MUL[v]);
           const _Float16 mul = (_Float16)Block<BITS>::MUL[v];
           pr = pr * half2_t{inv, inv};
-          if constexpr (MV == 1) xs = __builtin_amdgcn_fdot2(pr, half2_t{mul, mul}, xs, false);
+          if constexpr (!kSumsByMfma) xs = __builtin_amdgcn_fdot2(pr, half2_t{mul, mul}, xs, false);
         }
         av[2 * v] = pr[0];
         av[2 * v + 1] = pr[1];
@@ -290,7 +295,7 @@ void decode_kernel(GemmArgs a) {
       *reinterpret_cast<half8_t*>(frag + (((cl * 4 + kbe) * M + m) << 3)) = av;
       // one-row instantiation: the chunk's sum of x (x' MUL) for the zero
       // term; the multi-row one gets its sums from an MFMA at compute time
-      if constexpr (!PER_ELEM && MV == 1) {
+      if constexpr (!PER_ELEM && !kSumsByMfma) {
         xs += __shfl_xor(xs, 1);
         xs += __shfl_xor(xs, 2);
         if (kbe == 0) corr[cl * Mp + m] = xs;
@@ -488,7 +493,7 @@ void decode_kernel(GemmArgs a) {
     const _Float16* frag = reinterpret_cast<const _Float16*>(base);
     // rows >= M of A only feed rows >= M of D, which are never used
     o.A = *reinterpret_cast<const half8_t*>(frag + (((u * 4 + kb) * M + min(q, M - 1)) << 3));
-    if constexpr (MV == 1) {
+    if constexpr (!kSumsByMfma) {
       const float* corr = reinterpret_cast<const float*>(base + lay.corr_off) + u * Mp + 4 * kbc;
       o.X[0] = corr[0];
     }
@@ -544,7 +549,7 @@ void decode_kernel(GemmArgs a) {
       // holding each register's MUL, i.e. sum x' MUL = what the one-row
       // staging computes with dot products (D rows 4 kb + v = this lane's rows)
       float X[MV];
-      if constexpr (MV == 1) {
+      if constexpr (!kSumsByMfma) {
         X[0] = fo.X[0];
       } else {
         half8_t ones;

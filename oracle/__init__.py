@@ -13,6 +13,9 @@ or format document is available to pin it.
 """
 from .gptq_ref import (  # noqa: F401
     fp16_rne,
+    bf16_rne,
+    bf16_bits,
+    bf16_from_bits,
     max_q,
     num_groups,
     group_of_rows,

@@ -31,7 +31,11 @@ Readings where the pages are silent (each listed in the design notes):
 - qweight is [K*b/32, N] (packed along K), qzeros is [G, N*b/32] (packed along
   N), scales is fp16 [G, N], g_idx[k] is the group of row k (absent: k // gs);
 - dequant is one round-to-nearest-even of the exact product (q - z)*s to fp16;
-- the GEMM is y = x @ W^ with x and W^ widened to fp64.
+- the GEMM is y = x @ W^ with x and W^ widened to fp64;
+- bfloat16 activations (named beside fp16 by "Weight-only INT4 quantization:
+  GPTQ, AWQ and the Marlin kernel", section 1.2, which gives no formula for
+  them): x, the scales and W^ are bfloat16, W^ = bf16_RNE((q - z) * s), the
+  same one rounding as the fp16 formula with the other 16-bit type.
 """
 from __future__ import annotations
 
@@ -49,6 +53,44 @@ def fp16_rne(a) -> np.ndarray:
     numpy converts float64 to float16 directly (one rounding), which is the
     rounding the dequant formula needs [P1-WQ]."""
     return np.asarray(a, dtype=np.float64).astype(np.float16)
+
+
+_BF16_MAX = float.fromhex("0x1.fep127")    # largest finite bfloat16, (2 - 2^-7) 2^127
+
+
+def bf16_rne(a) -> np.ndarray:
+    """Round fp64 values to bfloat16 (8 significant bits, fp32's exponent range),
+    nearest-even; subnormals kept, overflow -> inf.  Returns the rounded values
+    as float64 (every bfloat16 value is exact there).
+
+    The 16-bit activation type the pages allow besides fp16 ("Weight-only INT4
+    quantization: GPTQ, AWQ and the Marlin kernel", section 1.2).  A value with
+    |a| in [2^(e-1), 2^e) has bf16 spacing 2^(e-8); below the smallest normal
+    2^-126 the spacing stays 2^-133."""
+    a = np.asarray(a, dtype=np.float64)
+    out = a.copy()
+    fin = np.isfinite(a) & (a != 0)
+    v = a[fin]
+    _, e = np.frexp(v)
+    step = np.maximum(e, -125) - 8
+    r = np.ldexp(np.rint(np.ldexp(v, -step)), step)
+    r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, r), r)
+    out[fin] = r
+    return out
+
+
+def bf16_bits(values) -> np.ndarray:
+    """bfloat16 values (float, exactly representable) -> their 16-bit patterns."""
+    v = np.asarray(values, dtype=np.float64)
+    if not np.array_equal(bf16_rne(v), v, equal_nan=True):
+        raise ValueError("values are not exact bfloat16 values")
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_from_bits(bits) -> np.ndarray:
+    """16-bit bfloat16 patterns -> float64 values."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
 
 
 def max_q(bits: int) -> int:
@@ -240,12 +282,19 @@ def unrepack_tiled(tiled: np.ndarray, bits: int, K: int, N: int) -> np.ndarray:
 
 def dequant_ref(qweight: np.ndarray, qzeros: np.ndarray, scales: np.ndarray,
                 g_idx: Optional[np.ndarray], bits: int, group_size: int, is_v2: bool,
-                K: int, N: int, cols: Optional[np.ndarray] = None) -> np.ndarray:
+                K: int, N: int, cols: Optional[np.ndarray] = None, act: str = "fp16") -> np.ndarray:
     """W^[k, n] = fp16_rne((q[k,n] - z[g(k), n]) * s[g(k), n]) from packed data only.
 
     z = stored zero + zero_offset, zero_offset = 0 for v2 and 1 for v1
     [P1-ADJ]; the sum is a plain integer (a stored 2^b - 1 under v1 gives 2^b).
-    ``cols`` optionally restricts the result to a subset of output columns."""
+    ``cols`` optionally restricts the result to a subset of output columns.
+
+    act="bf16": the layer of a bfloat16 model -- scales are bfloat16 values
+    (given as floats, each exactly representable) and W^ is the product
+    rounded once to bfloat16 (returned as float64 values); the pages name
+    bfloat16 next to fp16 as the activation type (P3 section 1.2)."""
+    if act not in ("fp16", "bf16"):
+        raise ValueError("act must be 'fp16' or 'bf16'")
     G = num_groups(K, group_size)
     if cols is None:
         cols = np.arange(N)
@@ -257,6 +306,12 @@ def dequant_ref(qweight: np.ndarray, qzeros: np.ndarray, scales: np.ndarray,
     g = group_of_rows(K, group_size, g_idx)
     if g.size and (g.min() < 0 or g.max() >= G):
         raise ValueError("g_idx entries must lie in [0, G)")
+    if act == "bf16":
+        s = np.asarray(scales, dtype=np.float64)[:, cols]
+        if not np.array_equal(bf16_rne(s), s):
+            raise ValueError("bf16 scales must be exact bfloat16 values")
+        prod = (q - z[g]).astype(np.float64) * s[g]  # exact: <= 9 + 8 significant bits
+        return bf16_rne(prod)
     s = np.asarray(scales, dtype=np.float16)[:, cols].astype(np.float64)
     prod = (q - z[g]).astype(np.float64) * s[g]     # exact: <= 9 + 11 significant bits
     return fp16_rne(prod)
@@ -268,10 +323,11 @@ def gemm_ref(x: np.ndarray, W_hat: np.ndarray) -> np.ndarray:
 
 
 def gptq_gemm_ref(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K, N,
-                  cols=None) -> np.ndarray:
-    """The whole path on the CPU: dequantize from the packed arrays, then multiply."""
+                  cols=None, act: str = "fp16") -> np.ndarray:
+    """The whole path on the CPU: dequantize from the packed arrays, then multiply.
+    act="bf16": x and scales hold bfloat16 values (see dequant_ref)."""
     return gemm_ref(x, dequant_ref(qweight, qzeros, scales, g_idx, bits, group_size,
-                                   is_v2, K, N, cols=cols))
+                                   is_v2, K, N, cols=cols, act=act))
 
 
 def sort_act_order(qweight: np.ndarray, g_idx: np.ndarray, bits: int, group_size: int, K: int):

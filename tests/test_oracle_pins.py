@@ -2,7 +2,8 @@
 
 - hand-derived packed words and worked quantization examples (tests/golden);
 - an independent pure-Python extractor (one big integer per column);
-- Python's own half-precision packing (struct 'e') for fp16 rounding;
+- Python's own half-precision packing (struct 'e') for fp16 rounding, and
+  torch's float32 -> bfloat16 conversion for bfloat16 rounding;
 - closed forms and invariants of the min/max formulas and of the v1/v2 zero
   formats ("Enhancing vLLM's support for the GPTQv2 format", sections "Weight
   quantization of LLMs" and "From GPTQv1 to GPTQv2");
@@ -414,6 +415,91 @@ def test_gemm_closed_forms():
                             np.ones((K // gs, N), np.float16), None, bits, gs, True, K, N)
     xi = rng.integers(-3, 4, (2, K)).astype(np.float16)
     assert np.array_equal(oracle.gemm_ref(xi, wi), xi.astype(np.int64) @ qi)
+
+
+# ---------------------------------------------------------------- bfloat16 activations
+def bf16_torch(values):
+    """Round float32-exact values to bfloat16 with torch's own conversion."""
+    import torch
+    t = torch.from_numpy(np.asarray(values, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_rne_closed_forms():
+    r = oracle.bf16_rne
+    one = 1.0
+    assert r(np.array([one + 2.0 ** -8]))[0] == one                        # tie -> even
+    assert r(np.array([one + 3 * 2.0 ** -8]))[0] == one + 2.0 ** -6        # tie -> even (up)
+    assert r(np.array([one + 2.0 ** -8 + 2.0 ** -30]))[0] == one + 2.0 ** -7
+    assert r(np.array([2.0 ** -133]))[0] == 2.0 ** -133                     # smallest subnormal
+    assert r(np.array([2.0 ** -134]))[0] == 0.0                             # tie -> even zero
+    assert r(np.array([3 * 2.0 ** -134]))[0] == 2.0 ** -132                 # 1.5 ulp -> 2 ulp
+    assert r(np.array([-(2.0 ** -126) * 1.00390625]))[0] == -(2.0 ** -126)  # normal, tie to even
+    big = float.fromhex("0x1.fep127")
+    assert r(np.array([big]))[0] == big
+    assert r(np.array([big + 2.0 ** 118]))[0] == big                          # below the tie at max
+    assert np.isinf(r(np.array([big + 2.0 ** 119, -1e39]))).all()          # the tie at max overflows
+    assert r(np.array([0.0]))[0] == 0.0 and np.isnan(r(np.array([np.nan])))[0]
+    # the bit helpers agree with the format's layout: sign, 8 exponent, 7 mantissa bits
+    assert oracle.bf16_bits(np.array([1.0, -2.0, 2.0 ** -133])).tolist() == [0x3F80, 0xC000, 0x0001]
+    assert oracle.bf16_from_bits(np.array([0x3F80, 0x4049])).tolist() == [1.0, 3.140625]
+
+
+def test_bf16_rne_matches_torch():
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal(200000).astype(np.float32)
+    with np.errstate(over="ignore"):
+        v = (v * np.exp2(rng.integers(-140, 129, v.size)).astype(np.float32)).astype(np.float32)
+    # exact ties (8 significant bits + a half ulp)
+    t = (rng.integers(128, 256, 2000) * 2 + 1).astype(np.float64) * np.exp2(rng.integers(-20, 20, 2000) - 9)
+    vals = np.concatenate([v.astype(np.float64), t, -t])
+    assert np.array_equal(oracle.bf16_rne(vals), bf16_torch(vals.astype(np.float32)), equal_nan=True)
+
+
+@pytest.mark.parametrize("bits,is_v2,act", list(itertools.product(BITS, (False, True), (False, True))))
+def test_dequant_bf16_matches_bruteforce(bits, is_v2, act):
+    K, N, gs = 64, 32, 32
+    rng = np.random.default_rng(bits * 10 + is_v2 * 2 + act + 100)
+    qweight = random_words(rng, (K * bits // 32, N))
+    qzeros = random_words(rng, (K // gs, N * bits // 32))
+    scales = bf16_torch(rng.standard_normal((K // gs, N)) * 0.02)
+    scales[0, 0] = 2.0 ** -130                # products land in the bf16 subnormal range
+    g_idx = rng.permutation(np.arange(K) // gs).astype(np.int32) if act else None
+    got = oracle.dequant_ref(qweight, qzeros, scales, g_idx, bits, gs, is_v2, K, N, act="bf16")
+    cols = [bigint_fields(qweight[:, n], bits, K) for n in range(N)]
+    zrows = [bigint_fields(qzeros[g], bits, N) for g in range(K // gs)]
+    exact = np.empty((K, N))
+    for k in range(K):
+        g = int(g_idx[k]) if g_idx is not None else k // gs
+        for n in range(N):
+            exact[k, n] = (cols[n][k] - zrows[g][n] - (0 if is_v2 else 1)) * float(scales[g, n])
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)   # exact in fp32
+    assert np.array_equal(got, bf16_torch(exact))
+
+
+def test_dequant_bf16_rejects_inexact_scales():
+    K, N, bits = 32, 32, 4
+    qw = np.zeros((K * bits // 32, N), np.int32)
+    qz = np.zeros((1, N * bits // 32), np.int32)
+    with pytest.raises(ValueError):
+        oracle.dequant_ref(qw, qz, np.full((1, N), 1.0 + 2.0 ** -10), None, bits, K, True, K, N, act="bf16")
+
+
+def test_gemm_bf16_matches_triple_loop():
+    M, K, N, gs, bits = 3, 64, 32, 32, 3
+    d = draw_layer(K, N, M, sigma=0.02, group_size=gs, act_order=True, seed=6)
+    L = oracle.quantize_layer(d.W, bits, gs, sym=False, is_v2=True, g_idx=d.g_idx)
+    s16 = bf16_torch(L.scales.astype(np.float64))
+    x16 = bf16_torch(d.x.astype(np.float64))
+    y = oracle.gptq_gemm_ref(x16, L.qweight, L.qzeros, s16, L.g_idx, bits, gs, True, K, N, act="bf16")
+    cols = [bigint_fields(L.qweight[:, n], bits, K) for n in range(N)]
+    zrows = [bigint_fields(L.qzeros[g], bits, N) for g in range(K // gs)]
+    for m in range(M):
+        for n in range(N):
+            w = [bf16_torch([(cols[n][k] - zrows[int(L.g_idx[k])][n]) * float(s16[int(L.g_idx[k]), n])])[0]
+                 for k in range(K)]
+            exact = math.fsum(float(x16[m, k]) * w[k] for k in range(K))
+            assert abs(y[m, n] - exact) <= 1e-12 * max(1.0, abs(exact))
 
 
 # ---------------------------------------------------------------- the low-bit workload

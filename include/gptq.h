@@ -262,7 +262,35 @@ GPTQ_API int gptq_gemm_sorted(const void* x, const int32_t* qweight_sorted, cons
                               int decode_waves);
 
 /*
- * Grouped (mixture-of-experts) decode GEMM/*
+ * bfloat16 activations (page "Weight-only INT4 quantization: GPTQ, AWQ and
+ * the Marlin kernel", section 1.2: activations stay 16-bit, fp16 or bf16).
+ * Same arguments, layouts, checks, return codes and workspace rules as
+ * gptq_gemm / gptq_gemm_ex / gptq_gemm_describe / gptq_dequant, with x,
+ * scales and out (w_out) holding bfloat16 instead of fp16:
+ *   W^[k, n] = bf16_RNE((q - z) * s),  y = x . W^ (fp32 accumulate, one
+ *   bfloat16 rounding of each output).
+ * gptq_dequant_bf16 is bit-exact with that formula.  The GEMM kernels form
+ * the same W^ values as fma(q, s, -z s) in fp32, exact while |s| < 2^119 (so
+ * that z s stays finite; real scales are many orders below).  Decode (M <= 16) always
+ * dequantizes element by element (act order or not); prefill uses the same
+ * tiles as the fp16 kernel.  Checkpoint qweight layout only (no tiled,
+ * sorted or grouped variants).
+ */
+GPTQ_API int gptq_gemm_bf16(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                            const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N,
+                            int64_t K, void* out, void* stream);
+GPTQ_API int gptq_gemm_bf16_ex(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N,
+                               int64_t K, void* out, void* stream, int path, int decode_waves);
+GPTQ_API int gptq_gemm_bf16_describe(const void* x, const int32_t* qweight, const int32_t* qzeros,
+                                     const void* scales, const int32_t* g_idx, int bits, int group_size, int is_v2,
+                                     int64_t M, int64_t N, int64_t K, const void* out, int path, int decode_waves,
+                                     char* buf, int64_t buflen);
+GPTQ_API int gptq_dequant_bf16(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t N, int64_t K,
+                               void* w_out, void* stream);
+
+/*
  * Grouped (mixture-of-experts) decode GEMM: for every expert e,
  *   out[r, :] = x[r, :] . dequant(expert e's weights)   for r in [off[e], off[e+1])
  * i.e. one gptq_gemm per expert over the tokens routed to it, in one launch

@@ -18,7 +18,7 @@ needs_lib = pytest.mark.skipif(not os.path.exists(gq.library_path()),
 
 def declared_functions():
     text = open(HEADER).read()
-    return re.findall(r"GPTQ_API\s+[A-Za-z_][A-Za-z0-9_\s\*]*?\b(gptq_[a-z_]+)\s*\(", text)
+    return re.findall(r"GPTQ_API\s+[A-Za-z_][A-Za-z0-9_\s\*]*?\b(gptq_[a-z0-9_]+)\s*\(", text)
 
 
 def declared_status():
@@ -32,6 +32,7 @@ def test_header_declares_api():
               "gptq_gemm_describe", "gptq_dequant_check", "gptq_convert_zeros", "gptq_convert_zeros_check",
               "gptq_repack_tiled", "gptq_unrepack_tiled", "gptq_gemm_tiled", "gptq_gemm_tiled_ex",
               "gptq_gemm_tiled_describe", "gptq_moe_gemm", "gptq_sort_act_order", "gptq_gemm_sorted",
+              "gptq_gemm_bf16", "gptq_gemm_bf16_ex", "gptq_gemm_bf16_describe", "gptq_dequant_bf16",
               "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
     assert declared_status() == gq.STATUS
@@ -268,3 +269,24 @@ def test_describe_names_the_kernel():
     small = ctypes.create_string_buffer(8)
     assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, 0, 0, small, 8) == 0
     assert len(small.value) == 7
+
+
+@needs_lib
+def test_describe_bf16_kernels():
+    """bfloat16 activations: decode always on the element-wise bf16 kernel (no
+    64-column tiles at one row), prefill on the bf16 twin of the fp16 tiles;
+    the same argument checks."""
+    lib = gq.library()
+    buf = ctypes.create_string_buffer(256)
+    for K, N in ((4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096)):
+        assert lib.gptq_gemm_bf16_describe(X, QW, QZ, SC, None, 4, 128, 0, 1, N, K, OUT, 0, 0, buf, 256) == 0
+        d = buf.value.decode()
+        assert d.startswith("gptq::decode_bf16_kernel<4, 1, ") and not d.startswith("gptq::decode_bf16_kernel<4, 1, 4,")
+    assert lib.gptq_gemm_bf16_describe(X, QW, QZ, SC, GI, 3, 128, 1, 16, 5120, 13824, OUT, 0, 0, buf, 256) == 0
+    assert buf.value.decode().startswith("gptq::decode_bf16_kernel<3, 4, ")
+    assert lib.gptq_gemm_bf16_describe(X, QW, QZ, SC, None, 4, 128, 0, 2048, 28672, 8192, OUT, 0, 0, buf, 256) == 0
+    assert buf.value.decode().startswith("gptq::prefill_bf16_kernel<4, false, true>")
+    assert lib.gptq_gemm_bf16_describe(X, QW, QZ, SC, None, 5, 128, 1, 1, 4096, 4096, OUT, 0, 0, buf, 256) == -2
+    assert lib.gptq_gemm_bf16_describe(X, QW, QZ, SC, None, 4, 100, 1, 1, 4096, 4096, OUT, 0, 0, buf, 256) == -4
+    assert lib.gptq_dequant_bf16(QW, QZ, SC, None, 4, 100, 1, 4096, 4096, OUT, None) == -4
+    assert lib.gptq_gemm_bf16(X, QW, QZ, SC, None, 4, 100, 1, 1, 4096, 4096, OUT, None) == -4

@@ -60,6 +60,13 @@ def library() -> ctypes.CDLL:
         lib.gptq_gemm_ex.argtypes = gemm_args + [i32, i32]
         lib.gptq_gemm_ex.restype = i32
         lib.gptq_dequant.argtypes = [i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, vp, vp]
+        for name in ("gptq_gemm_bf16", "gptq_gemm_bf16_ex", "gptq_gemm_bf16_describe", "gptq_dequant_bf16"):
+            getattr(lib, name).restype = i32
+        lib.gptq_gemm_bf16.argtypes = gemm_args
+        lib.gptq_gemm_bf16_ex.argtypes = gemm_args + [i32, i32]
+        lib.gptq_gemm_bf16_describe.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, i32,
+                                                i32, ctypes.c_char_p, i64]
+        lib.gptq_dequant_bf16.argtypes = [i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, vp, vp]
         lib.gptq_dequant.restype = i32
         lib.gptq_gemm_check.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp]
         lib.gptq_gemm_check.restype = i32
@@ -125,8 +132,9 @@ def _check_tensor(name, t, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K=None):
+def _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K=None, sdtype=None):
     import torch
+    sdtype = torch.float16 if sdtype is None else sdtype
     if bits not in (2, 3, 4, 8):
         raise ValueError("bits must be 2, 3, 4 or 8")
     if is_v2 not in (0, 1, True, False):
@@ -134,7 +142,7 @@ def _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K=None):
     dev = qweight.device if isinstance(qweight, torch.Tensor) else None
     _check_tensor("qweight", qweight, torch.int32, dev)
     _check_tensor("qzeros", qzeros, torch.int32, dev)
-    _check_tensor("scales", scales, torch.float16, dev)
+    _check_tensor("scales", scales, sdtype, dev)
     if g_idx is not None:
         _check_tensor("g_idx", g_idx, torch.int32, dev)
     if qzeros.dim() != 2 or scales.dim() != 2:
@@ -167,29 +175,45 @@ def _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K=None):
     return dev, N, K
 
 
+def _act_dtype(x, qweight):
+    """Activation type of a call: x's dtype, fp16 or (checkpoint layout only) bf16."""
+    import torch
+    dt = getattr(x, "dtype", None)
+    if dt == torch.bfloat16:
+        if getattr(qweight, "dim", lambda: 2)() == 4:
+            raise ValueError("bfloat16 activations take the checkpoint qweight layout")
+        return dt
+    return torch.float16
+
+
 def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,
          is_v2: bool, *, out=None, path: int = PATH_AUTO, decode_waves: int = 0):
-    """out[M, N] (fp16) = x[M, K] (fp16) . dequant(qweight, qzeros, scales, g_idx).
+    """out[M, N] = x[M, K] . dequant(qweight, qzeros, scales, g_idx).
 
-    qweight is the checkpoint layout [K*bits/32, N] or, 4-D, the tiled layout
-    made by `repack_tiled`.  Enqueued on the current HIP stream of x's device
-    (asynchronous)."""
+    x, scales and out are all fp16, or all bfloat16 (gptq_gemm_bf16; checkpoint
+    layout only).  qweight is the checkpoint layout [K*bits/32, N] or, 4-D,
+    the tiled layout made by `repack_tiled`.  Enqueued on the current HIP
+    stream of x's device (asynchronous)."""
     import torch
-    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
-    _check_tensor("x", x, torch.float16, dev)
+    act = _act_dtype(x, qweight)
+    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, sdtype=act)
+    _check_tensor("x", x, act, dev)
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [M, {K}], got {tuple(x.shape)}")
     M = x.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+        out = torch.empty((M, N), dtype=act, device=dev)
     else:
-        _check_tensor("out", out, torch.float16, dev)
+        _check_tensor("out", out, act, dev)
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out must be [{M}, {N}]")
     lib = library()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        fn = lib.gptq_gemm_tiled_ex if qweight.dim() == 4 else lib.gptq_gemm_ex
+        if act == torch.bfloat16:
+            fn = lib.gptq_gemm_bf16_ex
+        else:
+            fn = lib.gptq_gemm_tiled_ex if qweight.dim() == 4 else lib.gptq_gemm_ex
         code = fn(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
                   None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
                   int(bool(is_v2)), M, N, K, out.data_ptr(), stream, int(path), int(decode_waves))
@@ -201,13 +225,17 @@ def describe(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, gro
              is_v2: bool, *, out=None, path: int = PATH_AUTO, decode_waves: int = 0) -> str:
     """Kernel instantiation and launch shape `gemm` with these arguments uses."""
     import torch
-    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
-    _check_tensor("x", x, torch.float16, dev)
+    act = _act_dtype(x, qweight)
+    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, sdtype=act)
+    _check_tensor("x", x, act, dev)
     M = x.shape[0]
     out_ptr = out.data_ptr() if out is not None else x.data_ptr()
     buf = ctypes.create_string_buffer(256)
     lib = library()
-    fn = lib.gptq_gemm_tiled_describe if qweight.dim() == 4 else lib.gptq_gemm_describe
+    if act == torch.bfloat16:
+        fn = lib.gptq_gemm_bf16_describe
+    else:
+        fn = lib.gptq_gemm_tiled_describe if qweight.dim() == 4 else lib.gptq_gemm_describe
     code = fn(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
               None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
               int(bool(is_v2)), M, N, K, out_ptr, int(path), int(decode_waves), buf, 256)
@@ -217,21 +245,24 @@ def describe(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, gro
 
 def dequant(qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,
             is_v2: bool, *, out=None):
-    """W^ [K, N] fp16, bit-exact dequantization of the packed weights (checkpoint layout)."""
+    """W^ [K, N], bit-exact dequantization of the packed weights (checkpoint layout),
+    in the scales' type: fp16, or bfloat16 (gptq_dequant_bf16)."""
     import torch
     if isinstance(qweight, torch.Tensor) and qweight.dim() == 4:
         raise ValueError("dequant takes the checkpoint qweight layout (unrepack_tiled the tiled one)")
-    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
+    act = torch.bfloat16 if getattr(scales, "dtype", None) == torch.bfloat16 else torch.float16
+    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, sdtype=act)
     if out is None:
-        out = torch.empty((K, N), dtype=torch.float16, device=dev)
+        out = torch.empty((K, N), dtype=act, device=dev)
     else:
-        _check_tensor("out", out, torch.float16, dev)
+        _check_tensor("out", out, act, dev)
         if tuple(out.shape) != (K, N):
             raise ValueError(f"out must be [{K}, {N}]")
     lib = library()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        code = lib.gptq_dequant(qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+        fn = lib.gptq_dequant_bf16 if act == torch.bfloat16 else lib.gptq_dequant
+        code = fn(qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
                                 None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
                                 int(bool(is_v2)), N, K, out.data_ptr(), stream)
     _raise(code)

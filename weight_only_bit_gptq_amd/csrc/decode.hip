@@ -72,9 +72,11 @@ __host__ __device__ constexpr int decode_max_threads(int bits, bool per_elem, in
 
 // CPW values compiled: at most 64 weight words per lane in flight where that
 // leaves room for the rest (M = 1, 32- and 64-column tiles), 32 otherwise.
-__host__ __device__ constexpr bool decode_cpw_ok(int bits, bool per_elem, int cpl, int cpw, int mv) {
+// bfloat16 at M = 1 has no 64-column tiles (they spill in its register budget).
+__host__ __device__ constexpr bool decode_cpw_ok(int bits, bool per_elem, int cpl, int cpw, int mv, bool bf16 = false) {
   return (cpw == 8 || cpw == 16 || cpw == 32) &&
-         decode_words(bits, per_elem, cpl, cpw, mv) <= ((mv == 1 && cpl > 1) ? 64 : 32);
+         decode_words(bits, per_elem, cpl, cpw, mv) <= ((mv == 1 && cpl > 1) ? 64 : 32) &&
+         !(bf16 && (!per_elem || (mv == 1 && cpl == 4)));
 }
 
 template <int CPL> struct WordVec;
@@ -106,7 +108,7 @@ __host__ __device__ inline int decode_corr_rows(int M) { return M == 1 ? 1 : (M 
 // by the workgroup (two when K takes several phases: x fragments and the
 // phase's g_idx slice) plus the whole scale/zero table, behind a barrier.
 __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg,
-                                                      int phases) {
+                                                      int phases, bool bf16 = false) {
   DecodeLayout L;
   const size_t tn = (size_t)16 * cpl;
   const int cpw = pc / nw;
@@ -122,7 +124,9 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   L.buf_stride = align16(L.ptab_off + (size_t)L.ptab_rows * tn * 8);
   const int regions = per_elem ? (phases > 1 ? 2 : 1) : nw;
   L.tab_off = (size_t)regions * L.buf_stride;            // whole table (per-element path)
-  const size_t tab = per_elem ? (size_t)G * tn * 4 : 0;
+  // per-element table entry: (zero << 16 | fp16 scale), or the fp32 pair
+  // (s, -z s) for bfloat16
+  const size_t tab = per_elem ? (size_t)G * tn * (bf16 ? 8 : 4) : 0;
   // a wave stages its rows in one round; the whole table (per-element path) loops
   L.fits_staging = per_elem || (size_t)L.ptab_rows * tn / 4 <= (size_t)decode_table_quads(per_elem, cpl, cpw) * 64;
   const size_t data = L.tab_off + tab;
@@ -131,8 +135,8 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   return L;
 }
 
-size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg, int phases) {
-  const DecodeLayout L = decode_layout(M, pc, nw, cpl, per_elem, G, cpg, phases);
+size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg, int phases, bool bf16) {
+  const DecodeLayout L = decode_layout(M, pc, nw, cpl, per_elem, G, cpg, phases, bf16);
   return L.fits_staging ? L.total : ~(size_t)0;
 }
 
@@ -143,17 +147,21 @@ int decode_waves_per_simd_for(int bits, bool per_elem, int cpl, int cpw, int M) 
 int decode_max_threads_for(int bits, bool per_elem, int cpl, int cpw, int M) {
   return decode_max_threads(bits, per_elem, cpl, cpw, M == 1 ? 1 : 4);
 }
-bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M) {
-  return decode_cpw_ok(bits, per_elem, cpl, cpw, M == 1 ? 1 : 4);
+bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M, bool bf16) {
+  return decode_cpw_ok(bits, per_elem, cpl, cpw, M == 1 ? 1 : 4, bf16);
 }
 
-// Each instantiation is compiled for a fixed number of waves per SIMD, which
-// the host uses to size the grid and to know how many workgroups a CU holds.
-template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(BITS, PER_ELEM, CPL, CPW, MV))))
-__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, PER_ELEM, CPL, CPW, MV))))
-void decode_kernel(GemmArgs a) {
+// The kernel body; BF16 (per-element path only): x, scales and out are
+// bfloat16, B is the element-wise bfloat16 dequant and the MFMA the bf16 one.
+template <int BITS, bool PER_ELEM, bool BF16, int MV, int CPL, int CPW>
+__device__ __forceinline__ void decode_body(GemmArgs a) {
+  static_assert(!BF16 || PER_ELEM, "bfloat16 decode runs the per-element path");
   extern __shared__ __align__(16) unsigned char lds[];
+  // one output element, rounded to the activation type (nearest even)
+  auto store_out = [](_Float16* out, int64_t i, float v) __attribute__((always_inline)) {
+    if constexpr (BF16) reinterpret_cast<__bf16*>(out)[i] = (__bf16)v;
+    else out[i] = (_Float16)v;
+  };
   // workgroup -> (column tile t, K split sk); consecutive units share an XCD
   int unit = blockIdx.x;
   if (a.n_experts > 0) {
@@ -212,7 +220,7 @@ void decode_kernel(GemmArgs a) {
   // per-chunk sums of x in groups of four rows, so it lays out at least two
   // rows (four sums) even for a one-row block of a grouped launch
   const int ML = MV == 1 ? 1 : max(M, 2);
-  const DecodeLayout lay = decode_layout(ML, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases);
+  const DecodeLayout lay = decode_layout(ML, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases, BF16);
   const int Mp = decode_corr_rows(ML);
   const uint32_t sel = block_sel<BITS>(kb);
 
@@ -381,7 +389,18 @@ void decode_kernel(GemmArgs a) {
         sb[j] = (j & 1) ? (tsr[i][j >> 1] >> 16) : (tsr[i][j >> 1] & 0xFFFFu);
         z[j] = ((zw >> (BITS * j)) & ((1u << BITS) - 1u)) + (uint32_t)a.zero_offset;
       }
-      if constexpr (PER_ELEM) {                      // (zero + offset) << 16 | fp16 scale bits
+      if constexpr (BF16) {                          // (s, -s (zero + offset)) as fp32, exact
+        f32x4_t v0, v1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sc = real ? bf16_to_f32(sb[j]) : 0.f;
+          f32x4_t& v = j < 2 ? v0 : v1;
+          v[2 * (j & 1)] = sc;
+          v[2 * (j & 1) + 1] = -sc * (float)z[j];
+        }
+        *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8) = v0;
+        *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8 + 16) = v1;
+      } else if constexpr (PER_ELEM) {               // (zero + offset) << 16 | fp16 scale bits
         u32x4_t v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = real ? ((z[j] << 16) | sb[j]) : 0u;
@@ -529,20 +548,37 @@ void decode_kernel(GemmArgs a) {
       const u16x8_t gv = *reinterpret_cast<const u16x8_t*>(gl + 32 * cl + 8 * kb);
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        uint32_t pr[4];
-        unpack_block<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], sel, pr);
-        u32x4_t bw;
+        if constexpr (BF16) {
+          // fields in the staging's order F, each with its row's (s, -z s)
+          const f32x2_t* tab2 = reinterpret_cast<const f32x2_t*>(lds + lay.tab_off);
+          float f[8];
+          block_fields_f32<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], kb, f);
+          u32x4_t bw;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t ea = full_tab[(int)gv[Block<BITS>::F[2 * v]] * TN + CPL * q + j];
-          const uint32_t eb = full_tab[(int)gv[Block<BITS>::F[2 * v + 1]] * TN + CPL * q + j];
-          const half2_t neg = {neg_offset<BITS>(v, (int)(ea >> 16)), neg_offset<BITS>(v, (int)(eb >> 16))};
-          const half2_t d = pair_minus_zero<BITS>(pr[v], v, neg);
-          const half2_t s = {__builtin_bit_cast(_Float16, (uint16_t)(ea & 0xFFFFu)),
-                             __builtin_bit_cast(_Float16, (uint16_t)(eb & 0xFFFFu))};
-          bw[v] = as_u32(d * s);
+          for (int v = 0; v < 4; ++v) {
+            const int fa = Block<BITS>::F[2 * v], fb = Block<BITS>::F[2 * v + 1];
+            const f32x2_t ta = tab2[(int)gv[fa] * TN + CPL * q + j];
+            const f32x2_t tb = tab2[(int)gv[fb] * TN + CPL * q + j];
+            bw[v] = bf16_pair(__builtin_fmaf(f[fa], ta[0], ta[1]), __builtin_fmaf(f[fb], tb[0], tb[1]));
+          }
+          accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                            __builtin_bit_cast(bf16x8_t, bw), accg[j], 0, 0, 0);
+        } else {
+          uint32_t pr[4];
+          unpack_block<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], sel, pr);
+          u32x4_t bw;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t ea = full_tab[(int)gv[Block<BITS>::F[2 * v]] * TN + CPL * q + j];
+            const uint32_t eb = full_tab[(int)gv[Block<BITS>::F[2 * v + 1]] * TN + CPL * q + j];
+            const half2_t neg = {neg_offset<BITS>(v, (int)(ea >> 16)), neg_offset<BITS>(v, (int)(eb >> 16))};
+            const half2_t d = pair_minus_zero<BITS>(pr[v], v, neg);
+            const half2_t s = {__builtin_bit_cast(_Float16, (uint16_t)(ea & 0xFFFFu)),
+                               __builtin_bit_cast(_Float16, (uint16_t)(eb & 0xFFFFu))};
+            bw[v] = as_u32(d * s);
+          }
+          accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), accg[j], 0, 0, 0);
         }
-        accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), accg[j], 0, 0, 0);
       }
     } else {
       // sums of x over the chunk for every row: one MFMA against a B operand
@@ -706,7 +742,7 @@ void decode_kernel(GemmArgs a) {
       if (n0 + col < a.N) {
         float s = 0.f;
         for (int w = 0; w < nw; ++w) s += red[(w * M + m) * TN + col];
-        a.out[(int64_t)m * a.N + n0 + col] = (_Float16)s;
+        store_out(a.out, (int64_t)m * a.N + n0 + col, s);
       }
     }
     return;
@@ -746,10 +782,27 @@ void decode_kernel(GemmArgs a) {
       for (int k = 0; k < a.ks; ++k)
         s += __hip_atomic_load(a.ws + ((int64_t)k * M + m) * a.N + n0 + col, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-      a.out[(int64_t)m * a.N + n0 + col] = (_Float16)s;
+      store_out(a.out, (int64_t)m * a.N + n0 + col, s);
     }
   }
   if (tid == 0) __hip_atomic_store(a.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Each instantiation is compiled for a fixed number of waves per SIMD, which
+// the host uses to size the grid and to know how many workgroups a CU holds.
+template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(BITS, PER_ELEM, CPL, CPW, MV))))
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, PER_ELEM, CPL, CPW, MV))))
+void decode_kernel(GemmArgs a) {
+  decode_body<BITS, PER_ELEM, false, MV, CPL, CPW>(a);
+}
+
+// bfloat16 activations: the per-element path's launch shapes and registers
+template <int BITS, int MV, int CPL, int CPW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(BITS, true, CPL, CPW, MV))))
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, true, CPL, CPW, MV))))
+void decode_bf16_kernel(GemmArgs a) {
+  decode_body<BITS, true, true, MV, CPL, CPW>(a);
 }
 
 template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
@@ -757,8 +810,14 @@ static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
   if constexpr (!decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV)) {
     return hipErrorInvalidValue;
   } else {
-    const size_t lds = decode_lds_bytes(a.n_experts > 0 ? 16 : a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg, a.phases);
+    const size_t lds = decode_lds_bytes(a.n_experts > 0 ? 16 : a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg, a.phases,
+                                        a.bf16 != 0);
     auto kern = decode_kernel<BITS, PER_ELEM, MV, CPL, CPW>;
+    if constexpr (decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV, true)) {
+      if (a.bf16) kern = decode_bf16_kernel<BITS, MV, CPL, CPW>;
+    } else {
+      if (a.bf16) return hipErrorInvalidValue;
+    }
     if (lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

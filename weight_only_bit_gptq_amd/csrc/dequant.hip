@@ -64,19 +64,65 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   }
 }
 
+// bfloat16 layer (scales and W^ bfloat16): same grid and loads, the field
+// unpack and bfloat16 rounding of the bfloat16 GEMM kernels.  (q - z) s is
+// formed as written (the GEMM kernels' fma(q, s, -z s) gives the same value,
+// except that an exact zero there is always +0, which no sum can see).
 template <int BITS>
-static hipError_t launch_dequant_bits(const DequantArgs& a, hipStream_t stream) {
+__global__ __launch_bounds__(256) void dequant_bf16_kernel(DequantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int kb = lane >> 4;
+  const int col4 = lane & 15;
+  const int c = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int n = blockIdx.x * 64 + 4 * col4;
+  if (c >= a.chunks || n >= a.N) return;
+
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.qweight);
+  const u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(qw + (int64_t)block_row0<BITS>(c, kb) * a.N + n);
+  u32x4_t r1 = r0;
+  if constexpr (Block<BITS>::LOADS == 2)
+    r1 = *reinterpret_cast<const u32x4_t*>(qw + (int64_t)block_row1<BITS>(c, kb) * a.N + n);
+  const int k0 = 32 * c + 8 * kb;
+  const uint16_t* sc = reinterpret_cast<const uint16_t*>(a.scales);
+
+  uint32_t w[8][2];   // [row h][column pair]
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const int g = group_of(a.g_idx, k0 + h, a.group_size, a.G);
+    const uint32_t z4 = load_zero4<BITS>(a.qzeros, a.zrow_words, g, n);
+    const u32x2_t s4 = *reinterpret_cast<const u32x2_t*>(sc + (int64_t)g * a.N + n);
+    float o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float f[8];
+      block_fields_f32<BITS>(r0[j], r1[j], kb, f);
+      const float s = bf16_to_f32((s4[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      const float z = (float)(field_of4(z4, j, BITS) + a.zero_offset);
+      o[j] = (f[h] - z) * s;                     // both steps exact in fp32 (<= 9 + 8 bits)
+    }
+    w[h][0] = bf16_pair(o[0], o[1]);
+    w[h][1] = bf16_pair(o[2], o[3]);
+  }
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+    *reinterpret_cast<u32x2_t*>(out + (int64_t)(k0 + h) * a.N + n) = u32x2_t{w[h][0], w[h][1]};
+}
+
+template <int BITS>
+static hipError_t launch_dequant_bits(const DequantArgs& a, bool bf16, hipStream_t stream) {
   const dim3 grid((a.N + 63) / 64, (a.chunks + 3) / 4);
-  hipLaunchKernelGGL(dequant_kernel<BITS>, grid, dim3(256), 0, stream, a);
+  if (bf16) hipLaunchKernelGGL(dequant_bf16_kernel<BITS>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(dequant_kernel<BITS>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(int bits, const DequantArgs& a, hipStream_t stream) {
+hipError_t launch_dequant(int bits, const DequantArgs& a, bool bf16, hipStream_t stream) {
   switch (bits) {
-    case 2: return launch_dequant_bits<2>(a, stream);
-    case 3: return launch_dequant_bits<3>(a, stream);
-    case 4: return launch_dequant_bits<4>(a, stream);
-    default: return launch_dequant_bits<8>(a, stream);
+    case 2: return launch_dequant_bits<2>(a, bf16, stream);
+    case 3: return launch_dequant_bits<3>(a, bf16, stream);
+    case 4: return launch_dequant_bits<4>(a, bf16, stream);
+    default: return launch_dequant_bits<8>(a, bf16, stream);
   }
 }
 

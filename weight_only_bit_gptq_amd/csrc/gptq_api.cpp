@@ -91,10 +91,10 @@ bool better_choice(const DecodeChoice& a, const DecodeChoice& b) {
 // Launch shape of one (cpl, nw, cpw, ks) candidate, or false when it does not
 // fit (registers, LDS, x staging, split sizes).
 bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int cpl, int nw, int cpw, int ks,
-                      DecodeChoice* c, size_t* lds_out) {
+                      DecodeChoice* c, size_t* lds_out, bool bf16 = false) {
   const int C = K / 32;
   const int cpg = per_elem ? 1 : (K / G) / 32;
-  if (!gptq::decode_cpw_allowed(bits, per_elem, cpl, cpw, M)) return false;
+  if (!gptq::decode_cpw_allowed(bits, per_elem, cpl, cpw, M, bf16)) return false;
   if (cpw * M > 16 * gptq::decode_max_x_pieces(M)) return false;
   if (nw < 1 || 64 * nw > gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M)) return false;
   const int cks = (C + ks - 1) / ks;
@@ -102,7 +102,7 @@ bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int c
   if (ks > 1 && (int64_t)ks * M * N * 4 > kSplitWsCap) return false;
   const int pc = nw * cpw;
   const int phases = (cks + pc - 1) / pc;
-  const size_t lds = gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases);
+  const size_t lds = gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases, bf16);
   if (lds > kDecodeLdsBudget) return false;
   const int tiles = (N + 16 * cpl - 1) / (16 * cpl);
   const int units = tiles * ks;
@@ -133,7 +133,7 @@ void apply_choice(const DecodeChoice& c, int K, int G, bool per_elem, gptq::Gemm
 }
 
 bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_elem, bool allow_split,
-                     bool tiled, gptq::GemmArgs* a) {
+                     bool tiled, gptq::GemmArgs* a, bool bf16) {
   bool found = false;
   DecodeChoice best{};
   // tiled layout, M = 1, full-width: 16-column tiles with 8 waves of 16
@@ -153,7 +153,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
     const int waste8 = (cks + 63) / 64 * 64 - cks, waste4 = (cks + 31) / 32 * 32 - cks;
     const int nw = waste4 < waste8 ? 4 : 8;
     size_t lds;
-    if (decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, 8, ks, &best, &lds)) {
+    if (decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, 8, ks, &best, &lds, bf16)) {
       apply_choice(best, K, G, per_elem, a);
       return true;
     }
@@ -161,7 +161,8 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
   if (tiled && M == 1 && !per_elem && waves == 0 && N / 16 >= kCUs / 2) {
     size_t lds;
     const bool wide = N >= 16384;
-    if (decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, wide ? 4 : 8, wide ? 8 : 16, 1, &best, &lds)) {
+    if (decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, wide ? 4 : 8, wide ? 8 : 16, 1, &best, &lds,
+                         bf16)) {
       apply_choice(best, K, G, per_elem, a);
       return true;
     }
@@ -183,7 +184,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
           if (waves == 0 && (nw & (nw - 1)) != 0) continue;   // automatic: 1, 2, 4, 8, 16 waves
           DecodeChoice c;
           size_t lds;
-          if (!decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, cpw, ks, &c, &lds)) continue;
+          if (!decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, cpw, ks, &c, &lds, bf16)) continue;
           if (!found || better_choice(c, best)) {
             best = c;
             found = true;
@@ -198,10 +199,10 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
 }
 
 int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_split, bool tiled, bool* per_elem,
-                 gptq::GemmArgs* a) {
+                 gptq::GemmArgs* a, bool bf16 = false) {
   if ((K / G) % 32 != 0) *per_elem = true;
   for (int pe = *per_elem ? 1 : 0; pe < 2; ++pe) {
-    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, allow_split, tiled, a)) {
+    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, allow_split, tiled, a, bf16)) {
       *per_elem = pe == 1;
       return GPTQ_OK;
     }
@@ -213,7 +214,7 @@ int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_spl
 int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
               const void* out, int path, int decode_waves, bool tiled, gptq::GemmArgs* a, bool* use_decode,
-              bool* per_elem, bool allow_split = true) {
+              bool* per_elem, bool allow_split = true, bool bf16 = false) {
   if (path < 0 || path > 2 || decode_waves < 0 || decode_waves > 16) return GPTQ_ERR_BAD_ARG;
   int rc = check_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out);
   if (rc != GPTQ_OK) return rc;
@@ -234,11 +235,14 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
   a->chunks = (int)(K / 32);
   a->zrow_words = N * bits / 32;
   a->wtiled = tiled ? 1 : 0;
+  a->bf16 = bf16 ? 1 : 0;
   *use_decode = (path == 1) || (path == 0 && M <= 16);
   if (M == 0) return GPTQ_OK;
   if (*use_decode) {
-    *per_elem = (g_idx != nullptr) || (group_size % 32 != 0);
-    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, allow_split, tiled, per_elem, a);
+    // bfloat16: always the element-wise dequant (the fp16 exponent trick of
+    // the fast path does not carry over)
+    *per_elem = bf16 || (g_idx != nullptr) || (group_size % 32 != 0);
+    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, allow_split, tiled, per_elem, a, bf16);
     if (rc2 != kNoDecodePlan) return rc2;
     if (path == 1) return GPTQ_ERR_BAD_ARG;         // forced decode, but no launch shape fits
     *use_decode = false;                             // very many groups: the prefill kernel
@@ -314,11 +318,12 @@ bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, floa
 // gathered into that order first (x_perm[i] = original row of sorted row i).
 int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-              void* out, void* stream_ptr, int path, int decode_waves, bool tiled, const int32_t* x_perm = nullptr) {
+              void* out, void* stream_ptr, int path, int decode_waves, bool tiled, const int32_t* x_perm = nullptr,
+              bool bf16 = false) {
   gptq::GemmArgs a;
   bool use_decode = false, per_elem = false;
   const int rc = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
-                           decode_waves, tiled, &a, &use_decode, &per_elem);
+                           decode_waves, tiled, &a, &use_decode, &per_elem, true, bf16);
   if (rc != GPTQ_OK || M == 0) return rc;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   if (x_perm) {
@@ -330,7 +335,7 @@ int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
                               &a.ws, &a.cnt, xb, &xg);
     if (!ok && split) {
       const int rc2 = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
-                                decode_waves, tiled, &a, &use_decode, &per_elem, false);
+                                decode_waves, tiled, &a, &use_decode, &per_elem, false, bf16);
       if (rc2 != GPTQ_OK) return rc2;
       ok = split_workspace(stream, 0, 0, &a.ws, &a.cnt, xb, &xg);
     }
@@ -345,7 +350,7 @@ int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
       !split_workspace(stream, (size_t)a.ks * a.M * a.N * 4, (size_t)a.tiles * 4, &a.ws, &a.cnt)) {
     // no workspace (first use under stream capture, or out of memory): one split
     const int rc2 = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
-                              decode_waves, tiled, &a, &use_decode, &per_elem, false);
+                              decode_waves, tiled, &a, &use_decode, &per_elem, false, bf16);
     if (rc2 != GPTQ_OK) return rc2;
   }
   const hipError_t err = use_decode ? gptq::launch_decode(bits, per_elem, a, stream)
@@ -380,17 +385,22 @@ int gptq_gemm_ex_check(const void* x, const int32_t* qweight, const int32_t* qze
 namespace {
 int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
                   const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
-                  const void* out, int path, int decode_waves, bool tiled, char* buf, int64_t buflen) {
+                  const void* out, int path, int decode_waves, bool tiled, char* buf, int64_t buflen,
+                  bool bf16 = false) {
   if (!buf || buflen <= 0) return GPTQ_ERR_NULL_PTR;
   buf[0] = '\0';
   gptq::GemmArgs a;
   bool use_decode = false, per_elem = false;
   const int rc = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
-                           decode_waves, tiled, &a, &use_decode, &per_elem);
+                           decode_waves, tiled, &a, &use_decode, &per_elem, true, bf16);
   if (rc != GPTQ_OK) return rc;
   const char* pe = per_elem ? "true" : "false";
   if (M == 0) {
     std::snprintf(buf, (size_t)buflen, "none (M = 0)");
+  } else if (use_decode && bf16) {
+    std::snprintf(buf, (size_t)buflen,
+                  "gptq::decode_bf16_kernel<%d, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d k_splits=%d",
+                  bits, M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles * a.ks, 64 * a.nw, a.phases, a.pc, a.ks);
   } else if (use_decode) {
     std::snprintf(buf, (size_t)buflen,
                   "gptq::decode_kernel<%d, %s, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d k_splits=%d",
@@ -398,8 +408,9 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
   } else {
     // the pipelined full-tile body: fast path, K % 64 == 0, not 8-bit
     const bool full = !per_elem && K % 64 == 0 && bits != 8;
-    std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s, %s> grid=%dx%d block=256", bits, pe,
-                  full ? "true" : "false", a.tiles_n, a.tiles_m);
+    std::snprintf(buf, (size_t)buflen, "gptq::%s<%d, %s, %s> grid=%dx%d block=256",
+                  bf16 ? "prefill_bf16_kernel" : "prefill_kernel", bits, pe, full ? "true" : "false", a.tiles_n,
+                  a.tiles_m);
   }
   return GPTQ_OK;
 }
@@ -608,8 +619,35 @@ int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
   return gptq_gemm_ex(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, stream, 0, 0);
 }
 
-int gptq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx, int bits,
-                 int group_size, int is_v2, int64_t N, int64_t K, void* w_out, void* stream) {
+int gptq_gemm_bf16_ex(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                      const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                      void* out, void* stream, int path, int decode_waves) {
+  try {
+    return gemm_impl(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, stream, path,
+                     decode_waves, false, nullptr, true);
+  } catch (const std::bad_alloc&) {
+    return GPTQ_ERR_NO_MEM;
+  } catch (...) {
+    return GPTQ_ERR_DEVICE;
+  }
+}
+
+int gptq_gemm_bf16(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                   const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                   void* out, void* stream) {
+  return gptq_gemm_bf16_ex(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, stream, 0, 0);
+}
+
+int gptq_gemm_bf16_describe(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                            const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N,
+                            int64_t K, const void* out, int path, int decode_waves, char* buf, int64_t buflen) {
+  return describe_impl(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
+                       decode_waves, false, buf, buflen, true);
+}
+
+namespace {
+int dequant_impl(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx, int bits,
+                 int group_size, int is_v2, int64_t N, int64_t K, void* w_out, void* stream, bool bf16) {
   const int rc = gptq_dequant_check(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, N, K, w_out);
   if (rc != GPTQ_OK) return rc;
   gptq::DequantArgs a{};
@@ -625,8 +663,19 @@ int gptq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scal
   a.zero_offset = is_v2 ? 0 : 1;
   a.chunks = (int)(K / 32);
   a.zrow_words = N * bits / 32;
-  const hipError_t err = gptq::launch_dequant(bits, a, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t err = gptq::launch_dequant(bits, a, bf16, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
+}
+}  // namespace
+
+int gptq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx, int bits,
+                 int group_size, int is_v2, int64_t N, int64_t K, void* w_out, void* stream) {
+  return dequant_impl(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, N, K, w_out, stream, false);
+}
+
+int gptq_dequant_bf16(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,
+                      int bits, int group_size, int is_v2, int64_t N, int64_t K, void* w_out, void* stream) {
+  return dequant_impl(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, N, K, w_out, stream, true);
 }
 
 int gptq_quantize(const float* w, const int32_t* g_idx, int bits, int group_size, int sym, int is_v2, int64_t N,

@@ -227,6 +227,58 @@ __device__ __forceinline__ int field_of4(uint32_t z4, int j, int bits) {
   return (int)((z4 >> (bits * j)) & ((1u << bits) - 1u));
 }
 
+// ---- bfloat16 activations (the other 16-bit activation type of page
+// "Weight-only INT4 quantization: GPTQ, AWQ and the Marlin kernel", section
+// 1.2).  bfloat16 has 8 significant bits, too few for the fp16 exponent trick
+// (a 4-bit field shifted by 4 would run into the exponent), so these paths
+// dequantize element by element in fp32: a field becomes an exact float (a
+// byte conversion), W^ = fma(q, s, -z s) is exact in fp32 (q s and z s have
+// at most 8 + 9 significant bits, and so does their difference (q - z) s;
+// z s stays finite for |s| < 2^119), and one hardware conversion rounds a
+// pair to bfloat16, nearest-even -- the same single rounding as
+// bf16_RNE((q - z) s), up to the sign of an exact zero (always +0 here).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// The eight fields of one column's block kb as exact floats, natural order
+// f[0..7]; w0 / w1 are the column's words from block_row0 / block_row1.
+template <int BITS>
+__device__ __forceinline__ void block_fields_f32(uint32_t w0, uint32_t w1, int kb, float f[8]) {
+  if constexpr (BITS == 4) {
+    const uint32_t lo = w0 & 0x0F0F0F0Fu, hi = (w0 >> 4) & 0x0F0F0F0Fu;   // f0 f2 f4 f6 | f1 f3 f5 f7
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = (float)((lo >> (8 * i)) & 0xFFu);
+      f[2 * i + 1] = (float)((hi >> (8 * i)) & 0xFFu);
+    }
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (float)((w0 >> (8 * i)) & 0xFFu);
+      f[4 + i] = (float)((w1 >> (8 * i)) & 0xFFu);
+    }
+  } else if constexpr (BITS == 2) {
+    const uint32_t t = w0 >> (16 * (kb & 1));                               // the block's 16 bits
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t u = (t >> (2 * j)) & 0x0303u;                          // f_j in byte 0, f_{j+4} in byte 1
+      f[j] = (float)(u & 0xFFu);
+      f[j + 4] = (float)((u >> 8) & 0xFFu);
+    }
+  } else {
+    const uint32_t t = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)((24 * kb) & 31));   // 24-bit block
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)((t >> (3 * i)) & 7u);
+  }
+}
+
+// Two fp32 values -> a bfloat16 pair (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
 // Round-to-nearest-even fp32 -> fp16 with subnormals (hardware conversion).
 __device__ __forceinline__ _Float16 f32_to_f16(float f) { return (_Float16)f; }
 

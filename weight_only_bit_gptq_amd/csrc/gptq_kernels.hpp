@@ -53,6 +53,9 @@ struct GemmArgs {
   int64_t qw_stride, qz_stride, sc_stride, gi_stride;
   // prefill launch shape
   int tiles_m, tiles_n;
+  // activation type: 0 = fp16 (x, scales, out fp16), 1 = bfloat16 (x,
+  // scales and out hold bfloat16 bits behind the same pointers)
+  int bf16;
 };
 
 // LDS carve-up of the decode kernel: one phase buffer (two when K takes
@@ -81,18 +84,19 @@ __device__ __forceinline__ int group_of(const int32_t* __restrict__ g_idx, int k
   return k / group_size;
 }
 
-hipError_t launch_dequant(int bits, const DequantArgs& a, hipStream_t stream);
+hipError_t launch_dequant(int bits, const DequantArgs& a, bool bf16, hipStream_t stream);
 
 // Decode (M <= 16).  `per_elem` selects the per-element scale/zero path (act
 // order or group_size % 32 != 0).
 // LDS bytes of a launch shape (SIZE_MAX if its table cannot be staged)
-size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg, int phases);
+size_t decode_lds_bytes(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg, int phases,
+                        bool bf16 = false);
 int decode_max_x_pieces(int M);   // 16-byte x pieces each thread may stage per phase
 // per instantiation: workgroup size limit, waves per SIMD it is compiled for,
 // and whether that chunks-per-wave value is compiled at all
 int decode_max_threads_for(int bits, bool per_elem, int cpl, int cpw, int M);
 int decode_waves_per_simd_for(int bits, bool per_elem, int cpl, int cpw, int M);
-bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M);
+bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M, bool bf16 = false);
 hipError_t launch_decode(int bits, bool per_elem, const GemmArgs& a, hipStream_t stream);
 
 // Prefill (any M, used for M > 16).

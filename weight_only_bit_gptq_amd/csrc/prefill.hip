@@ -47,8 +47,10 @@ void prefill_shape(int M, int N, int* tiles_m, int* tiles_n) {
 // runs the software-pipelined tile body; otherwise (act order, other group
 // sizes, a last half tile) the plain body with a step count per tile.  Two
 // separate instantiations: one body with both paths behind a branch spills.
-template <int BITS, bool PER_ELEM, bool FULL>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
+// BF16: x, scales and out are bfloat16; B is the element-wise bfloat16
+// dequant of gptq_device.hpp and the MFMA the bf16 one (same tiles).
+template <int BITS, bool PER_ELEM, bool FULL, bool BF16>
+__device__ __forceinline__ void prefill_body(GemmArgs a) {
   constexpr int BM = kPrefillBM;
   constexpr int BK = kPrefillBK;
   constexpr int MS = kPrefillMS;
@@ -172,6 +174,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
 
   uint32_t magic;                                    // kMagicPair in a register (see unpack_block_natural)
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  auto mfma = [](const half8_t& A, const half8_t& B, const floatx16_t& c) __attribute__((always_inline)) {
+    if constexpr (BF16)
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, A), __builtin_bit_cast(bf16x8_t, B),
+                                                     c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B, c, 0, 0, 0);
+  };
 
   floatx16_t acc[MS][2];
 #pragma unroll
@@ -199,6 +207,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
     }
   };
 
+  // bfloat16: the lane's two columns' s and -z s for the tile's group
+  auto group_consts_bf16 = [&](int set, float bs[2], float bc[2]) __attribute__((always_inline)) {
+    const int n4 = nc & ~3;
+    uint32_t z4;
+    if constexpr (BITS == 3) z4 = __builtin_amdgcn_alignbit(zw1[set], zw0[set], (uint32_t)((3 * (n4 & 31)) & 31));
+    else z4 = zw0[set] >> ((n4 * BITS) & 31);
+    const uint32_t z2 = z4 >> (BITS * (nc & 3));
+    const uint32_t s2 = as_u32(sw[set]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float sc = bf16_to_f32((s2 >> (16 * j)) & 0xFFFFu);
+      bs[j] = sc;
+      bc[j] = -(float)(field_of4(z2, j, BITS) + a.zero_offset) * sc;
+    }
+  };
+  // B fragment j of block kb from the words, bfloat16 with one (s, -z s)
+  auto make_B_bf16 = [&](uint32_t w0j, uint32_t w1j, int kb, float s, float c) __attribute__((always_inline)) {
+    float f[8];
+    block_fields_f32<BITS>(w0j, w1j, kb, f);
+    u32x4_t bw;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) bw[v] = bf16_pair(__builtin_fmaf(f[2 * v], s, c), __builtin_fmaf(f[2 * v + 1], s, c));
+    return __builtin_bit_cast(half8_t, bw);
+  };
+
   // fast path, a whole k tile: the B operands of step s + 1 are made (VALU)
   // while the MFMAs of step s run, in the same wave, so the two pipes overlap
   // without relying on the other wave of the SIMD
@@ -206,11 +239,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
     constexpr int set = decltype(set_c)::value % NSR;
     const _Float16* sl = stage_lds(set_c);
     half2_t negp[2][4], sp[2];
-    group_consts(set, negp, sp);
+    float bs[2], bc[2];
+    if constexpr (BF16) group_consts_bf16(set, bs, bc);
+    else group_consts(set, negp, sp);
     auto make_B = [&](int s, half8_t (&B)[2]) __attribute__((always_inline)) {
       const int kb = 2 * (s & 1) + kb2;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        if constexpr (BF16) {
+          B[j] = make_B_bf16(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, bs[j], bc[j]);
+          continue;
+        }
         uint32_t p[4];
         unpack_block_natural<BITS>(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p, magic);
         u32x4_t bw;
@@ -230,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
         const int kblk = 2 * s + kb2;
         const half8_t A = *reinterpret_cast<const half8_t*>(sl + (m * 8 + (kblk ^ ((m >> 1) & 7))) * 8);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bc[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(A, Bc[j], acc[i][j]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -249,7 +288,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
     const int ksteps = min(4, (a.K - kt * BK) >> 4);
     const _Float16* sl = stage_lds(set_c);
     half2_t negp[2][4], sp[2];
-    if constexpr (!PER_ELEM) group_consts(set, negp, sp);
+    float bs[2], bc[2];
+    if constexpr (!PER_ELEM && BF16) group_consts_bf16(set, bs, bc);
+    else if constexpr (!PER_ELEM) group_consts(set, negp, sp);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s >= ksteps) break;
@@ -257,6 +298,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
       half8_t B[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        if constexpr (BF16) {
+          const uint32_t w0j = w0[set][s][j], w1j = L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u;
+          if constexpr (PER_ELEM) {
+            // each row its own group: (s, -z s) per field
+            const uint16_t* scb = reinterpret_cast<const uint16_t*>(a.scales);
+            const int k0 = kt * BK + 16 * s + 8 * kb2;
+            float f[8];
+            block_fields_f32<BITS>(w0j, w1j, kb, f);
+            u32x4_t bw;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float o[2];
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int g = group_of(a.g_idx, k0 + 2 * v + h, a.group_size, a.G);
+                const uint32_t z = load_zero4<BITS>(a.qzeros, a.zrow_words, g, nc & ~3) >> (BITS * ((nc & 3) + j));
+                const float sc = bf16_to_f32(scb[(int64_t)g * a.N + nc + j]);
+                const float zf = (float)((int)(z & ((1u << BITS) - 1u)) + a.zero_offset);
+                o[h] = __builtin_fmaf(f[2 * v + h], sc, -zf * sc);
+              }
+              bw[v] = bf16_pair(o[0], o[1]);
+            }
+            B[j] = __builtin_bit_cast(half8_t, bw);
+          } else {
+            B[j] = make_B_bf16(w0j, w1j, kb, bs[j], bc[j]);
+          }
+          continue;
+        }
         uint32_t p[4];
         unpack_block_natural<BITS>(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p, magic);
         u32x4_t bw;
@@ -285,8 +354,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
         const int kblk = 2 * s + kb2;
         const half8_t A = *reinterpret_cast<const half8_t*>(sl + (m * 8 + (kblk ^ ((m >> 1) & 7))) * 8);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(A, B[j], acc[i][j]);
       }
     }
   };
@@ -338,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
     step(kt + 2, S2{}, S1{});
   }
 
-  // ---- epilogue: fp32 -> fp16, two adjacent columns per store
+  // ---- epilogue: fp32 -> fp16 (bfloat16), two adjacent columns per store
   if (!col_ok) return;
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
@@ -346,17 +414,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
     for (int v = 0; v < 16; ++v) {
       const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kb2 + (v & 3);
       if (row < a.M) {
-        const half2_t o = {(_Float16)acc[i][0][v], (_Float16)acc[i][1][v]};
-        *reinterpret_cast<half2_t*>(a.out + (int64_t)row * a.N + n) = o;
+        if constexpr (BF16) {
+          *reinterpret_cast<uint32_t*>(a.out + (int64_t)row * a.N + n) = bf16_pair(acc[i][0][v], acc[i][1][v]);
+        } else {
+          const half2_t o = {(_Float16)acc[i][0][v], (_Float16)acc[i][1][v]};
+          *reinterpret_cast<half2_t*>(a.out + (int64_t)row * a.N + n) = o;
+        }
       }
     }
   }
 }
 
 template <int BITS, bool PER_ELEM, bool FULL>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
+  prefill_body<BITS, PER_ELEM, FULL, false>(a);
+}
+
+template <int BITS, bool PER_ELEM, bool FULL>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(GemmArgs a) {
+  prefill_body<BITS, PER_ELEM, FULL, true>(a);
+}
+
+template <int BITS, bool PER_ELEM, bool FULL>
 static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(a.tiles_m * a.tiles_n);
-  hipLaunchKernelGGL((prefill_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
+  if (a.bf16) hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((prefill_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ DECODE_SOURCES = ["weight_only_bit_gptq_amd/csrc/decode.hip", "weight_only_bit_g
 PMC_COPY_BYTES = 256 << 20      # plain copy of known size that calibrates FETCH_SIZE / WRITE_SIZE
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
-MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 (and bf16) MFMA
 ROTATE_BYTES = 1 << 30          # rotate >= 1 GiB of distinct weight copies
 
 
@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--no-checkpoint-layout", action="store_true",
                    help="skip the decode step on the checkpoint qweight layout (reported beside the tiled one)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bf16", action="store_true",
+                   help="skip the bfloat16-activation lines (decode layers and 4-bit prefill)")
     p.add_argument("--cpu-sample-cols", type=int, default=12288,
                    help="columns of the qkv layer the CPU oracle processes (default: all)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -118,20 +120,29 @@ def make_layer(torch, gq, wl, layer, M, dev, tiled=False):
     return dict(qweight=qw, qzeros=qz, scales=sc, g_idx=gi, x=x, K=layer.K, N=layer.N)
 
 
-def bench_decode(torch, gq, args, dev, tiled):
+def to_bf16(torch, L):
+    """The same layer with bfloat16 activations: x and scales rounded to bfloat16."""
+    return {**L, "x": L["x"].to(torch.bfloat16), "scales": L["scales"].to(torch.bfloat16)}
+
+
+def bench_decode(torch, gq, args, dev, tiled, bf16=False):
     """Decode step timing.  Launches are captured in HIP graphs so the Python
     binding's per-call overhead stays out of the timed region: one graph holds
     R steps (R rotated weight copies x 4 layers); per-layer graphs hold R launches
     of one layer and give the kernel's mean launch time.  `tiled`: qweight in
-    the tiled layout (repacked once at load), else the checkpoint layout."""
+    the tiled layout (repacked once at load), else the checkpoint layout.
+    `bf16`: bfloat16 activations and scales (gptq_gemm_bf16)."""
     from workload import WORKLOADS
     wl = WORKLOADS["llama7b_decode_w4g128"]
     base = [make_layer(torch, gq, wl, l, 1, dev, tiled) for l in wl.layers]
+    if bf16:
+        base = [to_bf16(torch, L) for L in base]
+    adt = torch.bfloat16 if bf16 else torch.float16
     wbytes = sum(layer_bytes(L["K"], L["N"], wl.bits, wl.group_size) for L in base)
     copies = max(1, -(-ROTATE_BYTES // wbytes))
     sets = [base] + [[{**L, "qweight": L["qweight"].clone(), "qzeros": L["qzeros"].clone(),
                        "scales": L["scales"].clone()} for L in base] for _ in range(copies - 1)]
-    outs = [torch.empty((1, L["N"]), dtype=torch.float16, device=dev) for L in base]
+    outs = [torch.empty((1, L["N"]), dtype=adt, device=dev) for L in base]
 
     def launch(r, j):
         L = sets[r][j]
@@ -199,14 +210,21 @@ def bench_decode(torch, gq, args, dev, tiled):
                 mean_launch_us=mean_launch_ms * 1e3, layers=layers, base=base)
 
 
-def bench_prefill(torch, gq, args, dev):
+def bench_prefill(torch, gq, args, dev, bf16=False):
+    """Prefill GEMM timing per layer (plus, for the 4-bit workload, the vendor
+    dense GEMM in the same activation type on the same shape, as context).
+    `bf16`: bfloat16 activations and scales, 4-bit workload only."""
     from workload import WORKLOADS
     res = []
-    for name in ("mlp70b_prefill_w4g128", "mlp70b_prefill_w8g128"):
+    adt = torch.bfloat16 if bf16 else torch.float16
+    names = ("mlp70b_prefill_w4g128",) if bf16 else ("mlp70b_prefill_w4g128", "mlp70b_prefill_w8g128")
+    for name in names:
         wl = WORKLOADS[name]
         for layer in wl.layers:
             L = make_layer(torch, gq, wl, layer, 2048, dev)
-            out = torch.empty((2048, layer.N), dtype=torch.float16, device=dev)
+            if bf16:
+                L = to_bf16(torch, L)
+            out = torch.empty((2048, layer.N), dtype=adt, device=dev)
             run = lambda: gq.gemm(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits,
                                   wl.group_size, wl.is_v2, out=out)
             t0 = time.perf_counter()
@@ -230,8 +248,8 @@ def bench_prefill(torch, gq, args, dev):
                    "bits": wl.bits, "ms": round(ms, 4), "TFLOPs": round(tf, 1),
                    "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
             if name == "mlp70b_prefill_w4g128":
-                # context: the vendor dense fp16 GEMM (torch.matmul) on the same shape, unquantized W
-                W = torch.randn((layer.K, layer.N), dtype=torch.float16, device=dev)
+                # context: the vendor dense GEMM (torch.matmul) on the same shape, unquantized W
+                W = torch.randn((layer.K, layer.N), dtype=adt, device=dev)
                 t0 = time.perf_counter()
                 while time.perf_counter() - t0 < args.warm_seconds:
                     for _ in range(5):
@@ -242,7 +260,8 @@ def bench_prefill(torch, gq, args, dev):
                     torch.matmul(L["x"], W, out=out)
                 b.record()
                 torch.cuda.synchronize()
-                row["dense_fp16_matmul_TFLOPs"] = round(flops / (a.elapsed_time(b) / args.prefill_steps * 1e-3) / 1e12, 1)
+                key = "dense_bf16_matmul_TFLOPs" if bf16 else "dense_fp16_matmul_TFLOPs"
+                row[key] = round(flops / (a.elapsed_time(b) / args.prefill_steps * 1e-3) / 1e12, 1)
                 del W
             res.append(row)
             del L, out
@@ -555,6 +574,19 @@ def main():
     prefill = None if args.no_prefill else bench_prefill(torch, gq, args, dev)
     if prefill:
         print(f"# prefill: {prefill}", file=sys.stderr, flush=True)
+    bf16 = None
+    if not args.no_bf16:
+        torch.cuda.empty_cache()
+        dec_bf = bench_decode(torch, gq, args, dev, tiled=False, bf16=True)
+        del dec_bf["base"]
+        torch.cuda.empty_cache()
+        bf16 = {"decode": {"workload": dec_bf["wl"].name + " with bf16 x and scales (checkpoint layout)",
+                           "value": round(dec_bf["wbytes"] / (dec_bf["ms_per_step"] * 1e-3) / 1e9, 1),
+                           "ms_per_step": round(dec_bf["ms_per_step"], 5), "achieved": round(dec_bf["achieved"], 1),
+                           "frac": round(dec_bf["achieved"] / HBM_PEAK_GBPS, 4),
+                           "mean_launch_us": round(dec_bf["mean_launch_us"], 3), "per_layer": dec_bf["layers"]},
+                "prefill": None if args.no_prefill else bench_prefill(torch, gq, args, dev, bf16=True)}
+        print(f"# bf16: {bf16}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args)
 
     wl = dec["wl"]
@@ -599,6 +631,7 @@ def main():
         "moe": moe,
         "copy_GBps": round(ceiling, 1),
         "prefill": prefill,
+        "bf16": bf16,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

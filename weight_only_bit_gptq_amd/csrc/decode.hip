@@ -223,6 +223,8 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   const DecodeLayout lay = decode_layout(ML, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases, BF16);
   const int Mp = decode_corr_rows(ML);
   const uint32_t sel = block_sel<BITS>(kb);
+  // every row of a 32-row chunk in one group (no g_idx, whole-chunk groups)
+  const bool rows_share_group = a.g_idx == nullptr && (a.group_size & 31) == 0;
 
   // ---- staging scope: the fast path stages per wave (its own CPW chunks, in
   // its own LDS region), the per-element path per workgroup (the phase's pc
@@ -549,17 +551,28 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         if constexpr (BF16) {
-          // fields in the staging's order F, each with its row's (s, -z s)
-          const f32x2_t* tab2 = reinterpret_cast<const f32x2_t*>(lds + lay.tab_off);
+          // fields in the staging's order F, each with its row's (s, -z s);
+          // without g_idx and with groups of whole chunks the block's rows
+          // share one group: one table read
+          const f32x2_t* tab2 = reinterpret_cast<const f32x2_t*>(lds + lay.tab_off) + CPL * q + j;
           float f[8];
           block_fields_f32<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], kb, f);
           u32x4_t bw;
+          if (rows_share_group) {
+            const f32x2_t t = tab2[(int)gv[0] * TN];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int fa = Block<BITS>::F[2 * v], fb = Block<BITS>::F[2 * v + 1];
-            const f32x2_t ta = tab2[(int)gv[fa] * TN + CPL * q + j];
-            const f32x2_t tb = tab2[(int)gv[fb] * TN + CPL * q + j];
-            bw[v] = bf16_pair(__builtin_fmaf(f[fa], ta[0], ta[1]), __builtin_fmaf(f[fb], tb[0], tb[1]));
+            for (int v = 0; v < 4; ++v) {
+              const int fa = Block<BITS>::F[2 * v], fb = Block<BITS>::F[2 * v + 1];
+              bw[v] = bf16_pair(__builtin_fmaf(f[fa], t[0], t[1]), __builtin_fmaf(f[fb], t[0], t[1]));
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int fa = Block<BITS>::F[2 * v], fb = Block<BITS>::F[2 * v + 1];
+              const f32x2_t ta = tab2[(int)gv[fa] * TN];
+              const f32x2_t tb = tab2[(int)gv[fb] * TN];
+              bw[v] = bf16_pair(__builtin_fmaf(f[fa], ta[0], ta[1]), __builtin_fmaf(f[fb], tb[0], tb[1]));
+            }
           }
           accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
                                                             __builtin_bit_cast(bf16x8_t, bw), accg[j], 0, 0, 0);

@@ -153,9 +153,14 @@ bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M, bool b
 
 // The kernel body; BF16 (per-element path only): x, scales and out are
 // bfloat16, B is the element-wise bfloat16 dequant and the MFMA the bf16 one.
-template <int BITS, bool PER_ELEM, bool BF16, int MV, int CPL, int CPW>
+// FOLD (fast path, one row): the scale and zero are folded into the sums once
+// per block of FOLD consecutive chunks of one group (the MFMA accumulates the
+// block's chunks) instead of once per chunk; needs group_size % (32 FOLD) == 0
+// and every wave's run and K split starting on a multiple of FOLD chunks.
+template <int BITS, bool PER_ELEM, bool BF16, int MV, int CPL, int CPW, int FOLD>
 __device__ __forceinline__ void decode_body(GemmArgs a) {
   static_assert(!BF16 || PER_ELEM, "bfloat16 decode runs the per-element path");
+  static_assert(FOLD == 1 || (!PER_ELEM && MV == 1 && CPW % (2 * FOLD) == 0), "block fold: one-row fast path");
   extern __shared__ __align__(16) unsigned char lds[];
   // one output element, rounded to the activation type (nearest even)
   auto store_out = [](_Float16* out, int64_t i, float v) __attribute__((always_inline)) {
@@ -303,12 +308,16 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
         av[2 * v + 1] = pr[1];
       }
       *reinterpret_cast<half8_t*>(frag + (((cl * 4 + kbe) * M + m) << 3)) = av;
-      // one-row instantiation: the chunk's sum of x (x' MUL) for the zero
-      // term; the multi-row one gets its sums from an MFMA at compute time
+      // one-row instantiation: the chunk's (with FOLD > 1 the fold block's)
+      // sum of x (x' MUL) for the zero term; lanes 4 cl .. 4 cl + 3 hold
+      // chunk cl, so a block of FOLD chunks is 4 FOLD aligned lanes.  The
+      // multi-row instantiation gets its sums from an MFMA at compute time
       if constexpr (!PER_ELEM && !kSumsByMfma) {
         xs += __shfl_xor(xs, 1);
         xs += __shfl_xor(xs, 2);
-        if (kbe == 0) corr[cl * Mp + m] = xs;
+        if constexpr (FOLD >= 2) xs += __shfl_xor(xs, 4);
+        if constexpr (FOLD >= 4) xs += __shfl_xor(xs, 8);
+        if (kbe == 0 && cl % FOLD == 0) corr[(cl / FOLD) * Mp + m] = xs;
       }
     }
     if constexpr (PER_ELEM) {
@@ -479,7 +488,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   // fast path: the previous chunk's MFMA results and scales, folded one chunk
   // later; the empty asm pins each fold in place (otherwise the whole chain is
   // sunk past the loop and every chunk's results stay live)
-  constexpr bool kDeferFold = CPL < 4;
+  constexpr bool kDeferFold = CPL < 4 || FOLD > 1;
   floatx4_t d_prev[CPL];
   float s_prev[CPL];
 #pragma unroll
@@ -658,6 +667,77 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
         compute_chunk(p, u, row, S0{}, FastOps{});
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else if constexpr (FOLD > 1) {
+      // blocks of FOLD chunks of one group: the block's MFMAs accumulate its
+      // sum of x' B, and its scale and zero are applied once, with the
+      // block's sum of x (staged).  The previous block's scale multiply is
+      // issued after this block's first MFMA (its result is not waited on at
+      // once).  A fragments are read one chunk ahead, the block's table
+      // entries and sum of x one block ahead.  row / rem (the group row and
+      // the position in the group of chunk u0, a multiple of FOLD) are
+      // wave-uniform and advance once per block.
+      struct BlockOps {
+        float X;
+        float s1[CPL], s2[CPL];
+      };
+      auto block_ops = [&](int u, int r) __attribute__((always_inline)) {
+        BlockOps o;
+        const unsigned char* base = stage_base(p);
+        o.X = reinterpret_cast<const float*>(base + lay.corr_off)[u / FOLD];
+        const int row_bytes = __builtin_amdgcn_readfirstlane(r * TN * 8);
+        const float* te = reinterpret_cast<const float*>(base + lay.ptab_off + row_bytes);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          o.s1[j] = te[tab_pos(CPL * q + j)];
+          o.s2[j] = te[tab_pos(CPL * q + j) + 1];
+        }
+        return o;
+      };
+      auto frag_A = [&](int u) __attribute__((always_inline)) {
+        const _Float16* frag = reinterpret_cast<const _Float16*>(stage_base(p));
+        return *reinterpret_cast<const half8_t*>(frag + ((u * 4 + kb) << 3));
+      };
+      row = __builtin_amdgcn_readfirstlane(row);
+      rem = __builtin_amdgcn_readfirstlane(rem);
+      BlockOps cur = block_ops(u0, row);
+      half8_t A = frag_A(u0);
+#pragma unroll
+      for (int b = u0 / FOLD; b < u1 / FOLD; ++b) {
+        const int inc = 1 - (int)min(1u, (uint32_t)((rem + FOLD) ^ cpg));
+        row = __builtin_amdgcn_readfirstlane(row + inc);
+        rem = __builtin_amdgcn_readfirstlane((rem + FOLD) * (1 - inc));
+        BlockOps nxt = cur;
+        if (b + 1 < u1 / FOLD) nxt = block_ops(FOLD * (b + 1), row);
+        floatx4_t d[CPL];
+#pragma unroll
+        for (int i = 0; i < FOLD; ++i) {
+          const int u = FOLD * b + i;
+          half8_t An = A;
+          if (u + 1 < u1) An = frag_A(u + 1);
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            uint32_t pr[4];
+            const uint32_t w1j = L == 2 ? word_of<CPL>(w1[0][L == 2 ? u : 0], j) : 0u;
+            unpack_block<BITS>(word_of<CPL>(w0[0][u], j), w1j, sel, pr, 0u);
+            const u32x4_t bw = {pr[0], pr[1], pr[2], pr[3]};
+            d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw),
+                                                          i == 0 ? floatx4_t{0.f, 0.f, 0.f, 0.f} : d[j], 0, 0, 0);
+          }
+          if (i == 0) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) acc[j][0] = __builtin_fmaf(cur.s2[j], cur.X, acc[j][0]);
+            fold_prev();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          A = An;
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          d_prev[j] = d[j];
+          s_prev[j] = cur.s1[j];
+        }
+        cur = nxt;
+      }
     } else {
       // the LDS operands of chunk u + 1 are read before chunk u is computed
       // (one chunk ahead only: hoisting all of them ahead of the weight waits
@@ -803,11 +883,11 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
 
 // Each instantiation is compiled for a fixed number of waves per SIMD, which
 // the host uses to size the grid and to know how many workgroups a CU holds.
-template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
+template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW, int FOLD>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(BITS, PER_ELEM, CPL, CPW, MV))))
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, PER_ELEM, CPL, CPW, MV))))
 void decode_kernel(GemmArgs a) {
-  decode_body<BITS, PER_ELEM, false, MV, CPL, CPW>(a);
+  decode_body<BITS, PER_ELEM, false, MV, CPL, CPW, FOLD>(a);
 }
 
 // bfloat16 activations: the per-element path's launch shapes and registers
@@ -815,18 +895,18 @@ template <int BITS, int MV, int CPL, int CPW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, decode_max_threads(BITS, true, CPL, CPW, MV))))
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(BITS, true, CPL, CPW, MV))))
 void decode_bf16_kernel(GemmArgs a) {
-  decode_body<BITS, true, true, MV, CPL, CPW>(a);
+  decode_body<BITS, true, true, MV, CPL, CPW, 1>(a);
 }
 
-template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
+template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW, int FOLD>
 static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
   if constexpr (!decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV)) {
     return hipErrorInvalidValue;
   } else {
     const size_t lds = decode_lds_bytes(a.n_experts > 0 ? 16 : a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg, a.phases,
                                         a.bf16 != 0);
-    auto kern = decode_kernel<BITS, PER_ELEM, MV, CPL, CPW>;
-    if constexpr (decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV, true)) {
+    auto kern = decode_kernel<BITS, PER_ELEM, MV, CPL, CPW, FOLD>;
+    if constexpr (FOLD == 1 && decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV, true)) {
       if (a.bf16) kern = decode_bf16_kernel<BITS, MV, CPL, CPW>;
     } else {
       if (a.bf16) return hipErrorInvalidValue;
@@ -842,12 +922,27 @@ static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
   }
 }
 
+// block fold (a.fold > 1): one-row fast path only
+template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
+static hipError_t launch_decode_fold(const GemmArgs& a, hipStream_t stream) {
+  if constexpr (!PER_ELEM && MV == 1) {
+    switch (a.fold) {
+      case 1: return launch_decode_k<BITS, PER_ELEM, MV, CPL, CPW, 1>(a, stream);
+      case 2: return launch_decode_k<BITS, PER_ELEM, MV, CPL, CPW, 2>(a, stream);
+      case 4: return launch_decode_k<BITS, PER_ELEM, MV, CPL, CPW, 4>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return a.fold == 1 ? launch_decode_k<BITS, PER_ELEM, MV, CPL, CPW, 1>(a, stream) : hipErrorInvalidValue;
+  }
+}
+
 template <int BITS, bool PER_ELEM, int MV, int CPL>
 static hipError_t launch_decode_cpw(const GemmArgs& a, hipStream_t stream) {
   switch (a.cpw) {
-    case 8: return launch_decode_k<BITS, PER_ELEM, MV, CPL, 8>(a, stream);
-    case 16: return launch_decode_k<BITS, PER_ELEM, MV, CPL, 16>(a, stream);
-    case 32: return launch_decode_k<BITS, PER_ELEM, MV, CPL, 32>(a, stream);
+    case 8: return launch_decode_fold<BITS, PER_ELEM, MV, CPL, 8>(a, stream);
+    case 16: return launch_decode_fold<BITS, PER_ELEM, MV, CPL, 16>(a, stream);
+    case 32: return launch_decode_fold<BITS, PER_ELEM, MV, CPL, 32>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -119,7 +119,7 @@ bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int c
   return true;
 }
 
-void apply_choice(const DecodeChoice& c, int K, int G, bool per_elem, gptq::GemmArgs* a) {
+void apply_choice(const DecodeChoice& c, int M, int K, int G, bool per_elem, bool bf16, gptq::GemmArgs* a) {
   const int C = K / 32;
   a->tiles = c.tiles;
   a->cpl = c.cpl;
@@ -130,6 +130,18 @@ void apply_choice(const DecodeChoice& c, int K, int G, bool per_elem, gptq::Gemm
   a->cpg = per_elem ? 1 : (K / G) / 32;
   a->ks = c.ks;
   a->cks = (C + c.ks - 1) / c.ks;
+  // one-row fast path: fold scale and zero once per block of 4 (or 2)
+  // chunks of one group; every wave's run (cpw chunks, halved at a phase's
+  // midpoint) and every K split must start on a block boundary
+  a->fold = 1;
+  if (!per_elem && M == 1 && !bf16) {
+    for (int f : {4, 2}) {
+      if (a->cpg % f == 0 && (c.cpw / 2) % f == 0 && (c.ks == 1 || a->cks % f == 0)) {
+        a->fold = f;
+        break;
+      }
+    }
+  }
 }
 
 bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_elem, bool allow_split,
@@ -154,7 +166,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
     const int nw = waste4 < waste8 ? 4 : 8;
     size_t lds;
     if (decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, 8, ks, &best, &lds, bf16)) {
-      apply_choice(best, K, G, per_elem, a);
+      apply_choice(best, M, K, G, per_elem, bf16, a);
       return true;
     }
   }
@@ -163,7 +175,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
     const bool wide = N >= 16384;
     if (decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, wide ? 4 : 8, wide ? 8 : 16, 1, &best, &lds,
                          bf16)) {
-      apply_choice(best, K, G, per_elem, a);
+      apply_choice(best, M, K, G, per_elem, bf16, a);
       return true;
     }
   }
@@ -194,7 +206,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
     }
   }
   if (!found) return false;
-  apply_choice(best, K, G, per_elem, a);
+  apply_choice(best, M, K, G, per_elem, bf16, a);
   return true;
 }
 
@@ -403,8 +415,9 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
                   bits, M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles * a.ks, 64 * a.nw, a.phases, a.pc, a.ks);
   } else if (use_decode) {
     std::snprintf(buf, (size_t)buflen,
-                  "gptq::decode_kernel<%d, %s, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d k_splits=%d",
-                  bits, pe, M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles * a.ks, 64 * a.nw, a.phases, a.pc, a.ks);
+                  "gptq::decode_kernel<%d, %s, %d, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d "
+                  "k_splits=%d",
+                  bits, pe, M == 1 ? 1 : 4, a.cpl, a.cpw, a.fold, a.tiles * a.ks, 64 * a.nw, a.phases, a.pc, a.ks);
   } else {
     // the pipelined full-tile body: fast path, K % 64 == 0, not 8-bit
     const bool full = !per_elem && K % 64 == 0 && bits != 8;

@@ -147,7 +147,7 @@ def test_tiled_describe_shapes():
     lib = gq.library()
     buf = ctypes.create_string_buffer(256)
     for (bits, gs, M, K, N, want) in ((4, 128, 1, 4096, 12288, "<4, false, 1, 1, 16, 4> grid=768 block=512"),
-                                      (4, 128, 1, 4096, 22016, "<4, false, 1, 2, 8, 4> grid=688 block=256"),
+                                      (4, 128, 1, 4096, 22016, "<4, false, 1, 2, 16, 4> grid=688 block=512"),
                                       (4, 128, 1, 11008, 4096, "<4, false, 1, 1, 16, 4> grid=256 block=512"),
                                       (2, 64, 16, 4096, 12288, "<2, false, 4, "),
                                       (3, 128, 16, 5120, 13824, "<3, false, 4, ")):

@@ -153,14 +153,15 @@ bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M, bool b
 
 // The kernel body; BF16 (per-element path only): x, scales and out are
 // bfloat16, B is the element-wise bfloat16 dequant and the MFMA the bf16 one.
-// FOLD (fast path, one row): the scale and zero are folded into the sums once
-// per block of FOLD consecutive chunks of one group (the MFMA accumulates the
-// block's chunks) instead of once per chunk; needs group_size % (32 FOLD) == 0
-// and every wave's run and K split starting on a multiple of FOLD chunks.
+// FOLD (fast path): the scale and zero are folded into the sums once per
+// block of FOLD consecutive chunks of one group (the MFMAs accumulate the
+// block's chunks, also the multi-row sums of x) instead of once per chunk;
+// needs group_size % (32 FOLD) == 0 and every wave's run and K split starting
+// on a multiple of FOLD chunks.
 template <int BITS, bool PER_ELEM, bool BF16, int MV, int CPL, int CPW, int FOLD>
 __device__ __forceinline__ void decode_body(GemmArgs a) {
   static_assert(!BF16 || PER_ELEM, "bfloat16 decode runs the per-element path");
-  static_assert(FOLD == 1 || (!PER_ELEM && MV == 1 && CPW % (2 * FOLD) == 0), "block fold: one-row fast path");
+  static_assert(FOLD == 1 || (!PER_ELEM && CPW % (2 * FOLD) == 0), "block fold: fast path");
   extern __shared__ __align__(16) unsigned char lds[];
   // one output element, rounded to the activation type (nearest even)
   auto store_out = [](_Float16* out, int64_t i, float v) __attribute__((always_inline)) {
@@ -506,6 +507,22 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       }
     }
   };
+  // block fold: the previous block's zero term too (its sums of x come from
+  // the block's MFMAs for several rows)
+  float s2_prev[CPL];
+  floatx4_t x_prev = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) s2_prev[j] = 0.f;
+  auto fold_prev_block = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        acc[j][v] = __builtin_fmaf(s_prev[j], d_prev[j][v], __builtin_fmaf(s2_prev[j], x_prev[v], acc[j][v]));
+        asm volatile("" : "+v"(acc[j][v]));
+      }
+    }
+  };
   const uint32_t* full_tab = reinterpret_cast<const uint32_t*>(lds + lay.tab_off);
   const int kbc = MV == 1 ? 0 : min(kb, Mp / 4 - 1);  // rows 4 kbc + v of the correction sums
 
@@ -669,9 +686,10 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       }
     } else if constexpr (FOLD > 1) {
       // blocks of FOLD chunks of one group: the block's MFMAs accumulate its
-      // sum of x' B, and its scale and zero are applied once, with the
-      // block's sum of x (staged).  The previous block's scale multiply is
-      // issued after this block's first MFMA (its result is not waited on at
+      // sum of x' B (and, for several rows, its sums of x against the MUL
+      // pattern), and its scale and zero are applied once, with the block's
+      // sum of x (staged for one row).  The previous block's fold is issued
+      // after this block's first MFMA (its results are not waited on at
       // once).  A fragments are read one chunk ahead, the block's table
       // entries and sum of x one block ahead.  row / rem (the group row and
       // the position in the group of chunk u0, a multiple of FOLD) are
@@ -683,7 +701,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       auto block_ops = [&](int u, int r) __attribute__((always_inline)) {
         BlockOps o;
         const unsigned char* base = stage_base(p);
-        o.X = reinterpret_cast<const float*>(base + lay.corr_off)[u / FOLD];
+        o.X = kSumsByMfma ? 0.f : reinterpret_cast<const float*>(base + lay.corr_off)[u / FOLD];
         const int row_bytes = __builtin_amdgcn_readfirstlane(r * TN * 8);
         const float* te = reinterpret_cast<const float*>(base + lay.ptab_off + row_bytes);
 #pragma unroll
@@ -694,9 +712,16 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
         return o;
       };
       auto frag_A = [&](int u) __attribute__((always_inline)) {
+        // rows >= M of A only feed rows >= M of D, which are never used
         const _Float16* frag = reinterpret_cast<const _Float16*>(stage_base(p));
-        return *reinterpret_cast<const half8_t*>(frag + ((u * 4 + kb) << 3));
+        return *reinterpret_cast<const half8_t*>(frag + (((u * 4 + kb) * M + min(q, M - 1)) << 3));
       };
+      half8_t ones;                                  // each register's MUL (sums of x, several rows)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        ones[2 * v] = (_Float16)Block<BITS>::MUL[v];
+        ones[2 * v + 1] = (_Float16)Block<BITS>::MUL[v];
+      }
       row = __builtin_amdgcn_readfirstlane(row);
       rem = __builtin_amdgcn_readfirstlane(rem);
       BlockOps cur = block_ops(u0, row);
@@ -709,11 +734,13 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
         BlockOps nxt = cur;
         if (b + 1 < u1 / FOLD) nxt = block_ops(FOLD * (b + 1), row);
         floatx4_t d[CPL];
+        floatx4_t dx = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < FOLD; ++i) {
           const int u = FOLD * b + i;
           half8_t An = A;
           if (u + 1 < u1) An = frag_A(u + 1);
+          if constexpr (kSumsByMfma) dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, dx, 0, 0, 0);
 #pragma unroll
           for (int j = 0; j < CPL; ++j) {
             uint32_t pr[4];
@@ -723,11 +750,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
             d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw),
                                                           i == 0 ? floatx4_t{0.f, 0.f, 0.f, 0.f} : d[j], 0, 0, 0);
           }
-          if (i == 0) {
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) acc[j][0] = __builtin_fmaf(cur.s2[j], cur.X, acc[j][0]);
-            fold_prev();
-          }
+          if (i == 0) fold_prev_block();
           __builtin_amdgcn_sched_barrier(0);
           A = An;
         }
@@ -735,7 +758,10 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
         for (int j = 0; j < CPL; ++j) {
           d_prev[j] = d[j];
           s_prev[j] = cur.s1[j];
+          s2_prev[j] = cur.s2[j];
         }
+        if constexpr (kSumsByMfma) x_prev = dx;
+        else x_prev = floatx4_t{cur.X, 0.f, 0.f, 0.f};
         cur = nxt;
       }
     } else {
@@ -814,7 +840,8 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
     int row = 0, rem = (c0 + stage_chunk(p, 0)) % cpg;
     compute_range(p, U0{}, UE{}, row, rem);
   }
-  if constexpr (!PER_ELEM && kDeferFold) fold_prev();
+  if constexpr (!PER_ELEM && FOLD > 1) fold_prev_block();
+  else if constexpr (!PER_ELEM && kDeferFold) fold_prev();
 
   // ---- reduce the waves through LDS (rows < M), write fp16
   __syncthreads();
@@ -922,10 +949,10 @@ static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
   }
 }
 
-// block fold (a.fold > 1): one-row fast path only
+// block fold (a.fold > 1): fast path only
 template <int BITS, bool PER_ELEM, int MV, int CPL, int CPW>
 static hipError_t launch_decode_fold(const GemmArgs& a, hipStream_t stream) {
-  if constexpr (!PER_ELEM && MV == 1) {
+  if constexpr (!PER_ELEM) {
     switch (a.fold) {
       case 1: return launch_decode_k<BITS, PER_ELEM, MV, CPL, CPW, 1>(a, stream);
       case 2: return launch_decode_k<BITS, PER_ELEM, MV, CPL, CPW, 2>(a, stream);

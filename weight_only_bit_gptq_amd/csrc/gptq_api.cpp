@@ -130,11 +130,11 @@ void apply_choice(const DecodeChoice& c, int M, int K, int G, bool per_elem, boo
   a->cpg = per_elem ? 1 : (K / G) / 32;
   a->ks = c.ks;
   a->cks = (C + c.ks - 1) / c.ks;
-  // one-row fast path: fold scale and zero once per block of 4 (or 2)
-  // chunks of one group; every wave's run (cpw chunks, halved at a phase's
-  // midpoint) and every K split must start on a block boundary
+  // fast path: fold scale and zero once per block of 4 (or 2) chunks of one
+  // group; every wave's run (cpw chunks, halved at a phase's midpoint) and
+  // every K split must start on a block boundary
   a->fold = 1;
-  if (!per_elem && M == 1 && !bf16) {
+  if (!per_elem && !bf16) {
     for (int f : {4, 2}) {
       if (a->cpg % f == 0 && (c.cpw / 2) % f == 0 && (c.ks == 1 || a->cks % f == 0)) {
         a->fold = f;
@@ -148,10 +148,10 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
                      bool tiled, gptq::GemmArgs* a, bool bf16) {
   bool found = false;
   DecodeChoice best{};
-  // tiled layout, M = 1, full-width: 16-column tiles with 8 waves of 16
-  // chunks (32-column tiles with 4 waves of 8 chunks from N = 16384 on) were
-  // the fastest or within 3% of it on every Llama-7B decode layer in MI355X
-  // sweeps, where the general rules below lose up to 10%
+  // tiled layout, M = 1, full-width: 8 waves of 16 chunks over 16-column
+  // tiles (32-column tiles from N = 16384 on) were the fastest or within 2%
+  // of it on every Llama-7B decode layer in MI355X sweeps, where the general
+  // rules below lose up to 10%
   // tiled layout, 2..16 rows, full-width: 8 chunks per wave, 64-column tiles
   // for 2/4-bit layers from N = 8192 on (32-column otherwise), 8 or 4 waves,
   // whichever pads K less (8 on a tie), two K splits for N <= 4096 with
@@ -173,8 +173,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
   if (tiled && M == 1 && !per_elem && waves == 0 && N / 16 >= kCUs / 2) {
     size_t lds;
     const bool wide = N >= 16384;
-    if (decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, wide ? 4 : 8, wide ? 8 : 16, 1, &best, &lds,
-                         bf16)) {
+    if (decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, 8, 16, 1, &best, &lds, bf16)) {
       apply_choice(best, M, K, G, per_elem, bf16, a);
       return true;
     }

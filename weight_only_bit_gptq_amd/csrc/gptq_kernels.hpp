@@ -33,8 +33,8 @@ struct GemmArgs {
   // K in phases of pc = nw * cpw chunks, cpw chunks per wave per phase,
   // cpg = group_size / 32 chunks per group on the fast path (else 1)
   int tiles, cpl, nw, cpw, pc, phases, cpg;
-  // fast path at one row: scale and zero folded once per `fold` consecutive
-  // chunks (1, 2 or 4; a divisor of cpg, of cpw / 2 and, with ks > 1, of cks)
+  // fast path: scale and zero folded once per `fold` consecutive chunks (1, 2
+  // or 4; a divisor of cpg, of cpw / 2 and, with ks > 1, of cks)
   int fold;
   // split K: ks workgroups per column tile, each over cks consecutive chunks
   // (the last one over the rest); with ks > 1 every workgroup stores its fp32

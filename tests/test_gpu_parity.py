@@ -165,6 +165,42 @@ def test_decode_multi_phase_k(dev, bits, M):
         assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, f"N={N}")
 
 
+FOLD_CASES = [
+    # bits, gs, M, K, N, waves, tiled: group rows spanning 2 blocks (gs 256), blocks of 2 (gs 64),
+    # no block fold (gs 96, 32), K splits whose length is not a multiple of 4 chunks, several rows
+    (4, 256, 1, 2048, 256, 0, False), (4, 64, 1, 1024, 256, 0, True), (4, 96, 1, 960, 128, 0, False),
+    (3, 32, 1, 512, 96, 0, False), (4, 128, 1, 11008, 1024, 0, False), (2, 128, 1, 12288, 512, 0, True),
+    (3, 256, 4, 4096, 224, 0, False), (2, 64, 16, 4096, 256, 0, True), (8, 128, 7, 2048, 160, 3, False),
+    (4, 128, 16, 11008, 1536, 0, True), (4, 256, 2, 8192, 96, 5, False),
+    # K splits starting in the middle of a group (36 and 70 chunks per split, 8 chunks per group)
+    (4, 256, 1, 9216, 256, 0, False), (4, 256, 1, 13312, 512, 0, False)]
+
+
+@pytest.mark.parametrize("bits,gs,M,K,N,waves,tiled", FOLD_CASES)
+def test_decode_block_fold(dev, bits, gs, M, K, N, waves, tiled):
+    """Decode fast path with the scale and zero folded once per block of 2 or
+    4 chunks: the fold the launch uses (the last template argument) divides
+    the chunks per group and is 1 where the group is not a multiple of 64
+    rows; oracle parity (asymmetric GPTQv1 data, zeros up to 2^b) on every
+    column, repeated calls bit-identical."""
+    d, L = quantized(K, N, M, bits, gs, False, False, False, seed=K + 3 * N + M)
+    qw, qz, sc, gi = upload(L, dev)
+    if tiled:
+        qw = gq.repack_tiled(qw, bits)
+    x = torch.from_numpy(d.x).to(dev)
+    desc = gq.describe(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, decode_waves=waves)
+    fold = int(desc.split(">")[0].split(",")[-1])
+    cpg = gs // 32
+    assert fold in (1, 2, 4) and cpg % fold == 0, desc
+    if gs % 64 != 0:
+        assert fold == 1, desc
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, False, K, N)
+    y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, decode_waves=waves)
+    y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False, path=gq.PATH_DECODE, decode_waves=waves)
+    assert_close(y1, ref, desc)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), desc
+
+
 SPLIT_CASES = [(4, 128, 1, 8192, 512, False), (4, 128, 3, 8192, 96, False), (8, 128, 7, 8192, 512, True),
                (2, 64, 4, 12288, 1024, False), (3, 128, 16, 13824, 640, True), (4, 128, 1, 11008, 1024, False),
                (3, 32, 2, 9216, 352, False), (4, 128, 16, 8192, 1536, False)]

@@ -29,6 +29,11 @@ Counter passes (HBM traffic of the decode kernel, see `--pmc-driver`):
   python3 bench.py --summarize-pmc D/fetch/run_counter_collection.csv D/write/run_counter_collection.csv
 The summary goes to profiles/; `roofline.traffic` is read from it while the
 decode sources still hash to the value recorded there (null otherwise).
+
+Counter pass (MFMA utilisation of the prefill kernel, see `--pmc-prefill-driver`):
+  rocprofv3 --pmc MfmaUtil GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA --kernel-trace -d D/mfma -o run -f csv \
+      -- python3 bench.py --pmc-prefill-driver
+  python3 bench.py --summarize-prefill-pmc D/mfma/run_counter_collection.csv D/mfma/run_kernel_trace.csv
 """
 from __future__ import annotations
 
@@ -46,6 +51,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama7b_w4g128_hbm_traffic.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_mlp70b_mfma_util.txt")
 # sources that decide the decode kernel's code and launch shapes
 DECODE_SOURCES = ["weight_only_bit_gptq_amd/csrc/decode.hip", "weight_only_bit_gptq_amd/csrc/gptq_device.hpp",
                   "weight_only_bit_gptq_amd/csrc/gptq_kernels.hpp", "weight_only_bit_gptq_amd/csrc/gptq_api.cpp"]
@@ -77,6 +83,10 @@ def parse():
                    help="repeat the oracle on the sample until this much CPU time has passed")
     p.add_argument("--pmc-driver", action="store_true",
                    help="only launch each decode layer 3 times and a plain copy, for a rocprofv3 --pmc pass")
+    p.add_argument("--pmc-prefill-driver", action="store_true",
+                   help="only launch each 70B-MLP prefill layer twice, for a rocprofv3 --pmc pass")
+    p.add_argument("--summarize-prefill-pmc", nargs=2, metavar=("COUNTER_CSV", "TRACE_CSV"),
+                   help="write the prefill MFMA-utilisation summary to profiles/ from a --pmc-prefill-driver pass")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the HBM traffic summary from two counter passes (no GPU needed)")
     return p.parse_args()
@@ -472,6 +482,83 @@ def pmc_driver(torch, gq, dev):
     print("pmc driver done", flush=True)
 
 
+PREFILL_WORKLOADS = ("mlp70b_prefill_w4g128", "mlp70b_prefill_w8g128")
+MI355X_XCDS = 8
+
+
+def pmc_prefill_driver(torch, gq, dev):
+    """Each 70B-MLP prefill layer (M = 2048) twice on its own weights; no timing."""
+    from workload import WORKLOADS
+    for name in PREFILL_WORKLOADS:
+        wl = WORKLOADS[name]
+        for layer in wl.layers:
+            L = make_layer(torch, gq, wl, layer, 2048, dev)
+            out = torch.empty((2048, layer.N), dtype=torch.float16, device=dev)
+            torch.cuda.synchronize()
+            for _ in range(2):
+                gq.gemm(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits, wl.group_size, wl.is_v2,
+                        out=out)
+            torch.cuda.synchronize()
+            print(f"{name} {layer.name}: {gq.describe(L['x'], L['qweight'], L['qzeros'], L['scales'], None, wl.bits, wl.group_size, wl.is_v2, out=out)}",
+                  flush=True)
+            del L, out
+            torch.cuda.empty_cache()
+    print("pmc prefill driver done", flush=True)
+
+
+def summarize_prefill_pmc(counter_csv, trace_csv):
+    """MfmaUtil (MFMA busy cycles / (GPU active cycles x SIMDs)), the clock the
+    kernel ran at (GRBM_GUI_ACTIVE / kernel duration) and VALU / MFMA
+    instruction counts of the second launch of each prefill layer."""
+    from workload import WORKLOADS
+    vals = {}
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            if "prefill_kernel" in r["Kernel_Name"]:
+                d = vals.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dur = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            dur[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    ids = sorted(vals)
+    layers = [(n, l) for n in PREFILL_WORKLOADS for l in WORKLOADS[n].layers]
+    if len(ids) != 2 * len(layers):
+        raise SystemExit(f"expected {2 * len(layers)} prefill dispatches, got {len(ids)}")
+    lines = [
+        "# MFMA utilisation of the prefill kernel, 70B-MLP shapes at M=2048 (4-bit g128 sym v1, 8-bit g128 asym",
+        "# v2), one MI355X; second of two launches per layer, counters summed over the chip.",
+        "# Command (run from /tmp with TMPDIR=/tmp; R = repository root):",
+        "#   rocprofv3 --pmc MfmaUtil GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA --kernel-trace -d D/mfma -o run -f csv "
+        "-- python3 R/bench.py --pmc-prefill-driver",
+        "#   python3 R/bench.py --summarize-prefill-pmc D/mfma/run_counter_collection.csv D/mfma/run_kernel_trace.csv",
+        "# MfmaUtil = sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) (rocprofv3's derived counter);",
+        "# clock = GRBM_GUI_ACTIVE / 8 / kernel duration (the CSV sums the counter over the 8 XCDs);",
+        "# TFLOP/s from the kernel duration under the profiler (no warm-up: clocks are still rising).",
+        "# SQ_INSTS_VALU counts the MFMA instructions too (so the other VALU per MFMA is the ratio minus 1).",
+        "layer | kernel | us | TFLOP/s | clock GHz | MfmaUtil % | SQ_INSTS_VALU / SQ_INSTS_MFMA",
+    ]
+    rec = []
+    for i, (name, layer) in enumerate(layers):
+        did = ids[2 * i + 1]
+        v = vals[did]
+        us = dur[did] / 1e3
+        flops = 2.0 * 2048 * layer.K * layer.N
+        # GRBM_GUI_ACTIVE has one instance per XCD and the CSV holds their sum: per-XCD cycles are 1/8
+        clk = v.get("GRBM_GUI_ACTIVE", 0.0) / MI355X_XCDS / dur[did]
+        ratio = v.get("SQ_INSTS_VALU", 0.0) / max(v.get("SQ_INSTS_MFMA", 0.0), 1.0)
+        rec.append({"workload": name, "layer": layer.name, "kernel": v["kernel"], "us": round(us, 2),
+                    "TFLOPs": round(flops / us / 1e6, 1), "clock_GHz": round(clk, 3),
+                    "MfmaUtil": round(v.get("MfmaUtil", float("nan")), 2), "valu_per_mfma": round(ratio, 2)})
+        lines.append(f"{name} {layer.name} | {v['kernel']} | {us:.1f} | {flops / us / 1e6:.1f} | {clk:.3f} | "
+                     f"{v.get('MfmaUtil', float('nan')):.1f} | {ratio:.2f}")
+    lines.append("json: " + json.dumps(rec))
+    os.makedirs(os.path.dirname(MFMA_FILE), exist_ok=True)
+    with open(MFMA_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_pmc(fetch_csv, write_csv):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode launches, scaled
     by what the same counters read for the plain copy of PMC_COPY_BYTES."""
@@ -539,6 +626,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
+    if args.summarize_prefill_pmc:
+        summarize_prefill_pmc(*args.summarize_prefill_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(run with --gpus 1)", file=sys.stderr)
@@ -552,6 +642,9 @@ def main():
     gq.library()
     if args.pmc_driver:
         pmc_driver(torch, gq, dev)
+        return
+    if args.pmc_prefill_driver:
+        pmc_prefill_driver(torch, gq, dev)
         return
 
     dec = bench_decode(torch, gq, args, dev, tiled=True)

@@ -223,7 +223,11 @@ def bench_decode(torch, gq, args, dev, tiled, bf16=False):
 def bench_prefill(torch, gq, args, dev, bf16=False):
     """Prefill GEMM timing per layer (plus, for the 4-bit workload, the vendor
     dense GEMM in the same activation type on the same shape, as context).
-    `bf16`: bfloat16 activations and scales, 4-bit workload only."""
+    fp16: qweight in the tiled layout, the same re-laid-out copy the decode
+    step reads (4-bit tiled words hold their fields in pair order, which the
+    prefill kernel unpacks with fewer instructions).  `bf16`: bfloat16
+    activations and scales, 4-bit workload only, checkpoint layout (the only
+    one bfloat16 reads)."""
     from workload import WORKLOADS
     res = []
     adt = torch.bfloat16 if bf16 else torch.float16
@@ -231,7 +235,7 @@ def bench_prefill(torch, gq, args, dev, bf16=False):
     for name in names:
         wl = WORKLOADS[name]
         for layer in wl.layers:
-            L = make_layer(torch, gq, wl, layer, 2048, dev)
+            L = make_layer(torch, gq, wl, layer, 2048, dev, tiled=not bf16)
             if bf16:
                 L = to_bf16(torch, L)
             out = torch.empty((2048, layer.N), dtype=adt, device=dev)
@@ -255,8 +259,8 @@ def bench_prefill(torch, gq, args, dev, bf16=False):
             flops = 2.0 * 2048 * layer.K * layer.N
             tf = flops / (ms * 1e-3) / 1e12
             row = {"workload": name, "layer": layer.name, "M": 2048, "K": layer.K, "N": layer.N,
-                   "bits": wl.bits, "ms": round(ms, 4), "TFLOPs": round(tf, 1),
-                   "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+                   "bits": wl.bits, "qweight_layout": "checkpoint" if bf16 else "tiled", "ms": round(ms, 4),
+                   "TFLOPs": round(tf, 1), "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
             if name == "mlp70b_prefill_w4g128":
                 # context: the vendor dense GEMM (torch.matmul) on the same shape, unquantized W
                 W = torch.randn((layer.K, layer.N), dtype=adt, device=dev)
@@ -487,12 +491,12 @@ MI355X_XCDS = 8
 
 
 def pmc_prefill_driver(torch, gq, dev):
-    """Each 70B-MLP prefill layer (M = 2048) twice on its own weights; no timing."""
+    """Each 70B-MLP prefill layer (M = 2048, tiled layout) twice on its own weights; no timing."""
     from workload import WORKLOADS
     for name in PREFILL_WORKLOADS:
         wl = WORKLOADS[name]
         for layer in wl.layers:
-            L = make_layer(torch, gq, wl, layer, 2048, dev)
+            L = make_layer(torch, gq, wl, layer, 2048, dev, tiled=True)      # as the bench times it
             out = torch.empty((2048, layer.N), dtype=torch.float16, device=dev)
             torch.cuda.synchronize()
             for _ in range(2):

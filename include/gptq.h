@@ -195,19 +195,24 @@ GPTQ_API int gptq_convert_zeros_check(const int32_t* qzeros_in, const int32_t* q
                                       int64_t N, int to_v2, const int32_t* lossy_count);
 
 /*
- * Tiled qweight layout: the same words as the checkpoint layout, reordered so
+ * Tiled qweight layout: the words of the checkpoint layout, reordered so
  * that each 16-column tile is one contiguous run (an offline re-layout in the
  * spirit of the page "Weight-only INT4 quantization: GPTQ, AWQ and the Marlin
  * kernel", section 6.1; the order is this library's own):
  *   qweight_tiled int32 [N/16][K/32][bits][16],
- *   qweight_tiled[t][c][r][j] = qweight[c*bits + r][16*t + j].
+ *   qweight_tiled[t][c][r][j] = qweight[c*bits + r][16*t + j]
+ * for 2, 3 and 8 bits; a 4-bit word also has its eight fields in pair order
+ * (field 2i of the checkpoint word in nibble i, field 2i + 1 in nibble i + 4,
+ * i < 4), so that one mask per 16-bit half gives two consecutive fields (the
+ * prefill kernel builds its MFMA operand with one shift and four masks per
+ * word instead of four byte permutes).
  * The decode kernel then streams each workgroup's weights from one contiguous
  * region instead of 64-256-byte pieces of rows N*4 bytes apart (measured on
  * MI355X: 5-11% less time per Llama-7B-shaped decode layer at M = 1).
  * qzeros, scales and g_idx are unchanged.
  *
  * gptq_repack_tiled / gptq_unrepack_tiled convert between the layouts on
- * `stream` (one kernel, a pure word permutation).  Same N, K, bits rules as
+ * `stream` (one kernel).  Same N, K, bits rules as
  * gptq_gemm; both buffers 16-byte aligned, K*bits/32*N int32 words each,
  * and they must not overlap (GPTQ_ERR_BAD_ARG, also for in == out).
  */

@@ -257,26 +257,49 @@ def convert_zeros_packed(qzeros: np.ndarray, bits: int, N: int, to_v2: bool):
 TILE_COLS = 16   # columns of one tile of the tiled qweight layout
 
 
+# 4-bit words of the tiled layout hold their eight fields in pair order:
+# nibble i holds the field that nibble PAIR_NIBBLES[i] holds in the checkpoint
+# word, i.e. field 2i in nibble i and field 2i+1 in nibble i+4 (i < 4).
+PAIR_NIBBLES = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def _permute_nibbles(w: np.ndarray, to_pairs: bool) -> np.ndarray:
+    u = np.asarray(w).view(np.uint32)
+    out = np.zeros_like(u)
+    for i, src in enumerate(PAIR_NIBBLES):
+        if to_pairs:
+            out |= ((u >> np.uint32(4 * src)) & np.uint32(0xF)) << np.uint32(4 * i)
+        else:
+            out |= ((u >> np.uint32(4 * i)) & np.uint32(0xF)) << np.uint32(4 * src)
+    return out.view(np.int32)
+
+
 def repack_tiled(qweight: np.ndarray, bits: int) -> np.ndarray:
     """Checkpoint qweight [K*b/32, N] -> the tiled layout, int32 [N/16, K/32, b, 16].
 
     Word (t, c, r, j) is packed row c*b + r of column 16*t + j: each 16-column
     tile holds, chunk after chunk (32 rows of K), the b packed rows of that
-    chunk, 16 words each.  A pure permutation of words: the bits inside a word
-    are untouched.  (An offline re-layout in the spirit of the page "Weight-only
-    INT4 quantization: GPTQ, AWQ and the Marlin kernel", section 6.1; the
-    concrete order is this library's own, so the pages fix no expected value.)"""
+    chunk, 16 words each.  For 2, 3 and 8 bits the bits inside a word are
+    untouched; a 4-bit word holds its eight fields in pair order
+    (PAIR_NIBBLES), so that each 16-bit half masked at one position gives two
+    consecutive fields.  (An offline re-layout in the spirit of the page
+    "Weight-only INT4 quantization: GPTQ, AWQ and the Marlin kernel", section
+    6.1; the concrete order is this library's own, so the pages fix no
+    expected value.)"""
     w = np.ascontiguousarray(qweight)
     R, N = w.shape
     if R % bits != 0 or N % TILE_COLS != 0:
         raise ValueError("qweight must be [K*b/32, N] with N % 16 == 0")
     C = R // bits
-    return np.ascontiguousarray(w.reshape(C, bits, N // TILE_COLS, TILE_COLS).transpose(2, 0, 1, 3))
+    t = np.ascontiguousarray(w.reshape(C, bits, N // TILE_COLS, TILE_COLS).transpose(2, 0, 1, 3))
+    return _permute_nibbles(t, True) if bits == 4 else t
 
 
 def unrepack_tiled(tiled: np.ndarray, bits: int, K: int, N: int) -> np.ndarray:
     """Inverse of repack_tiled: the tiled layout -> checkpoint qweight [K*b/32, N]."""
     t = np.asarray(tiled).reshape(N // TILE_COLS, K // 32, bits, TILE_COLS)
+    if bits == 4:
+        t = _permute_nibbles(np.ascontiguousarray(t), False)
     return np.ascontiguousarray(t.transpose(1, 2, 0, 3).reshape(K // 32 * bits, N))
 
 

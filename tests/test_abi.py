@@ -154,7 +154,7 @@ def test_tiled_describe_shapes():
         assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, bits, gs, 1, M, N, K, OUT, 0, 0, buf, 256) == 0
         assert buf.value.decode().startswith("gptq::decode_kernel" + want), buf.value
     assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, 4, 128, 1, 2048, 8192, 8192, OUT, 0, 0, buf, 256) == 0
-    assert buf.value.decode().startswith("gptq::prefill_kernel<4, false, true>")
+    assert buf.value.decode().startswith("gptq::prefill_kernel<4, false, true, true>")
 
 
 def test_moe_argument_codes():
@@ -263,7 +263,7 @@ def test_describe_names_the_kernel():
     assert lib.gptq_gemm_describe(X, QW, QZ, SC, GI, 3, 128, 1, 16, 5120, 13824, OUT, 0, 0, buf, 256) == 0
     assert buf.value.decode().startswith("gptq::decode_kernel<3, true, 4, ")
     assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 8, 128, 1, 2048, 28672, 8192, OUT, 0, 0, buf, 256) == 0
-    assert buf.value.decode().startswith("gptq::prefill_kernel<8, false, false>")
+    assert buf.value.decode().startswith("gptq::prefill_kernel<8, false, false, false>")
     assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 5, 128, 1, 1, 4096, 4096, OUT, 0, 0, buf, 256) == -2
     assert lib.gptq_gemm_describe(X, QW, QZ, SC, None, 4, 128, 1, 1, 4096, 4096, OUT, 0, 0, None, 256) == -1
     small = ctypes.create_string_buffer(8)

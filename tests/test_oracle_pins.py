@@ -282,7 +282,10 @@ def test_convert_zeros_packed_keeps_dequant(bits):
 @pytest.mark.parametrize("bits", BITS)
 def test_repack_tiled_index_map(bits):
     """Tiled layout against its element-wise definition, written as loops:
-    word (t, c, r, j) = qweight[c*b + r, 16 t + j]; and the inverse."""
+    word (t, c, r, j) = qweight[c*b + r, 16 t + j], except that a 4-bit word
+    holds field 2i in nibble i and field 2i + 1 in nibble i + 4 (i < 4; field
+    m of checkpoint word is its nibble m, row 32 c + 8 r + m); and the
+    inverse."""
     K, N = 96, 48
     qw = random_words(np.random.default_rng(bits), (K * bits // 32, N))
     tiled = oracle.repack_tiled(qw, bits)
@@ -291,7 +294,14 @@ def test_repack_tiled_index_map(bits):
         for c in range(K // 32):
             for r in range(bits):
                 for j in range(16):
-                    assert tiled[t, c, r, j] == qw[c * bits + r, 16 * t + j]
+                    src = int(qw[c * bits + r, 16 * t + j]) & 0xFFFFFFFF
+                    got = int(tiled[t, c, r, j]) & 0xFFFFFFFF
+                    if bits != 4:
+                        assert got == src
+                        continue
+                    for i in range(4):
+                        assert (got >> (4 * i)) & 15 == (src >> (4 * (2 * i))) & 15
+                        assert (got >> (4 * (i + 4))) & 15 == (src >> (4 * (2 * i + 1))) & 15
     assert np.array_equal(oracle.unrepack_tiled(tiled.ravel(), bits, K, N), qw)
 
 

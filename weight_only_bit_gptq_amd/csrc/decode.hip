@@ -231,6 +231,9 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   const uint32_t sel = block_sel<BITS>(kb);
   // every row of a 32-row chunk in one group (no g_idx, whole-chunk groups)
   const bool rows_share_group = a.g_idx == nullptr && (a.group_size & 31) == 0;
+  // 4-bit words of the tiled layout hold their fields in pair order, so the
+  // unpack's register v holds fields (2v, 2v + 1) instead of (F[2v], F[2v + 1])
+  const bool pairs4 = BITS == 4 && a.wtiled != 0;
 
   // ---- staging scope: the fast path stages per wave (its own CPW chunks, in
   // its own LDS region), the per-element path per workgroup (the phase's pc
@@ -298,7 +301,8 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       for (int v = 0; v < 4; ++v) {
         // the pair of register v in field order; x' = x / MUL is exact in fp16
         // (a power-of-two scaling) up to subnormal rounding, like the scalar form
-        half2_t pr = {xv[Block<BITS>::F[2 * v]], xv[Block<BITS>::F[2 * v + 1]]};
+        half2_t pr = pairs4 ? half2_t{xv[2 * v], xv[2 * v + 1]}
+                            : half2_t{xv[Block<BITS>::F[2 * v]], xv[Block<BITS>::F[2 * v + 1]]};
         if constexpr (!PER_ELEM) {
           const _Float16 inv = (_Float16)(1.0f / (float)Block<BITS>::MUL[v]);
           const _Float16 mul = (_Float16)Block<BITS>::MUL[v];
@@ -608,8 +612,10 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
           u32x4_t bw;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const uint32_t ea = full_tab[(int)gv[Block<BITS>::F[2 * v]] * TN + CPL * q + j];
-            const uint32_t eb = full_tab[(int)gv[Block<BITS>::F[2 * v + 1]] * TN + CPL * q + j];
+            const int ga = pairs4 ? gv[2 * v] : gv[Block<BITS>::F[2 * v]];
+            const int gb = pairs4 ? gv[2 * v + 1] : gv[Block<BITS>::F[2 * v + 1]];
+            const uint32_t ea = full_tab[ga * TN + CPL * q + j];
+            const uint32_t eb = full_tab[gb * TN + CPL * q + j];
             const half2_t neg = {neg_offset<BITS>(v, (int)(ea >> 16)), neg_offset<BITS>(v, (int)(eb >> 16))};
             const half2_t d = pair_minus_zero<BITS>(pr[v], v, neg);
             const half2_t s = {__builtin_bit_cast(_Float16, (uint16_t)(ea & 0xFFFFu)),

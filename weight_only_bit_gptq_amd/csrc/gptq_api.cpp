@@ -436,9 +436,12 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
   } else {
     // the pipelined full-tile body: fast path, K % 64 == 0, not 8-bit
     const bool full = !per_elem && K % 64 == 0 && bits != 8;
-    std::snprintf(buf, (size_t)buflen, "gptq::%s<%d, %s, %s> grid=%dx%d block=256",
-                  bf16 ? "prefill_bf16_kernel" : "prefill_kernel", bits, pe, full ? "true" : "false", a.tiles_n,
-                  a.tiles_m);
+    if (bf16)
+      std::snprintf(buf, (size_t)buflen, "gptq::prefill_bf16_kernel<%d, %s, %s> grid=%dx%d block=256", bits, pe,
+                    full ? "true" : "false", a.tiles_n, a.tiles_m);
+    else   // last argument: 4-bit tiled words with fields in pair order
+      std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s, %s, %s> grid=%dx%d block=256", bits, pe,
+                    full ? "true" : "false", (bits == 4 && tiled) ? "true" : "false", a.tiles_n, a.tiles_m);
   }
   return GPTQ_OK;
 }

@@ -49,8 +49,12 @@ void prefill_shape(int M, int N, int* tiles_m, int* tiles_n) {
 // separate instantiations: one body with both paths behind a branch spills.
 // BF16: x, scales and out are bfloat16; B is the element-wise bfloat16
 // dequant of gptq_device.hpp and the MFMA the bf16 one (same tiles).
-template <int BITS, bool PER_ELEM, bool FULL, bool BF16>
+// PAIRS (4-bit, tiled layout): the words hold their fields in pair order, so
+// one shift and four mask-ors make the four registers (fields 2v, 2v + 1,
+// multiplier 1, 16, 1, 16 for both halves) instead of four byte permutes.
+template <int BITS, bool PER_ELEM, bool FULL, bool BF16, bool PAIRS>
 __device__ __forceinline__ void prefill_body(GemmArgs a) {
+  static_assert(!PAIRS || (BITS == 4 && !BF16), "pair-order words: 4-bit fp16");
   constexpr int BM = kPrefillBM;
   constexpr int BK = kPrefillBK;
   constexpr int MS = kPrefillMS;
@@ -174,6 +178,20 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
 
   uint32_t magic;                                    // kMagicPair in a register (see unpack_block_natural)
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  // a block's four magic pairs, each pair (fields 2v, 2v + 1) -> exact (q - z),
+  // and the offsets -(1024 / MUL + z) of both halves of register v
+  auto unpack_B = [&](uint32_t w0v, uint32_t w1v, int kb, uint32_t p[4]) __attribute__((always_inline)) {
+    if constexpr (PAIRS) unpack_block<4>(w0v, 0u, 0u, p, magic);
+    else unpack_block_natural<BITS>(w0v, w1v, kb, p, magic);
+  };
+  auto minus_zero = [](uint32_t pv, int v, half2_t neg) __attribute__((always_inline)) {
+    if constexpr (PAIRS) return pair_minus_zero<4>(pv, v, neg);
+    else return pair_minus_zero_natural<BITS>(pv, v, neg);
+  };
+  auto neg_off = [](int v, int zlo, int zhi) __attribute__((always_inline)) {
+    if constexpr (PAIRS) return half2_t{neg_offset<4>(v, zlo), neg_offset<4>(v, zhi)};
+    else return neg_offset_natural<BITS>(v, zlo, zhi);
+  };
   auto mfma = [](const half8_t& A, const half8_t& B, const floatx16_t& c) __attribute__((always_inline)) {
     if constexpr (BF16)
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, A), __builtin_bit_cast(bf16x8_t, B),
@@ -203,7 +221,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
       const int z = field_of4(z2, j, BITS) + a.zero_offset;
       sp[j] = half2_t{s2[j], s2[j]};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) negp[j][v] = neg_offset_natural<BITS>(v, z, z);
+      for (int v = 0; v < 4; ++v) negp[j][v] = neg_off(v, z, z);
     }
   };
 
@@ -251,10 +269,10 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
           continue;
         }
         uint32_t p[4];
-        unpack_block_natural<BITS>(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p, magic);
+        unpack_B(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p);
         u32x4_t bw;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) bw[v] = as_u32(pair_minus_zero_natural<BITS>(p[v], v, negp[j][v]) * sp[j]);
+        for (int v = 0; v < 4; ++v) bw[v] = as_u32(minus_zero(p[v], v, negp[j][v]) * sp[j]);
         B[j] = __builtin_bit_cast(half8_t, bw);
       }
     };
@@ -327,7 +345,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
           continue;
         }
         uint32_t p[4];
-        unpack_block_natural<BITS>(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p, magic);
+        unpack_B(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p);
         u32x4_t bw;
         if constexpr (PER_ELEM) {
           const int k0 = kt * BK + 16 * s + 8 * kb2;
@@ -337,14 +355,14 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
             const int gb = group_of(a.g_idx, k0 + 2 * v + 1, a.group_size, a.G);
             const uint32_t za = load_zero4<BITS>(a.qzeros, a.zrow_words, ga, nc & ~3) >> (BITS * ((nc & 3) + j));
             const uint32_t zb = load_zero4<BITS>(a.qzeros, a.zrow_words, gb, nc & ~3) >> (BITS * ((nc & 3) + j));
-            const half2_t neg = neg_offset_natural<BITS>(v, (int)(za & ((1u << BITS) - 1u)) + a.zero_offset,
-                                                         (int)(zb & ((1u << BITS) - 1u)) + a.zero_offset);
+            const half2_t neg = neg_off(v, (int)(za & ((1u << BITS) - 1u)) + a.zero_offset,
+                                        (int)(zb & ((1u << BITS) - 1u)) + a.zero_offset);
             const half2_t sc = {a.scales[(int64_t)ga * a.N + nc + j], a.scales[(int64_t)gb * a.N + nc + j]};
-            bw[v] = as_u32(pair_minus_zero_natural<BITS>(p[v], v, neg) * sc);
+            bw[v] = as_u32(minus_zero(p[v], v, neg) * sc);
           }
         } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) bw[v] = as_u32(pair_minus_zero_natural<BITS>(p[v], v, negp[j][v]) * sp[j]);
+          for (int v = 0; v < 4; ++v) bw[v] = as_u32(minus_zero(p[v], v, negp[j][v]) * sp[j]);
         }
         B[j] = __builtin_bit_cast(half8_t, bw);
       }
@@ -425,21 +443,28 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   }
 }
 
-template <int BITS, bool PER_ELEM, bool FULL>
+template <int BITS, bool PER_ELEM, bool FULL, bool PAIRS>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
-  prefill_body<BITS, PER_ELEM, FULL, false>(a);
+  prefill_body<BITS, PER_ELEM, FULL, false, PAIRS>(a);
 }
 
 template <int BITS, bool PER_ELEM, bool FULL>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(GemmArgs a) {
-  prefill_body<BITS, PER_ELEM, FULL, true>(a);
+  prefill_body<BITS, PER_ELEM, FULL, true, false>(a);
 }
 
 template <int BITS, bool PER_ELEM, bool FULL>
 static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(a.tiles_m * a.tiles_n);
-  if (a.bf16) hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((prefill_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
+  if (a.bf16) {
+    if (a.wtiled) return hipErrorInvalidValue;     // bfloat16 reads the checkpoint layout only
+    hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
+  } else if (BITS == 4 && a.wtiled) {
+    // 4-bit tiled words hold their fields in pair order
+    hipLaunchKernelGGL((prefill_kernel<BITS, PER_ELEM, FULL, BITS == 4>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<BITS, PER_ELEM, FULL, false>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -277,6 +277,20 @@ hipError_t launch_convert_zeros(const int32_t* in, int32_t* out, int bits, int64
 // contiguous run, chunk (32 rows of K) after chunk.  Words move unchanged.
 // One thread per word of the tiled array (its writes coalesce; its reads are
 // 64-byte pieces of checkpoint rows).
+// 4-bit words of the tiled layout hold their eight fields in pair order:
+// field 2i in nibble i and field 2i + 1 in nibble i + 4 (i < 4), so that one
+// mask per 16-bit half gives two consecutive fields.  to_pairs = 0 inverts.
+__device__ __forceinline__ uint32_t pair_order_nibbles(uint32_t w, int to_pairs) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int f = i < 4 ? 2 * i : 2 * (i - 4) + 1;  // field held by tiled nibble i
+    if (to_pairs) out |= ((w >> (4 * f)) & 0xFu) << (4 * i);
+    else out |= ((w >> (4 * i)) & 0xFu) << (4 * f);
+  }
+  return out;
+}
+
 __global__ void __launch_bounds__(256) repack_kernel(const int32_t* __restrict__ in, int32_t* __restrict__ out,
                                                      int bits, int64_t N, int64_t K, int to_tiled) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;     // tiled index
@@ -287,8 +301,8 @@ __global__ void __launch_bounds__(256) repack_kernel(const int32_t* __restrict__
   const int64_t cr = rest % rows;                  // c * bits + r: the packed row
   const int64_t t = rest / rows;
   const int64_t src = cr * N + 16 * t + j;         // checkpoint index
-  if (to_tiled) out[i] = in[src];
-  else out[src] = in[i];
+  if (to_tiled) out[i] = bits == 4 ? (int32_t)pair_order_nibbles((uint32_t)in[src], 1) : in[src];
+  else out[src] = bits == 4 ? (int32_t)pair_order_nibbles((uint32_t)in[i], 0) : in[i];
 }
 
 hipError_t launch_repack(const int32_t* in, int32_t* out, int bits, int64_t N, int64_t K, int to_tiled,

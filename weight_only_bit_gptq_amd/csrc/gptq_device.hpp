@@ -145,10 +145,13 @@ __device__ __forceinline__ void unpack_block_natural(uint32_t w0, uint32_t w1, i
     for (int v = 0; v < 4; ++v)
       p[v] = (__builtin_amdgcn_perm(0u, w0, dup_byte_sel(v)) & 0x00F0000Fu) | kMagicPair;
   } else if constexpr (BITS == 8) {
+    // one byte permute per register: field bytes b, b + 1 of the word into
+    // bytes 0 and 2, and the magic's 0x64 (its byte 1, selector 5) into bytes
+    // 1 and 3, i.e. the fp16 pair (1024 + f_b, 1024 + f_{b+1})
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const uint32_t b = 2 * (v & 1);
-      p[v] = __builtin_amdgcn_perm(0u, v < 2 ? w0 : w1, 0x0C000C00u | b | ((b + 1) << 16)) | kMagicPair;
+      p[v] = __builtin_amdgcn_perm(kMagicPair, v < 2 ? w0 : w1, 0x05000500u | b | ((b + 1) << 16));
     }
   } else if constexpr (BITS == 2) {
     const int b0 = 2 * (kb & 1);                 // the block's two bytes: f0..f3, f4..f7

@@ -276,8 +276,8 @@ def test_decode_split_k_other_stream_and_graph(dev):
 # ------------------------------------------------------------------ tiled qweight layout
 @pytest.mark.parametrize("bits", BITS)
 def test_repack_tiled_bit_exact(dev, bits):
-    """gptq_repack_tiled reproduces the oracle's word permutation exactly and
-    gptq_unrepack_tiled inverts it."""
+    """gptq_repack_tiled reproduces the oracle's tiled layout exactly (words
+    moved, 4-bit fields in pair order) and gptq_unrepack_tiled inverts it."""
     for K, N in ((96, 32), (4096, 544), (11008, 64)):
         qw = random_words(np.random.default_rng(K + N + bits), (K * bits // 32, N))
         t = torch.from_numpy(qw).to(dev)

@@ -426,7 +426,8 @@ def moe_gemm(x, qweight, qzeros, scales, g_idx: Optional[object], expert_offsets
 
 
 def repack_tiled(qweight, bits: int):
-    """Checkpoint qweight [K*bits/32, N] (int32, GPU) -> tiled layout [N/16, K/32, bits, 16]."""
+    """Checkpoint qweight [K*bits/32, N] (int32, GPU) -> tiled layout [N/16, K/32, bits, 16]
+    (4-bit words with their fields in pair order; see gptq_repack_tiled)."""
     import torch
     if bits not in (2, 3, 4, 8):
         raise ValueError("bits must be 2, 3, 4 or 8")

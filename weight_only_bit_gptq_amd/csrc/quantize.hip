@@ -274,7 +274,8 @@ hipError_t launch_convert_zeros(const int32_t* in, int32_t* out, int bits, int64
 // qweight re-layout.  Checkpoint layout: int32 [K*b/32, N] (packed row r,
 // column n).  Tiled layout: int32 [N/16][K/32][b][16]: word (t, c, r, j) is
 // packed row c*b + r of column 16 t + j, so a 16-column tile's words are one
-// contiguous run, chunk (32 rows of K) after chunk.  Words move unchanged.
+// contiguous run, chunk (32 rows of K) after chunk.  2/3/8-bit words move
+// unchanged; 4-bit words also get their fields in pair order (below).
 // One thread per word of the tiled array (its writes coalesce; its reads are
 // 64-byte pieces of checkpoint rows).
 // 4-bit words of the tiled layout hold their eight fields in pair order:

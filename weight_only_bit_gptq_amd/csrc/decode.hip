@@ -98,6 +98,14 @@ __device__ __forceinline__ typename WordVec<CPL>::T buffer_words(__amdgpu_buffer
 
 __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
+// v / d and v % d for v >= 0, d > 0: a shift or a mask when d is a power of
+// two (every whole-chunk group size of 2^j * 32 rows), so the kernel's
+// prologue spends no integer-division sequence on them
+__host__ __device__ inline int div_pos(int v, int d) {
+  return (d & (d - 1)) == 0 ? v >> __builtin_ctz((unsigned)d) : v / d;
+}
+__host__ __device__ inline int mod_pos(int v, int d) { return (d & (d - 1)) == 0 ? v & (d - 1) : v % d; }
+
 // rows of x a chunk's sums are laid out for (multiple of 4 for M > 1)
 __host__ __device__ inline int decode_corr_rows(int M) { return M == 1 ? 1 : (M + 3) & ~3; }
 
@@ -108,10 +116,10 @@ __host__ __device__ inline int decode_corr_rows(int M) { return M == 1 ? 1 : (M 
 // by the workgroup (two when K takes several phases: x fragments and the
 // phase's g_idx slice) plus the whole scale/zero table, behind a barrier.
 __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int cpl, bool per_elem, int G, int cpg,
-                                                      int phases, bool bf16 = false) {
+                                                      int phases, bool bf16 = false, int cpw_known = 0) {
   DecodeLayout L;
   const size_t tn = (size_t)16 * cpl;
-  const int cpw = pc / nw;
+  const int cpw = cpw_known > 0 ? cpw_known : pc / nw;   // the kernel passes its compile-time value
   const int chunks = per_elem ? pc : cpw;                // chunks one staging region holds
   const size_t frag = align16((size_t)chunks * 4 * M * 16);
   L.corr_off = frag;
@@ -120,7 +128,7 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   const size_t gidx = per_elem ? align16((size_t)chunks * 32 * 2) : 0;
   L.ptab_off = L.gidx_off + gidx;
   // fast path: the groups a run of cpw consecutive chunks can touch
-  L.ptab_rows = per_elem ? 0 : (cpw - 1) / cpg + 2;
+  L.ptab_rows = per_elem ? 0 : div_pos(cpw - 1, cpg) + 2;
   L.buf_stride = align16(L.ptab_off + (size_t)L.ptab_rows * tn * 8);
   const int regions = per_elem ? (phases > 1 ? 2 : 1) : nw;
   L.tab_off = (size_t)regions * L.buf_stride;            // whole table (per-element path)
@@ -214,7 +222,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int kb = lane >> 4;          // 8-row block of the chunk (A and B operands)
   const int q = lane & 15;           // column slot (B) and x row (A)
-  const int t = unit / a.ks;
+  const int t = a.ks == 1 ? unit : unit / a.ks;
   const int sk = unit - t * a.ks;
   const int c0 = sk * a.cks;                         // first chunk of this split
   const int n0 = t * TN;
@@ -226,7 +234,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   // per-chunk sums of x in groups of four rows, so it lays out at least two
   // rows (four sums) even for a one-row block of a grouped launch
   const int ML = MV == 1 ? 1 : max(M, 2);
-  const DecodeLayout lay = decode_layout(ML, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases, BF16);
+  const DecodeLayout lay = decode_layout(ML, pc, a.nw, CPL, PER_ELEM, a.G, cpg, phases, BF16, CPW);
   const int Mp = decode_corr_rows(ML);
   const uint32_t sel = block_sel<BITS>(kb);
   // every row of a 32-row chunk in one group (no g_idx, whole-chunk groups)
@@ -437,7 +445,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   };
   // fast path: row r of a wave's table holds group stage_chunk(p, 0) / cpg + r
   auto chunk_group = [&](int p) __attribute__((always_inline)) {
-    const int g0 = (c0 + stage_chunk(p, 0)) / cpg;
+    const int g0 = div_pos(c0 + stage_chunk(p, 0), cpg);
     return [g0](int r) __attribute__((always_inline)) { return g0 + r; };
   };
   auto whole_table = [](int r) { return r; };
@@ -833,7 +841,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
     wave_fence();
     int p = 0;
     for (; p + 1 < phases; ++p) {
-      int row = 0, rem = (c0 + stage_chunk(p, 0)) % cpg;
+      int row = 0, rem = mod_pos(c0 + stage_chunk(p, 0), cpg);
       compute_range(p, U0{}, UH{}, row, rem);
       stage_next(p + 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -843,7 +851,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       wave_fence();
       load_w(p + 1, S0{}, UH{}, UE{});
     }
-    int row = 0, rem = (c0 + stage_chunk(p, 0)) % cpg;
+    int row = 0, rem = mod_pos(c0 + stage_chunk(p, 0), cpg);
     compute_range(p, U0{}, UE{}, row, rem);
   }
   if constexpr (!PER_ELEM && FOLD > 1) fold_prev_block();

@@ -261,21 +261,29 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   // zero when it is stored) and keep raw words, so they issue as one burst.
   half8_t xr[XP];
   const int xpieces = sc * M * 4;
-  auto x_piece = [&](int p, int i, int& m, int& cl, int& kbe) __attribute__((always_inline)) {
-    const int e = st + i * sn;
-    kbe = e & 3;
-    const int rest = e >> 2;
-    m = rest % M;
-    cl = rest / M;
-    return e < xpieces && stage_chunk(p, cl) < C;
+  // piece i of this thread: e = st + i sn, kbe = e & 3, rest = e >> 2 = cl M + m
+  // (row m, chunk cl).  rest grows by sn / 4 per piece, so (m, cl) advance by
+  // (dm, dcl) with at most one carry: no integer division per piece
+  const int xr0 = st >> 2, xrd = sn >> 2;
+  const int xcl0 = MV == 1 ? xr0 : xr0 / M, xm0 = xr0 - xcl0 * M;
+  const int xdcl = MV == 1 ? xrd : xrd / M, xdm = xrd - xdcl * M;
+  auto x_next = [&](int& m, int& cl) __attribute__((always_inline)) {
+    m += xdm;
+    cl += xdcl;
+    if (m >= M) {
+      m -= M;
+      ++cl;
+    }
   };
   auto load_x = [&](int p) __attribute__((always_inline)) {
+    int m = xm0, cl = xcl0;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      int m, cl, kbe;
-      const bool ok = x_piece(p, i, m, cl, kbe);
+      const int e = st + i * sn;
+      const bool ok = e < xpieces && stage_chunk(p, cl) < C;
       const int c = ok ? stage_chunk(p, cl) : 0;
-      xr[i] = *reinterpret_cast<const half8_t*>(a.x + (int64_t)(ok ? m : 0) * a.K + 32 * (c0 + c) + 8 * kbe);
+      xr[i] = *reinterpret_cast<const half8_t*>(a.x + (int64_t)(ok ? m : 0) * a.K + 32 * (c0 + c) + 8 * (e & 3));
+      x_next(m, cl);
     }
   };
   i32x4_t gr[PER_ELEM ? GP : 1];
@@ -297,10 +305,12 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
     unsigned char* base = stage_base(p);
     _Float16* frag = reinterpret_cast<_Float16*>(base);
     float* corr = reinterpret_cast<float*>(base + lay.corr_off);
+    int m_next = xm0, cl_next = xcl0;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      int m, cl, kbe;
-      const bool ok = x_piece(p, i, m, cl, kbe);
+      const int m = m_next, cl = cl_next, kbe = (st + i * sn) & 3;
+      x_next(m_next, cl_next);
+      const bool ok = st + i * sn < xpieces && stage_chunk(p, cl) < C;
       if (st + i * sn >= xpieces) continue;          // xpieces % 4 == 0: groups of four stay together
       half8_t av;
       float xs = 0.f;                                // sum of x' MUL over the piece

@@ -8,18 +8,29 @@ M=1, 4-bit g128 symmetric GPTQv1, synthetic seeded weights quantized on the
 GPU by the library's own quantizer, qweight then re-laid out once into the
 tiled layout (gptq_repack_tiled, untimed).  `value` = packed weight bytes
 (qweight + qzeros + scales) per step / step time.  Distinct weight copies
-(>= 1 GB in total) are rotated so the 256 MB Infinity Cache cannot serve them.
-The same step on the checkpoint qweight layout is reported beside it.
+(>= 1 GiB in total) are rotated so the 256 MB Infinity Cache cannot serve them.
+
+Every GEMM call timed here is one of workload.BENCH_CASES, the list the GPU
+parity tests run (tests/test_gpu_bench_parity.py).  Timing: launches are
+captured in HIP graphs (no Python overhead in the timed region) and timed with
+HIP events on the stream the graphs replay on; a per-call figure is the median
+over 5 replays of a graph of >= 50 launches.  The headline step time is one
+replay of a graph of exactly --steps steps, after --warmup eager steps and
+--warm-seconds of untimed replays (MI355X raises its clocks over hundreds of
+milliseconds of load).
 
 The JSON line also carries:
   roofline      the decode kernel: algorithmic bytes per launch (weights + x +
-                y) / its mean launch time (HIP events around replays of a HIP
-                graph of that layer's launches over the rotated copies),
-                against 8 TB/s;
-  prefill       the 70B-MLP M=2048 GEMMs (4-bit g128 sym v1, 8-bit g128 asym
-                v2): TFLOP/s against 2.5 PFLOP/s dense fp16 MFMA;
+                y) / its median launch time, against 8 TB/s, and per layer the
+                time of gptq_read_ceiling (a plain read of the same bytes) as
+                the achievable floor;
+  decode_checkpoint, decode_other, moe, prefill, prefill_checkpoint, bf16:
+                the other benchmarked calls;
   cpu_baseline  the CPU oracle (numpy, fp64) on a bounded column slice of the
-                qkv layer, same unit.
+                qkv layer, same unit, dequant and matmul timed apart;
+  parity        every timed call's output on sampled 32-column blocks against
+                the oracle (run in the same leg as cpu_baseline; a mismatch
+                makes the run exit with status 3).
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 
@@ -31,7 +42,7 @@ The summary goes to profiles/; `roofline.traffic` is read from it while the
 decode sources still hash to the value recorded there (null otherwise).
 
 Counter pass (MFMA utilisation of the prefill kernel, see `--pmc-prefill-driver`):
-  rocprofv3 --pmc MfmaUtil GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA --kernel-trace -d D/mfma -o run -f csv \
+  rocprofv3 --pmc MfmaUtil GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA --kernel-trace -d D/mfma -o run -f csv \\
       -- python3 bench.py --pmc-prefill-driver
   python3 bench.py --summarize-prefill-pmc D/mfma/run_counter_collection.csv D/mfma/run_kernel_trace.csv
 """
@@ -42,6 +53,7 @@ import csv
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -55,11 +67,17 @@ MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_mlp70b_mfma_util.txt")
 # sources that decide the decode kernel's code and launch shapes
 DECODE_SOURCES = ["weight_only_bit_gptq_amd/csrc/decode.hip", "weight_only_bit_gptq_amd/csrc/gptq_device.hpp",
                   "weight_only_bit_gptq_amd/csrc/gptq_kernels.hpp", "weight_only_bit_gptq_amd/csrc/gptq_api.cpp"]
+ALL_SOURCES = DECODE_SOURCES + ["weight_only_bit_gptq_amd/csrc/prefill.hip", "weight_only_bit_gptq_amd/csrc/dequant.hip",
+                                "weight_only_bit_gptq_amd/csrc/quantize.hip", "weight_only_bit_gptq_amd/csrc/ceiling.hip",
+                                "bench.py"]
 PMC_COPY_BYTES = 256 << 20      # plain copy of known size that calibrates FETCH_SIZE / WRITE_SIZE
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 (and bf16) MFMA
 ROTATE_BYTES = 1 << 30          # rotate >= 1 GiB of distinct weight copies
+MIN_LAUNCHES = 50               # launches per timed graph replay
+REPS = 5                        # timed replays per figure (median reported)
+TOL = 5e-3                      # GEMM parity bar: max|y - y_ref| <= TOL * rms(y_ref)
 
 
 def parse():
@@ -67,20 +85,21 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--prefill-steps", type=int, default=10)
+    p.add_argument("--prefill-steps", type=int, default=10, help="launches per timed prefill repetition")
     p.add_argument("--warm-seconds", type=float, default=0.5,
                    help="untimed GPU work before each timed region (MI355X raises its clocks over "
                         "hundreds of milliseconds of load; measured without it, prefill reads ~15%% low)")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-checkpoint-layout", action="store_true",
-                   help="skip the decode step on the checkpoint qweight layout (reported beside the tiled one)")
-    p.add_argument("--no-cpu-baseline", action="store_true")
+                   help="skip the calls on the checkpoint qweight layout (reported beside the tiled ones)")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle leg (cpu_baseline and the parity check of the timed outputs)")
     p.add_argument("--no-bf16", action="store_true",
                    help="skip the bfloat16-activation lines (decode layers and 4-bit prefill)")
+    p.add_argument("--no-other", action="store_true", help="skip decode_other and moe")
     p.add_argument("--cpu-sample-cols", type=int, default=12288,
                    help="columns of the qkv layer the CPU oracle processes (default: all)")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="repeat the oracle on the sample until this much CPU time has passed")
+    p.add_argument("--cpu-reps", type=int, default=3, help="oracle calls on the sample (median reported)")
     p.add_argument("--pmc-driver", action="store_true",
                    help="only launch each decode layer 3 times and a plain copy, for a rocprofv3 --pmc pass")
     p.add_argument("--pmc-prefill-driver", action="store_true",
@@ -92,12 +111,25 @@ def parse():
     return p.parse_args()
 
 
-def decode_sources_hash():
+def sources_hash(paths):
     h = hashlib.sha256()
-    for rel in DECODE_SOURCES:
+    for rel in paths:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def decode_sources_hash():
+    return sources_hash(DECODE_SOURCES)
+
+
+def git_head():
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], stdout=subprocess.PIPE,
+                           stderr=subprocess.DEVNULL, text=True, timeout=10)
+        return r.stdout.strip() or None
+    except Exception:
+        return None
 
 
 def read_traffic():
@@ -117,235 +149,224 @@ def layer_bytes(K, N, bits, gs):
     return K * bits // 8 * N + G * N * bits // 8 + G * N * 2   # qweight + qzeros + scales
 
 
-def make_layer(torch, gq, wl, layer, M, dev, tiled=False):
-    from workload import draw_workload_layer
-    d = draw_workload_layer(wl, layer, M, seed=0)
-    w = torch.from_numpy(d.W).to(dev)
-    gi = None if d.g_idx is None else torch.from_numpy(d.g_idx).to(dev)
-    qw, qz, sc = gq.quantize(w, gi, wl.bits, wl.group_size, wl.sym, wl.is_v2)
-    del w
-    if tiled:                      # one-time re-layout at load (not timed)
-        qw = gq.repack_tiled(qw, wl.bits)
-    x = torch.from_numpy(d.x).to(dev)
-    return dict(qweight=qw, qzeros=qz, scales=sc, g_idx=gi, x=x, K=layer.K, N=layer.N)
-
-
-def to_bf16(torch, L):
-    """The same layer with bfloat16 activations: x and scales rounded to bfloat16."""
-    return {**L, "x": L["x"].to(torch.bfloat16), "scales": L["scales"].to(torch.bfloat16)}
-
-
-def bench_decode(torch, gq, args, dev, tiled, bf16=False):
-    """Decode step timing.  Launches are captured in HIP graphs so the Python
-    binding's per-call overhead stays out of the timed region: one graph holds
-    R steps (R rotated weight copies x 4 layers); per-layer graphs hold R launches
-    of one layer and give the kernel's mean launch time.  `tiled`: qweight in
-    the tiled layout (repacked once at load), else the checkpoint layout.
-    `bf16`: bfloat16 activations and scales (gptq_gemm_bf16)."""
+def wl_layer(case):
     from workload import WORKLOADS
-    wl = WORKLOADS["llama7b_decode_w4g128"]
-    base = [make_layer(torch, gq, wl, l, 1, dev, tiled) for l in wl.layers]
-    if bf16:
-        base = [to_bf16(torch, L) for L in base]
-    adt = torch.bfloat16 if bf16 else torch.float16
-    wbytes = sum(layer_bytes(L["K"], L["N"], wl.bits, wl.group_size) for L in base)
-    copies = max(1, -(-ROTATE_BYTES // wbytes))
-    sets = [base] + [[{**L, "qweight": L["qweight"].clone(), "qzeros": L["qzeros"].clone(),
-                       "scales": L["scales"].clone()} for L in base] for _ in range(copies - 1)]
-    outs = [torch.empty((1, L["N"]), dtype=adt, device=dev) for L in base]
+    wl = WORKLOADS[case.workload]
+    return wl, next(l for l in wl.layers if l.name == case.layer)
 
-    def launch(r, j):
-        L = sets[r][j]
-        gq.gemm(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits, wl.group_size, wl.is_v2,
-                out=outs[j])
 
+def check_cols(N):
+    """Output columns the oracle checks: three 32-column blocks (first, middle,
+    last), so the oracle can quantize just those columns (columns are
+    quantized independently; qzeros packs 32 columns per 32*b/32 words)."""
+    mid = (N // 2) // 32 * 32
+    return np.unique(np.concatenate([np.arange(0, 32), np.arange(mid, mid + 32), np.arange(N - 32, N)]))
+
+
+# ---------------------------------------------------------------- timing helpers
+def warm(torch, fn, seconds):
+    """Untimed calls of fn until `seconds` have passed (clocks settle)."""
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+
+
+def median_replay_ms(torch, graph, reps=REPS):
+    """Median over `reps` replays of a graph, each bracketed by HIP events on
+    the stream the replay runs on (torch's current stream)."""
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e0.record(st)
+        graph.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts)), ts
+
+
+def capture(torch, dev, launches):
+    """A HIP graph of the given launch closures (captured on a side stream
+    after one eager pass that also allocates any library workspace)."""
     side = torch.cuda.Stream(dev)
     side.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(side):
-        for i in range(max(args.warmup, 1)):          # also allocates the split-K workspace of `side`
-            for j in range(len(base)):
-                launch(i % copies, j)
+        for f in launches:
+            f()
     torch.cuda.synchronize()
-
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all, stream=side):
-        for r in range(copies):
-            for j in range(len(base)):
-                launch(r, j)
-    g_layer = []
-    for j in range(len(base)):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            for r in range(copies):
-                launch(r, j)
-        g_layer.append(g)
-
-    def timed(graph, reps):
-        graph.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        st = torch.cuda.current_stream(dev)
-        e0.record(st)
-        for _ in range(reps):
-            graph.replay()
-        e1.record(st)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
-
-    def warm(graph):
-        # untimed replays until the clocks have settled (see --warm-seconds)
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < args.warm_seconds:
-            for _ in range(20):
-                graph.replay()
-            torch.cuda.synchronize()
-
-    replays = max(1, -(-args.steps // copies))
-    steps = replays * copies
-    warm(g_all)
-    ms_per_step = timed(g_all, replays) / steps
-    per_layer_ms = [timed(g, replays) / steps for g in g_layer]
-
-    alg = [layer_bytes(L["K"], L["N"], wl.bits, wl.group_size) + 2 * L["K"] + 2 * L["N"] for L in base]
-    mean_launch_ms = float(np.mean(per_layer_ms))
-    achieved = (sum(alg) / len(alg)) / (mean_launch_ms * 1e-3) / 1e9
-    kernels = [gq.describe(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits, wl.group_size, wl.is_v2,
-                           out=o) for L, o in zip(base, outs)]
-    layers = [{"layer": l.name, "K": l.K, "N": l.N, "kernel": kn, "alg_bytes": a, "us": round(t * 1e3, 2),
-               "GBps": round(a / (t * 1e-3) / 1e9, 1)}
-              for l, kn, a, t in zip(wl.layers, kernels, alg, per_layer_ms)]
-    del g_all, g_layer
-    return dict(wl=wl, wbytes=wbytes, copies=copies, ms_per_step=ms_per_step, achieved=achieved, steps=steps,
-                mean_launch_us=mean_launch_ms * 1e3, layers=layers, base=base)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for f in launches:
+            f()
+    torch.cuda.synchronize()
+    return g
 
 
-def bench_prefill(torch, gq, args, dev, bf16=False):
-    """Prefill GEMM timing per layer (plus, for the 4-bit workload, the vendor
-    dense GEMM in the same activation type on the same shape, as context).
-    fp16: qweight in the tiled layout, the same re-laid-out copy the decode
-    step reads (4-bit tiled words hold their fields in pair order, which the
-    prefill kernel unpacks with fewer instructions).  `bf16`: bfloat16
-    activations and scales, 4-bit workload only, checkpoint layout (the only
-    one bfloat16 reads)."""
-    from workload import WORKLOADS
+# ---------------------------------------------------------------- one benchmarked call
+def prepare(torch, gq, case, dev):
+    """The call's inputs on the GPU: seeded draw, quantized by the library's
+    quantizer, tiled / sorted at load as the case says, bf16 x and scales for
+    bf16 cases.  Returns a dict with a `call(qweight, out)` closure."""
+    from workload import draw_workload_layer
+    wl, layer = wl_layer(case)
+    d = draw_workload_layer(wl, layer, max(wl.Ms), seed=0)
+    w = torch.from_numpy(d.W).to(dev)
+    gi = None if d.g_idx is None else torch.from_numpy(d.g_idx).to(dev)
+    qw, qz, sc = gq.quantize(w, gi, wl.bits, wl.group_size, wl.sym, wl.is_v2)
+    del w, d.W
+    perm = None
+    if case.entry == "gemm_sorted":
+        qw, perm = gq.sort_act_order(qw, gi, wl.bits, wl.group_size)
+    if case.layout == "tiled":
+        qw = gq.repack_tiled(qw, wl.bits)
+    x = torch.from_numpy(d.x[:case.M]).to(dev)
+    if case.act == "bf16":
+        x, sc = x.to(torch.bfloat16), sc.to(torch.bfloat16)
+    gi_call = None if case.entry == "gemm_sorted" else gi
+
+    def call(qweight, out):
+        if perm is not None:
+            gq.gemm_sorted(x, qweight, qz, sc, perm, wl.bits, wl.group_size, wl.is_v2, out=out)
+        else:
+            gq.gemm(x, qweight, qz, sc, gi_call, wl.bits, wl.group_size, wl.is_v2, out=out)
+
+    desc = gq.describe(x, qw, qz, sc, gi_call, wl.bits, wl.group_size, wl.is_v2)
+    if perm is not None:
+        desc = "x gathered by perm, then " + desc
+    wb = layer_bytes(layer.K, layer.N, wl.bits, wl.group_size) + (4 * layer.K if gi_call is not None else 0)
+    alg = wb + 2 * case.M * layer.K + 2 * case.M * layer.N
+    return dict(case=case, wl=wl, layer=layer, qweight=qw, x=x, call=call, desc=desc, wbytes=wb, alg=alg,
+                act=torch.bfloat16 if case.act == "bf16" else torch.float16)
+
+
+def rotated_copies(torch, P, nbytes_per_set):
+    """[qweight, clone, ...]: enough distinct copies that together they exceed
+    ROTATE_BYTES (each call then reads weights no cache holds)."""
+    copies = max(2, -(-ROTATE_BYTES // nbytes_per_set))
+    return [P["qweight"]] + [P["qweight"].clone() for _ in range(copies - 1)]
+
+
+def time_decode_call(torch, P, dev, args, sets=None):
+    """Median launch time (us) of one decode call over rotated weight copies;
+    also returns the output of a launch on the first copy."""
+    sets = sets or rotated_copies(torch, P, P["wbytes"])
+    out = torch.empty((P["case"].M, P["layer"].N), dtype=P["act"], device=dev)
+    n = max(MIN_LAUNCHES, len(sets))
+    g = capture(torch, dev, [lambda i=i: P["call"](sets[i % len(sets)], out) for i in range(n)])
+    warm(torch, g.replay, args.warm_seconds / 4)
+    ms, ts = median_replay_ms(torch, g)
+    del g
+    P["call"](sets[0], out)
+    torch.cuda.synchronize()
+    return ms * 1e3 / n, [round(t * 1e3 / n, 3) for t in ts], out
+
+
+def time_read_ceiling(torch, gq, nbytes, dev, args):
+    """Median time (us) of gptq_read_ceiling over `nbytes` (rounded up to 16),
+    rotated over distinct buffers like the decode weights."""
+    nb = (nbytes + 4095) // 4096 * 4096
+    copies = max(2, -(-ROTATE_BYTES // nb))
+    buf = torch.ones(copies * nb // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    n = max(MIN_LAUNCHES, copies)
+    g = capture(torch, dev, [lambda i=i: gq.read_ceiling(buf[(i % copies) * nb // 4:((i % copies) + 1) * nb // 4],
+                                                         (nbytes + 15) // 16 * 16, sink=sink) for i in range(n)])
+    warm(torch, g.replay, args.warm_seconds / 4)
+    ms, _ = median_replay_ms(torch, g)
+    del g, buf
+    return ms * 1e3 / n
+
+
+# ---------------------------------------------------------------- decode step (headline)
+def bench_decode_step(torch, gq, args, dev, group, outputs):
+    """The four Llama-7B layers as a decode step: per-layer median launch
+    times, the step time (one replay of exactly --steps steps) and the read
+    ceiling of each layer's bytes."""
+    from workload import bench_cases
+    cases = bench_cases(group)
+    Ps = [prepare(torch, gq, c, dev) for c in cases]
+    step_bytes = sum(P["wbytes"] for P in Ps)
+    copies = max(2, -(-ROTATE_BYTES // step_bytes))
+    sets = [[P["qweight"]] + [P["qweight"].clone() for _ in range(copies - 1)] for P in Ps]
+    outs = [torch.empty((P["case"].M, P["layer"].N), dtype=P["act"], device=dev) for P in Ps]
+
+    def step(i):
+        for j, P in enumerate(Ps):
+            P["call"](sets[j][i % copies], outs[j])
+
+    for i in range(args.warmup):                        # untimed warm-up steps
+        step(i)
+    torch.cuda.synchronize()
+    g_step = capture(torch, dev, [lambda i=i: step(i) for i in range(args.steps)])
+    layers = []
+    for j, P in enumerate(Ps):
+        us, reps, out = time_decode_call(torch, P, dev, args, sets=sets[j])
+        outputs[P["case"].key] = out[:, torch.from_numpy(check_cols(P["layer"].N)).to(dev)].float().cpu().numpy()
+        layers.append(dict(layer=P["layer"].name, K=P["layer"].K, N=P["layer"].N, kernel=P["desc"],
+                           alg_bytes=P["alg"], us=round(us, 3), reps_us=reps,
+                           GBps=round(P["alg"] / (us * 1e-6) / 1e9, 1)))
+    warm(torch, g_step.replay, args.warm_seconds)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_step.replay()                                     # exactly args.steps steps
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    del g_step
+    mean_us = float(np.mean([l["us"] for l in layers]))
+    mean_alg = float(np.mean([l["alg_bytes"] for l in layers]))
+    return dict(wl=Ps[0]["wl"], wbytes=step_bytes, copies=copies, ms_per_step=ms_per_step, layers=layers,
+                mean_launch_us=mean_us, achieved=mean_alg / (mean_us * 1e-6) / 1e9,
+                value=step_bytes / (ms_per_step * 1e-3) / 1e9)
+
+
+def add_ceilings(torch, gq, args, dev, layers, bits, gs):
+    for l in layers:
+        wb = layer_bytes(l["K"], l["N"], bits, gs)
+        c = time_read_ceiling(torch, gq, wb, dev, args)
+        l["read_ceiling_us"] = round(c, 3)
+        l["of_ceiling"] = round(c / l["us"], 4)
+
+
+# ---------------------------------------------------------------- the other decode calls
+def bench_decode_other(torch, gq, args, dev, outputs, skip_checkpoint):
+    """2-bit g64 (M = 1, 4, 16; tiled), 3-bit act-order M = 16 (rows sorted at
+    load, tiled; and the unsorted layer through gptq_gemm with g_idx on the
+    checkpoint layout): per-call median launch time and the read ceiling of
+    the call's weight bytes."""
+    from workload import bench_cases
     res = []
-    adt = torch.bfloat16 if bf16 else torch.float16
-    names = ("mlp70b_prefill_w4g128",) if bf16 else ("mlp70b_prefill_w4g128", "mlp70b_prefill_w8g128")
-    for name in names:
-        wl = WORKLOADS[name]
-        for layer in wl.layers:
-            L = make_layer(torch, gq, wl, layer, 2048, dev, tiled=not bf16)
-            if bf16:
-                L = to_bf16(torch, L)
-            out = torch.empty((2048, layer.N), dtype=adt, device=dev)
-            run = lambda: gq.gemm(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits,
-                                  wl.group_size, wl.is_v2, out=out)
-            t0 = time.perf_counter()
-            while True:                       # untimed warm-up (see --warm-seconds)
-                for _ in range(5):
-                    run()
-                torch.cuda.synchronize()
-                if time.perf_counter() - t0 >= args.warm_seconds:
-                    break
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(args.prefill_steps):
-                run()
-            b.record()
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / args.prefill_steps
-            flops = 2.0 * 2048 * layer.K * layer.N
-            tf = flops / (ms * 1e-3) / 1e12
-            row = {"workload": name, "layer": layer.name, "M": 2048, "K": layer.K, "N": layer.N,
-                   "bits": wl.bits, "qweight_layout": "checkpoint" if bf16 else "tiled", "ms": round(ms, 4),
-                   "TFLOPs": round(tf, 1), "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
-            if name == "mlp70b_prefill_w4g128":
-                # context: the vendor dense GEMM (torch.matmul) on the same shape, unquantized W
-                W = torch.randn((layer.K, layer.N), dtype=adt, device=dev)
-                t0 = time.perf_counter()
-                while time.perf_counter() - t0 < args.warm_seconds:
-                    for _ in range(5):
-                        torch.matmul(L["x"], W, out=out)
-                    torch.cuda.synchronize()
-                a.record()
-                for _ in range(args.prefill_steps):
-                    torch.matmul(L["x"], W, out=out)
-                b.record()
-                torch.cuda.synchronize()
-                key = "dense_bf16_matmul_TFLOPs" if bf16 else "dense_fp16_matmul_TFLOPs"
-                row[key] = round(flops / (a.elapsed_time(b) / args.prefill_steps * 1e-3) / 1e12, 1)
-                del W
-            res.append(row)
-            del L, out
+    ceilings = {}
+    cur = None
+    sets = None
+    for case in bench_cases("decode_other"):
+        if skip_checkpoint and case.layout == "checkpoint":
+            continue
+        P = prepare(torch, gq, case, dev)
+        key = (case.workload, case.layer, case.layout, case.entry)
+        if key != cur:
+            sets, cur = None, key
             torch.cuda.empty_cache()
-    return res
-
-
-def bench_decode_configs(torch, gq, args, dev):
-    """The other decode workloads (2-bit g64 asym v2 with outliers at M = 1, 4,
-    16; 3-bit g128 act-order at M = 16, rows sorted by group once at load and
-    x gathered per call), tiled layout: per-layer launch time
-    from a graph of launches over rotated weight copies, and algorithmic
-    bytes (weights + g_idx + x + y) per launch against 8 TB/s."""
-    from workload import WORKLOADS
-    res = []
-    for name in ("lowbit_decode_w2g64", "actorder_decode_w3g128"):
-        wl = WORKLOADS[name]
-        for layer in wl.layers:
-            L = make_layer(torch, gq, wl, layer, max(wl.Ms), dev, tiled=not wl.act_order)
-            perm = None
-            if wl.act_order:               # rows sorted by group once at load, x gathered per call
-                qs, perm = gq.sort_act_order(L["qweight"], L["g_idx"], wl.bits, wl.group_size)
-                L["qweight"] = gq.repack_tiled(qs, wl.bits)
-                del qs
-            wb = layer_bytes(layer.K, layer.N, wl.bits, wl.group_size) + (4 * layer.K if wl.act_order else 0)
-            copies = max(2, -(-ROTATE_BYTES // wb))
-            sets = [L["qweight"]] + [L["qweight"].clone() for _ in range(copies - 1)]
-            for M in wl.Ms:
-                x = L["x"][:M].contiguous()
-                out = torch.empty((M, layer.N), dtype=torch.float16, device=dev)
-                if perm is None:
-                    run = lambda qw: gq.gemm(x, qw, L["qzeros"], L["scales"], None, wl.bits, wl.group_size,
-                                             wl.is_v2, out=out)
-                else:
-                    run = lambda qw: gq.gemm_sorted(x, qw, L["qzeros"], L["scales"], perm, wl.bits, wl.group_size,
-                                                    wl.is_v2, out=out)
-                side = torch.cuda.Stream(dev)
-                side.wait_stream(torch.cuda.current_stream(dev))
-                with torch.cuda.stream(side):
-                    for qw in sets:
-                        run(qw)
-                torch.cuda.synchronize()
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    for qw in sets:
-                        run(qw)
-                t0 = time.perf_counter()
-                while time.perf_counter() - t0 < args.warm_seconds / 4:
-                    for _ in range(10):
-                        g.replay()
-                    torch.cuda.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                reps = 20
-                e0.record()
-                for _ in range(reps):
-                    g.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-                alg = wb + 2 * M * layer.K + 2 * M * layer.N
-                res.append({"workload": name, "layer": f"{layer.name} {layer.K}->{layer.N}", "M": M,
-                            "kernel": ("x gathered by perm, then " if perm is not None else "") +
-                                      gq.describe(x, sets[0], L["qzeros"], L["scales"], None, wl.bits,
-                                                  wl.group_size, wl.is_v2, out=out),
-                            "us": round(us, 2), "GBps": round(alg / (us * 1e-6) / 1e9, 1),
-                            "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
-                del g
-            del L, sets
-            torch.cuda.empty_cache()
+        sets = sets or rotated_copies(torch, P, P["wbytes"])
+        us, reps, out = time_decode_call(torch, P, dev, args, sets=sets)
+        outputs[case.key] = out[:, torch.from_numpy(check_cols(P["layer"].N)).to(dev)].float().cpu().numpy()
+        ck = (P["layer"].K, P["layer"].N, P["wl"].bits, P["wl"].group_size)
+        if ck not in ceilings:
+            ceilings[ck] = time_read_ceiling(torch, gq, layer_bytes(*ck), dev, args)
+        res.append({"workload": case.workload, "layer": f"{case.layer} {P['layer'].K}->{P['layer'].N}", "M": case.M,
+                    "layout": case.layout, "entry": case.entry, "kernel": P["desc"], "us": round(us, 3),
+                    "reps_us": reps, "GBps": round(P["alg"] / (us * 1e-6) / 1e9, 1),
+                    "frac": round(P["alg"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "read_ceiling_us": round(ceilings[ck], 3), "of_ceiling": round(ceilings[ck] / us, 4)})
+        del P
     return res
 
 
@@ -376,60 +397,78 @@ def bench_moe(torch, gq, args, dev):
     copies = max(2, -(-ROTATE_BYTES // (E * layer_bytes(K, N, bits, gs))))
     sets = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
     mt = int(counts.max())
-    run = lambda st: gq.moe_gemm(x, st[0], st[1], st[2], None, offsets, mt, bits, gs, False, out=out)
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(torch.cuda.current_stream(dev))
-    with torch.cuda.stream(side):
-        for st in sets:
-            run(st)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=side):
-        for st in sets:
-            run(st)
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < args.warm_seconds:     # untimed warm-up
-        for _ in range(10):
-            g.replay()
-        torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    reps = 20
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    n = max(MIN_LAUNCHES, copies)
+    g = capture(torch, dev, [lambda i=i: gq.moe_gemm(x, *sets[i % copies], None, offsets, mt, bits, gs, False, out=out)
+                             for i in range(n)])
+    warm(torch, g.replay, args.warm_seconds)
+    ms, _ = median_replay_ms(torch, g)
+    us = ms * 1e3 / n
     del g, sets, base
     torch.cuda.empty_cache()
+    ceil_us = time_read_ceiling(torch, gq, wbytes, dev, args)
     return {"workload": "mixtral_expert_w1_w4g128", "experts": E, "K": K, "N": N, "tokens": 16, "top_k": 2,
             "active_experts": active, "us": round(us, 2), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
-            "frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+            "frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4), "read_ceiling_us": round(ceil_us, 2),
+            "of_ceiling": round(ceil_us / us, 4)}
 
 
-def copy_ceiling(torch, dev):
-    """Plain device copy of 1 GiB: read + write GB/s (context for the HBM roofline)."""
-    a = torch.empty(1 << 29, dtype=torch.float16, device=dev)
-    b = torch.empty_like(a)
-    a.fill_(1.0)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 10
-    return 2 * a.numel() * 2 / (ms * 1e-3) / 1e9
+# ---------------------------------------------------------------- prefill
+def bench_prefill(torch, gq, args, dev, group, outputs):
+    """Prefill GEMM (M = 2048) timing per call: median over 5 repetitions of
+    --prefill-steps launches each; for the fp16 4-bit tiled calls the vendor
+    dense GEMM in the same activation type on the same shape, as context."""
+    from workload import bench_cases
+    res = []
+    for case in bench_cases(group):
+        P = prepare(torch, gq, case, dev)
+        layer, wl = P["layer"], P["wl"]
+        out = torch.empty((case.M, layer.N), dtype=P["act"], device=dev)
+        run = lambda: P["call"](P["qweight"], out)
+        warm(torch, run, args.warm_seconds)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(REPS):
+            e0.record()
+            for _ in range(args.prefill_steps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / args.prefill_steps)
+        ms = float(np.median(ts))
+        outputs[case.key] = out[:, torch.from_numpy(check_cols(layer.N)).to(dev)].float().cpu().numpy()
+        flops = 2.0 * case.M * layer.K * layer.N
+        tf = flops / (ms * 1e-3) / 1e12
+        row = {"workload": case.workload, "layer": layer.name, "M": case.M, "K": layer.K, "N": layer.N,
+               "bits": wl.bits, "qweight_layout": case.layout, "kernel": P["desc"], "ms": round(ms, 4),
+               "reps_ms": [round(t, 4) for t in ts], "TFLOPs": round(tf, 1),
+               "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        if wl.bits == 4 and case.layout == "tiled" or case.act == "bf16":
+            W = torch.randn((layer.K, layer.N), dtype=P["act"], device=dev)
+            dense = lambda: torch.matmul(P["x"], W, out=out)
+            warm(torch, dense, args.warm_seconds)
+            dts = []
+            for _ in range(REPS):
+                e0.record()
+                for _ in range(args.prefill_steps):
+                    dense()
+                e1.record()
+                torch.cuda.synchronize()
+                dts.append(e0.elapsed_time(e1) / args.prefill_steps)
+            key = "dense_bf16_matmul_TFLOPs" if case.act == "bf16" else "dense_fp16_matmul_TFLOPs"
+            row[key] = round(flops / (float(np.median(dts)) * 1e-3) / 1e12, 1)
+            del W
+        res.append(row)
+        del P, out
+        torch.cuda.empty_cache()
+    return res
 
 
+# ---------------------------------------------------------------- oracle leg
 def cpu_baseline(args):
-    """The oracle (dequant from packed arrays + fp64 matmul) on a column slice of
-    the qkv layer; inputs quantized by the oracle itself from the same draw."""
+    """The oracle (dequant from packed arrays + fp64 matmul) on a column slice
+    of the qkv layer, quantized by the oracle itself from the same draw;
+    median of --cpu-reps calls, dequant and matmul timed apart."""
     import oracle
     from workload import WORKLOADS, draw_workload_layer
     wl = WORKLOADS["llama7b_decode_w4g128"]
@@ -438,45 +477,90 @@ def cpu_baseline(args):
     ncols = min(args.cpu_sample_cols, layer.N)
     W = np.ascontiguousarray(d.W[:, :ncols])
     L = oracle.quantize_layer(W, wl.bits, wl.group_size, wl.sym, wl.is_v2)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, wl.bits, wl.group_size, wl.is_v2,
-                             layer.K, ncols)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or reps >= 200:
-            break
-    sec = el / reps
+    t_dq, t_mm = [], []
+    for _ in range(max(1, args.cpu_reps)):
+        t0 = time.perf_counter()
+        Wh = oracle.dequant_ref(L.qweight, L.qzeros, L.scales, None, wl.bits, wl.group_size, wl.is_v2,
+                                layer.K, ncols)
+        t1 = time.perf_counter()
+        oracle.gemm_ref(d.x, Wh)
+        t2 = time.perf_counter()
+        t_dq.append(t1 - t0)
+        t_mm.append(t2 - t1)
+    sec = float(np.median(np.array(t_dq) + np.array(t_mm)))
     gbps = layer_bytes(layer.K, ncols, wl.bits, wl.group_size) / sec / 1e9
-    threads = 1
+    blas = 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+        blas = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
     except Exception:
         pass
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"qkv layer K={layer.K}, first {ncols} of {layer.N} columns, M=1; "
-                      f"{reps} run(s), {sec:.2f} s each (numpy fp64 dequant + matmul; elementwise ops "
-                      f"single-threaded, BLAS up to {threads} threads)"}
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": blas, "kind": "oracle",
+            "cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas_threads": blas,
+            "dequant_s": round(float(np.median(t_dq)), 3), "matmul_s": round(float(np.median(t_mm)), 3),
+            "sample": f"qkv layer K={layer.K}, first {ncols} of {layer.N} columns, M=1; median of "
+                      f"{len(t_dq)} oracle calls of {sec:.2f} s (numpy fp64 dequant, single-threaded: "
+                      f"{np.median(t_dq):.2f} s; fp64 matmul through BLAS on up to {blas} threads: "
+                      f"{np.median(t_mm):.3f} s)"}
 
 
+def parity_check(outputs):
+    """Every timed call's output on its check columns against the oracle: the
+    oracle quantizes only those columns of the same seeded draw (columns are
+    independent) and runs its dequant + matmul."""
+    import oracle
+    import torch
+    from workload import BENCH_CASES, draw_workload_layer
+    draws = {}
+    res = []
+    for case in BENCH_CASES:
+        if case.key not in outputs:
+            continue
+        wl, layer = wl_layer(case)
+        cols = check_cols(layer.N)
+        # the draw depends on the shape and the recipe's random parts only (the
+        # 4- and 8-bit 70B-MLP workloads share it)
+        dk = (layer.K, layer.N, max(wl.Ms), wl.sigma, wl.outlier_rate, wl.outlier_mult, wl.act_order,
+              wl.group_size if wl.act_order else 0)
+        if dk not in draws:
+            d = draw_workload_layer(wl, layer, max(wl.Ms), seed=0)
+            draws[dk] = (np.ascontiguousarray(d.W[:, cols]), d.x, d.g_idx)
+            del d
+        Wc, x, g_idx = draws[dk]
+        L = oracle.quantize_layer(Wc, wl.bits, wl.group_size, wl.sym, wl.is_v2, g_idx)
+        xm, sc = x[:case.M], L.scales
+        if case.act == "bf16":
+            bf = lambda a: torch.from_numpy(np.ascontiguousarray(a.astype(np.float32))).to(torch.bfloat16).to(
+                torch.float64).numpy()
+            xm, sc = bf(xm), bf(sc)
+        ref = oracle.gptq_gemm_ref(xm, L.qweight, L.qzeros, sc, L.g_idx, wl.bits, wl.group_size, wl.is_v2,
+                                   layer.K, len(cols), act=case.act)
+        y = outputs[case.key].astype(np.float64)
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        bound = TOL * rms + (2.0 ** -8 * np.abs(ref) if case.act == "bf16" else 0.0)
+        err = np.abs(y - ref)
+        ok = bool(np.isfinite(y).all() and (err <= bound).all())
+        res.append({"case": case.key, "cols": int(len(cols)), "max_err_over_rms": round(float(err.max()) / rms, 6),
+                    "ok": ok})
+    return res
+
+
+# ---------------------------------------------------------------- counter drivers / summaries
 def pmc_driver(torch, gq, dev):
     """Each decode layer 3 times (distinct weight copies, so no launch finds its
     weights in L2), then a plain copy of PMC_COPY_BYTES; no timing."""
-    from workload import WORKLOADS
-    wl = WORKLOADS["llama7b_decode_w4g128"]
-    for layer in wl.layers:
-        L = make_layer(torch, gq, wl, layer, 1, dev, tiled=True)
-        out = torch.empty((1, layer.N), dtype=torch.float16, device=dev)
-        copies = [(L["qweight"].clone(), L["qzeros"].clone(), L["scales"].clone()) for _ in range(3)]
+    from workload import bench_cases
+    for case in bench_cases("decode"):
+        P = prepare(torch, gq, case, dev)
+        out = torch.empty((1, P["layer"].N), dtype=torch.float16, device=dev)
+        copies = [P["qweight"].clone() for _ in range(3)]
         torch.cuda.synchronize()
-        for qw, qz, sc in copies:
-            gq.gemm(L["x"], qw, qz, sc, None, wl.bits, wl.group_size, wl.is_v2, out=out)
+        for qw in copies:
+            P["call"](qw, out)
         torch.cuda.synchronize()
-        print(f"{layer.name}: {gq.describe(L['x'], qw, qz, sc, None, wl.bits, wl.group_size, wl.is_v2, out=out)}",
-              flush=True)
-        del L, copies
+        print(f"{case.layer}: {P['desc']}", flush=True)
+        del P, copies
     a = torch.ones(PMC_COPY_BYTES // 2, dtype=torch.float16, device=dev)
     b = torch.empty_like(a)
     torch.cuda.synchronize()
@@ -492,21 +576,17 @@ MI355X_XCDS = 8
 
 def pmc_prefill_driver(torch, gq, dev):
     """Each 70B-MLP prefill layer (M = 2048, tiled layout) twice on its own weights; no timing."""
-    from workload import WORKLOADS
-    for name in PREFILL_WORKLOADS:
-        wl = WORKLOADS[name]
-        for layer in wl.layers:
-            L = make_layer(torch, gq, wl, layer, 2048, dev, tiled=True)      # as the bench times it
-            out = torch.empty((2048, layer.N), dtype=torch.float16, device=dev)
-            torch.cuda.synchronize()
-            for _ in range(2):
-                gq.gemm(L["x"], L["qweight"], L["qzeros"], L["scales"], None, wl.bits, wl.group_size, wl.is_v2,
-                        out=out)
-            torch.cuda.synchronize()
-            print(f"{name} {layer.name}: {gq.describe(L['x'], L['qweight'], L['qzeros'], L['scales'], None, wl.bits, wl.group_size, wl.is_v2, out=out)}",
-                  flush=True)
-            del L, out
-            torch.cuda.empty_cache()
+    from workload import bench_cases
+    for case in bench_cases("prefill"):
+        P = prepare(torch, gq, case, dev)
+        out = torch.empty((case.M, P["layer"].N), dtype=torch.float16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            P["call"](P["qweight"], out)
+        torch.cuda.synchronize()
+        print(f"{case.workload} {case.layer}: {P['desc']}", flush=True)
+        del P, out
+        torch.cuda.empty_cache()
     print("pmc prefill driver done", flush=True)
 
 
@@ -625,6 +705,13 @@ def summarize_pmc(fetch_csv, write_csv):
     print("\n".join(lines))
 
 
+# ---------------------------------------------------------------- main
+def decode_summary(d):
+    return {"value": round(d["value"], 1), "ms_per_step": round(d["ms_per_step"], 5), "achieved": round(d["achieved"], 1),
+            "frac": round(d["achieved"] / HBM_PEAK_GBPS, 4), "mean_launch_us": round(d["mean_launch_us"], 3),
+            "per_layer": d["layers"]}
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -636,6 +723,9 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
     import torch
     import weight_only_bit_gptq_amd as gq
@@ -651,43 +741,46 @@ def main():
         pmc_prefill_driver(torch, gq, dev)
         return
 
-    dec = bench_decode(torch, gq, args, dev, tiled=True)
+    outputs = {}
+    dec = bench_decode_step(torch, gq, args, dev, "decode", outputs)
+    wl = dec["wl"]
+    add_ceilings(torch, gq, args, dev, dec["layers"], wl.bits, wl.group_size)
     print(f"# decode (tiled): {dec['ms_per_step'] * 1e3:.2f} us/step, layers: {dec['layers']}", file=sys.stderr,
           flush=True)
-    del dec["base"]
     torch.cuda.empty_cache()
     dec_ck = None
     if not args.no_checkpoint_layout:
-        dec_ck = bench_decode(torch, gq, args, dev, tiled=False)
+        dec_ck = bench_decode_step(torch, gq, args, dev, "decode_checkpoint", outputs)
         print(f"# decode (checkpoint layout): {dec_ck['ms_per_step'] * 1e3:.2f} us/step, layers: {dec_ck['layers']}",
               file=sys.stderr, flush=True)
-        del dec_ck["base"]
-    torch.cuda.empty_cache()
-    dec_other = bench_decode_configs(torch, gq, args, dev)
-    print(f"# other decode configs: {dec_other}", file=sys.stderr, flush=True)
-    moe = bench_moe(torch, gq, args, dev)
-    print(f"# moe: {moe}", file=sys.stderr, flush=True)
-    ceiling = copy_ceiling(torch, dev)
-    prefill = None if args.no_prefill else bench_prefill(torch, gq, args, dev)
-    if prefill:
+        torch.cuda.empty_cache()
+    dec_other = moe = None
+    if not args.no_other:
+        dec_other = bench_decode_other(torch, gq, args, dev, outputs, args.no_checkpoint_layout)
+        print(f"# other decode calls: {dec_other}", file=sys.stderr, flush=True)
+        moe = bench_moe(torch, gq, args, dev)
+        print(f"# moe: {moe}", file=sys.stderr, flush=True)
+    prefill = prefill_ck = None
+    if not args.no_prefill:
+        prefill = bench_prefill(torch, gq, args, dev, "prefill", outputs)
         print(f"# prefill: {prefill}", file=sys.stderr, flush=True)
+        if not args.no_checkpoint_layout:
+            prefill_ck = bench_prefill(torch, gq, args, dev, "prefill_checkpoint", outputs)
+            print(f"# prefill (checkpoint layout): {prefill_ck}", file=sys.stderr, flush=True)
     bf16 = None
     if not args.no_bf16:
         torch.cuda.empty_cache()
-        dec_bf = bench_decode(torch, gq, args, dev, tiled=False, bf16=True)
-        del dec_bf["base"]
-        torch.cuda.empty_cache()
+        dec_bf = bench_decode_step(torch, gq, args, dev, "bf16_decode", outputs)
         bf16 = {"decode": {"workload": dec_bf["wl"].name + " with bf16 x and scales (checkpoint layout)",
-                           "value": round(dec_bf["wbytes"] / (dec_bf["ms_per_step"] * 1e-3) / 1e9, 1),
-                           "ms_per_step": round(dec_bf["ms_per_step"], 5), "achieved": round(dec_bf["achieved"], 1),
-                           "frac": round(dec_bf["achieved"] / HBM_PEAK_GBPS, 4),
-                           "mean_launch_us": round(dec_bf["mean_launch_us"], 3), "per_layer": dec_bf["layers"]},
-                "prefill": None if args.no_prefill else bench_prefill(torch, gq, args, dev, bf16=True)}
+                           **decode_summary(dec_bf)},
+                "prefill": None if args.no_prefill else bench_prefill(torch, gq, args, dev, "bf16_prefill", outputs)}
         print(f"# bf16: {bf16}", file=sys.stderr, flush=True)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args)
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args)
+        parity = parity_check(outputs)
+        print(f"# parity: {parity}", file=sys.stderr, flush=True)
 
-    wl = dec["wl"]
-    value = dec["wbytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
     traffic = read_traffic()
     traffic_bytes = None
     if traffic is not None:
@@ -696,12 +789,13 @@ def main():
             for l in dec["layers"]:
                 l["traffic_bytes"] = by_layer[l["layer"]]["traffic_bytes"]
             traffic_bytes = int(np.mean([l["traffic_bytes"] for l in dec["layers"]]))
+    ceil_sum = sum(l["read_ceiling_us"] for l in dec["layers"])
     line = {
         "metric": "GPTQ W4A16 GEMM: weight GB/s at M=1 and TFLOP/s at M=2048, % of roofline",
-        "value": round(value, 1),
+        "value": round(dec["value"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": dec["steps"],
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 5),
         "higher_is_better": True,
@@ -716,22 +810,30 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes,
                      "kernel": "gptq::decode_kernel, one instantiation per layer (per_layer[].kernel); achieved = "
-                               "mean algorithmic bytes per launch / mean launch time over the 4 layers; traffic = "
-                               "mean HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "mean_launch_us": round(dec["mean_launch_us"], 3), "per_layer": dec["layers"]},
-        "checkpoint_layout": None if dec_ck is None else {
-            "value": round(dec_ck["wbytes"] / (dec_ck["ms_per_step"] * 1e-3) / 1e9, 1),
-            "ms_per_step": round(dec_ck["ms_per_step"], 5), "achieved": round(dec_ck["achieved"], 1),
-            "frac": round(dec_ck["achieved"] / HBM_PEAK_GBPS, 4), "mean_launch_us": round(dec_ck["mean_launch_us"], 3),
-            "per_layer": dec_ck["layers"]},
+                               "mean algorithmic bytes per launch / mean of the per-layer median launch times; "
+                               "traffic = mean HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "mean_launch_us": round(dec["mean_launch_us"], 3),
+                     "read_ceiling_step_us": round(ceil_sum, 3),
+                     "step_of_read_ceiling": round(ceil_sum / (dec["ms_per_step"] * 1e3), 4),
+                     "per_layer": dec["layers"]},
+        "decode_checkpoint": None if dec_ck is None else decode_summary(dec_ck),
         "decode_other": dec_other,
         "moe": moe,
-        "copy_GBps": round(ceiling, 1),
         "prefill": prefill,
+        "prefill_checkpoint": prefill_ck,
         "bf16": bf16,
         "cpu_baseline": cpu,
+        "parity": parity,
+        "context": {"pages_kernel_figure": "page 'GPTQ quantization principles and engineering practice', section "
+                                           "2.2: a per-column-packed GPTQ kernel ran 17% faster than a block-packed "
+                                           "AWQ kernel on an NVIDIA A10 (shapes not given); another machine and "
+                                           "metric, not comparable, so vs_baseline stays null",
+                    "sources_sha16": sources_hash(ALL_SOURCES), "git": git_head()},
     }
     print(json.dumps(line), flush=True)
+    if parity is not None and not all(p["ok"] for p in parity):
+        print("parity check failed: " + ", ".join(p["case"] for p in parity if not p["ok"]), file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

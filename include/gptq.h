@@ -29,17 +29,23 @@
  * returns.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  * stream) and is asynchronous: buffers must stay valid until that work
  * completes, and a device-side fault surfaces at the caller's next
- * synchronisation.  The library's own device memory: a split-K workspace per
- * (device, stream), allocated (hipMalloc, zeroed on the stream) by the first
- * decode call on that stream whose launch splits K, grown when a later call
- * needs more (after synchronising that stream), and freed by gptq_release;
- * gptq_quantize uses a stream-ordered temporary freed on the same stream.
- * Calls on one stream may be captured in a HIP graph: a capture never
- * allocates (a split-K call captured before its stream has a workspace runs
- * unsplit instead), and the graph keeps using the workspace that existed at
- * capture time, so gptq_release must not run while such a graph may replay.
- * Concurrent calls on different streams are safe; two host threads enqueuing
- * on the same stream at once are not.
+ * synchronisation.  The library's own device memory: a workspace per
+ * (device, stream) -- split-K partial sums and arrival counters, and the
+ * gathered x of gptq_gemm_sorted -- allocated (hipMalloc, zeroed on the
+ * stream) by the first call on that stream that needs it, and replaced by a
+ * larger one when a later call needs more; a replaced buffer is not freed
+ * until gptq_release, because work queued earlier and graphs captured earlier
+ * on that stream keep its address.  gptq_quantize uses a stream-ordered
+ * temporary freed on the same stream.
+ * HIP graphs: calls on one stream may be captured.  A capture never allocates
+ * (a split-K call captured before its stream has a workspace runs unsplit
+ * instead; gptq_gemm_sorted returns GPTQ_ERR_NO_MEM), and the graph keeps
+ * using the workspace its capture stream had at capture time.  So a replay
+ * shares that workspace with every other call on the capture stream: replays
+ * (on any stream) must not overlap such calls or each other, and
+ * gptq_release must not run while such a graph may still replay.
+ * Concurrent calls on different streams are otherwise safe; two host threads
+ * enqueuing on the same stream at once are not.
  *
  * Errors: every function returns GPTQ_OK (0) or a negative gptq_status code;
  * nothing is launched when an argument check fails, and no C++ exception
@@ -71,7 +77,7 @@ typedef enum gptq_status {
   GPTQ_ERR_BAD_SHAPE = -3,   /* M < 0, N <= 0, K <= 0, K % 32, N % 32, or a size limit */
   GPTQ_ERR_BAD_GROUP = -4,   /* group_size <= 0 or K % group_size != 0 */
   GPTQ_ERR_MISALIGNED = -5,  /* x, qweight, g_idx, out not 16-byte aligned; scales not 8; qzeros not 4 */
-  GPTQ_ERR_NO_MEM = -6,      /* the quantizer's temporary could not be allocated */
+  GPTQ_ERR_NO_MEM = -6,      /* a temporary or workspace could not be allocated */
   GPTQ_ERR_LAUNCH = -7,      /* a kernel launch failed */
   GPTQ_ERR_DEVICE = -8,      /* no current HIP device or a HIP runtime call failed */
   GPTQ_ERR_BAD_ARG = -9      /* is_v2 / sym / to_v2 not 0 or 1, a gptq_gemm_ex option out of range,
@@ -322,6 +328,20 @@ GPTQ_API int gptq_moe_gemm(const void* x, const int32_t* qweight, const int32_t*
                            const int32_t* g_idx, const int32_t* expert_offsets, int n_experts,
                            int max_tokens_per_expert, int bits, int group_size, int is_v2, int64_t T, int64_t N,
                            int64_t K, void* out, void* stream);
+
+/*
+ * Memory-read reference for the decode kernels: reads `bytes` bytes at buf
+ * (device memory) exactly once with 16-byte nontemporal loads and does
+ * nothing else (decode reads every packed weight once per call, page
+ * "Weight-only INT4 quantization: GPTQ, AWQ and the Marlin kernel", section
+ * 1.1, so a plain read of a layer's weight bytes is the achievable floor of
+ * its decode launch).  bytes is a multiple of 16, at most 2^40; buf is 16-byte
+ * aligned.  sink is a 4-byte aligned device word that the kernel writes only
+ * for contents it never meets in practice (it keeps the loads from being
+ * optimized away); its value is meaningless.  Enqueues one kernel on
+ * `stream`; bytes == 0 launches nothing.
+ */
+GPTQ_API int gptq_read_ceiling(const void* buf, int64_t bytes, void* sink, void* stream);
 
 /* Static text for a gptq_status code ("unknown error" for other values). */
 GPTQ_API const char* gptq_strerror(int code);

@@ -273,6 +273,82 @@ def test_decode_split_k_other_stream_and_graph(dev):
         assert_close(out, y0.float().cpu().numpy().astype(np.float64), "graph replay")
 
 
+
+def test_workspace_growth_keeps_captured_graph(dev):
+    """A graph captured on stream s keeps the workspace s had at capture time.
+    A later eager call on s that needs a larger workspace (a sorted act-order
+    call gathering a big x) replaces it, and the replaced buffer must stay
+    allocated: replays after the growth still match the eager result bit for
+    bit (same kernel, same split order) and the oracle."""
+    bits, gs, M, K, N = 4, 128, 1, 8192, 512
+    d, L = quantized(K, N, M, bits, gs, True, False, False, seed=78)
+    qw, qz, sc, gi = upload(L, dev)
+    x = torch.from_numpy(d.x).to(dev)
+    assert "k_splits=1" not in gq.describe(x, qw, qz, sc, gi, bits, gs, False)
+    cols = np.arange(0, N, 7)
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, False, K, N, cols=cols)
+    # a big act-order layer for the eager call that grows the workspace
+    Kb, Nb, Mb = 4096, 64, 512
+    db, Lb = quantized(Kb, Nb, Mb, bits, gs, False, True, True, seed=79)
+    qwb, qzb, scb, gib = upload(Lb, dev)
+    qsb, permb = gq.sort_act_order(qwb, gib, bits, gs)
+    xb = torch.from_numpy(db.x).to(dev)
+    colsb = np.arange(0, Nb, 5)
+    refb = oracle.gptq_gemm_ref(db.x, Lb.qweight, Lb.qzeros, Lb.scales, Lb.g_idx, bits, gs, True, Kb, Nb, cols=colsb)
+    s = torch.cuda.Stream()
+    out = torch.zeros((M, N), dtype=torch.float16, device=dev)
+    with torch.cuda.stream(s):
+        y_eager = gq.gemm(x, qw, qz, sc, gi, bits, gs, False)       # allocates s's workspace (split K)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gq.gemm(x, qw, qz, sc, gi, bits, gs, False, out=out)
+    with torch.cuda.stream(s):
+        yb = gq.gemm_sorted(xb, qsb, qzb, scb, permb, bits, gs, True)   # Mb * Kb * 2 = 4 MiB: grows it
+    s.synchronize()
+    assert_close(yb[:, torch.from_numpy(colsb).to(dev)], refb, "sorted call that grew the workspace")
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), y_eager.view(torch.int16)), f"replay {rep}"
+        assert_close(out[:, torch.from_numpy(cols).to(dev)], ref, f"replay {rep}")
+
+
+def test_workspace_allocation_failure(dev, monkeypatch):
+    """With workspace allocation failing (the library's GPTQ_TEST_FAIL_WORKSPACE
+    hook), a split-K decode call on a stream without a workspace runs unsplit
+    (documented fallback, same result within tolerance) and a sorted act-order
+    call reports GPTQ_ERR_NO_MEM; once allocation works again both succeed."""
+    bits, gs, M, K, N = 4, 128, 1, 8192, 512
+    d, L = quantized(K, N, M, bits, gs, True, False, False, seed=80)
+    qw, qz, sc, gi = upload(L, dev)
+    x = torch.from_numpy(d.x).to(dev)
+    assert "k_splits=1" not in gq.describe(x, qw, qz, sc, gi, bits, gs, False)
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, False, K, N)
+    da, La = quantized(1024, 64, 4, bits, gs, False, True, True, seed=81)
+    qwa, qza, sca, gia = upload(La, dev)
+    qsa, perma = gq.sort_act_order(qwa, gia, bits, gs)
+    xa = torch.from_numpy(da.x).to(dev)
+    refa = oracle.gptq_gemm_ref(da.x, La.qweight, La.qzeros, La.scales, La.g_idx, bits, gs, True, 1024, 64)
+    s = torch.cuda.Stream()
+    monkeypatch.setenv("GPTQ_TEST_FAIL_WORKSPACE", "1")
+    with torch.cuda.stream(s):
+        y = gq.gemm(x, qw, qz, sc, gi, bits, gs, False)
+        with pytest.raises(gq.GptqError) as err:
+            gq.gemm_sorted(xa, qsa, qza, sca, perma, bits, gs, True)
+    s.synchronize()
+    assert err.value.code == -6
+    assert_close(y, ref, "unsplit fallback")
+    monkeypatch.delenv("GPTQ_TEST_FAIL_WORKSPACE")
+    with torch.cuda.stream(s):
+        y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False)
+        ya = gq.gemm_sorted(xa, qsa, qza, sca, perma, bits, gs, True)
+    s.synchronize()
+    assert_close(y2, ref, "split after the hook is off")
+    assert_close(ya, refa, "sorted after the hook is off")
+
 # ------------------------------------------------------------------ tiled qweight layout
 @pytest.mark.parametrize("bits", BITS)
 def test_repack_tiled_bit_exact(dev, bits):
@@ -573,13 +649,16 @@ QZ_GRID = list(itertools.product(BITS, (False, True), (False, True), (False, Tru
 @pytest.mark.parametrize("bits,sym,is_v2,act", QZ_GRID)
 def test_quantize_bit_exact(dev, bits, sym, is_v2, act):
     """gptq_quantize reproduces the oracle's min/max quantizer and packers bit for
-    bit (codes decided in fp64 on both sides)."""
+    bit (codes decided in fp64 on both sides), including degenerate groups and
+    groups whose weights all share one sign (the clamped asymmetric zero)."""
     for K, N, gs in ((512, 544, 64), (256, 96, 128), (96, 32, 32)):
         d = draw_layer(K, N, 1, sigma=0.02, group_size=gs, outlier_rate=0.01, act_order=act, seed=bits + K)
         W = d.W.copy()
         W[:, 3] = 0.125                      # constant column: degenerate group -> scale 1
         W[:gs, 5] = 1e-9                     # scale underflows to 0 in fp16 -> 1
         W[:, 7] *= 1e-4                      # fp16-subnormal scales
+        W[:, 9] = np.abs(W[:, 9]) + 0.01     # one-signed groups: the asymmetric zero clamps to 0 ...
+        W[:, 11] = -np.abs(W[:, 11]) - 0.01  # ... and to 2^b - 1
         L = oracle.quantize_layer(W, bits, gs, sym, is_v2, d.g_idx)
         gi = None if d.g_idx is None else torch.from_numpy(d.g_idx).to(dev)
         qw, qz, sc = gq.quantize(torch.from_numpy(W).to(dev), gi, bits, gs, sym, is_v2)

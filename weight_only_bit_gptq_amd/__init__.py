@@ -16,7 +16,7 @@ import threading
 from typing import Optional
 
 __all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "repack_tiled", "unrepack_tiled", "moe_gemm",
-           "sort_act_order", "gemm_sorted", "release", "library", "library_path", "GptqError",
+           "sort_act_order", "gemm_sorted", "read_ceiling", "release", "library", "library_path", "GptqError",
            "STATUS", "PATH_AUTO", "PATH_DECODE", "PATH_PREFILL"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -104,6 +104,8 @@ def library() -> ctypes.CDLL:
         lib.gptq_strerror.restype = ctypes.c_char_p
         lib.gptq_release.argtypes = []
         lib.gptq_release.restype = None
+        lib.gptq_read_ceiling.argtypes = [vp, i64, vp, vp]
+        lib.gptq_read_ceiling.restype = i32
         lib.gptq_abi_version.argtypes = []
         lib.gptq_abi_version.restype = i32
         if lib.gptq_abi_version() != 1:
@@ -465,3 +467,27 @@ def unrepack_tiled(qweight_tiled, bits: int):
 def release():
     """Release library-owned device memory (the split-K workspaces), after synchronising the devices."""
     library().gptq_release()
+
+
+def read_ceiling(buf, nbytes: Optional[int] = None, *, sink=None):
+    """Read the first `nbytes` bytes of the contiguous GPU tensor `buf` once
+    (gptq_read_ceiling: 16-byte nontemporal loads, nothing else), on the
+    current stream: the memory-read reference the decode launches are measured
+    against.  `sink` is an int32 GPU tensor the kernel may write (allocated if
+    omitted)."""
+    import torch
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    total = buf.numel() * buf.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if nbytes < 0 or nbytes > total:
+        raise ValueError(f"nbytes must lie in [0, {total}]")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check_tensor("sink", sink, torch.int32, buf.device)
+    lib = library()
+    with torch.cuda.device(buf.device):
+        code = lib.gptq_read_ceiling(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                     torch.cuda.current_stream(buf.device).cuda_stream)
+    _raise(code)
+    return sink

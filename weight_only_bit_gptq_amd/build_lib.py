@@ -21,7 +21,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libgptq.so")
 ARCH = "gfx950"
 
-SOURCES = ["gptq_api.cpp", "dequant.hip", "decode.hip", "prefill.hip", "quantize.hip"]
+SOURCES = ["gptq_api.cpp", "dequant.hip", "decode.hip", "prefill.hip", "quantize.hip", "ceiling.hip"]
 
 
 def hipcc() -> str:

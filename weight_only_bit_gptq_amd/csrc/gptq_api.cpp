@@ -91,7 +91,7 @@ bool better_choice(const DecodeChoice& a, const DecodeChoice& b) {
 // Launch shape of one (cpl, nw, cpw, ks) candidate, or false when it does not
 // fit (registers, LDS, x staging, split sizes).
 bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int cpl, int nw, int cpw, int ks,
-                      DecodeChoice* c, size_t* lds_out, bool bf16 = false) {
+                      DecodeChoice* c, size_t* lds_out, bool bf16 = false, int64_t ws_cap = kSplitWsCap) {
   const int C = K / 32;
   const int cpg = per_elem ? 1 : (K / G) / 32;
   if (!gptq::decode_cpw_allowed(bits, per_elem, cpl, cpw, M, bf16)) return false;
@@ -99,7 +99,7 @@ bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int c
   if (nw < 1 || 64 * nw > gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M)) return false;
   const int cks = (C + ks - 1) / ks;
   if (ks < 1 || (ks - 1) * cks >= C || (ks > 1 && cks < kMinSplitChunks)) return false;
-  if (ks > 1 && (int64_t)ks * M * N * 4 > kSplitWsCap) return false;
+  if (ks > 1 && (int64_t)ks * M * N * 4 > ws_cap) return false;
   const int pc = nw * cpw;
   const int phases = (cks + pc - 1) / pc;
   const size_t lds = gptq::decode_lds_bytes(M, pc, nw, cpl, per_elem, G, cpg, phases, bf16);
@@ -145,7 +145,7 @@ void apply_choice(const DecodeChoice& c, int M, int K, int G, bool per_elem, boo
 }
 
 bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_elem, bool allow_split,
-                     bool tiled, gptq::GemmArgs* a, bool bf16) {
+                     bool tiled, gptq::GemmArgs* a, bool bf16, int64_t ws_cap) {
   bool found = false;
   DecodeChoice best{};
   // tiled layout, M = 1, full-width: 16 chunks per wave over 16-column tiles
@@ -169,7 +169,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
     const int waste8 = (cks + 63) / 64 * 64 - cks, waste4 = (cks + 31) / 32 * 32 - cks;
     const int nw = waste4 < waste8 ? 4 : 8;
     size_t lds;
-    if (decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, 8, ks, &best, &lds, bf16)) {
+    if (decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, 8, ks, &best, &lds, bf16, ws_cap)) {
       apply_choice(best, M, K, G, per_elem, bf16, a);
       return true;
     }
@@ -180,7 +180,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
     int64_t best_slots = 0;
     for (int nw = 8; nw <= 16; ++nw) {
       DecodeChoice c;
-      if (!decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, nw, 16, 1, &c, &lds, bf16)) continue;
+      if (!decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, nw, 16, 1, &c, &lds, bf16, ws_cap)) continue;
       const int64_t slots = (int64_t)c.phases * nw * 16;
       if (!found || c.rounds < best.rounds ||
           (c.rounds == best.rounds && (slots < best_slots || (slots == best_slots && c.phases < best.phases)))) {
@@ -211,7 +211,7 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
           if (waves == 0 && (nw & (nw - 1)) != 0) continue;   // automatic: 1, 2, 4, 8, 16 waves
           DecodeChoice c;
           size_t lds;
-          if (!decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, cpw, ks, &c, &lds, bf16)) continue;
+          if (!decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, cpw, ks, &c, &lds, bf16, ws_cap)) continue;
           if (!found || better_choice(c, best)) {
             best = c;
             found = true;
@@ -226,10 +226,10 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
 }
 
 int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_split, bool tiled, bool* per_elem,
-                 gptq::GemmArgs* a, bool bf16 = false) {
+                 gptq::GemmArgs* a, bool bf16 = false, int64_t ws_cap = kSplitWsCap) {
   if ((K / G) % 32 != 0) *per_elem = true;
   for (int pe = *per_elem ? 1 : 0; pe < 2; ++pe) {
-    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, allow_split, tiled, a, bf16)) {
+    if (decode_plan_for(bits, M, N, K, G, waves, pe == 1, allow_split, tiled, a, bf16, ws_cap)) {
       *per_elem = pe == 1;
       return GPTQ_OK;
     }
@@ -241,7 +241,7 @@ int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_spl
 int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
               const void* out, int path, int decode_waves, bool tiled, gptq::GemmArgs* a, bool* use_decode,
-              bool* per_elem, bool allow_split = true, bool bf16 = false) {
+              bool* per_elem, bool allow_split = true, bool bf16 = false, int64_t ws_cap = kSplitWsCap) {
   if (path < 0 || path > 2 || decode_waves < 0 || decode_waves > 16) return GPTQ_ERR_BAD_ARG;
   int rc = check_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out);
   if (rc != GPTQ_OK) return rc;
@@ -269,7 +269,8 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
     // bfloat16: always the element-wise dequant (the fp16 exponent trick of
     // the fast path does not carry over)
     *per_elem = bf16 || (g_idx != nullptr) || (group_size % 32 != 0);
-    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, allow_split, tiled, per_elem, a, bf16);
+    const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, allow_split, tiled, per_elem, a, bf16,
+                                 ws_cap);
     if (rc2 != kNoDecodePlan) return rc2;
     if (path == 1) return GPTQ_ERR_BAD_ARG;         // forced decode, but no launch shape fits
     *use_decode = false;                             // very many groups: the prefill kernel
@@ -283,8 +284,10 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
 // at a fixed place (the first kCounterBytes, enough for every tile count),
 // then the fp32 partial sums.  Counters are zeroed once at allocation and
 // every kernel leaves them at zero, so calls of any shape can share them.
-// Grown (after draining the stream) when a call needs more; never allocated
-// while the stream is being captured.
+// Grown when a call needs more; never allocated while the stream is being
+// captured.  A superseded buffer is not freed: a HIP graph captured earlier on
+// that stream holds its address and keeps using it on every replay, so it is
+// kept on a retired list until gptq_release.
 constexpr size_t kCounterBytes = (size_t)4 << 16;   // N <= 2^20 columns: at most 2^16 tiles
 struct SplitWorkspace {
   int device;
@@ -292,8 +295,21 @@ struct SplitWorkspace {
   char* base;
   size_t bytes;
 };
+struct RetiredBuffer {
+  int device;
+  char* base;
+};
 std::mutex g_ws_mu;
 std::vector<SplitWorkspace> g_ws;
+std::vector<RetiredBuffer> g_retired;
+
+// Test hook: with GPTQ_TEST_FAIL_WORKSPACE=1 in the environment every
+// workspace allocation fails, so tests can reach the no-memory paths (the
+// unsplit fallback, GPTQ_ERR_NO_MEM) without exhausting device memory.
+bool workspace_alloc_disabled() {
+  const char* v = std::getenv("GPTQ_TEST_FAIL_WORKSPACE");
+  return v != nullptr && v[0] == '1';
+}
 
 // x_bytes > 0 also reserves a buffer after the partial sums (the gathered x
 // of gptq_gemm_sorted), returned in *xbuf.
@@ -310,14 +326,9 @@ bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, floa
   if (e == nullptr || e->bytes < need) {
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return false;
+    if (workspace_alloc_disabled()) return false;
     size_t bytes = std::max(need, (size_t)1 << 20);
-    if (e != nullptr) {
-      bytes = std::max(bytes, 2 * e->bytes);
-      if (hipStreamSynchronize(stream) != hipSuccess) return false;   // queued kernels may use the old one
-      (void)hipFree(e->base);
-      e->base = nullptr;
-      e->bytes = 0;
-    }
+    if (e != nullptr) bytes = std::max(bytes, 2 * e->bytes);
     char* base = nullptr;
     if (hipMalloc(reinterpret_cast<void**>(&base), bytes) != hipSuccess) {
       (void)hipGetLastError();
@@ -331,6 +342,9 @@ bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, floa
       g_ws.push_back(SplitWorkspace{dev, stream, base, bytes});
       e = &g_ws.back();
     } else {
+      // kernels queued on the stream and graphs captured on it may still use
+      // the old buffer: retire it (freed by gptq_release), never free it here
+      g_retired.push_back(RetiredBuffer{dev, e->base});
       e->base = base;
       e->bytes = bytes;
     }
@@ -777,8 +791,24 @@ void gptq_release(void) {
       (void)hipFree(w.base);
     }
   }
+  for (auto& r : g_retired) {
+    if (hipSetDevice(r.device) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(r.base);
+    }
+  }
   g_ws.clear();
+  g_retired.clear();
   if (have) (void)hipSetDevice(cur);
+}
+
+int gptq_read_ceiling(const void* buf, int64_t bytes, void* sink, void* stream) {
+  if (!buf || !sink) return GPTQ_ERR_NULL_PTR;
+  if (bytes < 0 || bytes % 16 != 0 || bytes > ((int64_t)1 << 40)) return GPTQ_ERR_BAD_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return GPTQ_ERR_MISALIGNED;
+  if (bytes == 0) return GPTQ_OK;
+  const hipError_t err = gptq::launch_read_ceiling(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
 }
 
 int gptq_abi_version(void) { return 1; }

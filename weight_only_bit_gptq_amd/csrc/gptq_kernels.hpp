@@ -120,6 +120,9 @@ hipError_t launch_sort_rows(const int32_t* in, const int32_t* perm, int32_t* out
                             hipStream_t stream);
 hipError_t launch_gather_cols(const void* x, const int32_t* perm, void* xg, int64_t M, int64_t K, hipStream_t stream);
 
+// Memory-read reference: reads `bytes` (a multiple of 16) at buf once.
+hipError_t launch_read_ceiling(const void* buf, int64_t bytes, void* sink, hipStream_t stream);
+
 // GPTQv1 <-> GPTQv2 stored zero conversion of a packed qzeros [G, N*b/32].
 hipError_t launch_convert_zeros(const int32_t* in, int32_t* out, int bits, int64_t G, int64_t N, int to_v2,
                                 int32_t* lossy_count, hipStream_t stream);

@@ -93,6 +93,50 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+
+@dataclass(frozen=True)
+class BenchCase:
+    """One call the benchmark times: a workload layer at M rows, with qweight in
+    the checkpoint layout or re-laid out into the tiled one, fp16 or bfloat16
+    activations, through gptq_gemm (act-order layers: g_idx passed as is) or
+    gptq_gemm_sorted (act-order rows sorted by group once at load).  The GPU
+    parity tests run exactly these calls."""
+    group: str                    # the bench line that reports it
+    workload: str
+    layer: str
+    M: int
+    layout: str                   # "tiled" | "checkpoint"
+    act: str = "fp16"             # "fp16" | "bf16"
+    entry: str = "gemm"           # "gemm" | "gemm_sorted"
+
+    @property
+    def key(self) -> str:
+        return f"{self.group}:{self.workload}:{self.layer}:M{self.M}:{self.layout}:{self.act}:{self.entry}"
+
+
+def _cases(group, wname, Ms, layout, act="fp16", entry="gemm"):
+    wl = WORKLOADS[wname]
+    return [BenchCase(group, wname, l.name, M, layout, act, entry) for l in wl.layers for M in Ms]
+
+
+# Every GEMM call bench.py times, grouped by the line of its JSON output.
+BENCH_CASES: List[BenchCase] = (
+    _cases("decode", "llama7b_decode_w4g128", [1], "tiled")
+    + _cases("decode_checkpoint", "llama7b_decode_w4g128", [1], "checkpoint")
+    + _cases("decode_other", "lowbit_decode_w2g64", [1, 4, 16], "tiled")
+    + _cases("decode_other", "actorder_decode_w3g128", [16], "tiled", entry="gemm_sorted")
+    + _cases("decode_other", "actorder_decode_w3g128", [16], "checkpoint")
+    + _cases("prefill", "mlp70b_prefill_w4g128", [2048], "tiled")
+    + _cases("prefill", "mlp70b_prefill_w8g128", [2048], "tiled")
+    + _cases("prefill_checkpoint", "mlp70b_prefill_w4g128", [2048], "checkpoint")
+    + _cases("bf16_decode", "llama7b_decode_w4g128", [1], "checkpoint", act="bf16")
+    + _cases("bf16_prefill", "mlp70b_prefill_w4g128", [2048], "checkpoint", act="bf16")
+)
+
+
+def bench_cases(group: str) -> List[BenchCase]:
+    return [c for c in BENCH_CASES if c.group == group]
+
 @dataclass
 class LayerDraw:
     """Random inputs for one layer."""

@@ -107,6 +107,27 @@ GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qze
               int is_v2, int64_t M, int64_t N, int64_t K, void* out, void* stream);
 
 /*
+ * gptq_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, checks, launch plan and result as gptq_gemm (bit for bit); it
+ * calls no hipMalloc / hipFree.  Where gptq_gemm splits K over workgroups
+ * (decode, narrow N, long K), the arrival counters and fp32 partial sums live
+ * in a static device array of 2 MiB that the library holds on every device it
+ * runs on until the process ends (gptq_release does not free it); the plan
+ * keeps the partial sums within it (at most ks * M * N * 4 bytes of 2 MiB -
+ * 64 KiB, and 4 bytes per column tile in the first 64 KiB), and a plan that
+ * needed more would return GPTQ_ERR_NO_MEM before launching.  The counters
+ * are cleared by a kernel on `stream` at the first call on a device (the
+ * array also starts zeroed) and every split-K kernel leaves them at zero.
+ * All calls on one device share that one array: calls that may overlap on a
+ * device (concurrent streams, or graph replays overlapping each other or
+ * eager calls) race on it and must be serialized by the caller.
+ */
+GPTQ_API int gptq_gemm_noalloc(const void* x, const int32_t* qweight, const int32_t* qzeros,
+                               const void* scales, const int32_t* g_idx, int bits, int group_size,
+                               int is_v2, int64_t M, int64_t N, int64_t K, void* out, void* stream);
+
+/*
  * gptq_gemm with explicit kernel choice, for tests and tuning.
  *   path          0 = automatic (as gptq_gemm), 1 = decode kernel (requires
  *                 M <= 16), 2 = prefill kernel (any M).

@@ -15,7 +15,7 @@ import os
 import threading
 from typing import Optional
 
-__all__ = ["gemm", "describe", "dequant", "quantize", "convert_zeros", "repack_tiled", "unrepack_tiled", "moe_gemm",
+__all__ = ["gemm", "gemm_noalloc", "describe", "dequant", "quantize", "convert_zeros", "repack_tiled", "unrepack_tiled", "moe_gemm",
            "sort_act_order", "gemm_sorted", "read_ceiling", "release", "library", "library_path", "GptqError",
            "STATUS", "PATH_AUTO", "PATH_DECODE", "PATH_PREFILL"]
 
@@ -58,6 +58,8 @@ def library() -> ctypes.CDLL:
         lib.gptq_gemm.argtypes = gemm_args
         lib.gptq_gemm.restype = i32
         lib.gptq_gemm_ex.argtypes = gemm_args + [i32, i32]
+        lib.gptq_gemm_noalloc.argtypes = gemm_args
+        lib.gptq_gemm_noalloc.restype = i32
         lib.gptq_gemm_ex.restype = i32
         lib.gptq_dequant.argtypes = [i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, vp, vp]
         for name in ("gptq_gemm_bf16", "gptq_gemm_bf16_ex", "gptq_gemm_bf16_describe", "gptq_dequant_bf16"):
@@ -219,6 +221,32 @@ def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_s
         code = fn(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
                   None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
                   int(bool(is_v2)), M, N, K, out.data_ptr(), stream, int(path), int(decode_waves))
+    _raise(code)
+    return out
+
+
+def gemm_noalloc(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int, is_v2: bool, *,
+                 out):
+    """gemm through gptq_gemm_noalloc: the library allocates nothing (split-K
+    scratch in a static per-device array); `out` must be given, fp16 [M, N],
+    checkpoint qweight layout."""
+    import torch
+    dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2)
+    if qweight.dim() != 2:
+        raise ValueError("gemm_noalloc takes the checkpoint qweight layout")
+    _check_tensor("x", x, torch.float16, dev)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M, {K}], got {tuple(x.shape)}")
+    M = x.shape[0]
+    _check_tensor("out", out, torch.float16, dev)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}, {N}]")
+    lib = library()
+    with torch.cuda.device(dev):
+        code = lib.gptq_gemm_noalloc(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                                     None if g_idx is None else g_idx.data_ptr(), int(bits), int(group_size),
+                                     int(bool(is_v2)), M, N, K, out.data_ptr(),
+                                     torch.cuda.current_stream(dev).cuda_stream)
     _raise(code)
     return out
 

@@ -355,6 +355,41 @@ bool split_workspace(hipStream_t stream, size_t ws_bytes, size_t cnt_bytes, floa
   return true;
 }
 
+// Scratch of gptq_gemm_noalloc: a static device array (each device holds its
+// own copy for the life of the process) instead of the allocated workspace:
+// the split-K arrival counters in the first kScratchCounterBytes, the fp32
+// partial sums after them.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)2 << 20;
+constexpr size_t kScratchCounterBytes = (size_t)64 << 10;   // 16384 tiles
+constexpr int64_t kScratchSumBytes = (int64_t)(kScratchBytes - kScratchCounterBytes);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // device address of `scratch`, per device
+
+// The calling thread's current device's scratch address; on first use on a
+// device the counters are cleared by a kernel on `stream` (the array also
+// starts zeroed when the code object loads; every split-K kernel leaves the
+// counters it used at zero).
+int scratch_for_device(hipStream_t stream, char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GPTQ_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (g_scratch_ptr[(size_t)dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return GPTQ_ERR_DEVICE;
+    }
+    if (gptq::launch_zero_words(p, (int64_t)(kScratchCounterBytes / 4), stream) != hipSuccess) return GPTQ_ERR_LAUNCH;
+    g_scratch_ptr[(size_t)dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[(size_t)dev]);
+  return GPTQ_OK;
+}
+
 // x_perm (nullable): rows of qweight are sorted by act-order group and x is
 // gathered into that order first (x_perm[i] = original row of sorted row i).
 int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
@@ -800,6 +835,37 @@ void gptq_release(void) {
   g_ws.clear();
   g_retired.clear();
   if (have) (void)hipSetDevice(cur);
+}
+
+int gptq_gemm_noalloc(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                      const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                      void* out, void* stream_ptr) {
+  try {
+    gptq::GemmArgs a;
+    bool use_decode = false, per_elem = false;
+    // the same plan as gptq_gemm, with split-K partial sums limited to what
+    // the scratch holds (the planner never needs more than about 1 MiB)
+    const int rc = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, 0, 0, false,
+                             &a, &use_decode, &per_elem, true, false, kScratchSumBytes);
+    if (rc != GPTQ_OK || M == 0) return rc;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    if (use_decode && a.ks > 1) {
+      if ((size_t)a.tiles * 4 > kScratchCounterBytes || (int64_t)a.ks * a.M * a.N * 4 > kScratchSumBytes)
+        return GPTQ_ERR_NO_MEM;                      // beyond the static scratch (not reached by the planner)
+      char* p = nullptr;
+      const int rs = scratch_for_device(stream, &p);
+      if (rs != GPTQ_OK) return rs;
+      a.cnt = reinterpret_cast<uint32_t*>(p);
+      a.ws = reinterpret_cast<float*>(p + kScratchCounterBytes);
+    }
+    const hipError_t err = use_decode ? gptq::launch_decode(bits, per_elem, a, stream)
+                                      : gptq::launch_prefill(bits, per_elem, a, stream);
+    return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
+  } catch (const std::bad_alloc&) {
+    return GPTQ_ERR_NO_MEM;
+  } catch (...) {
+    return GPTQ_ERR_DEVICE;
+  }
 }
 
 int gptq_read_ceiling(const void* buf, int64_t bytes, void* sink, void* stream) {

@@ -120,6 +120,9 @@ hipError_t launch_sort_rows(const int32_t* in, const int32_t* perm, int32_t* out
                             hipStream_t stream);
 hipError_t launch_gather_cols(const void* x, const int32_t* perm, void* xg, int64_t M, int64_t K, hipStream_t stream);
 
+// Zero `words` int32 words with a kernel (capture-safe, unlike a memset node).
+hipError_t launch_zero_words(void* p, int64_t words, hipStream_t stream);
+
 // Memory-read reference: reads `bytes` (a multiple of 16) at buf once.
 hipError_t launch_read_ceiling(const void* buf, int64_t bytes, void* sink, hipStream_t stream);
 

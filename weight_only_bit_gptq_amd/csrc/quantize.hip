@@ -390,4 +390,18 @@ hipError_t launch_gather_cols(const void* x, const int32_t* perm, void* xg, int6
   return hipGetLastError();
 }
 
+// Zero `words` 32-bit words (a fill kernel rather than hipMemsetAsync, so the
+// clear is an ordinary kernel node when the caller captures the stream).
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* __restrict__ p, int64_t words) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < words) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(void* p, int64_t words, hipStream_t stream) {
+  if (words <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
 }  // namespace gptq

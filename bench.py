@@ -64,6 +64,8 @@ sys.path.insert(0, ROOT)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama7b_w4g128_hbm_traffic.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_mlp70b_mfma_util.txt")
+DECODE_PMC_FILE = os.path.join(ROOT, "profiles", "decode_all_instructions_and_stalls.txt")
+DECODE_PMC_GROUPS = ("decode", "decode_other")
 # sources that decide the decode kernel's code and launch shapes
 DECODE_SOURCES = ["weight_only_bit_gptq_amd/csrc/decode.hip", "weight_only_bit_gptq_amd/csrc/gptq_device.hpp",
                   "weight_only_bit_gptq_amd/csrc/gptq_kernels.hpp", "weight_only_bit_gptq_amd/csrc/gptq_api.cpp"]
@@ -102,6 +104,10 @@ def parse():
     p.add_argument("--cpu-reps", type=int, default=3, help="oracle calls on the sample (median reported)")
     p.add_argument("--pmc-driver", action="store_true",
                    help="only launch each decode layer 3 times and a plain copy, for a rocprofv3 --pmc pass")
+    p.add_argument("--pmc-decode-driver", action="store_true",
+                   help="only launch every benchmarked decode call 3 times, for rocprofv3 --pmc passes")
+    p.add_argument("--summarize-decode-pmc", nargs="+", metavar="COUNTER_CSV",
+                   help="write the decode instruction / stall summary to profiles/ from --pmc-decode-driver passes")
     p.add_argument("--pmc-prefill-driver", action="store_true",
                    help="only launch each 70B-MLP prefill layer twice, for a rocprofv3 --pmc pass")
     p.add_argument("--summarize-prefill-pmc", nargs=2, metavar=("COUNTER_CSV", "TRACE_CSV"),
@@ -570,6 +576,92 @@ def pmc_driver(torch, gq, dev):
     print("pmc driver done", flush=True)
 
 
+def pmc_decode_driver(torch, gq, dev):
+    """Every benchmarked decode call (groups DECODE_PMC_GROUPS) launched 3
+    times on distinct weight copies; one line per call names it."""
+    from workload import bench_cases
+    for group in DECODE_PMC_GROUPS:
+        for case in bench_cases(group):
+            P = prepare(torch, gq, case, dev)
+            out = torch.empty((case.M, P["layer"].N), dtype=P["act"], device=dev)
+            copies = [P["qweight"].clone() for _ in range(3)]
+            torch.cuda.synchronize()
+            for qw in copies:
+                P["call"](qw, out)
+            torch.cuda.synchronize()
+            print(f"case {case.key}: {P['desc']}", flush=True)
+            del P, copies
+            torch.cuda.empty_cache()
+    print("pmc decode driver done", flush=True)
+
+
+def summarize_decode_pmc(paths):
+    """Per benchmarked decode call: the counters of its 3 launches (mean), from
+    one or more --pmc-decode-driver passes, with per-weight instruction counts
+    and stall fractions derived where the counters are present."""
+    from workload import bench_cases
+    cases = [c for g in DECODE_PMC_GROUPS for c in bench_cases(g)]
+    per_pass = []
+    for path in paths:
+        disp = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if "decode_kernel" not in r["Kernel_Name"] and "decode_bf16" not in r["Kernel_Name"]:
+                    continue
+                d = disp.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        ids = sorted(disp)
+        if len(ids) != 3 * len(cases):
+            raise SystemExit(f"{path}: expected {3 * len(cases)} decode dispatches, got {len(ids)}")
+        per_pass.append([disp[i] for i in ids])
+    rows = []
+    for k, case in enumerate(cases):
+        wl, layer = wl_layer(case)
+        vals = {"kernel": per_pass[0][3 * k]["kernel"]}
+        for launches in per_pass:
+            for name in launches[3 * k]:
+                if name != "kernel":
+                    vals[name] = float(np.mean([launches[3 * k + i][name] for i in range(3)]))
+        elems = layer.K * layer.N
+        d = {"case": case.key, "kernel": vals["kernel"]}
+        for name in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU"):
+            if name in vals:
+                d[name.replace("SQ_INSTS_", "").lower() + "_lane_per_weight"] = round(64 * vals[name] / elems, 3)
+        if "SQ_WAVE_CYCLES" in vals and vals["SQ_WAVE_CYCLES"] > 0:
+            for name in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                         "SQ_ACTIVE_INST_VMEM", "SQ_BUSY_CYCLES"):
+                if name in vals:
+                    d[name.lower() + "_over_wave_cycles"] = round(vals[name] / vals["SQ_WAVE_CYCLES"], 3)
+        if "SQ_LDS_BANK_CONFLICT" in vals and vals.get("SQ_INSTS_LDS", 0) > 0:
+            d["lds_bank_conflict_cycles_per_lds_inst"] = round(vals["SQ_LDS_BANK_CONFLICT"] / vals["SQ_INSTS_LDS"], 3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals:
+            d["mfma_busy_over_gpu_cycles_x_simds"] = round(
+                vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] / MI355X_XCDS * 1024), 4)
+        d["raw"] = {n: round(v, 1) for n, v in vals.items() if n != "kernel"}
+        rows.append(d)
+    lines = [
+        "# Instruction mix and stalls of every benchmarked decode call (MI355X), rocprofv3 counters",
+        "# summed over the chip, mean of 3 launches on distinct weight copies.",
+        "# Commands (from /tmp with TMPDIR=/tmp; R = repository root), one pass per counter set:",
+        "#   rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+        "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM -d D/p1 -o run -f csv -- python3 R/bench.py --pmc-decode-driver",
+        "#   rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_INSTS_VMEM_RD SQ_INSTS_SALU "
+        "SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -d D/p2 -o run -f csv -- python3 R/bench.py "
+        "--pmc-decode-driver",
+        "#   python3 R/bench.py --summarize-decode-pmc D/p1/run_counter_collection.csv D/p2/run_counter_collection.csv",
+        "# x_lane_per_weight = 64 * instructions / (K * N): lane-instructions per weight element.",
+        "# *_over_wave_cycles: cycles waves spent waiting / issuing, over all wave cycles.",
+    ]
+    for d in rows:
+        lines.append(d["case"] + " | " + d["kernel"].split("(")[0].replace("void ", "") + " | " +
+                     ", ".join(f"{k}={v}" for k, v in d.items() if k not in ("case", "kernel", "raw")))
+    lines.append("json: " + json.dumps({"sources_sha256": decode_sources_hash(), "rows": rows}))
+    os.makedirs(os.path.dirname(DECODE_PMC_FILE), exist_ok=True)
+    with open(DECODE_PMC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 PREFILL_WORKLOADS = ("mlp70b_prefill_w4g128", "mlp70b_prefill_w8g128")
 MI355X_XCDS = 8
 
@@ -720,6 +812,9 @@ def main():
     if args.summarize_prefill_pmc:
         summarize_prefill_pmc(*args.summarize_prefill_pmc)
         return
+    if args.summarize_decode_pmc:
+        summarize_decode_pmc(args.summarize_decode_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(run with --gpus 1)", file=sys.stderr)
@@ -739,6 +834,9 @@ def main():
         return
     if args.pmc_prefill_driver:
         pmc_prefill_driver(torch, gq, dev)
+        return
+    if args.pmc_decode_driver:
+        pmc_decode_driver(torch, gq, dev)
         return
 
     outputs = {}

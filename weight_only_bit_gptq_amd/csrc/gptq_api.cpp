@@ -95,7 +95,11 @@ bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int c
   const int C = K / 32;
   const int cpg = per_elem ? 1 : (K / G) / 32;
   if (!gptq::decode_cpw_allowed(bits, per_elem, cpl, cpw, M, bf16)) return false;
-  if (cpw * M > 16 * gptq::decode_max_x_pieces(M)) return false;
+  // x staged per phase (one row, or the per-element path): the staging
+  // registers bound the chunks per wave; several rows on the fast path load
+  // their A fragments directly (no staging)
+  const bool x_direct = M > 1 && !per_elem && !bf16;
+  if (!x_direct && cpw * M > 16 * gptq::decode_max_x_pieces(M)) return false;
   if (nw < 1 || 64 * nw > gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M)) return false;
   const int cks = (C + ks - 1) / ks;
   if (ks < 1 || (ks - 1) * cks >= C || (ks > 1 && cks < kMinSplitChunks)) return false;

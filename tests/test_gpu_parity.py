@@ -406,6 +406,27 @@ def test_gemm_tiled_shapes(dev, bits, gs, M, K, N, act):
     assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, desc)
 
 
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("M,K,N", [(1024, 512, 288), (1057, 576, 544), (2048, 1024, 256)])
+def test_prefill_big_tiles(dev, bits, M, K, N):
+    """Large M with few tiles takes the 256-row prefill tile (not 8-bit):
+    ragged rows (M % 256) and columns (N % 256), both qweight layouts, against
+    the oracle on sampled columns; the two layouts give the same bits."""
+    gs = 64
+    d, L = quantized(K, N, M, bits, gs, False, True, False, seed=M + K + N + bits)
+    qw, qz, sc, gi = upload(L, dev)
+    qt = upload_tiled(L, dev)[0]
+    x = torch.from_numpy(d.x).to(dev)
+    desc = gq.describe(x, qw, qz, sc, gi, bits, gs, True)
+    assert ("prefill_big_kernel" in desc) == (bits != 8), desc
+    cols = np.unique(np.concatenate([np.arange(0, N, 7), [N - 1]]))
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N, cols=cols)
+    yc = gq.gemm(x, qw, qz, sc, gi, bits, gs, True)
+    yt = gq.gemm(x, qt, qz, sc, gi, bits, gs, True)
+    assert_close(yc[:, torch.from_numpy(cols).to(dev)], ref, desc)
+    assert torch.equal(yc.view(torch.int16), yt.view(torch.int16)), desc
+
 # ------------------------------------------------------------------ act-order rows sorted by group
 @pytest.mark.parametrize("bits", BITS)
 def test_sort_act_order_bit_exact(dev, bits):

@@ -450,10 +450,13 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
         }
         *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8) = v0;
         *reinterpret_cast<f32x4_t*>(tw + (r * TN + 4 * c4) * 8 + 16) = v1;
-      } else if constexpr (PER_ELEM) {               // (zero + offset) << 16 | fp16 scale bits
+      } else if constexpr (PER_ELEM) {               // fp16 pair (s, -(zero + offset)), both exact
         u32x4_t v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = real ? ((z[j] << 16) | sb[j]) : 0u;
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t nz = __builtin_bit_cast(uint16_t, (_Float16)(-(float)z[j]));
+          v[j] = real ? ((nz << 16) | sb[j]) : 0u;
+        }
         *reinterpret_cast<u32x4_t*>(tw + (r * TN + 4 * c4) * 4) = v;
       } else {                                       // (s 2^24, -s (zero + offset)) as fp32, exact
         f32x4_t v0, v1;
@@ -672,24 +675,40 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
           }
           accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
                                                             __builtin_bit_cast(bf16x8_t, bw), accg[j], 0, 0, 0);
-        } else {
-          uint32_t pr[4];
-          unpack_block<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], sel, pr);
-          u32x4_t bw;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int ga = pairs4 ? gv[2 * v] : gv[Block<BITS>::F[2 * v]];
-            const int gb = pairs4 ? gv[2 * v + 1] : gv[Block<BITS>::F[2 * v + 1]];
-            const uint32_t ea = full_tab[ga * TN + CPL * q + j];
-            const uint32_t eb = full_tab[gb * TN + CPL * q + j];
-            const half2_t neg = {neg_offset<BITS>(v, (int)(ea >> 16)), neg_offset<BITS>(v, (int)(eb >> 16))};
-            const half2_t d = pair_minus_zero<BITS>(pr[v], v, neg);
-            const half2_t s = {__builtin_bit_cast(_Float16, (uint16_t)(ea & 0xFFFFu)),
-                               __builtin_bit_cast(_Float16, (uint16_t)(eb & 0xFFFFu))};
-            bw[v] = as_u32(d * s);
-          }
-          accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw), accg[j], 0, 0, 0);
         }
+      }
+      if constexpr (!BF16) {
+        // each field with its own row's group: the table row of (group, the
+        // lane's CPL columns) is one contiguous LDS vector of fp16 pairs
+        // (s, -z), read once per field for all CPL columns; per register pair
+        //   q   = (1024 + MUL q) / MUL - 1024 / MUL    (one packed FMA, exact)
+        //   W^  = (q - z) * s                          (packed add, packed multiply:
+        //                                               exact, then one rounding)
+        uint32_t pr[CPL][4];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) unpack_block<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], sel, pr[j]);
+        u32x4_t bw[CPL];
+        const unsigned char* tab_lane = lds + lay.tab_off + (size_t)(CPL * q) * 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int ga = pairs4 ? gv[2 * v] : gv[Block<BITS>::F[2 * v]];
+          const int gb = pairs4 ? gv[2 * v + 1] : gv[Block<BITS>::F[2 * v + 1]];
+          const wvec ea = *reinterpret_cast<const wvec*>(tab_lane + ga * (TN * 4));
+          const wvec eb = *reinterpret_cast<const wvec*>(tab_lane + gb * (TN * 4));
+          const _Float16 inv = (_Float16)(1.0f / (float)Block<BITS>::MUL[v]);
+          const _Float16 off = (_Float16)(-kMagic / (float)Block<BITS>::MUL[v]);
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            const uint32_t eaj = word_of<CPL>(ea, j), ebj = word_of<CPL>(eb, j);
+            const half2_t nz = as_half2(__builtin_amdgcn_perm(ebj, eaj, 0x07060302u));   // (-z_a, -z_b)
+            const half2_t sc = as_half2(__builtin_amdgcn_perm(ebj, eaj, 0x05040100u));   // (s_a, s_b)
+            const half2_t qv = as_half2(pr[j][v]) * half2_t{inv, inv} + half2_t{off, off};
+            bw[j][v] = as_u32((qv + nz) * sc);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+          accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bw[j]), accg[j], 0, 0, 0);
       }
     } else {
       // sums of x over the chunk for every row: one MFMA against a B operand

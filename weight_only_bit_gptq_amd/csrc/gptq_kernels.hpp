@@ -54,8 +54,9 @@ struct GemmArgs {
   const int32_t* moe_off;
   int n_experts, moe_blocks;
   int64_t qw_stride, qz_stride, sc_stride, gi_stride;
-  // prefill launch shape
-  int tiles_m, tiles_n;
+  // prefill launch shape: tiles_m x tiles_n workgroup tiles of pbm (128 or
+  // 256) rows by 256 columns
+  int tiles_m, tiles_n, pbm;
   // activation type: 0 = fp16 (x, scales, out fp16), 1 = bfloat16 (x,
   // scales and out hold bfloat16 bits behind the same pointers)
   int bf16;
@@ -103,7 +104,8 @@ bool decode_cpw_allowed(int bits, bool per_elem, int cpl, int cpw, int M, bool b
 hipError_t launch_decode(int bits, bool per_elem, const GemmArgs& a, hipStream_t stream);
 
 // Prefill (any M, used for M > 16).
-void prefill_shape(int M, int N, int* tiles_m, int* tiles_n);
+// big_ok: the 256-row tile may be used (fast path, fp16)
+void prefill_shape(int M, int N, bool big_ok, int* tiles_m, int* tiles_n, int* bm);
 hipError_t launch_prefill(int bits, bool per_elem, const GemmArgs& a, hipStream_t stream);
 
 // Min/max quantize + pack (fp32 W -> qweight, qzeros, scales).

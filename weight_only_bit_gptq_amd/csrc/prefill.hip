@@ -30,14 +30,24 @@
 
 namespace gptq {
 
-constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 256;
 constexpr int kPrefillBK = 64;
-constexpr int kPrefillMS = kPrefillBM / 32;      // 32-row MFMA subtiles per wave
 constexpr int kPrefillStages = 3;                 // x tiles in LDS: current + two in flight
+// Rows per workgroup tile: 128 (two workgroups per CU, each dequantized B
+// fragment feeds four MFMAs), or 256 (a wave tile of 256 x 64: each B fragment
+// feeds eight MFMAs, the 256 accumulators per lane fill the accumulation
+// registers, one workgroup per CU).  Measured on MI355X (70B-MLP shapes, M =
+// 2048, 4-bit): 256 rows win when all their tiles run in one round on the 256
+// CUs (28672 -> 8192: 1159 -> 1207 TFLOP/s) but lose when the grid takes
+// several rounds, whose last one runs partly empty and, at one workgroup per
+// CU, exposes every workgroup's prologue and epilogue (8192 -> 28672: 1160 ->
+// 1107); 8-bit lost on both shapes (its B operand is not pipelined).
+constexpr int kPrefillCUs = 256;
 
-void prefill_shape(int M, int N, int* tiles_m, int* tiles_n) {
-  *tiles_m = (M + kPrefillBM - 1) / kPrefillBM;
+void prefill_shape(int M, int N, bool big_ok, int* tiles_m, int* tiles_n, int* bm) {
+  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + kPrefillBN - 1) / kPrefillBN);
+  *bm = (big_ok && M >= 1024 && big_tiles <= kPrefillCUs) ? 256 : 128;
+  *tiles_m = (M + *bm - 1) / *bm;
   *tiles_n = (N + kPrefillBN - 1) / kPrefillBN;
 }
 
@@ -52,12 +62,12 @@ void prefill_shape(int M, int N, int* tiles_m, int* tiles_n) {
 // PAIRS (4-bit, tiled layout): the words hold their fields in pair order, so
 // one shift and four mask-ors make the four registers (fields 2v, 2v + 1,
 // multiplier 1, 16, 1, 16 for both halves) instead of four byte permutes.
-template <int BITS, bool PER_ELEM, bool FULL, bool BF16, bool PAIRS>
+template <int BITS, bool PER_ELEM, bool FULL, bool BF16, bool PAIRS, int BM>
 __device__ __forceinline__ void prefill_body(GemmArgs a) {
   static_assert(!PAIRS || (BITS == 4 && !BF16), "pair-order words: 4-bit fp16");
-  constexpr int BM = kPrefillBM;
+  static_assert(BM == 128 || BM == 256, "workgroup tile rows");
   constexpr int BK = kPrefillBK;
-  constexpr int MS = kPrefillMS;
+  constexpr int MS = BM / 32;                       // 32-row MFMA subtiles per wave
   constexpr int NST = kPrefillStages;
   constexpr int L = Block<BITS>::LOADS;
   constexpr int XI = BM * (BK / 8) / 256;          // 16-byte x pieces per thread (per wave: XI loads of 1 KB)
@@ -102,7 +112,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   uint32_t xoff[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
-    const int s = (4 * wave + i) * 64 + lane;
+    const int s = (XI * wave + i) * 64 + lane;
     const int m = s >> 3, kblk = (s & 7) ^ ((m >> 1) & 7);
     xoff[i] = ((uint32_t)(m0 + m) * (uint32_t)a.K + 8u * kblk) * 2u;
     // rows past M: an offset past the end of x (plus at most the K bytes of
@@ -115,7 +125,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrsrc, (__attribute__((address_space(3))) void*)(sl + (4 * wave + i) * 64 * 8), 16,
+          xrsrc, (__attribute__((address_space(3))) void*)(sl + (XI * wave + i) * 64 * 8), 16,
           xoff[i] + (uint32_t)min(kt, ktiles - 1) * BK * 2u, 0, 0, 0);
     }
   };
@@ -445,12 +455,18 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
 
 template <int BITS, bool PER_ELEM, bool FULL, bool PAIRS>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(GemmArgs a) {
-  prefill_body<BITS, PER_ELEM, FULL, false, PAIRS>(a);
+  prefill_body<BITS, PER_ELEM, FULL, false, PAIRS, 128>(a);
+}
+
+// 256-row tiles: one workgroup (one wave per SIMD) per CU
+template <int BITS, bool FULL, bool PAIRS>
+__global__ __launch_bounds__(256, 1) void prefill_big_kernel(GemmArgs a) {
+  prefill_body<BITS, false, FULL, false, PAIRS, 256>(a);
 }
 
 template <int BITS, bool PER_ELEM, bool FULL>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(GemmArgs a) {
-  prefill_body<BITS, PER_ELEM, FULL, true, false>(a);
+  prefill_body<BITS, PER_ELEM, FULL, true, false, 128>(a);
 }
 
 template <int BITS, bool PER_ELEM, bool FULL>
@@ -459,6 +475,14 @@ static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
   if (a.bf16) {
     if (a.wtiled) return hipErrorInvalidValue;     // bfloat16 reads the checkpoint layout only
     hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
+  } else if (a.pbm == 256) {
+    if constexpr (PER_ELEM) {
+      return hipErrorInvalidValue;                 // 256-row tiles: fast path only
+    } else if (BITS == 4 && a.wtiled) {
+      hipLaunchKernelGGL((prefill_big_kernel<BITS, FULL, BITS == 4>), grid, dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((prefill_big_kernel<BITS, FULL, false>), grid, dim3(256), 0, stream, a);
+    }
   } else if (BITS == 4 && a.wtiled) {
     // 4-bit tiled words hold their fields in pair order
     hipLaunchKernelGGL((prefill_kernel<BITS, PER_ELEM, FULL, BITS == 4>), grid, dim3(256), 0, stream, a);

@@ -116,7 +116,13 @@ bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int c
   const int resident = std::max(1, std::min({by_waves, by_lds, 16})) * kCUs;
   // weight bytes one phase of the resident workgroups has in flight
   const int64_t loads = (bits == 3 || bits == 8) ? 2 : 1;
-  const int64_t inflight = (int64_t)std::min(units, resident) * std::min(pc, cks) * 64 * cpl * loads * 4;
+  // bytes in flight matter where the stream is the bound; the per-element
+  // path with several rows is bound by its dequant work, which the cap does
+  // not describe (measured: a 3-bit act-order M = 16 layer ran 36% faster
+  // with 4 waves per workgroup than with the 2 the cap chose; one row, e.g.
+  // bfloat16 decode, keeps the cap: 20% slower without it)
+  const bool work_bound = per_elem && M > 1;
+  const int64_t inflight = work_bound ? 0 : (int64_t)std::min(units, resident) * std::min(pc, cks) * 64 * cpl * loads * 4;
   *c = DecodeChoice{(units + resident - 1) / resident, inflight > kInflightCap, inflight,
                     nw, cpl, cpw, ks, tiles, phases, phases * pc - cks, std::min(units, kCUs)};
   *lds_out = lds;
@@ -207,7 +213,11 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
       // slower than the best unsplit one; at N <= 1536 with K >= 8192 they
       // were 10-25% faster)
       if (ks > 1 && (!allow_split || N / 16 >= kCUs / 2 || K < kMinSplitK)) continue;
-      if (cpl > 1 && tiles * ks < 192) continue;
+      // wide tiles only while they leave enough workgroups for the stream (the
+      // per-element path with several rows, bound by its dequant work, takes
+      // them regardless: a 3-bit act-order 13824 -> 5120 layer at M = 16 ran
+      // 30% faster on 160 32-column tiles than on 320 16-column ones)
+      if (cpl > 1 && tiles * ks < 192 && !(per_elem && M > 1)) continue;
       for (int cpw : {8, 16, 32}) {
         const int maxw = gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M) / 64;
         const int lo = waves > 0 ? std::min(waves, maxw) : 1, hi = waves > 0 ? lo : maxw;
@@ -280,7 +290,7 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
     *use_decode = false;                             // very many groups: the prefill kernel
   }
   *per_elem = (g_idx != nullptr) || (group_size % 64 != 0);
-  gptq::prefill_shape(a->M, a->N, &a->tiles_m, &a->tiles_n);
+  gptq::prefill_shape(a->M, a->N, !*per_elem && !bf16 && bits != 8, &a->tiles_m, &a->tiles_n, &a->pbm);
   return GPTQ_OK;
 }
 
@@ -492,7 +502,10 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
     if (bf16)
       std::snprintf(buf, (size_t)buflen, "gptq::prefill_bf16_kernel<%d, %s, %s> grid=%dx%d block=256", bits, pe,
                     full ? "true" : "false", a.tiles_n, a.tiles_m);
-    else   // last argument: 4-bit tiled words with fields in pair order
+    else if (a.pbm == 256)   // last argument: 4-bit tiled words with fields in pair order
+      std::snprintf(buf, (size_t)buflen, "gptq::prefill_big_kernel<%d, %s, %s> grid=%dx%d block=256", bits,
+                    full ? "true" : "false", (bits == 4 && tiled) ? "true" : "false", a.tiles_n, a.tiles_m);
+    else
       std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s, %s, %s> grid=%dx%d block=256", bits, pe,
                     full ? "true" : "false", (bits == 4 && tiled) ? "true" : "false", a.tiles_n, a.tiles_m);
   }

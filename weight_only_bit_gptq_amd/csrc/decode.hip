@@ -126,10 +126,12 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   DecodeLayout L;
   const size_t tn = (size_t)16 * cpl;
   const int cpw = cpw_known > 0 ? cpw_known : pc / nw;   // the kernel passes its compile-time value
-  const int chunks = per_elem ? pc : cpw;                // chunks one staging region holds
-  // several rows on the fast path: the A fragments come straight from x in
-  // global memory (no x staging) and the sums of x from an MFMA (no sums)
-  const bool xdirect = !per_elem && M > 1;
+  // several rows (fp16): the A fragments come straight from x in global
+  // memory (no x staging; on the fast path the sums of x come from an MFMA),
+  // and every wave stages its own chunks' small operands in its own region
+  const bool xdirect = M > 1 && !bf16;
+  const bool per_wave = !per_elem || xdirect;
+  const int chunks = per_wave ? cpw : pc;                // chunks one staging region holds
   const size_t frag = xdirect ? 0 : align16((size_t)chunks * 4 * M * 16);
   L.corr_off = frag;
   const size_t corr = (per_elem || xdirect) ? 0 : align16((size_t)chunks * decode_corr_rows(M) * 4);
@@ -139,7 +141,7 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   // fast path: the groups a run of cpw consecutive chunks can touch
   L.ptab_rows = per_elem ? 0 : div_pos(cpw - 1, cpg) + 2;
   L.buf_stride = align16(L.ptab_off + (size_t)L.ptab_rows * tn * 8);
-  const int regions = per_elem ? (phases > 1 ? 2 : 1) : nw;
+  const int regions = per_wave ? nw : (phases > 1 ? 2 : 1);
   L.tab_off = (size_t)regions * L.buf_stride;            // whole table (per-element path)
   // per-element table entry: (zero << 16 | fp16 scale), or the fp32 pair
   // (s, -z s) for bfloat16
@@ -221,7 +223,11 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   // the unpack's field order in registers, instead of the wave staging x
   // through LDS per phase (as many bytes per chunk as 2-bit weights at 16
   // rows); the per-element path keeps its shared staging
-  constexpr bool XD = !PER_ELEM && MV != 1;
+  constexpr bool XD = !BF16 && MV != 1;
+  // staging per wave (own chunks, own LDS region, no workgroup barrier per
+  // phase): the fast path, and the per-element path with several rows (whose
+  // whole scale/zero table is staged once, behind one barrier)
+  constexpr bool PW = !PER_ELEM || XD;
   constexpr int GP = (CPW + 7) / 8;                  // g_idx pieces: 8 * CPW rows <= 64 * GP pieces of 4
   constexpr int TQ = decode_table_quads(PER_ELEM, CPL, CPW);
   constexpr int TN = 16 * CPL;
@@ -261,14 +267,18 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   // ---- staging scope: the fast path stages per wave (its own CPW chunks, in
   // its own LDS region), the per-element path per workgroup (the phase's pc
   // chunks, shared).  st / sn: this thread's index and the staging threads.
-  const int st = PER_ELEM ? tid : lane;
-  const int sn = PER_ELEM ? nthreads : 64;
-  const int sc = PER_ELEM ? pc : CPW;                // chunks one staging region holds
+  const int st = PW ? lane : tid;
+  const int sn = PW ? 64 : nthreads;
+  const int sc = PW ? CPW : pc;                      // chunks one staging region holds
+  // scale/zero table: the fast path stages its rows per wave, the per-element
+  // path the whole table once with the whole workgroup
+  const int tst = PER_ELEM ? tid : lane;
+  const int tsn = PER_ELEM ? nthreads : 64;
   // Chunk u of wave w in phase p is p*pc + w*CPW + u: each wave reads a run of
   // consecutive packed rows.
-  auto stage_chunk = [&](int p, int cl) __attribute__((always_inline)) { return PER_ELEM ? p * pc + cl : p * pc + wave * CPW + cl; };
+  auto stage_chunk = [&](int p, int cl) __attribute__((always_inline)) { return PW ? p * pc + wave * CPW + cl : p * pc + cl; };
   auto stage_base = [&](int p) __attribute__((always_inline)) {
-    return lds + (size_t)(PER_ELEM ? (phases > 1 ? (p & 1) : 0) : wave) * lay.buf_stride;
+    return lds + (size_t)(PW ? wave : (phases > 1 ? (p & 1) : 0)) * lay.buf_stride;
   };
 
   // ---- small operands of a phase: x, g_idx slice, scale/zero rows.  The loads
@@ -303,13 +313,13 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
     }
   };
   i32x4_t gr[PER_ELEM ? GP : 1];
-  const int gpieces = pc * 8;                        // 4 rows per piece
+  const int gpieces = sc * 8;                        // 4 rows per piece
   auto load_g = [&](int p) __attribute__((always_inline)) {
     if constexpr (PER_ELEM) {
 #pragma unroll
       for (int i = 0; i < GP; ++i) {
-        const int e = tid + i * nthreads;
-        const int k = 32 * p * pc + 4 * e;           // row within the split
+        const int e = st + i * sn;
+        const int k = 32 * stage_chunk(p, 0) + 4 * e;   // row within the split
         const int kk = (e < gpieces && k < 32 * C) ? 32 * c0 + k : 0;
         if (a.g_idx) gr[i] = *reinterpret_cast<const i32x4_t*>(a.g_idx + kk);
         else gr[i] = i32x4_t{kk / a.group_size, (kk + 1) / a.group_size, (kk + 2) / a.group_size,
@@ -363,9 +373,9 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       uint16_t* gl = reinterpret_cast<uint16_t*>(base + lay.gidx_off);
 #pragma unroll
       for (int i = 0; i < GP; ++i) {
-        const int e = tid + i * nthreads;
+        const int e = st + i * sn;
         if (e < gpieces) {
-          const bool ok = 32 * p * pc + 4 * e < 32 * C;
+          const bool ok = 32 * stage_chunk(p, 0) + 4 * e < 32 * C;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             int g = ok ? gr[i][r] : 0;
@@ -393,7 +403,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   uint32_t tz0[TQ], tz1[TQ];
   const uint32_t* qz = reinterpret_cast<const uint32_t*>(a.qzeros);
   auto table_quad = [&](int rows, int e0, int i, int& r, int& c4) __attribute__((always_inline)) {
-    const int e = e0 + st + i * sn;
+    const int e = e0 + tst + i * tsn;
     r = e / (TN / 4);
     c4 = e - r * (TN / 4);
     return e < rows * (TN / 4);
@@ -401,7 +411,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   auto load_table = [&](auto group_of_row, int rows, int e0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
-      if (i > 0 && e0 + i * sn >= rows * (TN / 4)) break;   // wave-uniform: no quad of this round left
+      if (i > 0 && e0 + i * tsn >= rows * (TN / 4)) break;   // wave-uniform: no quad of this round left
       int r, c4;
       const bool in = table_quad(rows, e0, i, r, c4);
       const int nn = n0 + 4 * c4;
@@ -428,7 +438,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   auto store_table = [&](unsigned char* tw, auto group_of_row, int rows, int e0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
-      if (i > 0 && e0 + i * sn >= rows * (TN / 4)) break;
+      if (i > 0 && e0 + i * tsn >= rows * (TN / 4)) break;
       int r, c4;
       if (!table_quad(rows, e0, i, r, c4)) continue;
       const bool real = group_of_row(r) < a.G && n0 + 4 * c4 < a.N;
@@ -587,7 +597,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
     for (int v = 0; v < 4; ++v) {
       half2_t pr = pairs4 ? half2_t{xv[2 * v], xv[2 * v + 1]}
                           : half2_t{xv[Block<BITS>::F[2 * v]], xv[Block<BITS>::F[2 * v + 1]]};
-      if (Block<BITS>::MUL[v] != 1) {                // a constant per unrolled v
+      if (!PER_ELEM && Block<BITS>::MUL[v] != 1) {   // a constant per unrolled v
         const _Float16 inv = (_Float16)(1.0f / (float)Block<BITS>::MUL[v]);
         pr = pr * half2_t{inv, inv};
       }
@@ -639,10 +649,11 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
     for (int j = 0; j < CPL; ++j) w1j[j] = L == 2 ? word_of<CPL>(w1[set][L == 2 ? u : 0], j) : 0u;
 
     if constexpr (PER_ELEM) {
-      const int cl = wave * CPW + u;
+      const int cl = PW ? u : wave * CPW + u;        // the chunk's place in its staging region
       const _Float16* frag = reinterpret_cast<const _Float16*>(base);
       // rows >= M of A only feed rows >= M of D, which are never used
-      const half8_t A = *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + min(q, M - 1)) << 3));
+      const half8_t A = XD ? direct_A(u)
+                           : *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + min(q, M - 1)) << 3));
       // per-row scale and zero: the block's 8 rows each carry their own group
       const uint16_t* gl = reinterpret_cast<const uint16_t*>(base + lay.gidx_off);
       typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
@@ -902,25 +913,30 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       load_table(whole_table, a.G, e0);
       store_table(tw, whole_table, a.G, e0);
     }
-    // ---- per phase: stage (one barrier), compute, issue the next phase
-    for (int p = 0; p < phases; ++p) {
-      store_stage(p);
-      __syncthreads();
-      int row = 0, rem = 0;
-      compute_range(p, U0{}, UE{}, row, rem);
-      if (p + 1 < phases) issue(p + 1);
+    if constexpr (!PW) {
+      // ---- per phase: stage (one barrier), compute, issue the next phase
+      for (int p = 0; p < phases; ++p) {
+        store_stage(p);
+        __syncthreads();
+        int row = 0, rem = 0;
+        compute_range(p, U0{}, UE{}, row, rem);
+        if (p + 1 < phases) issue(p + 1);
+      }
     }
-  } else {
+  }
+  if constexpr (PW) {
     // ---- per phase (staging wave-local): while the second half of phase p's
     // run is computed, the next phase's small operands and first half of
     // words are in flight; its second half is issued once the first half of
     // the register set is free.  So the bytes a wave has in flight stay at
     // about one run, and compute overlaps the memory stream.  The last phase
     // is peeled off so that every issued load is consumed and every wait is
-    // exact (no branch between a load and its use).
-    issue(0);
+    // exact (no branch between a load and its use).  The per-element path
+    // has issued phase 0 already and passes one barrier, for its table.
+    if constexpr (!PER_ELEM) issue(0);
     store_stage(0);
-    wave_fence();
+    if constexpr (PER_ELEM) __syncthreads();
+    else wave_fence();
     int p = 0;
     for (; p + 1 < phases; ++p) {
       int row = 0, rem = mod_pos(c0 + stage_chunk(p, 0), cpg);

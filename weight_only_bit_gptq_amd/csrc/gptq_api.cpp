@@ -95,10 +95,9 @@ bool decode_candidate(int bits, int M, int N, int K, int G, bool per_elem, int c
   const int C = K / 32;
   const int cpg = per_elem ? 1 : (K / G) / 32;
   if (!gptq::decode_cpw_allowed(bits, per_elem, cpl, cpw, M, bf16)) return false;
-  // x staged per phase (one row, or the per-element path): the staging
-  // registers bound the chunks per wave; several rows on the fast path load
-  // their A fragments directly (no staging)
-  const bool x_direct = M > 1 && !per_elem && !bf16;
+  // x staged per phase (one row, or bfloat16): the staging registers bound
+  // the chunks per wave; several rows (fp16) load their A fragments directly
+  const bool x_direct = M > 1 && !bf16;
   if (!x_direct && cpw * M > 16 * gptq::decode_max_x_pieces(M)) return false;
   if (nw < 1 || 64 * nw > gptq::decode_max_threads_for(bits, per_elem, cpl, cpw, M)) return false;
   const int cks = (C + ks - 1) / ks;
@@ -170,14 +169,20 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
   // for 2/4-bit layers from N = 8192 on (32-column otherwise), 8 or 4 waves,
   // whichever pads K less (8 on a tie), two K splits for N <= 4096 with
   // K >= 8192 -- the fastest shapes of MI355X sweeps at M = 4 and 16, where
-  // the general rules below are up to 40% slower
-  if (tiled && M > 1 && !per_elem && waves == 0 && N / 16 >= kCUs / 2) {
+  // the general rules below are up to 40% slower.  Two-word blocks (3 and 8
+  // bits) and the per-element path (either layout, several rows): 32-column
+  // tiles of 4 waves, three K splits for K >= 8192 (3-bit act-order layers at
+  // M = 16, sorted or not: the fastest shape of the sweeps on both shapes,
+  // 10-13% ahead of the next on 13824 -> 5120)
+  const bool two_word = bits == 3 || bits == 8;
+  if (((tiled && !per_elem) || (per_elem && !bf16)) && M > 1 && waves == 0 && N / 16 >= kCUs / 2) {
     const int C = K / 32;
-    const int cpl = (bits == 2 || bits == 4) && N >= 8192 ? 4 : 2;
-    const int ks = (allow_split && N <= 4096 && K >= 8192) ? 2 : 1;
+    const bool narrow = two_word || per_elem;
+    const int cpl = !narrow && N >= 8192 ? 4 : 2;
+    const int ks = !allow_split ? 1 : narrow ? (K >= 8192 ? 3 : 1) : (N <= 4096 && K >= 8192 ? 2 : 1);
     const int cks = (C + ks - 1) / ks;
     const int waste8 = (cks + 63) / 64 * 64 - cks, waste4 = (cks + 31) / 32 * 32 - cks;
-    const int nw = waste4 < waste8 ? 4 : 8;
+    const int nw = narrow ? 4 : waste4 < waste8 ? 4 : 8;
     size_t lds;
     if (decode_candidate(bits, M, N, K, G, per_elem, cpl, nw, 8, ks, &best, &lds, bf16, ws_cap)) {
       apply_choice(best, M, K, G, per_elem, bf16, a);

@@ -66,6 +66,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama7b_w4g128_hbm_traffic
 MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_mlp70b_mfma_util.txt")
 DECODE_PMC_FILE = os.path.join(ROOT, "profiles", "decode_all_instructions_and_stalls.txt")
 DECODE_PMC_GROUPS = ("decode", "decode_other")
+DECODE_TRACE_FILE = os.path.join(ROOT, "profiles", "decode_llama7b_w4g128_kernel_trace.txt")
+PREFILL_TRACE_FILE = os.path.join(ROOT, "profiles", "prefill_mlp70b_kernel_trace.txt")
+TRACE_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -f csv -d D/trace -o run -- python3 R/bench.py "
+             "--steps 50 --warmup 10 --prefill-steps 3 --no-cpu-baseline --no-checkpoint-layout --no-bf16 --no-other "
+             "> D/trace_bench.log; python3 R/bench.py --summarize-trace D/trace/run_kernel_stats.csv D/trace_bench.log")
 # sources that decide the decode kernel's code and launch shapes
 DECODE_SOURCES = ["weight_only_bit_gptq_amd/csrc/decode.hip", "weight_only_bit_gptq_amd/csrc/gptq_device.hpp",
                   "weight_only_bit_gptq_amd/csrc/gptq_kernels.hpp", "weight_only_bit_gptq_amd/csrc/gptq_api.cpp"]
@@ -112,6 +117,9 @@ def parse():
                    help="only launch each 70B-MLP prefill layer twice, for a rocprofv3 --pmc pass")
     p.add_argument("--summarize-prefill-pmc", nargs=2, metavar=("COUNTER_CSV", "TRACE_CSV"),
                    help="write the prefill MFMA-utilisation summary to profiles/ from a --pmc-prefill-driver pass")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"),
+                   help="write the decode and prefill kernel-trace summaries to profiles/ from a rocprofv3 "
+                        "--kernel-trace --stats run of this bench (TRACE_CMD) and that run's output")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the HBM traffic summary from two counter passes (no GPU needed)")
     return p.parse_args()
@@ -690,7 +698,7 @@ def summarize_prefill_pmc(counter_csv, trace_csv):
     vals = {}
     with open(counter_csv) as f:
         for r in csv.DictReader(f):
-            if "prefill_kernel" in r["Kernel_Name"]:
+            if "gptq::prefill_" in r["Kernel_Name"]:
                 d = vals.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
                 d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     dur = {}
@@ -733,6 +741,58 @@ def summarize_prefill_pmc(counter_csv, trace_csv):
     with open(MFMA_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_trace(stats_csv, bench_log):
+    """Kernel durations of the decode and prefill launches from rocprofv3's
+    kernel statistics, next to the same run's HIP-event figures."""
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3))
+    with open(bench_log) as f:
+        bench = json.loads([l for l in f if l.startswith("{")][-1])
+    avg = {n: a for n, c, a, mi, ma in rows}
+
+    def table(filt):
+        out = ["kernel | calls | average us | min us | max us"]
+        out += [f"{n} | {c} | {a:.2f} | {mi:.2f} | {ma:.2f}" for n, c, a, mi, ma in rows if filt(n)]
+        return out
+
+    def full(desc):
+        return "void " + desc.split(" grid=")[0] + "(gptq::GemmArgs)"
+
+    rf = bench["roofline"]
+    dec = ["# Kernel durations of the decode kernel, Llama-7B-shaped decode layers (M=1, 4-bit, group 128,",
+           "# symmetric, GPTQv1, qweight in the tiled layout), one MI355X; rocprofv3 kernel-trace statistics.",
+           "# Command (R = repository root, D = output folder): " + TRACE_CMD,
+           f"# sources_sha256 {decode_sources_hash()}", "#"]
+    dec += table(lambda n: "gptq::decode_kernel" in n)
+    dec += ["", "# Same layers timed by bench.py in the profiled run (HIP events on the launch stream; several",
+            "# layers share an instantiation, whose rocprofv3 average mixes them):",
+            "layer | kernel | bench us | rocprofv3 average us of its instantiation | read ceiling us"]
+    for l in rf["per_layer"]:
+        dec.append(f"{l['layer']} | {l['kernel']} | {l['us']:.2f} | {avg.get(full(l['kernel']), float('nan')):.2f} | "
+                   f"{l.get('read_ceiling_us', float('nan'))}")
+    mean_r = float(np.mean([avg.get(full(l["kernel"]), float("nan")) for l in rf["per_layer"]]))
+    mean_b = float(np.mean([l["us"] for l in rf["per_layer"]]))
+    dec.append(f"# four layers: rocprofv3 mean of the instantiations {mean_r:.3f} us, bench mean {mean_b:.3f} us; "
+               f"achieved {rf['achieved']} GB/s ({100 * rf['frac']:.1f}% of 8 TB/s), step value {bench['value']} GB/s")
+    with open(DECODE_TRACE_FILE, "w") as f:
+        f.write("\n".join(dec) + "\n")
+    pre = ["# Kernel durations of the prefill kernels, 70B-MLP shapes at M=2048 (4-bit g128 sym v1 and 8-bit g128",
+           "# asym v2; K=8192->N=28672 and K=28672->N=8192, tiled layout), one MI355X; rocprofv3 kernel-trace",
+           "# statistics (no warm-up of the clocks under the profiler: the HIP-event figures below had one).",
+           "# Command (R = repository root, D = output folder): " + TRACE_CMD, "#"]
+    pre += table(lambda n: "gptq::prefill_" in n)
+    pre += ["", "# bench.py (profiled run, HIP events): " + "; ".join(
+        f"{p['workload']} {p['layer']} {p['kernel'].split(' grid')[0]} {p['ms']} ms {p['TFLOPs']} TFLOP/s "
+        f"({100 * p['frac']:.1f}% of 2.5 PFLOP/s)" for p in bench.get("prefill") or [])]
+    with open(PREFILL_TRACE_FILE, "w") as f:
+        f.write("\n".join(pre) + "\n")
+    print("\n".join(dec))
+    print("\n".join(pre))
 
 
 def summarize_pmc(fetch_csv, write_csv):
@@ -814,6 +874,9 @@ def main():
         return
     if args.summarize_decode_pmc:
         summarize_decode_pmc(args.summarize_decode_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

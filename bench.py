@@ -106,7 +106,9 @@ def parse():
     p.add_argument("--no-other", action="store_true", help="skip decode_other and moe")
     p.add_argument("--cpu-sample-cols", type=int, default=12288,
                    help="columns of the qkv layer the CPU oracle processes (default: all)")
-    p.add_argument("--cpu-reps", type=int, default=3, help="oracle calls on the sample (median reported)")
+    p.add_argument("--cpu-reps", type=int, default=3, help="at least this many oracle calls on the sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="repeat the oracle on the sample until this much time has passed (median reported)")
     p.add_argument("--pmc-driver", action="store_true",
                    help="only launch each decode layer 3 times and a plain copy, for a rocprofv3 --pmc pass")
     p.add_argument("--pmc-decode-driver", action="store_true",
@@ -492,7 +494,8 @@ def cpu_baseline(args):
     W = np.ascontiguousarray(d.W[:, :ncols])
     L = oracle.quantize_layer(W, wl.bits, wl.group_size, wl.sym, wl.is_v2)
     t_dq, t_mm = [], []
-    for _ in range(max(1, args.cpu_reps)):
+    t_start = time.perf_counter()
+    while len(t_dq) < max(1, args.cpu_reps) or time.perf_counter() - t_start < args.cpu_seconds:
         t0 = time.perf_counter()
         Wh = oracle.dequant_ref(L.qweight, L.qzeros, L.scales, None, wl.bits, wl.group_size, wl.is_v2,
                                 layer.K, ncols)

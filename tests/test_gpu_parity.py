@@ -686,3 +686,25 @@ def test_quantize_bit_exact(dev, bits, sym, is_v2, act):
         assert np.array_equal(qw.cpu().numpy(), L.qweight), (K, N, gs, "qweight")
         assert np.array_equal(qz.cpu().numpy(), L.qzeros), (K, N, gs, "qzeros")
         assert np.array_equal(sc.cpu().numpy().view(np.uint16), L.scales.view(np.uint16)), (K, N, gs, "scales")
+
+
+# ------------------------------------------------------------------ read ceiling
+@pytest.mark.parametrize("nbytes", [0, 16, 8192, 8192 + 48, 3 * 8192 - 16, (1 << 20) + 4096 + 16])
+def test_read_ceiling_reads_and_leaves_sink(dev, nbytes):
+    """gptq_read_ceiling only reads: on a buffer of repeated words its keep-alive
+    store never fires, whatever the ragged length (whole and partial 8 KiB
+    workgroup spans), and the buffer is untouched."""
+    buf = torch.full(((1 << 20) // 4 + 2048,), 0x3C003C00, dtype=torch.int32, device=dev)
+    sink = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    gq.read_ceiling(buf, nbytes, sink=sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == -7
+    assert bool((buf == 0x3C003C00).all())
+
+
+def test_read_ceiling_rejects_bad_arguments(dev):
+    buf = torch.zeros(1024, dtype=torch.int32, device=dev)
+    with pytest.raises(gq.GptqError):
+        gq.read_ceiling(buf, 24)                           # not a multiple of 16 bytes
+    with pytest.raises(gq.GptqError):
+        gq.read_ceiling(buf[2:], 16)                       # not 16-byte aligned

@@ -386,14 +386,16 @@ def bench_decode_other(torch, gq, args, dev, outputs, skip_checkpoint):
     return res
 
 
-def bench_moe(torch, gq, args, dev):
-    """Grouped decode (gptq_moe_gemm) on a Mixtral-class expert layer: 8 experts
-    4096 -> 14336, 4-bit g128 sym v1, 16 tokens routed top-2 (seeded), weight
-    copies rotated past the Infinity Cache.  Reports weight GB/s over the
-    experts that received tokens (all of them read once per launch)."""
+def bench_moe(torch, gq, args, dev, tokens):
+    """Grouped GEMM (gptq_moe_gemm) on a Mixtral-class expert layer: 8 experts
+    4096 -> 14336, 4-bit g128 sym v1, `tokens` tokens routed top-2 (seeded),
+    weight copies rotated past the Infinity Cache.  16 tokens (at most 16 rows
+    per expert: the decode kernel) report weight GB/s over the experts that
+    received tokens (all of them read once per launch); 2048 tokens (hundreds
+    of rows per expert: the grouped prefill kernel) report TFLOP/s as well."""
     E, K, N, bits, gs = 8, 4096, 14336, 4, 128
     rng = np.random.default_rng(0)
-    picks = np.array([rng.choice(E, size=2, replace=False) for _ in range(16)]).ravel()
+    picks = np.array([rng.choice(E, size=2, replace=False) for _ in range(tokens)]).ravel()
     counts = np.bincount(picks, minlength=E)
     offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=dev)
     T = int(counts.sum())
@@ -413,7 +415,7 @@ def bench_moe(torch, gq, args, dev):
     copies = max(2, -(-ROTATE_BYTES // (E * layer_bytes(K, N, bits, gs))))
     sets = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
     mt = int(counts.max())
-    n = max(MIN_LAUNCHES, copies)
+    n = max(MIN_LAUNCHES, copies) if mt <= 16 else copies
     g = capture(torch, dev, [lambda i=i: gq.moe_gemm(x, *sets[i % copies], None, offsets, mt, bits, gs, False, out=out)
                              for i in range(n)])
     warm(torch, g.replay, args.warm_seconds)
@@ -421,11 +423,18 @@ def bench_moe(torch, gq, args, dev):
     us = ms * 1e3 / n
     del g, sets, base
     torch.cuda.empty_cache()
-    ceil_us = time_read_ceiling(torch, gq, wbytes, dev, args)
-    return {"workload": "mixtral_expert_w1_w4g128", "experts": E, "K": K, "N": N, "tokens": 16, "top_k": 2,
-            "active_experts": active, "us": round(us, 2), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
-            "frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4), "read_ceiling_us": round(ceil_us, 2),
-            "of_ceiling": round(ceil_us / us, 4)}
+    res = {"workload": "mixtral_expert_w1_w4g128", "experts": E, "K": K, "N": N, "tokens": tokens, "top_k": 2,
+           "active_experts": active, "max_rows_per_expert": mt,
+           "kernel": "decode (blocks of 16 rows)" if mt <= 16 else "prefill (128-row tiles per expert)",
+           "us": round(us, 2), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
+           "frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if mt <= 16:
+        ceil_us = time_read_ceiling(torch, gq, wbytes, dev, args)
+        res.update(read_ceiling_us=round(ceil_us, 2), of_ceiling=round(ceil_us / us, 4))
+    else:
+        tflops = 2.0 * T * K * N / (us * 1e-6) / 1e12
+        res.update(TFLOPs=round(tflops, 1), mfma_frac=round(tflops / MFMA_F16_PEAK_TFLOPS, 4))
+    return res
 
 
 # ---------------------------------------------------------------- prefill
@@ -918,12 +927,14 @@ def main():
         print(f"# decode (checkpoint layout): {dec_ck['ms_per_step'] * 1e3:.2f} us/step, layers: {dec_ck['layers']}",
               file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-    dec_other = moe = None
+    dec_other = moe = moe_prefill = None
     if not args.no_other:
         dec_other = bench_decode_other(torch, gq, args, dev, outputs, args.no_checkpoint_layout)
         print(f"# other decode calls: {dec_other}", file=sys.stderr, flush=True)
-        moe = bench_moe(torch, gq, args, dev)
+        moe = bench_moe(torch, gq, args, dev, 16)
         print(f"# moe: {moe}", file=sys.stderr, flush=True)
+        moe_prefill = bench_moe(torch, gq, args, dev, 2048)
+        print(f"# moe (prefill batch): {moe_prefill}", file=sys.stderr, flush=True)
     prefill = prefill_ck = None
     if not args.no_prefill:
         prefill = bench_prefill(torch, gq, args, dev, "prefill", outputs)
@@ -983,6 +994,7 @@ def main():
         "decode_checkpoint": None if dec_ck is None else decode_summary(dec_ck),
         "decode_other": dec_other,
         "moe": moe,
+        "moe_prefill": moe_prefill,
         "prefill": prefill,
         "prefill_checkpoint": prefill_ck,
         "bf16": bf16,

@@ -323,7 +323,7 @@ GPTQ_API int gptq_dequant_bf16(const int32_t* qweight, const int32_t* qzeros, co
                                void* w_out, void* stream);
 
 /*
- * Grouped (mixture-of-experts) decode GEMM: for every expert e,
+ * Grouped (mixture-of-experts) GEMM: for every expert e,
  *   out[r, :] = x[r, :] . dequant(expert e's weights)   for r in [off[e], off[e+1])
  * i.e. one gptq_gemm per expert over the tokens routed to it, in one launch
  * (page "Weight-only INT4 quantization: GPTQ, AWQ and the Marlin kernel",
@@ -335,20 +335,32 @@ GPTQ_API int gptq_dequant_bf16(const int32_t* qweight, const int32_t* qzeros, co
  *   expert_offsets  int32 [E+1] device: expert e's rows are [off[e], off[e+1]),
  *                   nondecreasing, off[0] = 0, off[E] <= T (values are clamped
  *                   to [0, T], so bad offsets never reach outside x / out)
- *   max_tokens_per_expert  host bound on off[e+1] - off[e]: the launch covers
- *                   that many rows per expert in blocks of 16; rows beyond it
- *                   are not computed (their out rows are left as they were)
+ *   max_tokens_per_expert  host bound on off[e+1] - off[e]: only the first
+ *                   max_tokens_per_expert rows of each expert are computed;
+ *                   rows beyond them keep their out contents
  *   out             fp16 [T, N]; rows of no expert are left as they were.
  * Same bits / group_size / is_v2 / N / K rules and alignment as gptq_gemm.
- * Uses the decode kernel (blocks of up to 16 rows, MFMA with rows padded to
- * 16), so it suits per-expert token counts of decode batches; allocates
- * nothing; deterministic.  T == 0 or max_tokens_per_expert == 0 launches
- * nothing.
+ * Batches of up to 16 rows per expert (max_tokens_per_expert <= 16) run the
+ * decode kernel (one block of up to 16 rows per expert, MFMA with rows padded
+ * to 16); larger ones the prefill kernel in 128-row tiles per expert (each
+ * tile reads its expert's weights once).  Allocates nothing;
+ * deterministic.  T == 0 or max_tokens_per_expert == 0 launches nothing.
  */
 GPTQ_API int gptq_moe_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
                            const int32_t* g_idx, const int32_t* expert_offsets, int n_experts,
                            int max_tokens_per_expert, int bits, int group_size, int is_v2, int64_t T, int64_t N,
                            int64_t K, void* out, void* stream);
+
+/*
+ * gptq_moe_gemm with the kernel chosen by the caller: path 0 = as
+ * gptq_moe_gemm, 1 = the decode kernel (blocks of 16 rows) whatever the batch,
+ * 2 = the prefill kernel (128-row tiles) whatever the batch.  Other path values
+ * give GPTQ_ERR_BAD_ARG.  Results of either kernel meet the gptq_gemm bar.
+ */
+GPTQ_API int gptq_moe_gemm_ex(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                              const int32_t* g_idx, const int32_t* expert_offsets, int n_experts,
+                              int max_tokens_per_expert, int bits, int group_size, int is_v2, int64_t T,
+                              int64_t N, int64_t K, void* out, void* stream, int path);
 
 /*
  * Memory-read reference for the decode kernels: reads `bytes` bytes at buf

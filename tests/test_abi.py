@@ -31,7 +31,7 @@ def test_header_declares_api():
     for f in ("gptq_gemm", "gptq_gemm_ex", "gptq_dequant", "gptq_gemm_check", "gptq_gemm_ex_check",
               "gptq_gemm_describe", "gptq_dequant_check", "gptq_convert_zeros", "gptq_convert_zeros_check",
               "gptq_repack_tiled", "gptq_unrepack_tiled", "gptq_gemm_tiled", "gptq_gemm_tiled_ex",
-              "gptq_gemm_tiled_describe", "gptq_moe_gemm", "gptq_sort_act_order", "gptq_gemm_sorted",
+              "gptq_gemm_tiled_describe", "gptq_moe_gemm", "gptq_moe_gemm_ex", "gptq_sort_act_order", "gptq_gemm_sorted",
               "gptq_gemm_bf16", "gptq_gemm_bf16_ex", "gptq_gemm_bf16_describe", "gptq_dequant_bf16",
               "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
@@ -180,6 +180,11 @@ def test_moe_argument_codes():
     assert mo(off=OFF + 2) == -5
     assert mo(T=0, x=None, o=None) == 0               # nothing to do, nothing launched
     assert mo(mt=0) == 0
+    mx = lambda path, **kw: lib.gptq_moe_gemm_ex(X, QW, QZ, SC, None, kw.get("off", OFF), 8, kw.get("mt", 16), 4, 128,
+                                                  1, 32, 4096, 4096, OUT, None, path)
+    assert mx(-1) == -9 and mx(3) == -9               # path out of range
+    assert mx(1, off=None) == -1 and mx(2, off=None) == -1
+    assert mx(2, mt=0) == 0 and mx(1, mt=0) == 0
 
 
 def test_sorted_argument_codes():

@@ -546,6 +546,61 @@ def test_moe_gemm_bounds(dev):
     assert_close(out2, ref)
 
 
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("bits,gs,act", [(4, 128, False), (4, 32, False), (3, 128, True), (8, 128, False),
+                                         (2, 64, False)])
+def test_moe_gemm_paths_parity(dev, path, bits, gs, act):
+    """Both grouped kernels on prefill-sized batches: the decode kernel (blocks
+    of 16 rows) and the prefill kernel (128-row tiles per expert: several row
+    tiles, a partial one, an empty expert, a one-row expert, a column tile
+    past N).  Rows of no expert keep their contents."""
+    E, K, N = 6, 768, 288
+    counts = [130, 0, 37, 200, 1, 64]
+    experts, x, offsets = moe_problem(E, K, N, counts, bits, gs, act, seed=bits * 17 + gs + path)
+    xt, qw, qz, sc, gi, off = moe_upload(experts, x, offsets, act, dev)
+    T = x.shape[0]
+    xt = torch.cat([xt, torch.ones((3, K), dtype=torch.float16, device=dev)])
+    out = torch.full((T + 3, N), 7.0, dtype=torch.float16, device=dev)
+    gq.moe_gemm(xt, qw, qz, sc, gi, off, max(counts), bits, gs, True, out=out, path=path)
+    ref = oracle.moe_gemm_ref(x, [(L.qweight, L.qzeros, L.scales, L.g_idx) for L in experts], offsets, bits, gs,
+                              True, K, N)
+    assert_close(out[:T], ref, f"path {path}")
+    assert bool((out[T:] == 7.0).all())
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_moe_gemm_row_cap(dev, path):
+    """max_tokens_per_expert that is not a multiple of the kernel's row block
+    (16) or tile (128): exactly each expert's first 100 rows are computed."""
+    E, K, N, bits, gs = 3, 256, 96, 4, 128
+    counts = [130, 20, 200]
+    experts, x, offsets = moe_problem(E, K, N, counts, bits, gs, False, seed=21 + path)
+    xt, qw, qz, sc, gi, off = moe_upload(experts, x, offsets, False, dev)
+    ref = oracle.moe_gemm_ref(x, [(L.qweight, L.qzeros, L.scales, None) for L in experts], offsets, bits, gs,
+                              True, K, N)
+    out = torch.full((x.shape[0], N), 7.0, dtype=torch.float16, device=dev)
+    gq.moe_gemm(xt, qw, qz, sc, None, off, 100, bits, gs, True, out=out, path=path)
+    done = np.zeros(x.shape[0], dtype=bool)
+    for e in range(E):
+        done[offsets[e]:offsets[e] + min(100, counts[e])] = True
+    rows = torch.from_numpy(np.nonzero(done)[0]).to(dev)
+    assert_close(out[rows], ref[done])
+    assert bool((out[torch.from_numpy(np.nonzero(~done)[0]).to(dev)] == 7.0).all())
+
+
+def test_moe_gemm_auto_path(dev):
+    """Path 0 runs the decode kernel up to 16 rows per expert and the prefill
+    kernel above: bit-identical to the forced path either way."""
+    E, K, N, bits, gs = 4, 512, 256, 4, 128
+    for counts in ([16, 3, 0, 9], [17, 3, 0, 9]):
+        experts, x, offsets = moe_problem(E, K, N, counts, bits, gs, False, seed=33)
+        xt, qw, qz, sc, gi, off = moe_upload(experts, x, offsets, False, dev)
+        mt = max(counts)
+        outs = [gq.moe_gemm(xt, qw, qz, sc, None, off, mt, bits, gs, True, path=p) for p in (0, 1, 2)]
+        want = outs[1] if mt <= 16 else outs[2]
+        assert torch.equal(outs[0].view(torch.int16), want.view(torch.int16)), counts
+
+
 def test_moe_gemm_full_size_mixtral(dev):
     """Mixtral-class expert FFN shape (4096 -> 14336, 8 experts, 16 tokens x
     top-2 routing), 4-bit g128: sampled columns against the oracle."""

@@ -94,6 +94,8 @@ def library() -> ctypes.CDLL:
         lib.gptq_gemm_sorted.restype = i32
         lib.gptq_moe_gemm.argtypes = [vp, i32p, i32p, vp, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, vp, vp]
         lib.gptq_moe_gemm.restype = i32
+        lib.gptq_moe_gemm_ex.argtypes = lib.gptq_moe_gemm.argtypes + [i32]
+        lib.gptq_moe_gemm_ex.restype = i32
         lib.gptq_repack_tiled.argtypes = [i32p, i32p, i32, i64, i64, vp]
         lib.gptq_repack_tiled.restype = i32
         lib.gptq_unrepack_tiled.argtypes = [i32p, i32p, i32, i64, i64, vp]
@@ -416,11 +418,13 @@ def gemm_sorted(x, qweight_sorted, qzeros, scales, perm, bits: int, group_size: 
 
 
 def moe_gemm(x, qweight, qzeros, scales, g_idx: Optional[object], expert_offsets, max_tokens_per_expert: int,
-             bits: int, group_size: int, is_v2: bool, *, out=None):
-    """Grouped decode GEMM: rows [off[e], off[e+1]) of x (tokens sorted by
-    expert) times expert e's weights.  qweight [E, K*bits/32, N], qzeros
+             bits: int, group_size: int, is_v2: bool, *, out=None, path: int = 0):
+    """Grouped GEMM: rows [off[e], off[e+1]) of x (tokens sorted by expert)
+    times expert e's weights.  qweight [E, K*bits/32, N], qzeros
     [E, G, N*bits/32], scales [E, G, N], g_idx [E, K] or None, expert_offsets
-    int32 [E+1] on the GPU.  Rows of no expert keep out's previous contents."""
+    int32 [E+1] on the GPU.  Rows of no expert keep out's previous contents.
+    path: 0 = by batch size (gptq_moe_gemm), 1 = decode kernel, 2 = prefill
+    kernel (gptq_moe_gemm_ex)."""
     import torch
     if qweight.dim() != 3 or qzeros.dim() != 3 or scales.dim() != 3:
         raise ValueError("qweight, qzeros, scales must be [E, ...] stacks")
@@ -447,10 +451,10 @@ def moe_gemm(x, qweight, qzeros, scales, g_idx: Optional[object], expert_offsets
             raise ValueError(f"out must be [{T}, {N}]")
     lib = library()
     with torch.cuda.device(dev):
-        code = lib.gptq_moe_gemm(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
-                                 None if g_idx is None else g_idx.data_ptr(), expert_offsets.data_ptr(), E,
-                                 int(max_tokens_per_expert), int(bits), int(group_size), int(bool(is_v2)), T, N, K,
-                                 out.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+        code = lib.gptq_moe_gemm_ex(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                                    None if g_idx is None else g_idx.data_ptr(), expert_offsets.data_ptr(), E,
+                                    int(max_tokens_per_expert), int(bits), int(group_size), int(bool(is_v2)), T, N,
+                                    K, out.data_ptr(), torch.cuda.current_stream(dev).cuda_stream, int(path))
     _raise(code)
     return out
 

@@ -191,14 +191,16 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
   int unit = blockIdx.x;
   if (a.n_experts > 0) {
     // grouped decode: (expert, block of up to 16 of its rows, column tile);
-    // blocks without rows leave at once (the expert's rows are clamped to M)
+    // blocks without rows leave at once (the expert's rows are clamped to M
+    // and to its first moe_rows)
     const int per_expert = a.tiles * a.moe_blocks;
     const int e = blockIdx.x / per_expert;
     const int rest = blockIdx.x - e * per_expert;
     const int b = rest / a.tiles;
     unit = rest - b * a.tiles;
-    const int r_end = min(max(a.moe_off[e + 1], 0), a.M);
-    const int r0 = min(max(a.moe_off[e], 0), a.M) + 16 * b;
+    const int e0 = min(max(a.moe_off[e], 0), a.M);
+    const int r_end = min(min(max(a.moe_off[e + 1], 0), a.M), e0 + min(a.moe_rows, a.M));
+    const int r0 = e0 + 16 * b;
     const int rows = min(16, r_end - r0);
     if (rows <= 0) return;
     a.M = rows;

@@ -578,13 +578,22 @@ int gptq_gemm_tiled(const void* x, const int32_t* qweight_tiled, const int32_t* 
 }
 
 namespace {
+// Grouped GEMM path: expert batches of one decode block (up to 16 rows) run
+// on the decode kernel, larger ones on the prefill kernel (128-row tiles, each
+// reading its expert's weights once, where every further block of 16 rows of
+// the decode kernel reads them again).  Measured on MI355X, 8 experts 4096 ->
+// 14336, 4-bit: decode 64 / 103 / 112 us at 16 / 24 / 32 rows per expert,
+// prefill 106 / 101 / 98 us.
+constexpr int kMoePrefillRows = 16;
+
 int moe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,
              const int32_t* expert_offsets, int n_experts, int max_tokens_per_expert, int bits, int group_size,
-             int is_v2, int64_t T, int64_t N, int64_t K, void* out, void* stream) {
+             int is_v2, int64_t T, int64_t N, int64_t K, void* out, void* stream, int path) {
   int rc = check_weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, N, K);
   if (rc != GPTQ_OK) return rc;
   if (!expert_offsets) return GPTQ_ERR_NULL_PTR;
   if (n_experts < 1 || n_experts > (1 << 16) || max_tokens_per_expert < 0) return GPTQ_ERR_BAD_ARG;
+  if (path < 0 || path > 2) return GPTQ_ERR_BAD_ARG;
   if (T < 0 || T > ((int64_t)1 << 24) || T * K >= kMaxElems || T * N >= kMaxElems) return GPTQ_ERR_BAD_SHAPE;
   if ((int64_t)n_experts * (K / 32 * bits) * N >= kMaxElems) return GPTQ_ERR_BAD_SHAPE;
   if (T == 0 || max_tokens_per_expert == 0) return GPTQ_OK;
@@ -605,17 +614,28 @@ int moe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const
   a.zero_offset = is_v2 ? 0 : 1;
   a.chunks = (int)(K / 32);
   a.zrow_words = N * bits / 32;
-  bool per_elem = (g_idx != nullptr) || (group_size % 32 != 0);
-  // launch shape for blocks of up to 16 rows, no K split (one workgroup per
-  // expert block and column tile)
-  if (decode_shape(bits, 16, a.N, a.K, a.G, 0, false, false, &per_elem, &a) != GPTQ_OK) return GPTQ_ERR_BAD_SHAPE;
   a.moe_off = expert_offsets;
   a.n_experts = n_experts;
-  a.moe_blocks = (max_tokens_per_expert + 15) / 16;
+  a.moe_rows = max_tokens_per_expert;
   a.qw_stride = K / 32 * bits * N;
   a.qz_stride = a.G * a.zrow_words;
   a.sc_stride = (int64_t)a.G * N;
   a.gi_stride = K;
+  const bool prefill = path == 2 || (path == 0 && max_tokens_per_expert > kMoePrefillRows);
+  bool per_elem;
+  if (prefill) {
+    // one launch of prefill tiles per expert: row tiles over the largest batch
+    per_elem = (g_idx != nullptr) || (group_size % 64 != 0);
+    gptq::prefill_shape(max_tokens_per_expert, a.N, false, &a.tiles_m, &a.tiles_n, &a.pbm);
+    if ((int64_t)n_experts * a.tiles_m * a.tiles_n >= ((int64_t)1 << 31)) return GPTQ_ERR_BAD_SHAPE;
+    const hipError_t err = gptq::launch_prefill(bits, per_elem, a, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
+  }
+  per_elem = (g_idx != nullptr) || (group_size % 32 != 0);
+  // launch shape for blocks of up to 16 rows, no K split (one workgroup per
+  // expert block and column tile)
+  if (decode_shape(bits, 16, a.N, a.K, a.G, 0, false, false, &per_elem, &a) != GPTQ_OK) return GPTQ_ERR_BAD_SHAPE;
+  a.moe_blocks = (max_tokens_per_expert + 15) / 16;
   if ((int64_t)n_experts * a.moe_blocks * a.tiles >= ((int64_t)1 << 31)) return GPTQ_ERR_BAD_SHAPE;
   const hipError_t err = gptq::launch_decode(bits, per_elem, a, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
@@ -694,15 +714,23 @@ int gptq_gemm_sorted(const void* x, const int32_t* qweight_sorted, const int32_t
   }
 }
 
-int gptq_moe_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
-                  const int32_t* g_idx, const int32_t* expert_offsets, int n_experts, int max_tokens_per_expert,
-                  int bits, int group_size, int is_v2, int64_t T, int64_t N, int64_t K, void* out, void* stream) {
+int gptq_moe_gemm_ex(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                     const int32_t* g_idx, const int32_t* expert_offsets, int n_experts, int max_tokens_per_expert,
+                     int bits, int group_size, int is_v2, int64_t T, int64_t N, int64_t K, void* out, void* stream,
+                     int path) {
   try {
     return moe_impl(x, qweight, qzeros, scales, g_idx, expert_offsets, n_experts, max_tokens_per_expert, bits,
-                    group_size, is_v2, T, N, K, out, stream);
+                    group_size, is_v2, T, N, K, out, stream, path);
   } catch (...) {
     return GPTQ_ERR_DEVICE;
   }
+}
+
+int gptq_moe_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                  const int32_t* g_idx, const int32_t* expert_offsets, int n_experts, int max_tokens_per_expert,
+                  int bits, int group_size, int is_v2, int64_t T, int64_t N, int64_t K, void* out, void* stream) {
+  return gptq_moe_gemm_ex(x, qweight, qzeros, scales, g_idx, expert_offsets, n_experts, max_tokens_per_expert, bits,
+                          group_size, is_v2, T, N, K, out, stream, 0);
 }
 
 int gptq_repack_tiled(const int32_t* qweight, int32_t* qweight_tiled, int bits, int64_t N, int64_t K,

@@ -46,13 +46,15 @@ struct GemmArgs {
   // qweight layout: 0 = checkpoint [K*b/32, N]; 1 = tiled [N/16][K/32][b][16]
   // (16-column tiles, each chunk's b packed rows contiguous)
   int wtiled;
-  // grouped (mixture-of-experts) decode, when n_experts > 0: expert e owns
+  // grouped (mixture-of-experts) GEMM, when n_experts > 0: expert e owns
   // rows [moe_off[e], moe_off[e + 1]) of x and out (tokens sorted by expert,
   // clamped to [0, M]) and the weights at qweight + e * qw_stride (qzeros,
-  // scales, g_idx likewise); the grid is n_experts x moe_blocks x tiles, each
-  // workgroup one block of up to 16 of its expert's rows
+  // scales, g_idx likewise).  Decode: the grid is n_experts x moe_blocks x
+  // tiles, each workgroup one block of up to 16 of its expert's rows.
+  // Prefill: n_experts x tiles_m x tiles_n, row tiles over the expert's rows.
+  // Either way only an expert's first moe_rows rows are computed.
   const int32_t* moe_off;
-  int n_experts, moe_blocks;
+  int n_experts, moe_blocks, moe_rows;
   int64_t qw_stride, qz_stride, sc_stride, gi_stride;
   // prefill launch shape: tiles_m x tiles_n workgroup tiles of pbm (128 or
   // 256) rows by 256 columns

@@ -88,11 +88,39 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  int t = blockIdx.x;
+  // workgroup -> tile t (column-major over tiles_m x tiles_n); a grouped launch
+  // first picks the expert (ntiles workgroups each)
   const int ntiles = a.tiles_m * a.tiles_n;
-  if ((ntiles & 7) == 0) t = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  int b = blockIdx.x, e = 0;
+  if (a.n_experts > 0) {
+    e = b / ntiles;
+    b -= e * ntiles;
+  }
+  int t = b;
+  if ((ntiles & 7) == 0) t = (b & 7) * (ntiles >> 3) + (b >> 3);
   const int tm = t % a.tiles_m, tn = t / a.tiles_m;
-  const int m0 = tm * BM;
+  int m0 = tm * BM;
+  if (a.n_experts > 0) {
+    // grouped (mixture-of-experts) prefill: expert e owns rows [moe_off[e],
+    // moe_off[e + 1]) of x and out (clamped to [0, M], and to its first
+    // moe_rows) and its own weights; row tile tm is rows tm BM .. of those, a
+    // tile past them leaves at once.
+    // x and out are moved to the tile's first row, M becomes its row count,
+    // so the body below runs unchanged on a tile at row 0.
+    const int e0 = min(max(a.moe_off[e], 0), a.M);
+    const int r_end = min(min(max(a.moe_off[e + 1], 0), a.M), e0 + min(a.moe_rows, a.M));
+    const int r0 = e0 + m0;
+    const int rows = min(BM, r_end - r0);
+    if (rows <= 0) return;
+    a.M = rows;
+    a.x += (int64_t)r0 * a.K;
+    a.out += (int64_t)r0 * a.N;
+    a.qweight += e * a.qw_stride;
+    a.qzeros += e * a.qz_stride;
+    a.scales += e * a.sc_stride;
+    if (a.g_idx) a.g_idx += e * a.gi_stride;
+    m0 = 0;
+  }
   const int q = lane & 31;           // A row in a subtile / B column pair
   const int kb2 = lane >> 5;         // 8-row block within a 16-row k step
   const int n = tn * kPrefillBN + wave * 64 + 2 * q;   // this lane's two columns n, n + 1
@@ -471,7 +499,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(GemmArgs a) {
 
 template <int BITS, bool PER_ELEM, bool FULL>
 static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
-  const dim3 grid(a.tiles_m * a.tiles_n);
+  const dim3 grid(a.tiles_m * a.tiles_n * (a.n_experts > 0 ? a.n_experts : 1));
   if (a.bf16) {
     if (a.wtiled) return hipErrorInvalidValue;     // bfloat16 reads the checkpoint layout only
     hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);

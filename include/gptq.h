@@ -305,8 +305,9 @@ GPTQ_API int gptq_gemm_sorted(const void* x, const int32_t* qweight_sorted, cons
  * the same W^ values as fma(q, s, -z s) in fp32, exact while |s| < 2^119 (so
  * that z s stays finite; real scales are many orders below).  Decode (M <= 16) always
  * dequantizes element by element (act order or not); prefill uses the same
- * tiles as the fp16 kernel.  Checkpoint qweight layout only (no tiled,
- * sorted or grouped variants).
+ * tiles as the fp16 kernel.  The gptq_gemm_tiled_bf16* calls take the tiled
+ * qweight layout of gptq_repack_tiled (as gptq_gemm_tiled*); there are no
+ * sorted or grouped bfloat16 variants.
  */
 GPTQ_API int gptq_gemm_bf16(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
                             const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N,
@@ -321,6 +322,17 @@ GPTQ_API int gptq_gemm_bf16_describe(const void* x, const int32_t* qweight, cons
 GPTQ_API int gptq_dequant_bf16(const int32_t* qweight, const int32_t* qzeros, const void* scales,
                                const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t N, int64_t K,
                                void* w_out, void* stream);
+GPTQ_API int gptq_gemm_tiled_bf16(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros,
+                                  const void* scales, const int32_t* g_idx, int bits, int group_size, int is_v2,
+                                  int64_t M, int64_t N, int64_t K, void* out, void* stream);
+GPTQ_API int gptq_gemm_tiled_bf16_ex(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros,
+                                     const void* scales, const int32_t* g_idx, int bits, int group_size, int is_v2,
+                                     int64_t M, int64_t N, int64_t K, void* out, void* stream, int path,
+                                     int decode_waves);
+GPTQ_API int gptq_gemm_tiled_bf16_describe(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros,
+                                           const void* scales, const int32_t* g_idx, int bits, int group_size,
+                                           int is_v2, int64_t M, int64_t N, int64_t K, const void* out, int path,
+                                           int decode_waves, char* buf, int64_t buflen);
 
 /*
  * Grouped (mixture-of-experts) GEMM: for every expert e,

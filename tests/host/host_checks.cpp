@@ -31,7 +31,7 @@ int main() {
     long long M, N, K;
     const std::string o(op);
     if (o == "gemm" || o == "gemm_ex" || o == "describe" || o == "tiled_describe" || o == "bf16_describe" ||
-        o == "gemm_call" || o == "noalloc_call") {
+        o == "tiled_bf16_describe" || o == "gemm_call" || o == "noalloc_call") {
       if (std::sscanf(line, "%*s %llx %llx %llx %llx %llx %d %d %d %lld %lld %lld %llx %d %d %d", &x, &qw, &qz, &sc,
                       &gi, &bits, &gs, &v2, &M, &N, &K, &out, &path, &waves, &buflen) != 15) {
         std::printf("parse error\n");
@@ -60,6 +60,9 @@ int main() {
         else if (o == "tiled_describe")
           rc = gptq_gemm_tiled_describe(ptr(x), iptr(qw), iptr(qz), ptr(sc), iptr(gi), bits, gs, v2, M, N, K,
                                         ptr(out), path, waves, b, bl);
+        else if (o == "tiled_bf16_describe")
+          rc = gptq_gemm_tiled_bf16_describe(ptr(x), iptr(qw), iptr(qz), ptr(sc), iptr(gi), bits, gs, v2, M, N, K,
+                                             ptr(out), path, waves, b, bl);
         else
           rc = gptq_gemm_bf16_describe(ptr(x), iptr(qw), iptr(qz), ptr(sc), iptr(gi), bits, gs, v2, M, N, K,
                                        ptr(out), path, waves, b, bl);

@@ -33,6 +33,7 @@ def test_header_declares_api():
               "gptq_repack_tiled", "gptq_unrepack_tiled", "gptq_gemm_tiled", "gptq_gemm_tiled_ex",
               "gptq_gemm_tiled_describe", "gptq_moe_gemm", "gptq_moe_gemm_ex", "gptq_sort_act_order", "gptq_gemm_sorted",
               "gptq_gemm_bf16", "gptq_gemm_bf16_ex", "gptq_gemm_bf16_describe", "gptq_dequant_bf16",
+              "gptq_gemm_tiled_bf16", "gptq_gemm_tiled_bf16_ex", "gptq_gemm_tiled_bf16_describe",
               "gptq_strerror", "gptq_release", "gptq_abi_version"):
         assert f in names
     assert declared_status() == gq.STATUS

@@ -183,8 +183,23 @@ def test_gemm_bf16_rejects_mixed_types(dev):
         gq.gemm(x_t.to(dev).half(), qw, qz, sct, gi, 4, 32, True)          # fp16 x, bf16 scales
     with pytest.raises(ValueError):
         gq.gemm(x_t.to(dev), qw, qz, sct.half(), gi, 4, 32, True)          # bf16 x, fp16 scales
-    with pytest.raises(ValueError):
-        gq.gemm(x_t.to(dev), gq.repack_tiled(qw, 4), qz, sct, gi, 4, 32, True)   # no tiled bf16
+
+
+@pytest.mark.parametrize("bits,is_v2,act,gs", list(itertools.product(BITS, (False, True), (False, True), (32, 128))))
+def test_gemm_bf16_tiled_layout(dev, bits, is_v2, act, gs):
+    """gptq_gemm_tiled_bf16: the tiled qweight layout (4-bit words in pair
+    order) through the bfloat16 decode and prefill kernels, against the oracle
+    on the checkpoint arrays."""
+    K, N = 512, 160
+    L, sc_t, sc, x_t, x = layer_bf16(K, N, 40, bits, gs, False, is_v2, act, seed=bits * 13 + gs + 5 * act)
+    qw, qz, sct, gi = upload(L, sc_t, dev)
+    qwt = gq.repack_tiled(qw, bits)
+    xt = x_t.to(dev)
+    for M in (1, 4, 16, 17, 40):
+        ref = oracle.gptq_gemm_ref(x[:M], L.qweight, L.qzeros, sc, L.g_idx, bits, gs, is_v2, K, N, act="bf16")
+        for p in ([gq.PATH_DECODE] if M <= 16 else []) + [gq.PATH_PREFILL]:
+            y = gq.gemm(xt[:M].contiguous(), qwt, qz, sct, gi, bits, gs, is_v2, path=p)
+            assert_close_bf16(y, ref, f"tiled M={M} path={p}")
 
 
 def test_gemm_bf16_describe_names_the_bf16_kernels(dev):
@@ -193,13 +208,19 @@ def test_gemm_bf16_describe_names_the_bf16_kernels(dev):
     xt = x_t.to(dev)
     assert gq.describe(xt[:1].contiguous(), qw, qz, sct, gi, 4, 128, False).startswith("gptq::decode_bf16_kernel<4, 1,")
     assert gq.describe(xt, qw, qz, sct, gi, 4, 128, False).startswith("gptq::prefill_bf16_kernel<4, false, true>")
+    qwt = gq.repack_tiled(qw, 4)
+    assert gq.describe(xt[:1].contiguous(), qwt, qz, sct, gi, 4, 128, False).startswith("gptq::decode_bf16_kernel<4,")
+    assert gq.describe(xt, qwt, qz, sct, gi, 4, 128, False).startswith("gptq::prefill_bf16_kernel<4, false, true>")
 
 
 # ------------------------------------------------------------------ full-size layers, sampled columns
-@pytest.mark.parametrize("wname,lname,M", [("llama7b_decode_w4g128", "qkv", 1), ("llama7b_decode_w4g128", "down", 1),
-                                           ("actorder_decode_w3g128", "up", 16),
-                                           ("mlp70b_prefill_w4g128", "up", 2048)])
-def test_gemm_bf16_full_size(dev, wname, lname, M):
+@pytest.mark.parametrize("wname,lname,M,tiled", [("llama7b_decode_w4g128", "qkv", 1, False),
+                                                 ("llama7b_decode_w4g128", "down", 1, False),
+                                                 ("llama7b_decode_w4g128", "gate_up", 1, True),
+                                                 ("actorder_decode_w3g128", "up", 16, False),
+                                                 ("mlp70b_prefill_w4g128", "up", 2048, False),
+                                                 ("mlp70b_prefill_w4g128", "down", 2048, True)])
+def test_gemm_bf16_full_size(dev, wname, lname, M, tiled):
     wl = WORKLOADS[wname]
     layer = next(l for l in wl.layers if l.name == lname)
     K, N = layer.K, layer.N
@@ -209,6 +230,8 @@ def test_gemm_bf16_full_size(dev, wname, lname, M):
     sc_t, sc = bf16(L.scales.astype(np.float32))
     x_t, x = bf16(d.x.astype(np.float32))
     qw, qz, sct, gi = upload(L, sc_t, dev)
+    if tiled:
+        qw = gq.repack_tiled(qw, wl.bits)
     y = gq.gemm(x_t.to(dev), qw, qz, sct, gi, wl.bits, wl.group_size, wl.is_v2)
     rng = np.random.default_rng(2)
     cols = np.unique(np.concatenate([rng.choice(N, 40, replace=False), [0, 1, N - 2, N - 1]]))

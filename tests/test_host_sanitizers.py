@@ -133,7 +133,8 @@ def test_host_code_under_sanitizers(driver):
         code = lib.gptq_gemm_ex_check(*args, a[12], a[13])
         want.append(str(code))
         for op, fn in (("describe", lib.gptq_gemm_describe), ("tiled_describe", lib.gptq_gemm_tiled_describe),
-                       ("bf16_describe", lib.gptq_gemm_bf16_describe)):
+                       ("bf16_describe", lib.gptq_gemm_bf16_describe),
+                       ("tiled_bf16_describe", lib.gptq_gemm_tiled_bf16_describe)):
             bl = rng.choice([256, 256, 256, 1, 8, 40, 0, -1])
             lines.append(fmt(op, a, bl))
             buf = ctypes.create_string_buffer(512)

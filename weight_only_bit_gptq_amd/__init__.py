@@ -69,6 +69,11 @@ def library() -> ctypes.CDLL:
         lib.gptq_gemm_bf16_describe.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp, i32,
                                                 i32, ctypes.c_char_p, i64]
         lib.gptq_dequant_bf16.argtypes = [i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, vp, vp]
+        for name in ("gptq_gemm_tiled_bf16", "gptq_gemm_tiled_bf16_ex", "gptq_gemm_tiled_bf16_describe"):
+            getattr(lib, name).restype = i32
+        lib.gptq_gemm_tiled_bf16.argtypes = gemm_args
+        lib.gptq_gemm_tiled_bf16_ex.argtypes = gemm_args + [i32, i32]
+        lib.gptq_gemm_tiled_bf16_describe.argtypes = lib.gptq_gemm_bf16_describe.argtypes
         lib.gptq_dequant.restype = i32
         lib.gptq_gemm_check.argtypes = [vp, i32p, i32p, vp, i32p, i32, i32, i32, i64, i64, i64, vp]
         lib.gptq_gemm_check.restype = i32
@@ -182,24 +187,19 @@ def _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, K=None, sd
 
 
 def _act_dtype(x, qweight):
-    """Activation type of a call: x's dtype, fp16 or (checkpoint layout only) bf16."""
+    """Activation type of a call: x's dtype, fp16 or bf16."""
     import torch
-    dt = getattr(x, "dtype", None)
-    if dt == torch.bfloat16:
-        if getattr(qweight, "dim", lambda: 2)() == 4:
-            raise ValueError("bfloat16 activations take the checkpoint qweight layout")
-        return dt
-    return torch.float16
+    return torch.bfloat16 if getattr(x, "dtype", None) == torch.bfloat16 else torch.float16
 
 
 def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_size: int,
          is_v2: bool, *, out=None, path: int = PATH_AUTO, decode_waves: int = 0):
     """out[M, N] = x[M, K] . dequant(qweight, qzeros, scales, g_idx).
 
-    x, scales and out are all fp16, or all bfloat16 (gptq_gemm_bf16; checkpoint
-    layout only).  qweight is the checkpoint layout [K*bits/32, N] or, 4-D,
-    the tiled layout made by `repack_tiled`.  Enqueued on the current HIP
-    stream of x's device (asynchronous)."""
+    x, scales and out are all fp16, or all bfloat16 (gptq_gemm_bf16,
+    gptq_gemm_tiled_bf16).  qweight is the checkpoint layout [K*bits/32, N]
+    or, 4-D, the tiled layout made by `repack_tiled`.  Enqueued on the current
+    HIP stream of x's device (asynchronous)."""
     import torch
     act = _act_dtype(x, qweight)
     dev, N, K = _weights(qweight, qzeros, scales, g_idx, bits, group_size, is_v2, sdtype=act)
@@ -217,7 +217,7 @@ def gemm(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, group_s
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         if act == torch.bfloat16:
-            fn = lib.gptq_gemm_bf16_ex
+            fn = lib.gptq_gemm_tiled_bf16_ex if qweight.dim() == 4 else lib.gptq_gemm_bf16_ex
         else:
             fn = lib.gptq_gemm_tiled_ex if qweight.dim() == 4 else lib.gptq_gemm_ex
         code = fn(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
@@ -265,7 +265,7 @@ def describe(x, qweight, qzeros, scales, g_idx: Optional[object], bits: int, gro
     buf = ctypes.create_string_buffer(256)
     lib = library()
     if act == torch.bfloat16:
-        fn = lib.gptq_gemm_bf16_describe
+        fn = lib.gptq_gemm_tiled_bf16_describe if qweight.dim() == 4 else lib.gptq_gemm_bf16_describe
     else:
         fn = lib.gptq_gemm_tiled_describe if qweight.dim() == 4 else lib.gptq_gemm_describe
     code = fn(x.data_ptr(), qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),

@@ -663,27 +663,35 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         if constexpr (BF16) {
-          // fields in the staging's order F, each with its row's (s, -z s);
-          // without g_idx and with groups of whole chunks the block's rows
-          // share one group: one table read
+          // fields in the staging's order (F, or pairs for 4-bit tiled
+          // words), each with its row's (s, -z s); without g_idx and with
+          // groups of whole chunks the block's rows share one group: one
+          // table read.  r[2v], r[2v + 1]: register v's two fields.
           const f32x2_t* tab2 = reinterpret_cast<const f32x2_t*>(lds + lay.tab_off) + CPL * q + j;
-          float f[8];
-          block_fields_f32<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], kb, f);
+          float r[8];
+          if constexpr (BITS == 4) {
+            block4_regs_f32(word_of<CPL>(w0[set][u], j), r);
+          } else {
+            float f[8];
+            block_fields_f32<BITS>(word_of<CPL>(w0[set][u], j), w1j[j], kb, f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[i] = f[Block<BITS>::F[i]];
+          }
           u32x4_t bw;
           if (rows_share_group) {
             const f32x2_t t = tab2[(int)gv[0] * TN];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int fa = Block<BITS>::F[2 * v], fb = Block<BITS>::F[2 * v + 1];
-              bw[v] = bf16_pair(__builtin_fmaf(f[fa], t[0], t[1]), __builtin_fmaf(f[fb], t[0], t[1]));
-            }
+            for (int v = 0; v < 4; ++v)
+              bw[v] = bf16_pair(__builtin_fmaf(r[2 * v], t[0], t[1]), __builtin_fmaf(r[2 * v + 1], t[0], t[1]));
           } else {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const int fa = Block<BITS>::F[2 * v], fb = Block<BITS>::F[2 * v + 1];
-              const f32x2_t ta = tab2[(int)gv[fa] * TN];
-              const f32x2_t tb = tab2[(int)gv[fb] * TN];
-              bw[v] = bf16_pair(__builtin_fmaf(f[fa], ta[0], ta[1]), __builtin_fmaf(f[fb], tb[0], tb[1]));
+              // the rows of register v's fields
+              const int ga = pairs4 ? gv[2 * v] : gv[Block<BITS>::F[2 * v]];
+              const int gb = pairs4 ? gv[2 * v + 1] : gv[Block<BITS>::F[2 * v + 1]];
+              const f32x2_t ta = tab2[ga * TN];
+              const f32x2_t tb = tab2[gb * TN];
+              bw[v] = bf16_pair(__builtin_fmaf(r[2 * v], ta[0], ta[1]), __builtin_fmaf(r[2 * v + 1], tb[0], tb[1]));
             }
           }
           accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),

@@ -775,6 +775,34 @@ int gptq_gemm_bf16_describe(const void* x, const int32_t* qweight, const int32_t
                        decode_waves, false, buf, buflen, true);
 }
 
+int gptq_gemm_tiled_bf16_ex(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros, const void* scales,
+                            const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N,
+                            int64_t K, void* out, void* stream, int path, int decode_waves) {
+  try {
+    return gemm_impl(x, qweight_tiled, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, stream, path,
+                     decode_waves, true, nullptr, true);
+  } catch (const std::bad_alloc&) {
+    return GPTQ_ERR_NO_MEM;
+  } catch (...) {
+    return GPTQ_ERR_DEVICE;
+  }
+}
+
+int gptq_gemm_tiled_bf16(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros, const void* scales,
+                         const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
+                         void* out, void* stream) {
+  return gptq_gemm_tiled_bf16_ex(x, qweight_tiled, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out,
+                                 stream, 0, 0);
+}
+
+int gptq_gemm_tiled_bf16_describe(const void* x, const int32_t* qweight_tiled, const int32_t* qzeros,
+                                  const void* scales, const int32_t* g_idx, int bits, int group_size, int is_v2,
+                                  int64_t M, int64_t N, int64_t K, const void* out, int path, int decode_waves,
+                                  char* buf, int64_t buflen) {
+  return describe_impl(x, qweight_tiled, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
+                       decode_waves, true, buf, buflen, true);
+}
+
 namespace {
 int dequant_impl(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx, int bits,
                  int group_size, int is_v2, int64_t N, int64_t K, void* w_out, void* stream, bool bf16) {

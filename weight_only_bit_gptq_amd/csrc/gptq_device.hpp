@@ -276,6 +276,18 @@ __device__ __forceinline__ void block_fields_f32(uint32_t w0, uint32_t w1, int k
   }
 }
 
+// A 4-bit block's fields in MFMA register order, for either qweight layout:
+// r[2v], r[2v + 1] are the nibbles at bits 4v and 16 + 4v, i.e. fields
+// (v, v + 4) of a checkpoint word (the unpack order F) or (2v, 2v + 1) of a
+// tiled word, whose fields are stored in pair order.
+__device__ __forceinline__ void block4_regs_f32(uint32_t w, float r[8]) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    r[2 * v] = (float)((w >> (4 * v)) & 0xFu);
+    r[2 * v + 1] = (float)((w >> (16 + 4 * v)) & 0xFu);
+  }
+}
+
 // Two fp32 values -> a bfloat16 pair (low half = a), round to nearest even.
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));

@@ -64,7 +64,7 @@ void prefill_shape(int M, int N, bool big_ok, int* tiles_m, int* tiles_n, int* b
 // multiplier 1, 16, 1, 16 for both halves) instead of four byte permutes.
 template <int BITS, bool PER_ELEM, bool FULL, bool BF16, bool PAIRS, int BM>
 __device__ __forceinline__ void prefill_body(GemmArgs a) {
-  static_assert(!PAIRS || (BITS == 4 && !BF16), "pair-order words: 4-bit fp16");
+  static_assert(!PAIRS || BITS == 4, "pair-order words: 4-bit");
   static_assert(BM == 128 || BM == 256, "workgroup tile rows");
   constexpr int BK = kPrefillBK;
   constexpr int MS = BM / 32;                       // 32-row MFMA subtiles per wave
@@ -280,8 +280,9 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   };
   // B fragment j of block kb from the words, bfloat16 with one (s, -z s)
   auto make_B_bf16 = [&](uint32_t w0j, uint32_t w1j, int kb, float s, float c) __attribute__((always_inline)) {
-    float f[8];
-    block_fields_f32<BITS>(w0j, w1j, kb, f);
+    float f[8];                                      // fields in k order
+    if constexpr (PAIRS) block4_regs_f32(w0j, f);    // a pair-order word's register order is k order
+    else block_fields_f32<BITS>(w0j, w1j, kb, f);
     u32x4_t bw;
 #pragma unroll
     for (int v = 0; v < 4; ++v) bw[v] = bf16_pair(__builtin_fmaf(f[2 * v], s, c), __builtin_fmaf(f[2 * v + 1], s, c));
@@ -360,8 +361,9 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
             // each row its own group: (s, -z s) per field
             const uint16_t* scb = reinterpret_cast<const uint16_t*>(a.scales);
             const int k0 = kt * BK + 16 * s + 8 * kb2;
-            float f[8];
-            block_fields_f32<BITS>(w0j, w1j, kb, f);
+            float f[8];                              // fields in k order
+            if constexpr (PAIRS) block4_regs_f32(w0j, f);
+            else block_fields_f32<BITS>(w0j, w1j, kb, f);
             u32x4_t bw;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -492,17 +494,19 @@ __global__ __launch_bounds__(256, 1) void prefill_big_kernel(GemmArgs a) {
   prefill_body<BITS, false, FULL, false, PAIRS, 256>(a);
 }
 
-template <int BITS, bool PER_ELEM, bool FULL>
+template <int BITS, bool PER_ELEM, bool FULL, bool PAIRS>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(GemmArgs a) {
-  prefill_body<BITS, PER_ELEM, FULL, true, false, 128>(a);
+  prefill_body<BITS, PER_ELEM, FULL, true, PAIRS, 128>(a);
 }
 
 template <int BITS, bool PER_ELEM, bool FULL>
 static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(a.tiles_m * a.tiles_n * (a.n_experts > 0 ? a.n_experts : 1));
   if (a.bf16) {
-    if (a.wtiled) return hipErrorInvalidValue;     // bfloat16 reads the checkpoint layout only
-    hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL>), grid, dim3(256), 0, stream, a);
+    if (BITS == 4 && a.wtiled)                     // pair-order words
+      hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL, BITS == 4>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL, false>), grid, dim3(256), 0, stream, a);
   } else if (a.pbm == 256) {
     if constexpr (PER_ELEM) {
       return hipErrorInvalidValue;                 // 256-row tiles: fast path only

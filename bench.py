@@ -946,8 +946,11 @@ def main():
     if not args.no_bf16:
         torch.cuda.empty_cache()
         dec_bf = bench_decode_step(torch, gq, args, dev, "bf16_decode", outputs)
+        dec_bft = bench_decode_step(torch, gq, args, dev, "bf16_decode_tiled", outputs)
         bf16 = {"decode": {"workload": dec_bf["wl"].name + " with bf16 x and scales (checkpoint layout)",
                            **decode_summary(dec_bf)},
+                "decode_tiled": {"workload": dec_bft["wl"].name + " with bf16 x and scales (tiled layout)",
+                                 **decode_summary(dec_bft)},
                 "prefill": None if args.no_prefill else bench_prefill(torch, gq, args, dev, "bf16_prefill", outputs)}
         print(f"# bf16: {bf16}", file=sys.stderr, flush=True)
     cpu = parity = None

@@ -55,7 +55,7 @@ def describe_case(lib, case):
     gi = GI if (wl.act_order and case.entry == "gemm") else None
     buf = ctypes.create_string_buffer(256)
     if case.act == "bf16":
-        fn = lib.gptq_gemm_bf16_describe
+        fn = lib.gptq_gemm_tiled_bf16_describe if case.layout == "tiled" else lib.gptq_gemm_bf16_describe
     else:
         fn = lib.gptq_gemm_tiled_describe if case.layout == "tiled" else lib.gptq_gemm_describe
     code = fn(X, QW, QZ, SC, gi, wl.bits, wl.group_size, int(wl.is_v2), case.M, layer.N, layer.K, OUT, 0, 0,

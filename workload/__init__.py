@@ -130,7 +130,9 @@ BENCH_CASES: List[BenchCase] = (
     + _cases("prefill", "mlp70b_prefill_w8g128", [2048], "tiled")
     + _cases("prefill_checkpoint", "mlp70b_prefill_w4g128", [2048], "checkpoint")
     + _cases("bf16_decode", "llama7b_decode_w4g128", [1], "checkpoint", act="bf16")
+    + _cases("bf16_decode_tiled", "llama7b_decode_w4g128", [1], "tiled", act="bf16")
     + _cases("bf16_prefill", "mlp70b_prefill_w4g128", [2048], "checkpoint", act="bf16")
+    + _cases("bf16_prefill", "mlp70b_prefill_w4g128", [2048], "tiled", act="bf16")
 )
 
 

@@ -657,6 +657,16 @@ def summarize_decode_pmc(paths):
         if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals:
             d["mfma_busy_over_gpu_cycles_x_simds"] = round(
                 vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] / MI355X_XCDS * 1024), 4)
+        # L2 side: bytes the L2 served to the CUs (32-byte sectors) over the
+        # call's weight bytes (qweight + qzeros + scales): what x and the
+        # tables add on top of one read of the weights, re-reads included
+        wbytes = layer_bytes(layer.K, layer.N, wl.bits, wl.group_size)
+        if "TCC_READ_SECTORS_sum" in vals:
+            d["l2_read_bytes_over_weight_bytes"] = round(32 * vals["TCC_READ_SECTORS_sum"] / wbytes, 3)
+        if "TCC_HIT_sum" in vals and "TCC_MISS_sum" in vals and vals["TCC_HIT_sum"] + vals["TCC_MISS_sum"] > 0:
+            d["l2_hit_rate"] = round(vals["TCC_HIT_sum"] / (vals["TCC_HIT_sum"] + vals["TCC_MISS_sum"]), 3)
+        if "TCP_TCC_READ_REQ_sum" in vals:
+            d["l1_to_l2_read_requests_per_kib_of_weights"] = round(vals["TCP_TCC_READ_REQ_sum"] / (wbytes / 1024), 2)
         d["raw"] = {n: round(v, 1) for n, v in vals.items() if n != "kernel"}
         rows.append(d)
     lines = [
@@ -668,9 +678,14 @@ def summarize_decode_pmc(paths):
         "#   rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_INSTS_VMEM_RD SQ_INSTS_SALU "
         "SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -d D/p2 -o run -f csv -- python3 R/bench.py "
         "--pmc-decode-driver",
-        "#   python3 R/bench.py --summarize-decode-pmc D/p1/run_counter_collection.csv D/p2/run_counter_collection.csv",
+        "#   rocprofv3 --pmc TCC_READ_SECTORS_sum TCC_HIT_sum TCC_MISS_sum TCP_TCC_READ_REQ_sum -d D/p3 -o run -f csv "
+        "-- python3 R/bench.py --pmc-decode-driver",
+        "#   python3 R/bench.py --summarize-decode-pmc D/p1/run_counter_collection.csv D/p2/run_counter_collection.csv "
+        "D/p3/run_counter_collection.csv",
         "# x_lane_per_weight = 64 * instructions / (K * N): lane-instructions per weight element.",
         "# *_over_wave_cycles: cycles waves spent waiting / issuing, over all wave cycles.",
+        "# l2_read_bytes_over_weight_bytes = 32 * TCC_READ_SECTORS / (qweight + qzeros + scales bytes): what the L2",
+        "# served the CUs, over one read of the weights (x and re-reads on top); l2_hit_rate = hits / (hits + misses).",
     ]
     for d in rows:
         lines.append(d["case"] + " | " + d["kernel"].split("(")[0].replace("void ", "") + " | " +

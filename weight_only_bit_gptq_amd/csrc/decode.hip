@@ -361,14 +361,22 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       *reinterpret_cast<half8_t*>(frag + (((cl * 4 + kbe) * M + m) << 3)) = av;
       // one-row instantiation: the chunk's (with FOLD > 1 the fold block's)
       // sum of x (x' MUL) for the zero term; lanes 4 cl .. 4 cl + 3 hold
-      // chunk cl, so a block of FOLD chunks is 4 FOLD aligned lanes.  The
-      // multi-row instantiation gets its sums from an MFMA at compute time
+      // chunk cl, so a block of FOLD chunks is 4 FOLD aligned lanes of one
+      // 16-lane row.  Summed into the block's last lane by DPP row shifts
+      // (lanes shifted in from outside the row read 0): the same pairwise
+      // sums as a butterfly of lane swaps, without their LDS round trips
+      // (measured on MI355X: the Llama-7B step 1.7% faster).  The multi-row
+      // instantiation gets its sums from an MFMA at compute time
       if constexpr (!PER_ELEM && !kSumsByMfma) {
-        xs += __shfl_xor(xs, 1);
-        xs += __shfl_xor(xs, 2);
-        if constexpr (FOLD >= 2) xs += __shfl_xor(xs, 4);
-        if constexpr (FOLD >= 4) xs += __shfl_xor(xs, 8);
-        if (kbe == 0 && cl % FOLD == 0) corr[(cl / FOLD) * Mp + m] = xs;
+        auto shr = [](float v, auto n_c) __attribute__((always_inline)) {
+          return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                      0x110 + decltype(n_c)::value, 0xF, 0xF, true));
+        };
+        xs += shr(xs, std::integral_constant<int, 1>{});     // row_shr:1
+        xs += shr(xs, std::integral_constant<int, 2>{});
+        if constexpr (FOLD >= 2) xs += shr(xs, std::integral_constant<int, 4>{});
+        if constexpr (FOLD >= 4) xs += shr(xs, std::integral_constant<int, 8>{});
+        if (kbe == 3 && cl % FOLD == FOLD - 1) corr[(cl / FOLD) * Mp + m] = xs;
       }
     }
     if constexpr (PER_ELEM) {

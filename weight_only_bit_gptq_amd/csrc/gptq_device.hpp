@@ -281,10 +281,14 @@ __device__ __forceinline__ void block_fields_f32(uint32_t w0, uint32_t w1, int k
 // (v, v + 4) of a checkpoint word (the unpack order F) or (2v, 2v + 1) of a
 // tiled word, whose fields are stored in pair order.
 __device__ __forceinline__ void block4_regs_f32(uint32_t w, float r[8]) {
+  // even nibbles (0, 2, 4, 6) and odd nibbles (1, 3, 5, 7) spread to bytes:
+  // every field is then one byte-to-float conversion
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t nib[8] = {lo, hi, lo >> 8, hi >> 8, lo >> 16, hi >> 16, lo >> 24, hi >> 24};   // nibble i in byte 0
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    r[2 * v] = (float)((w >> (4 * v)) & 0xFu);
-    r[2 * v + 1] = (float)((w >> (16 + 4 * v)) & 0xFu);
+    r[2 * v] = (float)(nib[v] & 0xFFu);
+    r[2 * v + 1] = (float)(nib[v + 4] & 0xFFu);
   }
 }
 

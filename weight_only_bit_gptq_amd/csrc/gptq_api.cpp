@@ -598,6 +598,8 @@ int moe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const
   if ((int64_t)n_experts * (K / 32 * bits) * N >= kMaxElems) return GPTQ_ERR_BAD_SHAPE;
   if (T == 0 || max_tokens_per_expert == 0) return GPTQ_OK;
   if (!x || !out) return GPTQ_ERR_NULL_PTR;
+  // an expert has at most T rows: a looser bound only adds empty blocks
+  max_tokens_per_expert = (int)std::min<int64_t>(max_tokens_per_expert, T);
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(expert_offsets, 4)) return GPTQ_ERR_MISALIGNED;
   gptq::GemmArgs a{};
   a.x = static_cast<const _Float16*>(x);

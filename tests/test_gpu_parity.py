@@ -201,6 +201,25 @@ def test_decode_block_fold(dev, bits, gs, M, K, N, waves, tiled):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), desc
 
 
+@pytest.mark.parametrize("bits,gs,K,N", [(4, 128, 2048, 4096), (2, 64, 2048, 8192), (3, 128, 2048, 2048),
+                                         (8, 128, 1024, 2048), (4, 32, 1024, 16384)])
+def test_decode_tiled_short_k_four_waves(dev, bits, gs, K, N):
+    """Tiled layout, one row, K <= 2048: the planner takes 4 waves of 16
+    chunks (no wave without chunks; 8 waves would leave half their slots
+    empty); oracle parity on every column, repeated calls bit-identical."""
+    d, L = quantized(K, N, 1, bits, gs, True, False, False, seed=K + N + bits)
+    qw, qz, sc, gi = upload(L, dev)
+    qw = gq.repack_tiled(qw, bits)
+    x = torch.from_numpy(d.x).to(dev)
+    desc = gq.describe(x, qw, qz, sc, gi, bits, gs, False)
+    assert desc.startswith("gptq::decode_kernel") and " block=256 " in desc and "phases=1 " in desc, desc
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, False, K, N)
+    y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False)
+    y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, False)
+    assert_close(y1, ref, desc)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), desc
+
+
 SPLIT_CASES = [(4, 128, 1, 8192, 512, False), (4, 128, 3, 8192, 96, False), (8, 128, 7, 8192, 512, True),
                (2, 64, 4, 12288, 1024, False), (3, 128, 16, 13824, 640, True), (4, 128, 1, 11008, 1024, False),
                (3, 32, 2, 9216, 352, False), (4, 128, 16, 8192, 1536, False)]

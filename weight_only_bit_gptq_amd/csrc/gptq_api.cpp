@@ -160,11 +160,13 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
   // tiled layout, M = 1, full-width: 16 chunks per wave over 16-column tiles
   // (32-column tiles from N = 16384 on) were the fastest or within 2% of it
   // on every Llama-7B decode layer in MI355X sweeps, where the general rules
-  // below lose up to 10%; the wave count (8..16) keeps the fewest rounds of
-  // resident workgroups, then pads K the least, then takes the fewest
-  // phases, then the fewest waves (8 when K is a multiple of 4096: one phase,
+  // below lose up to 10%; the wave count (8..16, also 4 for K <= 2048) keeps
+  // the fewest rounds of resident workgroups, then pads K the least, then
+  // takes the fewest phases, then the fewest waves (8 when K is a multiple of
+  // 4096: one phase,
   // no padding; 11 for K = 11008 at N = 4096: 2 phases of 176 chunks for 344,
-  // 5% faster than 8 waves in 3 phases of 128)
+  // 5% faster than 8 waves in 3 phases of 128; 4 for K = 2048: one phase with
+  // no padded waves, 11-12% faster than 8 at N = 4096, 2- and 4-bit)
   // tiled layout, 2..16 rows, full-width: 8 chunks per wave, 64-column tiles
   // for 2/4-bit layers from N = 8192 on (32-column otherwise), 8 or 4 waves,
   // whichever pads K less (8 on a tie), two K splits for N <= 4096 with
@@ -193,7 +195,8 @@ bool decode_plan_for(int bits, int M, int N, int K, int G, int waves, bool per_e
     size_t lds;
     const bool wide = N >= 16384;
     int64_t best_slots = 0;
-    for (int nw = 8; nw <= 16; ++nw) {
+    // 4 waves only where 8 would leave half of their chunk slots empty
+    for (int nw = K / 32 <= 64 ? 4 : 8; nw <= 16; nw += nw == 4 ? 4 : 1) {
       DecodeChoice c;
       if (!decode_candidate(bits, M, N, K, G, per_elem, wide ? 2 : 1, nw, 16, 1, &c, &lds, bf16, ws_cap)) continue;
       const int64_t slots = (int64_t)c.phases * nw * 16;

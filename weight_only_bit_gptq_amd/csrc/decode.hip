@@ -616,7 +616,6 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
     }
     return av;
   };
-  const uint32_t* full_tab = reinterpret_cast<const uint32_t*>(lds + lay.tab_off);
   const int kbc = MV == 1 ? 0 : min(kb, Mp / 4 - 1);  // rows 4 kbc + v of the correction sums
 
   // fast path: a chunk's LDS operands (A fragment, sum of x, the group row's

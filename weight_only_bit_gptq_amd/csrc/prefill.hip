@@ -427,7 +427,6 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   // the next tile's stay in flight, barrier (every wave's x pieces are in LDS
   // and the stage of tile kt - 1 is free), issue tile kt + 2, compute tile kt
   auto step = [&](int kt, auto set_c, auto next_c) __attribute__((always_inline)) {
-    constexpr int set = decltype(set_c)::value;
     if constexpr (PER_ELEM) {
       // one register set: the words of tile kt were the last loads issued
       __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);

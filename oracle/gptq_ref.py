@@ -51,8 +51,10 @@ def fp16_rne(a) -> np.ndarray:
     """Round fp64 values to fp16, nearest-even; subnormals kept, overflow -> inf.
 
     numpy converts float64 to float16 directly (one rounding), which is the
-    rounding the dequant formula needs [P1-WQ]."""
-    return np.asarray(a, dtype=np.float64).astype(np.float16)
+    rounding the dequant formula needs [P1-WQ].  Overflow to inf is the
+    intended result, so numpy's overflow warning is silenced."""
+    with np.errstate(over="ignore"):
+        return np.asarray(a, dtype=np.float64).astype(np.float16)
 
 
 _BF16_MAX = float.fromhex("0x1.fep127")    # largest finite bfloat16, (2 - 2^-7) 2^127

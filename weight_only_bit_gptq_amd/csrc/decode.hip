@@ -136,7 +136,9 @@ __host__ __device__ inline DecodeLayout decode_layout(int M, int pc, int nw, int
   L.corr_off = frag;
   const size_t corr = (per_elem || xdirect) ? 0 : align16((size_t)chunks * decode_corr_rows(M) * 4);
   L.gidx_off = frag + corr;
-  const size_t gidx = per_elem ? align16((size_t)chunks * 32 * 2) : 0;
+  // per-element path: each row's byte offset of its group's table row (4
+  // bytes per row, so that a lookup is one add to the lane's column offset)
+  const size_t gidx = per_elem ? align16((size_t)chunks * 32 * 4) : 0;
   L.ptab_off = L.gidx_off + gidx;
   // fast path: the groups a run of cpw consecutive chunks can touch
   L.ptab_rows = per_elem ? 0 : div_pos(cpw - 1, cpg) + 2;
@@ -380,18 +382,22 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       }
     }
     if constexpr (PER_ELEM) {
-      uint16_t* gl = reinterpret_cast<uint16_t*>(base + lay.gidx_off);
+      // row -> byte offset of its group's row in the whole table (groups
+      // clamped into [0, G))
+      u32x4_t* gl = reinterpret_cast<u32x4_t*>(base + lay.gidx_off);
 #pragma unroll
       for (int i = 0; i < GP; ++i) {
         const int e = st + i * sn;
         if (e < gpieces) {
           const bool ok = 32 * stage_chunk(p, 0) + 4 * e < 32 * C;
+          u32x4_t go;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             int g = ok ? gr[i][r] : 0;
             g = g < 0 ? 0 : (g >= a.G ? a.G - 1 : g);
-            gl[4 * e + r] = (uint16_t)g;
+            go[r] = (uint32_t)g * (uint32_t)(TN * (BF16 ? 8 : 4));
           }
+          gl[e] = go;
         }
       }
     }
@@ -663,10 +669,11 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
       // rows >= M of A only feed rows >= M of D, which are never used
       const half8_t A = XD ? direct_A(u)
                            : *reinterpret_cast<const half8_t*>(frag + (((cl * 4 + kb) * M + min(q, M - 1)) << 3));
-      // per-row scale and zero: the block's 8 rows each carry their own group
-      const uint16_t* gl = reinterpret_cast<const uint16_t*>(base + lay.gidx_off);
-      typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
-      const u16x8_t gv = *reinterpret_cast<const u16x8_t*>(gl + 32 * cl + 8 * kb);
+      // per-row scale and zero: the block's 8 rows each carry their own group,
+      // staged as the byte offset of the group's table row
+      const u32x4_t* gl = reinterpret_cast<const u32x4_t*>(base + lay.gidx_off) + 8 * cl + 2 * kb;
+      const u32x4_t gv0 = gl[0], gv1 = gl[1];
+      const uint32_t gv[8] = {gv0[0], gv0[1], gv0[2], gv0[3], gv1[0], gv1[1], gv1[2], gv1[3]};
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         if constexpr (BF16) {
@@ -674,7 +681,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
           // words), each with its row's (s, -z s); without g_idx and with
           // groups of whole chunks the block's rows share one group: one
           // table read.  r[2v], r[2v + 1]: register v's two fields.
-          const f32x2_t* tab2 = reinterpret_cast<const f32x2_t*>(lds + lay.tab_off) + CPL * q + j;
+          const unsigned char* tab2 = lds + lay.tab_off + (size_t)(CPL * q + j) * 8;
           float r[8];
           if constexpr (BITS == 4) {
             block4_regs_f32(word_of<CPL>(w0[set][u], j), r);
@@ -686,7 +693,7 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
           }
           u32x4_t bw;
           if (rows_share_group) {
-            const f32x2_t t = tab2[(int)gv[0] * TN];
+            const f32x2_t t = *reinterpret_cast<const f32x2_t*>(tab2 + gv[0]);
 #pragma unroll
             for (int v = 0; v < 4; ++v)
               bw[v] = bf16_pair(__builtin_fmaf(r[2 * v], t[0], t[1]), __builtin_fmaf(r[2 * v + 1], t[0], t[1]));
@@ -694,10 +701,10 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               // the rows of register v's fields
-              const int ga = pairs4 ? gv[2 * v] : gv[Block<BITS>::F[2 * v]];
-              const int gb = pairs4 ? gv[2 * v + 1] : gv[Block<BITS>::F[2 * v + 1]];
-              const f32x2_t ta = tab2[ga * TN];
-              const f32x2_t tb = tab2[gb * TN];
+              const uint32_t ga = pairs4 ? gv[2 * v] : gv[Block<BITS>::F[2 * v]];
+              const uint32_t gb = pairs4 ? gv[2 * v + 1] : gv[Block<BITS>::F[2 * v + 1]];
+              const f32x2_t ta = *reinterpret_cast<const f32x2_t*>(tab2 + ga);
+              const f32x2_t tb = *reinterpret_cast<const f32x2_t*>(tab2 + gb);
               bw[v] = bf16_pair(__builtin_fmaf(r[2 * v], ta[0], ta[1]), __builtin_fmaf(r[2 * v + 1], tb[0], tb[1]));
             }
           }
@@ -719,10 +726,10 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
         const unsigned char* tab_lane = lds + lay.tab_off + (size_t)(CPL * q) * 4;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int ga = pairs4 ? gv[2 * v] : gv[Block<BITS>::F[2 * v]];
-          const int gb = pairs4 ? gv[2 * v + 1] : gv[Block<BITS>::F[2 * v + 1]];
-          const wvec ea = *reinterpret_cast<const wvec*>(tab_lane + ga * (TN * 4));
-          const wvec eb = *reinterpret_cast<const wvec*>(tab_lane + gb * (TN * 4));
+          const uint32_t ga = pairs4 ? gv[2 * v] : gv[Block<BITS>::F[2 * v]];
+          const uint32_t gb = pairs4 ? gv[2 * v + 1] : gv[Block<BITS>::F[2 * v + 1]];
+          const wvec ea = *reinterpret_cast<const wvec*>(tab_lane + ga);
+          const wvec eb = *reinterpret_cast<const wvec*>(tab_lane + gb);
           const _Float16 inv = (_Float16)(1.0f / (float)Block<BITS>::MUL[v]);
           const _Float16 off = (_Float16)(-kMagic / (float)Block<BITS>::MUL[v]);
 #pragma unroll

@@ -72,7 +72,7 @@ struct GemmArgs {
 struct DecodeLayout {
   size_t buf_stride;        // bytes of one phase buffer
   size_t corr_off;          // correction sums inside a buffer (fast path)
-  size_t gidx_off;          // uint16 g_idx slice inside a buffer (per-element path)
+  size_t gidx_off;          // per-row table byte offsets of a buffer's chunks (per-element path)
   size_t ptab_off;          // the phase's scale/zero rows inside a buffer (fast path)
   int ptab_rows;            // groups a phase covers (fast path)
   size_t tab_off;           // whole scale/zero table (per-element path)

@@ -150,6 +150,10 @@ def test_tiled_describe_shapes():
     for (bits, gs, M, K, N, want) in ((4, 128, 1, 4096, 12288, "<4, false, 1, 1, 16, 4> grid=768 block=512"),
                                       (4, 128, 1, 4096, 22016, "<4, false, 1, 2, 16, 4> grid=688 block=512"),
                                       (4, 128, 1, 11008, 4096, "<4, false, 1, 1, 16, 4> grid=256 block=704 phases=2"),
+                                      # K <= 2048: 4 waves of 16 chunks, no empty chunk slots
+                                      (4, 128, 1, 2048, 4096, "<4, false, 1, 1, 16, 4> grid=256 block=256 phases=1"),
+                                      (2, 64, 1, 2048, 16384, "<2, false, 1, 2, 16, 2> grid=512 block=256 phases=1"),
+                                      (4, 128, 1, 3072, 4096, "<4, false, 1, 1, 16, 4> grid=256 block=512 phases=1"),
                                       (2, 64, 16, 4096, 12288, "<2, false, 4, "),
                                       (3, 128, 16, 5120, 13824, "<3, false, 4, ")):
         assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, bits, gs, 1, M, N, K, OUT, 0, 0, buf, 256) == 0

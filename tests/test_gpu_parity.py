@@ -245,6 +245,75 @@ def test_decode_split_k(dev, bits, gs, M, K, N, act):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), desc
 
 
+PREFILL_SPLIT_CASES = [
+    # bits, gs, M, K, N, act, tiled: small-M prefill grids whose tiles split K
+    # (fast path, per-element path through act order and 32-row groups, a K
+    # with a last half k tile, two-word blocks, ragged rows and columns)
+    (4, 128, 17, 4096, 1024, False, True), (4, 128, 64, 2048, 512, False, False),
+    (3, 128, 33, 4096, 256, True, False), (8, 128, 20, 2048, 768, False, True),
+    (2, 64, 50, 4096, 512, False, False), (4, 32, 40, 2048, 256, False, False),
+    (4, 32, 24, 2080, 288, False, True), (3, 128, 130, 8192, 160, False, True),
+    # more splits than one round of the reduction's loads reads (15)
+    (4, 128, 17, 16384, 256, False, False)]
+
+
+@pytest.mark.parametrize("bits,gs,M,K,N,act,tiled", PREFILL_SPLIT_CASES)
+def test_prefill_split_k(dev, bits, gs, M, K, N, act, tiled):
+    """Prefill launches whose grid of output tiles is small split K over
+    several workgroups per tile (the last to arrive adds the fp32 partial sums
+    in split order): oracle parity on every column, bit-identical repeated
+    calls, a second call that rewrites every output (counters re-armed), and
+    the same result from a graph captured after the stream has its workspace,
+    replayed three times."""
+    d, L = quantized(K, N, M, bits, gs, False, True, act, seed=K + 7 * N + M)
+    qw, qz, sc, gi = upload(L, dev)
+    if tiled:
+        qw = gq.repack_tiled(qw, bits)
+    x = torch.from_numpy(d.x).to(dev)
+    desc = gq.describe(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_PREFILL)
+    assert desc.startswith("gptq::prefill_kernel") and int(desc.split("k_splits=")[1]) > 1, desc
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, True, K, N)
+    y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_PREFILL)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_PREFILL, out=out)
+    assert_close(y1, ref, desc)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), desc
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        gq.gemm(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_PREFILL)   # the stream's workspace
+    s.synchronize()
+    outg = torch.zeros((M, N), dtype=torch.float16, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gq.gemm(x, qw, qz, sc, gi, bits, gs, True, path=gq.PATH_PREFILL, out=outg)
+    for _ in range(3):
+        outg.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outg.view(torch.int16), y1.view(torch.int16)), desc
+
+
+def test_prefill_split_k_full_size_small_batch(dev):
+    """Llama-7B qkv at 17 and 128 rows (tiled layout, the automatic plan: the
+    prefill kernel with K split 11 and 2 ways): oracle parity on sampled
+    columns, computed one by one."""
+    wl = WORKLOADS["llama7b_decode_w4g128"]
+    layer = wl.layers[0]
+    d = draw_workload_layer(wl, layer, 128, seed=3)
+    L = oracle.quantize_layer(d.W, wl.bits, wl.group_size, wl.sym, wl.is_v2, d.g_idx)
+    qw, qz, sc, gi = upload(L, dev)
+    qw = gq.repack_tiled(qw, wl.bits)
+    cols = np.unique(np.concatenate([np.arange(0, layer.N, 97), [layer.N - 1]]))
+    for M in (17, 128):
+        x = torch.from_numpy(d.x[:M]).to(dev)
+        desc = gq.describe(x, qw, qz, sc, gi, wl.bits, wl.group_size, wl.is_v2)
+        assert int(desc.split("k_splits=")[1]) > 1, desc
+        ref = oracle.gptq_gemm_ref(d.x[:M], L.qweight, L.qzeros, L.scales, None, wl.bits, wl.group_size, wl.is_v2,
+                                   layer.K, layer.N, cols=cols)
+        y = gq.gemm(x, qw, qz, sc, gi, wl.bits, wl.group_size, wl.is_v2)
+        assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, desc)
+
+
 def test_decode_split_k_alternating_shapes(dev):
     """Split-K calls of different shapes (different partial-sum sizes and tile
     counts) alternate on one stream and share its workspace; every call must

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -66,7 +67,8 @@ constexpr int64_t kInflightCap = 13ll << 20;
 constexpr int kNoDecodePlan = 1;
 constexpr int kMinSplitChunks = 32;                  // a K split covers at least 1024 rows
 constexpr int kMinSplitK = 8192;                     // ... of a K this long (shorter: not worth the reduction)
-constexpr int64_t kSplitWsCap = 16ll << 20;          // fp32 partial sums of all splits, bytes
+constexpr int64_t kSplitWsCap = 16ll << 20;          // fp32 partial sums of all splits, bytes (decode)
+constexpr int64_t kPrefillSplitWsCap = 64ll << 20;   // ... of a prefill launch
 
 struct DecodeChoice {
   int rounds;
@@ -259,11 +261,43 @@ int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_spl
   return kNoDecodePlan;                              // the scale/zero table does not fit LDS
 }
 
+// Prefill split K for small grids of 128-row tiles (small M, or N of a few
+// thousand columns): the tiles split K and the last split of a tile to
+// arrive adds the fp32 partial sums.  A workgroup's k tiles run as a chain of
+// about 0.9 us each when few workgroups share a CU (MFMA and dequant of one
+// wave per SIMD), and the last workgroup of a tile reads back ks * M rows of
+// partial sums, so the split count balances the two: ks ~ sqrt(32 k_tiles /
+// M), about 0.75 workgroups per CU in all, at least 4 k tiles (256 rows) per
+// split.  Measured on MI355X (4-bit, 4096 -> 4096 / 12288 / 22016 and
+// 11008 -> 4096, M = 17 .. 512, split counts 1 .. 12): within 10% of the best
+// count on every shape, and 1.2-5.6x faster than one split for M <= 256.
+// No split with 256-row tiles or in a grouped launch.
+constexpr int kPrefillMinSplitTiles = 4;
+
+void plan_prefill_split(gptq::GemmArgs* a, bool allow_split, int64_t ws_cap) {
+  a->ks = 1;
+  a->cks = a->chunks;
+  const int tiles = a->tiles_m * a->tiles_n;
+  if (!allow_split || a->pbm != 128) return;
+  const int ktiles = (a->K + 63) / 64;
+  int ks = (int)std::lround(std::sqrt(32.0 * ktiles / std::max(a->M, 1)));
+  ks = std::min({ks, (3 * kCUs / 4) / tiles, ktiles / kPrefillMinSplitTiles});
+  ks = (int)std::min<int64_t>(ks, ws_cap / ((int64_t)a->M * a->N * 4));
+  if (ks < 2) return;                                 // (at most 96 tiles: their counters always fit)
+  const int per = (ktiles + ks - 1) / ks;              // k tiles per split
+  a->ks = (ktiles + per - 1) / per;                    // no empty split
+  a->cks = 2 * per;                                    // in 32-row chunks
+  if (a->ks < 2) {
+    a->ks = 1;
+    a->cks = a->chunks;
+  }
+}
+
 // Argument checks plus kernel choice and launch shape: pure host code.
 int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
               const void* out, int path, int decode_waves, bool tiled, gptq::GemmArgs* a, bool* use_decode,
-              bool* per_elem, bool allow_split = true, bool bf16 = false, int64_t ws_cap = kSplitWsCap) {
+              bool* per_elem, bool allow_split = true, bool bf16 = false, int64_t ws_cap = kPrefillSplitWsCap) {
   if (path < 0 || path > 2 || decode_waves < 0 || decode_waves > 16) return GPTQ_ERR_BAD_ARG;
   int rc = check_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out);
   if (rc != GPTQ_OK) return rc;
@@ -292,14 +326,22 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
     // the fast path does not carry over)
     *per_elem = bf16 || (g_idx != nullptr) || (group_size % 32 != 0);
     const int rc2 = decode_shape(bits, a->M, a->N, a->K, a->G, decode_waves, allow_split, tiled, per_elem, a, bf16,
-                                 ws_cap);
+                                 std::min(ws_cap, kSplitWsCap));
     if (rc2 != kNoDecodePlan) return rc2;
     if (path == 1) return GPTQ_ERR_BAD_ARG;         // forced decode, but no launch shape fits
     *use_decode = false;                             // very many groups: the prefill kernel
   }
   *per_elem = (g_idx != nullptr) || (group_size % 64 != 0);
   gptq::prefill_shape(a->M, a->N, !*per_elem && !bf16 && bits != 8, &a->tiles_m, &a->tiles_n, &a->pbm);
+  plan_prefill_split(a, allow_split, ws_cap);
   return GPTQ_OK;
+}
+
+// Split-K arrival counters a plan needs (one per column tile in the decode
+// kernel, one per output tile in the prefill kernel); 0 without a split.
+size_t split_counter_bytes(const gptq::GemmArgs& a, bool use_decode) {
+  if (a.ks <= 1) return 0;
+  return (size_t)(use_decode ? a.tiles : a.tiles_m * a.tiles_n) * 4;
 }
 
 // Split-K workspace, one per (device, stream): the per-tile arrival counters
@@ -427,9 +469,9 @@ int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
   if (x_perm) {
     // one workspace request for the gathered x and (if planned) the split sums
     const size_t xb = (size_t)M * K * 2;
-    const bool split = use_decode && a.ks > 1;
+    const bool split = a.ks > 1;
     void* xg = nullptr;
-    bool ok = split_workspace(stream, split ? (size_t)a.ks * a.M * a.N * 4 : 0, split ? (size_t)a.tiles * 4 : 0,
+    bool ok = split_workspace(stream, split ? (size_t)a.ks * a.M * a.N * 4 : 0, split_counter_bytes(a, use_decode),
                               &a.ws, &a.cnt, xb, &xg);
     if (!ok && split) {
       const int rc2 = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
@@ -444,8 +486,8 @@ int gemm_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
                                       : gptq::launch_prefill(bits, per_elem, a, stream);
     return err == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH;
   }
-  if (use_decode && a.ks > 1 &&
-      !split_workspace(stream, (size_t)a.ks * a.M * a.N * 4, (size_t)a.tiles * 4, &a.ws, &a.cnt)) {
+  if (a.ks > 1 &&
+      !split_workspace(stream, (size_t)a.ks * a.M * a.N * 4, split_counter_bytes(a, use_decode), &a.ws, &a.cnt)) {
     // no workspace (first use under stream capture, or out of memory): one split
     const int rc2 = plan_gemm(x, qweight, qzeros, scales, g_idx, bits, group_size, is_v2, M, N, K, out, path,
                               decode_waves, tiled, &a, &use_decode, &per_elem, false, bf16);
@@ -508,14 +550,16 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
     // the pipelined full-tile body: fast path, K % 64 == 0, not 8-bit
     const bool full = !per_elem && K % 64 == 0 && bits != 8;
     if (bf16)
-      std::snprintf(buf, (size_t)buflen, "gptq::prefill_bf16_kernel<%d, %s, %s> grid=%dx%d block=256", bits, pe,
-                    full ? "true" : "false", a.tiles_n, a.tiles_m);
+      std::snprintf(buf, (size_t)buflen, "gptq::prefill_bf16_kernel<%d, %s, %s> grid=%dx%d block=256 k_splits=%d",
+                    bits, pe, full ? "true" : "false", a.tiles_n, a.tiles_m, a.ks);
     else if (a.pbm == 256)   // last argument: 4-bit tiled words with fields in pair order
-      std::snprintf(buf, (size_t)buflen, "gptq::prefill_big_kernel<%d, %s, %s> grid=%dx%d block=256", bits,
-                    full ? "true" : "false", (bits == 4 && tiled) ? "true" : "false", a.tiles_n, a.tiles_m);
+      std::snprintf(buf, (size_t)buflen, "gptq::prefill_big_kernel<%d, %s, %s> grid=%dx%d block=256 k_splits=%d",
+                    bits, full ? "true" : "false", (bits == 4 && tiled) ? "true" : "false", a.tiles_n, a.tiles_m,
+                    a.ks);
     else
-      std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s, %s, %s> grid=%dx%d block=256", bits, pe,
-                    full ? "true" : "false", (bits == 4 && tiled) ? "true" : "false", a.tiles_n, a.tiles_m);
+      std::snprintf(buf, (size_t)buflen, "gptq::prefill_kernel<%d, %s, %s, %s> grid=%dx%d block=256 k_splits=%d",
+                    bits, pe, full ? "true" : "false", (bits == 4 && tiled) ? "true" : "false", a.tiles_n,
+                    a.tiles_m, a.ks);
   }
   return GPTQ_OK;
 }
@@ -932,8 +976,9 @@ int gptq_gemm_noalloc(const void* x, const int32_t* qweight, const int32_t* qzer
                              &a, &use_decode, &per_elem, true, false, kScratchSumBytes);
     if (rc != GPTQ_OK || M == 0) return rc;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
-    if (use_decode && a.ks > 1) {
-      if ((size_t)a.tiles * 4 > kScratchCounterBytes || (int64_t)a.ks * a.M * a.N * 4 > kScratchSumBytes)
+    if (a.ks > 1) {
+      if (split_counter_bytes(a, use_decode) > kScratchCounterBytes ||
+          (int64_t)a.ks * a.M * a.N * 4 > kScratchSumBytes)
         return GPTQ_ERR_NO_MEM;                      // beyond the static scratch (not reached by the planner)
       char* p = nullptr;
       const int rs = scratch_for_device(stream, &p);

@@ -89,12 +89,17 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // workgroup -> tile t (column-major over tiles_m x tiles_n); a grouped launch
-  // first picks the expert (ntiles workgroups each)
+  // first picks the expert (ntiles workgroups each), a split-K launch the
+  // split sk of K (ks consecutive workgroups per tile)
   const int ntiles = a.tiles_m * a.tiles_n;
-  int b = blockIdx.x, e = 0;
+  const int ks = (BM != 128 || a.n_experts > 0) ? 1 : max(a.ks, 1);   // 128-row tiles only
+  int b = blockIdx.x, e = 0, sk = 0;
   if (a.n_experts > 0) {
     e = b / ntiles;
     b -= e * ntiles;
+  } else if (ks > 1) {
+    sk = b % ks;
+    b /= ks;
   }
   int t = b;
   if ((ntiles & 7) == 0) t = (b & 7) * (ntiles >> 3) + (b >> 3);
@@ -126,7 +131,11 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   const int n = tn * kPrefillBN + wave * 64 + 2 * q;   // this lane's two columns n, n + 1
   const bool col_ok = n < a.N;
   const int nc = col_ok ? n : 0;
-  const int ktiles = (a.K + BK - 1) / BK;
+  // this workgroup's k tiles: [kt0, kt0 + ktiles) of the whole K (a split
+  // covers cks chunks, an even count, the last split the rest)
+  const int ktiles_all = (a.K + BK - 1) / BK;
+  const int kt0 = ks > 1 ? sk * (a.cks / 2) : 0;
+  const int ktiles = ks > 1 ? min(a.cks / 2, ktiles_all - kt0) : ktiles_all;
 
   // ---- x tiles: slot s = m * 8 + (kblk ^ ((m >> 1) & 7)) of a stage holds
   // x[m0 + m, 8 kblk .. 8 kblk + 8) of the tile.  The swizzle puts the 16
@@ -154,7 +163,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
     for (int i = 0; i < XI; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xrsrc, (__attribute__((address_space(3))) void*)(sl + (XI * wave + i) * 64 * 8), 16,
-          xoff[i] + (uint32_t)min(kt, ktiles - 1) * BK * 2u, 0, 0, 0);
+          xoff[i] + (uint32_t)(kt0 + min(kt, ktiles - 1)) * BK * 2u, 0, 0, 0);
     }
   };
 
@@ -193,7 +202,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   auto load_w = [&](int kt, auto set_c) __attribute__((always_inline)) {
     constexpr int set = decltype(set_c)::value % NSR;
     if constexpr (!PER_ELEM) {
-      const int g = min((kt * BK) / a.group_size, a.G - 1);
+      const int g = min(((kt0 + kt) * BK) / a.group_size, a.G - 1);
       const uint32_t* zrow = qzr + (int64_t)g * a.zrow_words;
       const int n4 = nc & ~3;
       if constexpr (BITS == 3) {
@@ -205,8 +214,9 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
       }
       sw[set] = *reinterpret_cast<const half2_t*>(a.scales + (int64_t)g * a.N + nc);
     }
-    // rows past K lie past the end of qweight and read zero
-    const uint32_t tile_off = (uint32_t)kt * tile_bytes;
+    // rows past K lie past the end of qweight and read zero (tiles past the
+    // split, prefetched by its last steps, are loaded but never used)
+    const uint32_t tile_off = (uint32_t)(kt0 + kt) * tile_bytes;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       w0[set][s] = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, (int)(woff0[s] + tile_off), 0, 0);
@@ -342,7 +352,8 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
       if (kt < ktiles) compute_full_tile(set_c);
       return;
     }
-    const int ksteps = min(4, (a.K - kt * BK) >> 4);
+    // tiles past the split (the loop runs in threes) compute nothing
+    const int ksteps = kt < ktiles ? min(4, (a.K - (kt0 + kt) * BK) >> 4) : 0;
     const _Float16* sl = stage_lds(set_c);
     half2_t negp[2][4], sp[2];
     float bs[2], bc[2];
@@ -360,7 +371,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
           if constexpr (PER_ELEM) {
             // each row its own group: (s, -z s) per field
             const uint16_t* scb = reinterpret_cast<const uint16_t*>(a.scales);
-            const int k0 = kt * BK + 16 * s + 8 * kb2;
+            const int k0 = (kt0 + kt) * BK + 16 * s + 8 * kb2;
             float f[8];                              // fields in k order
             if constexpr (PAIRS) block4_regs_f32(w0j, f);
             else block_fields_f32<BITS>(w0j, w1j, kb, f);
@@ -388,7 +399,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
         unpack_B(w0[set][s][j], L == 2 ? w1[set][L == 2 ? s : 0][j] : 0u, kb, p);
         u32x4_t bw;
         if constexpr (PER_ELEM) {
-          const int k0 = kt * BK + 16 * s + 8 * kb2;
+          const int k0 = (kt0 + kt) * BK + 16 * s + 8 * kb2;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int ga = group_of(a.g_idx, k0 + 2 * v, a.group_size, a.G);
@@ -463,6 +474,105 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
     step(kt + 2, S2{}, S1{});
   }
 
+  // ---- split K: publish this split's fp32 sums (rows < M), count the tile's
+  // arrivals; the last split to arrive adds all of them in split order
+  // (deterministic), rounds once, writes the tile and re-arms the counter.
+  // The partial sums move only through agent-scope atomic stores and loads
+  // (coherent across the XCDs' L2s), and each wave waits for its stores
+  // before the arrival is counted.  The last workgroup reads the tile back
+  // with several splits and column groups per round of loads, so that the
+  // loads' latency is paid a few times, not once per split.
+  if (BM == 128 && ks > 1) {
+    if (col_ok) {
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kb2 + (v & 3);
+          if (row < a.M) {
+            float* w = a.ws + ((int64_t)sk * a.M + row) * a.N + n;
+            __hip_atomic_store(w, acc[i][0][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(w + 1, acc[i][1][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): this wave's stores are complete
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __shared__ int last_split;
+    __syncthreads();
+    if (tid == 0)
+      last_split = __hip_atomic_fetch_add(a.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (uint32_t)(ks - 1);
+    __syncthreads();
+    if (!last_split) return;
+    // the tile: rows [m0, m0 + rows) x columns [n00, n00 + cols), as groups of
+    // four columns; thread tid takes groups tid, tid + 256, ...
+    const int n00 = tn * kPrefillBN;
+    const int rows = min(BM, a.M - m0), cols = min(kPrefillBN, a.N - n00);
+    const int gpr = cols >> 2;                       // groups per row (cols % 32 == 0)
+    const int groups = rows * gpr;
+    const int64_t split_elems = (int64_t)a.M * a.N;
+    // KB splits x GB groups per round of loads: 16 pairs of 8-byte loads in
+    // flight per thread, spent on splits or on groups as ks asks
+    auto reduce = [&](auto kb_c, auto gb_c) __attribute__((always_inline)) {
+      constexpr int KB = decltype(kb_c)::value, GB = decltype(gb_c)::value;
+      for (int g0 = tid; g0 < groups; g0 += 256 * GB) {
+        floatx4_t sum[GB];
+        int64_t base[GB];
+#pragma unroll
+        for (int gi = 0; gi < GB; ++gi) {
+          sum[gi] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+          const int g = g0 + 256 * gi;
+          const int r = g / gpr, c = 4 * (g - r * gpr);
+          base[gi] = g < groups ? (int64_t)(m0 + r) * a.N + n00 + c : 0;   // groups past the tile read element 0
+        }
+        for (int k0 = 0; k0 < ks; k0 += KB) {
+          uint64_t pv[GB][KB][2];                    // each: two adjacent fp32 sums
+#pragma unroll
+          for (int gi = 0; gi < GB; ++gi)
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+              const uint64_t* w = reinterpret_cast<const uint64_t*>(
+                  a.ws + (k0 + kk < ks ? (int64_t)(k0 + kk) * split_elems + base[gi] : 0));
+              pv[gi][kk][0] = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              pv[gi][kk][1] = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+          for (int gi = 0; gi < GB; ++gi)
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+              if (k0 + kk < ks) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  sum[gi][c] += __builtin_bit_cast(float, (uint32_t)(pv[gi][kk][c >> 1] >> (32 * (c & 1))));
+              }
+        }
+#pragma unroll
+        for (int gi = 0; gi < GB; ++gi) {
+          const int g = g0 + 256 * gi;
+          if (g >= groups) continue;
+          const int r = g / gpr, c = 4 * (g - r * gpr);
+          _Float16* o = a.out + (int64_t)(m0 + r) * a.N + n00 + c;
+          if constexpr (BF16) {
+            *reinterpret_cast<u32x2_t*>(o) =
+                u32x2_t{bf16_pair(sum[gi][0], sum[gi][1]), bf16_pair(sum[gi][2], sum[gi][3])};
+          } else {
+            typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<half4_t*>(o) = half4_t{(_Float16)sum[gi][0], (_Float16)sum[gi][1],
+                                                     (_Float16)sum[gi][2], (_Float16)sum[gi][3]};
+          }
+        }
+      }
+    };
+    if (ks <= 2) reduce(std::integral_constant<int, 2>{}, std::integral_constant<int, 8>{});
+    else if (ks <= 4) reduce(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
+    else reduce(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
+    if (tid == 0) __hip_atomic_store(a.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+
   // ---- epilogue: fp32 -> fp16 (bfloat16), two adjacent columns per store
   if (!col_ok) return;
 #pragma unroll
@@ -500,7 +610,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(GemmArgs a) {
 
 template <int BITS, bool PER_ELEM, bool FULL>
 static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
-  const dim3 grid(a.tiles_m * a.tiles_n * (a.n_experts > 0 ? a.n_experts : 1));
+  const dim3 grid(a.tiles_m * a.tiles_n * (a.n_experts > 0 ? a.n_experts : (a.ks > 1 ? a.ks : 1)));
   if (a.bf16) {
     if (BITS == 4 && a.wtiled)                     // pair-order words
       hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL, BITS == 4>), grid, dim3(256), 0, stream, a);

@@ -66,6 +66,25 @@ def test_noalloc_matches_gemm_two_calls(dev):
         check(got, d, L, K, N, bits, gs, f"call {i}: {desc}")
 
 
+def test_noalloc_prefill_split_within_scratch(dev):
+    """A prefill shape whose split-K partial sums fit gptq_gemm's workspace
+    but not the 2 MiB scratch: the no-allocation call splits K less (here not
+    at all), so it matches the oracle to the GEMM bar and gptq_gemm to the
+    rounding of the fp32 sums' order; called twice, the second time smaller."""
+    for i, (K, N, M) in enumerate(((4096, 4096, 64), (4096, 1024, 20))):
+        d, L = layer(K, N, M, 4, 128, seed=300 + i)
+        x, qw, qz, sc, gi = upload(d, L, dev)
+        desc = gq.describe(x, qw, qz, sc, gi, 4, 128, True)
+        assert desc.startswith("gptq::prefill_kernel") and int(desc.split("k_splits=")[1]) > 1, desc
+        want = gq.gemm(x, qw, qz, sc, gi, 4, 128, True)
+        out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+        got = gq.gemm_noalloc(x, qw, qz, sc, gi, 4, 128, True, out=out)
+        torch.cuda.synchronize()
+        check(got, d, L, K, N, 4, 128, f"call {i}: {desc}")
+        diff = (got.float() - want.float()).abs().max().item()
+        assert diff <= TOL * want.float().pow(2).mean().sqrt().item(), (i, diff)
+
+
 def test_noalloc_graph_replays(dev):
     """Captured (no allocation can happen under capture), replayed three times
     with eager work in between: every replay equals the eager result."""

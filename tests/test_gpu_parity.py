@@ -496,9 +496,10 @@ def test_gemm_tiled_shapes(dev, bits, gs, M, K, N, act):
 
 
 @pytest.mark.parametrize("bits", BITS)
-@pytest.mark.parametrize("M,K,N", [(1024, 512, 288), (1057, 576, 544), (2048, 1024, 256)])
+@pytest.mark.parametrize("M,K,N", [(1024, 512, 12288), (1057, 576, 12320), (2048, 1024, 6144)])
 def test_prefill_big_tiles(dev, bits, M, K, N):
-    """Large M with few tiles takes the 256-row prefill tile (not 8-bit):
+    """Large M whose 256-row tiles fill one round of 3/4 .. all of the CUs
+    takes the 256-row prefill tile (not 8-bit):
     ragged rows (M % 256) and columns (N % 256), both qweight layouts, against
     the oracle on sampled columns; the two layouts give the same bits."""
     gs = 64

@@ -41,12 +41,15 @@ constexpr int kPrefillStages = 3;                 // x tiles in LDS: current + t
 // CUs (28672 -> 8192: 1159 -> 1207 TFLOP/s) but lose when the grid takes
 // several rounds, whose last one runs partly empty and, at one workgroup per
 // CU, exposes every workgroup's prologue and epilogue (8192 -> 28672: 1160 ->
-// 1107); 8-bit lost on both shapes (its B operand is not pipelined).
+// 1107); 8-bit lost on both shapes (its B operand is not pipelined).  They
+// also lose when their one round leaves many CUs idle: 4096 -> 4096 at M =
+// 1024 .. 2048 (64 .. 128 tiles) and 11008 -> 4096 ran at 340-710 TFLOP/s, so
+// they are taken only with at least 3/4 of the CUs busy.
 constexpr int kPrefillCUs = 256;
 
 void prefill_shape(int M, int N, bool big_ok, int* tiles_m, int* tiles_n, int* bm) {
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + kPrefillBN - 1) / kPrefillBN);
-  *bm = (big_ok && M >= 1024 && big_tiles <= kPrefillCUs) ? 256 : 128;
+  *bm = (big_ok && M >= 1024 && big_tiles <= kPrefillCUs && 4 * big_tiles >= 3 * kPrefillCUs) ? 256 : 128;
   *tiles_m = (M + *bm - 1) / *bm;
   *tiles_n = (N + kPrefillBN - 1) / kPrefillBN;
 }

@@ -207,10 +207,12 @@ def test_gemm_bf16_describe_names_the_bf16_kernels(dev):
     qw, qz, sct, gi = upload(L, sc_t, dev)
     xt = x_t.to(dev)
     assert gq.describe(xt[:1].contiguous(), qw, qz, sct, gi, 4, 128, False).startswith("gptq::decode_bf16_kernel<4, 1,")
-    assert gq.describe(xt, qw, qz, sct, gi, 4, 128, False).startswith("gptq::prefill_bf16_kernel<4, false, true>")
+    assert gq.describe(xt, qw, qz, sct, gi, 4, 128, False).startswith("gptq::prefill_bf16_small_kernel<4, false, true, false, 64>")
+    x2 = torch.cat([xt, xt]).contiguous()          # 128 rows: the 128-row tile
+    assert gq.describe(x2, qw, qz, sct, gi, 4, 128, False).startswith("gptq::prefill_bf16_kernel<4, false, true>")
     qwt = gq.repack_tiled(qw, 4)
     assert gq.describe(xt[:1].contiguous(), qwt, qz, sct, gi, 4, 128, False).startswith("gptq::decode_bf16_kernel<4,")
-    assert gq.describe(xt, qwt, qz, sct, gi, 4, 128, False).startswith("gptq::prefill_bf16_kernel<4, false, true>")
+    assert gq.describe(xt, qwt, qz, sct, gi, 4, 128, False).startswith("gptq::prefill_bf16_small_kernel<4, false, true, true, 64>")
 
 
 # ------------------------------------------------------------------ full-size layers, sampled columns

@@ -261,26 +261,29 @@ int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_spl
   return kNoDecodePlan;                              // the scale/zero table does not fit LDS
 }
 
-// Prefill split K for small grids of 128-row tiles (small M, or N of a few
-// thousand columns): the tiles split K and the last split of a tile to
-// arrive adds the fp32 partial sums.  A workgroup's k tiles run as a chain of
-// about 0.9 us each when few workgroups share a CU (MFMA and dequant of one
-// wave per SIMD), and the last workgroup of a tile reads back ks * M rows of
-// partial sums, so the split count balances the two: ks ~ sqrt(32 k_tiles /
-// M), about 0.75 workgroups per CU in all, at least 4 k tiles (256 rows) per
-// split.  Measured on MI355X (4-bit, 4096 -> 4096 / 12288 / 22016 and
-// 11008 -> 4096, M = 17 .. 512, split counts 1 .. 12): within 10% of the best
-// count on every shape, and 1.2-5.6x faster than one split for M <= 256.
-// No split with 256-row tiles or in a grouped launch.
+// Prefill split K for small grids of 32-, 64- or 128-row tiles (small M, or
+// N of a few thousand columns): the tiles split K and the last split of a tile
+// to arrive adds the fp32 partial sums.  A workgroup's k tiles run as a chain
+// (about 0.9 us each for a 128-row tile when few workgroups share a CU: MFMA
+// and dequant of one wave per SIMD), and the last workgroup of a tile reads
+// back ks * M rows of partial sums, so the split count balances the two:
+// ks ~ sqrt(c k_tiles / M), c fitted to measurement (32 for 128-row tiles, 16
+// for the smaller ones, whose k tiles are shorter), about 0.75 workgroups per
+// CU in all, at least 4 k tiles (256 rows) per split.  Measured on MI355X
+// (4-bit, 4096 -> 4096 / 12288 / 22016 and 11008 -> 4096, M = 17 .. 512,
+// split counts 1 .. 12): within 10% of the best count on every shape, and
+// 1.2-5.6x faster than one split for M <= 256.  No split with 256-row tiles
+// or in a grouped launch.
 constexpr int kPrefillMinSplitTiles = 4;
 
 void plan_prefill_split(gptq::GemmArgs* a, bool allow_split, int64_t ws_cap) {
   a->ks = 1;
   a->cks = a->chunks;
   const int tiles = a->tiles_m * a->tiles_n;
-  if (!allow_split || a->pbm != 128) return;
+  if (!allow_split || a->pbm > 128) return;
   const int ktiles = (a->K + 63) / 64;
-  int ks = (int)std::lround(std::sqrt(32.0 * ktiles / std::max(a->M, 1)));
+  const double c = a->pbm < 128 ? 16.0 : 32.0;
+  int ks = (int)std::lround(std::sqrt(c * ktiles / std::max(a->M, 1)));
   ks = std::min({ks, (3 * kCUs / 4) / tiles, ktiles / kPrefillMinSplitTiles});
   ks = (int)std::min<int64_t>(ks, ws_cap / ((int64_t)a->M * a->N * 4));
   if (ks < 2) return;                                 // (at most 96 tiles: their counters always fit)
@@ -549,7 +552,11 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
   } else {
     // the pipelined full-tile body: fast path, K % 64 == 0, not 8-bit
     const bool full = !per_elem && K % 64 == 0 && bits != 8;
-    if (bf16)
+    if (a.pbm < 128)         // 32- or 64-row tiles (M <= 64)
+      std::snprintf(buf, (size_t)buflen, "gptq::%s<%d, %s, %s, %s, %d> grid=%dx%d block=256 k_splits=%d",
+                    bf16 ? "prefill_bf16_small_kernel" : "prefill_small_kernel", bits, pe, full ? "true" : "false",
+                    (bits == 4 && tiled) ? "true" : "false", a.pbm, a.tiles_n, a.tiles_m, a.ks);
+    else if (bf16)
       std::snprintf(buf, (size_t)buflen, "gptq::prefill_bf16_kernel<%d, %s, %s> grid=%dx%d block=256 k_splits=%d",
                     bits, pe, full ? "true" : "false", a.tiles_n, a.tiles_m, a.ks);
     else if (a.pbm == 256)   // last argument: 4-bit tiled words with fields in pair order

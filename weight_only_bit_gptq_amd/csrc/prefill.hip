@@ -47,9 +47,12 @@ constexpr int kPrefillStages = 3;                 // x tiles in LDS: current + t
 // they are taken only with at least 3/4 of the CUs busy.
 constexpr int kPrefillCUs = 256;
 
+// Up to 64 rows: 32- or 64-row tiles, so that the MFMAs of rows past M are
+// not computed (a k tile's dequant is the same, its MFMAs a quarter or half).
 void prefill_shape(int M, int N, bool big_ok, int* tiles_m, int* tiles_n, int* bm) {
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + kPrefillBN - 1) / kPrefillBN);
   *bm = (big_ok && M >= 1024 && big_tiles <= kPrefillCUs && 4 * big_tiles >= 3 * kPrefillCUs) ? 256 : 128;
+  if (M <= 64) *bm = M <= 32 ? 32 : 64;
   *tiles_m = (M + *bm - 1) / *bm;
   *tiles_n = (N + kPrefillBN - 1) / kPrefillBN;
 }
@@ -68,7 +71,7 @@ void prefill_shape(int M, int N, bool big_ok, int* tiles_m, int* tiles_n, int* b
 template <int BITS, bool PER_ELEM, bool FULL, bool BF16, bool PAIRS, int BM>
 __device__ __forceinline__ void prefill_body(GemmArgs a) {
   static_assert(!PAIRS || BITS == 4, "pair-order words: 4-bit");
-  static_assert(BM == 128 || BM == 256, "workgroup tile rows");
+  static_assert(BM == 32 || BM == 64 || BM == 128 || BM == 256, "workgroup tile rows");
   constexpr int BK = kPrefillBK;
   constexpr int MS = BM / 32;                       // 32-row MFMA subtiles per wave
   constexpr int NST = kPrefillStages;
@@ -95,7 +98,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   // first picks the expert (ntiles workgroups each), a split-K launch the
   // split sk of K (ks consecutive workgroups per tile)
   const int ntiles = a.tiles_m * a.tiles_n;
-  const int ks = (BM != 128 || a.n_experts > 0) ? 1 : max(a.ks, 1);   // 128-row tiles only
+  const int ks = (BM > 128 || a.n_experts > 0) ? 1 : max(a.ks, 1);   // tiles of up to 128 rows
   int b = blockIdx.x, e = 0, sk = 0;
   if (a.n_experts > 0) {
     e = b / ntiles;
@@ -485,7 +488,7 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
   // before the arrival is counted.  The last workgroup reads the tile back
   // with several splits and column groups per round of loads, so that the
   // loads' latency is paid a few times, not once per split.
-  if (BM == 128 && ks > 1) {
+  if (BM <= 128 && ks > 1) {
     if (col_ok) {
 #pragma unroll
       for (int i = 0; i < MS; ++i) {
@@ -611,10 +614,35 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(GemmArgs a) {
   prefill_body<BITS, PER_ELEM, FULL, true, PAIRS, 128>(a);
 }
 
+// 32- and 64-row tiles (M <= 64), fp16 and bfloat16
+template <int BITS, bool PER_ELEM, bool FULL, bool PAIRS, int BM>
+__global__ __launch_bounds__(256, 2) void prefill_small_kernel(GemmArgs a) {
+  prefill_body<BITS, PER_ELEM, FULL, false, PAIRS, BM>(a);
+}
+template <int BITS, bool PER_ELEM, bool FULL, bool PAIRS, int BM>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_small_kernel(GemmArgs a) {
+  prefill_body<BITS, PER_ELEM, FULL, true, PAIRS, BM>(a);
+}
+
+template <int BITS, bool PER_ELEM, bool FULL, bool PAIRS>
+static void launch_small(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.bf16) {
+    if (a.pbm == 32) hipLaunchKernelGGL((prefill_bf16_small_kernel<BITS, PER_ELEM, FULL, PAIRS, 32>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((prefill_bf16_small_kernel<BITS, PER_ELEM, FULL, PAIRS, 64>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (a.pbm == 32) hipLaunchKernelGGL((prefill_small_kernel<BITS, PER_ELEM, FULL, PAIRS, 32>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((prefill_small_kernel<BITS, PER_ELEM, FULL, PAIRS, 64>), grid, dim3(256), 0, stream, a);
+  }
+}
+
 template <int BITS, bool PER_ELEM, bool FULL>
 static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid(a.tiles_m * a.tiles_n * (a.n_experts > 0 ? a.n_experts : (a.ks > 1 ? a.ks : 1)));
-  if (a.bf16) {
+  if (a.pbm < 128) {
+    // 4-bit tiled words hold their fields in pair order
+    if (BITS == 4 && a.wtiled) launch_small<BITS, PER_ELEM, FULL, BITS == 4>(a, grid, stream);
+    else launch_small<BITS, PER_ELEM, FULL, false>(a, grid, stream);
+  } else if (a.bf16) {
     if (BITS == 4 && a.wtiled)                     // pair-order words
       hipLaunchKernelGGL((prefill_bf16_kernel<BITS, PER_ELEM, FULL, BITS == 4>), grid, dim3(256), 0, stream, a);
     else

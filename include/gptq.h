@@ -100,9 +100,10 @@ typedef enum gptq_status {
  * padded to 16; for narrow N with K >= 8192 the workgroups of a tile split K
  * and the last to finish adds the fp32 partial sums, in a fixed order, so
  * results are deterministic either way); larger M runs the MFMA prefill
- * kernel (128- or 256-row tiles; when the 128-row tiles are too few to fill
- * the GPU, e.g. M <= 512 with N of a few thousand, their workgroups split K
- * the same way).
+ * kernel (32-, 64-, 128- or 256-row tiles; when the tiles of up to 128 rows
+ * are too few to fill the GPU, e.g. M <= 512 with N of a few thousand, their
+ * workgroups split K and store fp32 partial sums, which a second kernel on
+ * the same stream adds in split order, so results are deterministic too).
  */
 GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros,
               const void* scales, const int32_t* g_idx, int bits, int group_size,
@@ -113,17 +114,17 @@ GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qze
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments and checks as gptq_gemm; it calls no hipMalloc / hipFree.  Where
  * gptq_gemm splits K over workgroups (decode with narrow N and long K,
- * prefill with few tiles), the arrival counters and fp32 partial sums live
- * in a static device array of 2 MiB that the library holds on every device it
+ * prefill with few tiles), the decode arrival counters and the fp32 partial
+ * sums live in a static device array of 2 MiB that the library holds on every device it
  * runs on until the process ends (gptq_release does not free it); the plan
  * keeps the partial sums within it (at most ks * M * N * 4 bytes of 2 MiB -
- * 64 KiB, and 4 bytes per tile in the first 64 KiB), and a plan that needed
+ * 64 KiB, and 4 bytes per decode tile in the first 64 KiB), and a plan that needed
  * more would return GPTQ_ERR_NO_MEM before launching.  Decode plans are the
  * same as gptq_gemm's and so is the result, bit for bit; a prefill launch
  * whose partial sums would exceed the array splits K fewer times than
  * gptq_gemm (or not at all), which changes only the order of the fp32 sums.  The counters
  * are cleared by a kernel on `stream` at the first call on a device (the
- * array also starts zeroed) and every split-K kernel leaves them at zero.
+ * array also starts zeroed) and every split-K decode kernel leaves them at zero.
  * All calls on one device share that one array: calls that may overlap on a
  * device (concurrent streams, or graph replays overlapping each other or
  * eager calls) race on it and must be serialized by the caller.

@@ -140,16 +140,21 @@ def test_gemm_bf16_ragged_and_group_shapes(dev, bits, K, N, gs):
             assert_close_bf16(y, ref, f"M={M} path={p}")
 
 
-@pytest.mark.parametrize("bits,M,K,N", [(4, 1, 8192, 512), (3, 4, 8192, 96), (8, 16, 4096, 256), (2, 2, 12288, 64)])
+@pytest.mark.parametrize("bits,M,K,N", [(4, 1, 8192, 512), (3, 4, 8192, 96), (8, 16, 4096, 256), (2, 2, 12288, 64),
+                                        (4, 40, 4096, 512), (8, 100, 4096, 256)])
 def test_gemm_bf16_long_k(dev, bits, M, K, N):
     """K long enough for several decode phases and (narrow N) split K, whose
-    last workgroup writes the bfloat16 result."""
+    last workgroup writes the bfloat16 result; at M = 40 and 100 the prefill
+    kernels split K and the sum kernel writes it."""
     L, sc_t, sc, x_t, x = layer_bf16(K, N, M, bits, 128, False, True, False, seed=K + M)
     qw, qz, sct, gi = upload(L, sc_t, dev)
     ref = oracle.gptq_gemm_ref(x, L.qweight, L.qzeros, sc, None, bits, 128, True, K, N, act="bf16")
     y1 = gq.gemm(x_t.to(dev), qw, qz, sct, gi, bits, 128, True)
     y2 = gq.gemm(x_t.to(dev), qw, qz, sct, gi, bits, 128, True)
-    assert_close_bf16(y1, ref, gq.describe(x_t.to(dev), qw, qz, sct, gi, bits, 128, True))
+    desc = gq.describe(x_t.to(dev), qw, qz, sct, gi, bits, 128, True)
+    if M > 16:
+        assert desc.startswith("gptq::prefill_bf16") and int(desc.split("k_splits=")[1].split()[0]) > 1, desc
+    assert_close_bf16(y1, ref, desc)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))           # deterministic
 
 

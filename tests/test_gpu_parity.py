@@ -258,18 +258,19 @@ PREFILL_SPLIT_CASES = [
     (3, 128, 33, 4096, 256, True, False), (8, 128, 20, 2048, 768, False, True),
     (2, 64, 50, 4096, 512, False, False), (4, 32, 40, 2048, 256, False, False),
     (4, 32, 24, 2080, 288, False, True), (3, 128, 130, 8192, 160, False, True),
-    # more splits than one round of the reduction's loads reads (16)
-    (4, 128, 17, 16384, 256, False, False)]
+    (4, 128, 17, 16384, 256, False, False),
+    # the sum kernel's four widths: up to 4, 8, 16 and 32 splits (4 and 8 here)
+    (4, 128, 100, 1024, 8192, False, False), (3, 128, 48, 2048, 6144, False, True),
+    (4, 64, 24, 1024, 6144, False, True)]
 
 
 @pytest.mark.parametrize("bits,gs,M,K,N,act,tiled", PREFILL_SPLIT_CASES)
 def test_prefill_split_k(dev, bits, gs, M, K, N, act, tiled):
     """Prefill launches whose grid of output tiles is small split K over
-    several workgroups per tile (the last to arrive adds the fp32 partial sums
-    in split order): oracle parity on every column, bit-identical repeated
-    calls, a second call that rewrites every output (counters re-armed), and
-    the same result from a graph captured after the stream has its workspace,
-    replayed three times."""
+    several workgroups per tile (a second kernel adds the fp32 partial sums in
+    split order): oracle parity on every column, bit-identical repeated calls,
+    a second call that rewrites every output, and the same result from a graph
+    captured after the stream has its workspace, replayed three times."""
     d, L = quantized(K, N, M, bits, gs, False, True, act, seed=K + 7 * N + M)
     qw, qz, sc, gi = upload(L, dev)
     if tiled:
@@ -301,7 +302,7 @@ def test_prefill_split_k(dev, bits, gs, M, K, N, act, tiled):
 
 def test_prefill_split_k_full_size_small_batch(dev):
     """Llama-7B qkv at 17 and 128 rows (tiled layout, the automatic plan: the
-    32-row and the 128-row prefill tile, K split 4 ways at both): oracle parity
+    32-row and the 128-row prefill tile, K split 8 and 5 ways): oracle parity
     on sampled columns, computed one by one."""
     wl = WORKLOADS["llama7b_decode_w4g128"]
     layer = wl.layers[0]

@@ -262,38 +262,53 @@ int decode_shape(int bits, int M, int N, int K, int G, int waves, bool allow_spl
 }
 
 // Prefill split K for small grids of 32-, 64- or 128-row tiles (small M, or
-// N of a few thousand columns): the tiles split K and the last split of a tile
-// to arrive adds the fp32 partial sums.  A workgroup's k tiles run as a chain
-// (about 0.9 us each for a 128-row tile when few workgroups share a CU: MFMA
-// and dequant of one wave per SIMD), and the last workgroup of a tile reads
-// back ks * M rows of partial sums, so the split count balances the two:
-// ks ~ sqrt(c k_tiles / M), c fitted to measurement (32 for 128-row tiles, 16
-// for the smaller ones, whose k tiles are shorter), about 0.75 workgroups per
-// CU in all, at least 4 k tiles (256 rows) per split.  Measured on MI355X
-// (4-bit, 4096 -> 4096 / 12288 / 22016 and 11008 -> 4096, M = 17 .. 512,
-// split counts 1 .. 12): within 10% of the best count on every shape, and
-// 1.2-5.6x faster than one split for M <= 256.  No split with 256-row tiles
-// or in a grouped launch.
-constexpr int kPrefillMinSplitTiles = 4;
+// N of a few thousand columns): ks workgroups per tile each take a slice of
+// K and store fp32 partial sums, which a second kernel adds.  The split count
+// minimises a time model (us) fitted to measurements on MI355X (4-bit,
+// 4096 -> 4096 / 12288 / 22016 and 11008 -> 4096, M = 17 .. 512, 1 .. 32
+// splits: the pick is on average 1.9% slower than the best count): a
+// workgroup's k tiles run as a chain of t_tile each (0.53 / 0.67 / 0.93 us
+// for 32 / 64 / 128 rows at one workgroup per CU), stretched by (workgroups
+// per CU)^0.75 above that for the small tiles and by (rounds of one
+// workgroup per CU)^1.25 for the 128-row ones (the last round's CUs set the
+// time); a split launch costs about 4.3 us more (the sum kernel's launch and
+// latency) plus the partial sums' traffic, ks * M * N fp32 written and read
+// back, at 8 bytes per ns.  No split with 256-row tiles or in a grouped
+// launch.
+constexpr int kPrefillMinSplitTiles = 2;               // k tiles (128 rows of K) per split at least
+constexpr int kPrefillMaxSplits = 32;                  // the sum kernel's loads in flight per thread
+
+// Model time of a launch whose splits take `per` k tiles each (ks splits).
+double prefill_time_model(const gptq::GemmArgs& a, int per, int ks) {
+  const double per_cu = (double)a.tiles_m * a.tiles_n * ks / kCUs;
+  double t = per;
+  if (a.pbm < 128) t *= (a.pbm == 32 ? 0.53 : 0.67) * std::pow(std::max(1.0, per_cu), 0.75);
+  else t *= 0.93 * std::pow(std::ceil(per_cu - 1e-9), 1.25);
+  if (ks > 1) t += 4.3 + 2.0 * ks * a.M * a.N * 4 / 8.0e6;
+  return t;
+}
 
 void plan_prefill_split(gptq::GemmArgs* a, bool allow_split, int64_t ws_cap) {
   a->ks = 1;
   a->cks = a->chunks;
-  const int tiles = a->tiles_m * a->tiles_n;
   if (!allow_split || a->pbm > 128) return;
   const int ktiles = (a->K + 63) / 64;
-  const double c = a->pbm < 128 ? 16.0 : 32.0;
-  int ks = (int)std::lround(std::sqrt(c * ktiles / std::max(a->M, 1)));
-  ks = std::min({ks, (3 * kCUs / 4) / tiles, ktiles / kPrefillMinSplitTiles});
-  ks = (int)std::min<int64_t>(ks, ws_cap / ((int64_t)a->M * a->N * 4));
-  if (ks < 2) return;                                 // (at most 96 tiles: their counters always fit)
-  const int per = (ktiles + ks - 1) / ks;              // k tiles per split
-  a->ks = (ktiles + per - 1) / per;                    // no empty split
-  a->cks = 2 * per;                                    // in 32-row chunks
-  if (a->ks < 2) {
-    a->ks = 1;
-    a->cks = a->chunks;
+  int ks = 1;
+  double best = prefill_time_model(*a, ktiles, 1);
+  for (int k = 2; k <= std::min(kPrefillMaxSplits, ktiles / kPrefillMinSplitTiles); ++k) {
+    const int per = (ktiles + k - 1) / k;             // k tiles per split
+    const int eks = (ktiles + per - 1) / per;          // splits with no empty one
+    if ((int64_t)eks * a->M * a->N * 4 > ws_cap) break;
+    const double t = prefill_time_model(*a, per, eks);
+    if (t < best) {
+      best = t;
+      ks = eks;
+    }
   }
+  if (ks < 2) return;
+  const int per = (ktiles + ks - 1) / ks;
+  a->ks = (ktiles + per - 1) / per;
+  a->cks = 2 * per;                                    // in 32-row chunks
 }
 
 // Argument checks plus kernel choice and launch shape: pure host code.
@@ -341,10 +356,10 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
 }
 
 // Split-K arrival counters a plan needs (one per column tile in the decode
-// kernel, one per output tile in the prefill kernel); 0 without a split.
+// kernel; a prefill split is summed by a second kernel and counts nothing).
 size_t split_counter_bytes(const gptq::GemmArgs& a, bool use_decode) {
-  if (a.ks <= 1) return 0;
-  return (size_t)(use_decode ? a.tiles : a.tiles_m * a.tiles_n) * 4;
+  if (a.ks <= 1 || !use_decode) return 0;
+  return (size_t)a.tiles * 4;
 }
 
 // Split-K workspace, one per (device, stream): the per-tile arrival counters

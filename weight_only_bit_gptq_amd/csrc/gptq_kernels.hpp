@@ -36,10 +36,11 @@ struct GemmArgs {
   // fast path: scale and zero folded once per `fold` consecutive chunks (1, 2
   // or 4; a divisor of cpg, of cpw / 2 and, with ks > 1, of cks)
   int fold;
-  // split K: ks workgroups per column tile, each over cks consecutive chunks
+  // split K: ks workgroups per output tile, each over cks consecutive chunks
   // (the last one over the rest); with ks > 1 every workgroup stores its fp32
-  // partial sums to ws [ks, M, N] and the last of a tile to arrive (counted in
-  // cnt[tile], reset to 0 by that workgroup) adds them in split order
+  // partial sums to ws [ks, M, N], added in split order by the last decode
+  // workgroup of a tile to arrive (counted in cnt[tile], reset to 0 by that
+  // workgroup) or, after a prefill launch, by a second kernel
   int ks, cks;
   float* ws;
   uint32_t* cnt;

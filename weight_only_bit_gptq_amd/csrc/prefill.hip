@@ -23,7 +23,9 @@
 // Grid: one workgroup per output tile; when the tile count is a multiple of 8,
 // consecutive tiles of the column-major tile order go to the same XCD
 // (workgroup ids are dealt round-robin over the 8 XCDs), so an XCD's L2 holds
-// a few weight column tiles and the x row tiles they share.
+// a few weight column tiles and the x row tiles they share.  A grid of few
+// tiles (small M) splits K: ks workgroups per tile store fp32 partial sums
+// and a second, chip-wide kernel adds them in split order.
 #include <type_traits>
 
 #include "gptq_kernels.hpp"
@@ -163,13 +165,21 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
     // rows only feed output rows that are never stored
     if (m0 + m >= a.M) xoff[i] = 0xF0000000u;
   }
+  // Tiles past this workgroup's last (the loop runs in threes) load from
+  // offsets past the end of x and of qweight: they read zero without a
+  // memory access, so the step that waits for them does not wait for memory
+  // (their stage and registers are never used).
+  // x holds M K < 2^31 elements, K % 32 == 0: at most 2^32 - 64 bytes;
+  // qweight N K b / 8 < 2^31 bytes
+  constexpr uint32_t kPastEndX = 0xFFFFFFF0u, kPastEnd = 0x80000000u;
   auto load_x = [&](int kt, auto st_c) __attribute__((always_inline)) {
     _Float16* sl = stage_lds(st_c);
+    const bool live = kt < ktiles;
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xrsrc, (__attribute__((address_space(3))) void*)(sl + (XI * wave + i) * 64 * 8), 16,
-          xoff[i] + (uint32_t)(kt0 + min(kt, ktiles - 1)) * BK * 2u, 0, 0, 0);
+          live ? xoff[i] + (uint32_t)(kt0 + kt) * BK * 2u : kPastEndX, 0, 0, 0);
     }
   };
 
@@ -220,13 +230,15 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
       }
       sw[set] = *reinterpret_cast<const half2_t*>(a.scales + (int64_t)g * a.N + nc);
     }
-    // rows past K lie past the end of qweight and read zero (tiles past the
-    // split, prefetched by its last steps, are loaded but never used)
+    // rows past K lie past the end of qweight and read zero; tiles past this
+    // workgroup's last read nothing (see load_x)
+    const bool live = kt < ktiles;
     const uint32_t tile_off = (uint32_t)(kt0 + kt) * tile_bytes;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      w0[set][s] = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, (int)(woff0[s] + tile_off), 0, 0);
-      if constexpr (L == 2) w1[set][s] = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, (int)(woff1(s) + tile_off), 0, 0);
+      w0[set][s] = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, (int)(live ? woff0[s] + tile_off : kPastEnd), 0, 0);
+      if constexpr (L == 2)
+        w1[set][s] = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, (int)(live ? woff1(s) + tile_off : kPastEnd), 0, 0);
     }
   };
 
@@ -480,102 +492,23 @@ __device__ __forceinline__ void prefill_body(GemmArgs a) {
     step(kt + 2, S2{}, S1{});
   }
 
-  // ---- split K: publish this split's fp32 sums (rows < M), count the tile's
-  // arrivals; the last split to arrive adds all of them in split order
-  // (deterministic), rounds once, writes the tile and re-arms the counter.
-  // The partial sums move only through agent-scope atomic stores and loads
-  // (coherent across the XCDs' L2s), and each wave waits for its stores
-  // before the arrival is counted.  The last workgroup reads the tile back
-  // with several splits and column groups per round of loads, so that the
-  // loads' latency is paid a few times, not once per split.
+  // ---- split K: this split's fp32 sums (rows < M) go to its slice of ws
+  // [ks, M, N]; launch_prefill then runs split_sum_kernel on the same stream,
+  // which adds the slices in split order (deterministic) and rounds once
   if (BM <= 128 && ks > 1) {
-    if (col_ok) {
+    if (!col_ok) return;
 #pragma unroll
-      for (int i = 0; i < MS; ++i) {
+    for (int i = 0; i < MS; ++i) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kb2 + (v & 3);
-          if (row < a.M) {
-            float* w = a.ws + ((int64_t)sk * a.M + row) * a.N + n;
-            __hip_atomic_store(w, acc[i][0][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(w + 1, acc[i][1][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kb2 + (v & 3);
+        if (row < a.M) {
+          float* w = a.ws + ((int64_t)sk * a.M + row) * a.N + n;
+          w[0] = acc[i][0][v];
+          w[1] = acc[i][1][v];
         }
       }
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): this wave's stores are complete
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __shared__ int last_split;
-    __syncthreads();
-    if (tid == 0)
-      last_split = __hip_atomic_fetch_add(a.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   (uint32_t)(ks - 1);
-    __syncthreads();
-    if (!last_split) return;
-    // the tile: rows [m0, m0 + rows) x columns [n00, n00 + cols), as groups of
-    // four columns; thread tid takes groups tid, tid + 256, ...
-    const int n00 = tn * kPrefillBN;
-    const int rows = min(BM, a.M - m0), cols = min(kPrefillBN, a.N - n00);
-    const int gpr = cols >> 2;                       // groups per row (cols % 32 == 0)
-    const int groups = rows * gpr;
-    const int64_t split_elems = (int64_t)a.M * a.N;
-    // KB splits x GB groups per round of loads: 16 pairs of 8-byte loads in
-    // flight per thread, spent on splits or on groups as ks asks
-    auto reduce = [&](auto kb_c, auto gb_c) __attribute__((always_inline)) {
-      constexpr int KB = decltype(kb_c)::value, GB = decltype(gb_c)::value;
-      for (int g0 = tid; g0 < groups; g0 += 256 * GB) {
-        floatx4_t sum[GB];
-        int64_t base[GB];
-#pragma unroll
-        for (int gi = 0; gi < GB; ++gi) {
-          sum[gi] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-          const int g = g0 + 256 * gi;
-          const int r = g / gpr, c = 4 * (g - r * gpr);
-          base[gi] = g < groups ? (int64_t)(m0 + r) * a.N + n00 + c : 0;   // groups past the tile read element 0
-        }
-        for (int k0 = 0; k0 < ks; k0 += KB) {
-          uint64_t pv[GB][KB][2];                    // each: two adjacent fp32 sums
-#pragma unroll
-          for (int gi = 0; gi < GB; ++gi)
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) {
-              const uint64_t* w = reinterpret_cast<const uint64_t*>(
-                  a.ws + (k0 + kk < ks ? (int64_t)(k0 + kk) * split_elems + base[gi] : 0));
-              pv[gi][kk][0] = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              pv[gi][kk][1] = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-#pragma unroll
-          for (int gi = 0; gi < GB; ++gi)
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
-              if (k0 + kk < ks) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                  sum[gi][c] += __builtin_bit_cast(float, (uint32_t)(pv[gi][kk][c >> 1] >> (32 * (c & 1))));
-              }
-        }
-#pragma unroll
-        for (int gi = 0; gi < GB; ++gi) {
-          const int g = g0 + 256 * gi;
-          if (g >= groups) continue;
-          const int r = g / gpr, c = 4 * (g - r * gpr);
-          _Float16* o = a.out + (int64_t)(m0 + r) * a.N + n00 + c;
-          if constexpr (BF16) {
-            *reinterpret_cast<u32x2_t*>(o) =
-                u32x2_t{bf16_pair(sum[gi][0], sum[gi][1]), bf16_pair(sum[gi][2], sum[gi][3])};
-          } else {
-            typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<half4_t*>(o) = half4_t{(_Float16)sum[gi][0], (_Float16)sum[gi][1],
-                                                     (_Float16)sum[gi][2], (_Float16)sum[gi][3]};
-          }
-        }
-      }
-    };
-    if (ks <= 2) reduce(std::integral_constant<int, 2>{}, std::integral_constant<int, 8>{});
-    else if (ks <= 4) reduce(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
-    else reduce(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
-    if (tid == 0) __hip_atomic_store(a.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
 
@@ -664,6 +597,51 @@ static hipError_t launch_prefill_pe(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Split-K sum: y[r, c] = sum over s = 0 .. ks - 1, in that order, of ws[s, r, c],
+// rounded once to fp16 (bfloat16).  One thread per 4 adjacent columns (N is a
+// multiple of 32), 16-byte loads, all KB >= ks splits' loads in flight at once
+// (unconditional: loads j >= ks repeat split ks - 1 and are not added, so the
+// code has no branch between the loads and their waits).
+template <bool BF16, int KB>
+__global__ __launch_bounds__(128) void split_sum_kernel(const float* __restrict__ ws, _Float16* __restrict__ out,
+                                                        int64_t quads, int64_t split_elems, int ks) {
+  const int64_t qd = (int64_t)blockIdx.x * 128 + threadIdx.x;
+  if (qd >= quads) return;
+  const floatx4_t* p = reinterpret_cast<const floatx4_t*>(ws) + qd;
+  const int64_t stride = split_elems >> 2;
+  floatx4_t v[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) v[j] = p[(int64_t)min(j, ks - 1) * stride];
+  floatx4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KB; ++j)
+    if (j < ks) sum += v[j];
+  _Float16* o = out + 4 * qd;
+  if constexpr (BF16) {
+    *reinterpret_cast<u32x2_t*>(o) = u32x2_t{bf16_pair(sum[0], sum[1]), bf16_pair(sum[2], sum[3])};
+  } else {
+    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<half4_t*>(o) = half4_t{(_Float16)sum[0], (_Float16)sum[1], (_Float16)sum[2], (_Float16)sum[3]};
+  }
+}
+
+template <int KB>
+static void launch_split_sum_kb(const GemmArgs& a, hipStream_t stream) {
+  const int64_t elems = (int64_t)a.M * a.N;
+  const int64_t quads = elems >> 2;
+  const dim3 grid((unsigned)((quads + 127) / 128));
+  if (a.bf16) hipLaunchKernelGGL((split_sum_kernel<true, KB>), grid, dim3(128), 0, stream, a.ws, a.out, quads, elems, a.ks);
+  else hipLaunchKernelGGL((split_sum_kernel<false, KB>), grid, dim3(128), 0, stream, a.ws, a.out, quads, elems, a.ks);
+}
+
+static hipError_t launch_split_sum(const GemmArgs& a, hipStream_t stream) {
+  if (a.ks <= 4) launch_split_sum_kb<4>(a, stream);
+  else if (a.ks <= 8) launch_split_sum_kb<8>(a, stream);
+  else if (a.ks <= 16) launch_split_sum_kb<16>(a, stream);
+  else launch_split_sum_kb<32>(a, stream);
+  return hipGetLastError();
+}
+
 template <int BITS>
 static hipError_t launch_prefill_bits(bool per_elem, const GemmArgs& a, hipStream_t stream) {
   if (per_elem) return launch_prefill_pe<BITS, true, false>(a, stream);
@@ -676,12 +654,17 @@ static hipError_t launch_prefill_bits(bool per_elem, const GemmArgs& a, hipStrea
 }
 
 hipError_t launch_prefill(int bits, bool per_elem, const GemmArgs& a, hipStream_t stream) {
+  const bool split = a.ks > 1 && a.n_experts == 0 && a.pbm <= 128;
+  if (split && a.ks > 32) return hipErrorInvalidValue;   // the sum kernel adds at most 32 splits
+  hipError_t err;
   switch (bits) {
-    case 2: return launch_prefill_bits<2>(per_elem, a, stream);
-    case 3: return launch_prefill_bits<3>(per_elem, a, stream);
-    case 4: return launch_prefill_bits<4>(per_elem, a, stream);
-    default: return launch_prefill_bits<8>(per_elem, a, stream);
+    case 2: err = launch_prefill_bits<2>(per_elem, a, stream); break;
+    case 3: err = launch_prefill_bits<3>(per_elem, a, stream); break;
+    case 4: err = launch_prefill_bits<4>(per_elem, a, stream); break;
+    default: err = launch_prefill_bits<8>(per_elem, a, stream); break;
   }
+  if (err != hipSuccess || !split || a.M == 0) return err;
+  return launch_split_sum(a, stream);
 }
 
 }  // namespace gptq

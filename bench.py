@@ -103,7 +103,7 @@ def parse():
                    help="skip the oracle leg (cpu_baseline and the parity check of the timed outputs)")
     p.add_argument("--no-bf16", action="store_true",
                    help="skip the bfloat16-activation lines (decode layers and 4-bit prefill)")
-    p.add_argument("--no-other", action="store_true", help="skip decode_other and moe")
+    p.add_argument("--no-other", action="store_true", help="skip decode_other, small_batch and moe")
     p.add_argument("--cpu-sample-cols", type=int, default=12288,
                    help="columns of the qkv layer the CPU oracle processes (default: all)")
     p.add_argument("--cpu-reps", type=int, default=3, help="at least this many oracle calls on the sample")
@@ -382,6 +382,31 @@ def bench_decode_other(torch, gq, args, dev, outputs, skip_checkpoint):
                     "reps_us": reps, "GBps": round(P["alg"] / (us * 1e-6) / 1e9, 1),
                     "frac": round(P["alg"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                     "read_ceiling_us": round(ceilings[ck], 3), "of_ceiling": round(ceilings[ck] / us, 4)})
+        del P
+    return res
+
+
+def bench_small_batch(torch, gq, args, dev, outputs):
+    """The Llama-7B layers at M = 17, 64, 128, 512 (tiled 4-bit) through
+    gptq_gemm's automatic plan (prefill tiles of 32-128 rows, K split over
+    workgroups when the grid is small): per-call median launch time over
+    rotated weight copies, weight GB/s and TFLOP/s."""
+    from workload import bench_cases
+    res = []
+    cur = sets = None
+    for case in bench_cases("small_batch"):
+        P = prepare(torch, gq, case, dev)
+        if case.layer != cur:
+            sets, cur = None, case.layer
+            torch.cuda.empty_cache()
+        sets = sets or rotated_copies(torch, P, P["wbytes"])
+        us, reps, out = time_decode_call(torch, P, dev, args, sets=sets)
+        outputs[case.key] = out[:, torch.from_numpy(check_cols(P["layer"].N)).to(dev)].float().cpu().numpy()
+        K, N = P["layer"].K, P["layer"].N
+        res.append({"workload": case.workload, "layer": f"{case.layer} {K}->{N}", "M": case.M,
+                    "kernel": P["desc"], "us": round(us, 3), "reps_us": reps,
+                    "weight_GBps": round(P["wbytes"] / (us * 1e-6) / 1e9, 1),
+                    "TFLOPs": round(2.0 * case.M * K * N / (us * 1e-6) / 1e12, 1)})
         del P
     return res
 
@@ -942,10 +967,13 @@ def main():
         print(f"# decode (checkpoint layout): {dec_ck['ms_per_step'] * 1e3:.2f} us/step, layers: {dec_ck['layers']}",
               file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-    dec_other = moe = moe_prefill = None
+    dec_other = small = moe = moe_prefill = None
     if not args.no_other:
         dec_other = bench_decode_other(torch, gq, args, dev, outputs, args.no_checkpoint_layout)
         print(f"# other decode calls: {dec_other}", file=sys.stderr, flush=True)
+        small = bench_small_batch(torch, gq, args, dev, outputs)
+        print(f"# small batches: {small}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
         moe = bench_moe(torch, gq, args, dev, 16)
         print(f"# moe: {moe}", file=sys.stderr, flush=True)
         moe_prefill = bench_moe(torch, gq, args, dev, 2048)
@@ -1011,6 +1039,7 @@ def main():
                      "per_layer": dec["layers"]},
         "decode_checkpoint": None if dec_ck is None else decode_summary(dec_ck),
         "decode_other": dec_other,
+        "small_batch": small,
         "moe": moe,
         "moe_prefill": moe_prefill,
         "prefill": prefill,

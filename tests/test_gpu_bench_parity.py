@@ -7,9 +7,10 @@ benchmark reports has its result checked against the fp64 oracle:
 
 - decode calls (M <= 16): every output column, max|y - y_ref| <= 5e-3 rms(y_ref)
   (bfloat16: plus the output's own rounding, 2^-8 |y_ref|);
-- prefill calls (M = 2048): at least 96 sampled columns (the oracle's fp64 product over
-  the whole 2048 x K x N layer would take minutes on the host), spread so
-  that every 256-column block tile of the kernel contributes.
+- prefill calls (M > 16: the small-batch calls at 17-512 rows, M = 2048): at
+  least 96 sampled columns (the oracle's fp64 product over the whole 2048 x K
+  x N layer would take minutes on the host), spread so that every 256-column
+  block tile of the kernel contributes.
 
 Layers are quantized and packed by the oracle (seeded draws), the tiled layout
 is the oracle's re-layout; nothing the GPU computes is fed back to the oracle.

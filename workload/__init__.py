@@ -54,7 +54,7 @@ class Workload:
     description: str = ""
 
 
-# The five workloads.  Shapes stand in for Llama-7B, Llama/Qwen and a 70B MLP;
+# The workloads.  Shapes stand in for Llama-7B, Llama/Qwen and a 70B MLP;
 # no trained weights are used anywhere.
 WORKLOADS: Dict[str, Workload] = {
     "smoke_256": Workload(
@@ -68,6 +68,13 @@ WORKLOADS: Dict[str, Workload] = {
                 Layer("gate_up", 4096, 22016), Layer("down", 11008, 4096)],
         Ms=[1], bits=4, group_size=128, sym=True, is_v2=False, sigma=0.02,
         description="Llama-7B decode GEMVs, 4-bit g128 symmetric GPTQv1, M=1"),
+    "llama7b_batch_w4g128": Workload(
+        name="llama7b_batch_w4g128",
+        layers=[Layer("qkv", 4096, 12288), Layer("o_proj", 4096, 4096),
+                Layer("gate_up", 4096, 22016), Layer("down", 11008, 4096)],
+        Ms=[17, 64, 128, 512], bits=4, group_size=128, sym=True, is_v2=False, sigma=0.02,
+        description="the Llama-7B layers at small batches (M = 17-512: batched decode, short "
+                    "prompts), 4-bit g128 symmetric GPTQv1"),
     "lowbit_decode_w2g64": Workload(
         name="lowbit_decode_w2g64",
         layers=[Layer("up", 4096, 12288), Layer("down", 12288, 4096)],
@@ -126,6 +133,7 @@ BENCH_CASES: List[BenchCase] = (
     + _cases("decode_other", "lowbit_decode_w2g64", [1, 4, 16], "tiled")
     + _cases("decode_other", "actorder_decode_w3g128", [16], "tiled", entry="gemm_sorted")
     + _cases("decode_other", "actorder_decode_w3g128", [16], "checkpoint")
+    + _cases("small_batch", "llama7b_batch_w4g128", [17, 64, 128, 512], "tiled")
     + _cases("prefill", "mlp70b_prefill_w4g128", [2048], "tiled")
     + _cases("prefill", "mlp70b_prefill_w8g128", [2048], "tiled")
     + _cases("prefill_checkpoint", "mlp70b_prefill_w4g128", [2048], "checkpoint")

@@ -648,11 +648,12 @@ int gptq_gemm_tiled(const void* x, const int32_t* qweight_tiled, const int32_t* 
 
 namespace {
 // Grouped GEMM path: expert batches of one decode block (up to 16 rows) run
-// on the decode kernel, larger ones on the prefill kernel (128-row tiles, each
-// reading its expert's weights once, where every further block of 16 rows of
-// the decode kernel reads them again).  Measured on MI355X, 8 experts 4096 ->
-// 14336, 4-bit: decode 64 / 103 / 112 us at 16 / 24 / 32 rows per expert,
-// prefill 106 / 101 / 98 us.
+// on the decode kernel, larger ones on the prefill kernel (tiles of 32 to 128
+// rows, each reading its expert's weights once, where every further block of
+// 16 rows of the decode kernel reads them again).  Measured on MI355X, 8
+// experts 4096 -> 14336, 4-bit: decode 64 / 103 / 112 us at 16 / 24 / 32 rows
+// per expert, prefill with 128-row tiles 106 / 101 / 98 us (the 32- and
+// 64-row tiles now taken at such row counts skip the MFMAs of absent rows).
 constexpr int kMoePrefillRows = 16;
 
 int moe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,

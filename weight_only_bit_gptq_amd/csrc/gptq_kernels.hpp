@@ -57,8 +57,8 @@ struct GemmArgs {
   const int32_t* moe_off;
   int n_experts, moe_blocks, moe_rows;
   int64_t qw_stride, qz_stride, sc_stride, gi_stride;
-  // prefill launch shape: tiles_m x tiles_n workgroup tiles of pbm (128 or
-  // 256) rows by 256 columns
+  // prefill launch shape: tiles_m x tiles_n workgroup tiles of pbm (32, 64,
+  // 128 or 256) rows by 256 columns
   int tiles_m, tiles_n, pbm;
   // activation type: 0 = fp16 (x, scales, out fp16), 1 = bfloat16 (x,
   // scales and out hold bfloat16 bits behind the same pointers)

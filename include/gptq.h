@@ -104,6 +104,9 @@ typedef enum gptq_status {
  * are too few to fill the GPU, e.g. M <= 512 with N of a few thousand, their
  * workgroups split K and store fp32 partial sums, which a second kernel on
  * the same stream adds in split order, so results are deterministic too).
+ * Exception: a layer the prefill kernel would dequantize element by element
+ * (g_idx given, or group_size % 64 != 0) runs the decode kernel over blocks
+ * of 16 rows for 16 < M <= 4096, without a K split.
  */
 GPTQ_API int gptq_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros,
               const void* scales, const int32_t* g_idx, int bits, int group_size,

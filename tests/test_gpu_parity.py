@@ -300,6 +300,80 @@ def test_prefill_split_k(dev, bits, gs, M, K, N, act, tiled):
         assert torch.equal(outg.view(torch.int16), y1.view(torch.int16)), desc
 
 
+ROW_BLOCK_CASES = [
+    # bits, gs, M, K, N, act, tiled: per-element layers above 16 rows run the
+    # decode kernel over blocks of 16 rows (ragged last blocks; column tile
+    # counts with and without whole eighths, i.e. both workgroup mappings;
+    # act order, and 32- / 96-row groups on the fast path)
+    (3, 128, 17, 2048, 256, True, False), (4, 128, 40, 1024, 288, True, True), (2, 64, 100, 1024, 512, True, False),
+    (8, 128, 33, 1024, 256, True, True), (4, 32, 48, 2048, 1024, False, False), (4, 96, 70, 1152, 256, False, True),
+    (3, 32, 256, 1024, 256, False, True), (4, 128, 20, 8192, 256, True, False)]
+
+
+@pytest.mark.parametrize("bits,gs,M,K,N,act,tiled", ROW_BLOCK_CASES)
+def test_decode_row_blocks(dev, bits, gs, M, K, N, act, tiled):
+    """gptq_gemm's automatic plan for these layers is the decode kernel over
+    ceil(M / 16) row blocks: oracle parity on every output, bit-identical
+    repeats, and the same result through a graph replayed twice."""
+    d, L = quantized(K, N, M, bits, gs, False, True, act, seed=K + N + M + gs)
+    qw, qz, sc, gi = upload(L, dev)
+    if tiled:
+        qw = gq.repack_tiled(qw, bits)
+    x = torch.from_numpy(d.x).to(dev)
+    desc = gq.describe(x, qw, qz, sc, gi, bits, gs, True)
+    assert desc.startswith("gptq::decode_kernel") and f"row_blocks={(M + 15) // 16}" in desc, desc
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, True, K, N)
+    y1 = gq.gemm(x, qw, qz, sc, gi, bits, gs, True)
+    assert_close(y1, ref, desc)
+    y2 = gq.gemm(x, qw, qz, sc, gi, bits, gs, True)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        gq.gemm(x, qw, qz, sc, gi, bits, gs, True, out=out)
+    for _ in range(2):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), y1.view(torch.int16))
+
+
+def test_decode_row_blocks_full_size(dev):
+    """Llama-7B qkv (4096 -> 12288, 4-bit g128) with act-order g_idx at 600
+    rows, tiled: the decode kernel over 38 row blocks (the last of 8 rows);
+    oracle parity on sampled columns, computed one by one."""
+    K, N, M, bits, gs = 4096, 12288, 600, 4, 128
+    d, L = quantized(K, N, M, bits, gs, True, False, True, seed=600)
+    qw, qz, sc, gi = upload(L, dev)
+    qw = gq.repack_tiled(qw, bits)
+    x = torch.from_numpy(d.x).to(dev)
+    desc = gq.describe(x, qw, qz, sc, gi, bits, gs, False)
+    assert desc.startswith("gptq::decode_kernel<4, true,") and "row_blocks=38" in desc, desc
+    cols = np.unique(np.concatenate([np.arange(0, N, 101), [N - 1]]))
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, L.g_idx, bits, gs, False, K, N, cols=cols)
+    y = gq.gemm(x, qw, qz, sc, gi, bits, gs, False)
+    assert_close(y[:, torch.from_numpy(cols).to(dev)], ref, desc)
+
+
+def test_decode_row_blocks_bf16(dev):
+    """bfloat16 act-order layer at 40 rows: the decode kernel over row blocks,
+    within the bf16 bar (the element-wise bf16 dequant, fp32 sums)."""
+    K, N, M, bits, gs = 1024, 256, 40, 4, 128
+    d, L = quantized(K, N, M, bits, gs, False, True, True, seed=41)
+    sc_b = torch.from_numpy(L.scales.astype(np.float32)).to(torch.bfloat16)
+    x_b = torch.from_numpy(d.x.astype(np.float32)).to(torch.bfloat16)
+    qw, qz, _, gi = upload(L, dev)
+    desc = gq.describe(x_b.to(dev), qw, qz, sc_b.to(dev), gi, bits, gs, True)
+    assert desc.startswith("gptq::decode_bf16_kernel") and "row_blocks=3" in desc, desc
+    ref = oracle.gptq_gemm_ref(x_b.double().numpy(), L.qweight, L.qzeros, sc_b.double().numpy(), L.g_idx, bits, gs,
+                               True, K, N, act="bf16")
+    y = gq.gemm(x_b.to(dev), qw, qz, sc_b.to(dev), gi, bits, gs, True).to(torch.float64).cpu().numpy()
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.all(np.abs(y - ref) <= TOL * rms + 2.0 ** -8 * np.abs(ref)), desc
+
+
 def test_prefill_split_k_full_size_small_batch(dev):
     """Llama-7B qkv at 17 and 128 rows (tiled layout, the automatic plan: the
     32-row and the 128-row prefill tile, K split 8 and 5 ways): oracle parity

@@ -212,6 +212,23 @@ __device__ __forceinline__ void decode_body(GemmArgs a) {
     a.qzeros += e * a.qz_stride;
     a.scales += e * a.sc_stride;
     if (a.g_idx) a.g_idx += e * a.gi_stride;
+  } else if (a.row_blocks > 1) {
+    // rows in blocks of 16 (no K split): workgroup (b, unit) takes rows
+    // [16 b, 16 b + 16) of column tile `unit`.  With whole eighths of tiles,
+    // the row blocks of one tile run on one XCD, back to back, so its L2
+    // serves their repeated reads of the tile's weights.
+    int b;
+    if ((a.tiles & 7) == 0) {
+      const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+      b = slot % a.row_blocks;
+      unit = (slot / a.row_blocks) * 8 + xcd;
+    } else {
+      b = blockIdx.x / a.tiles;
+      unit = blockIdx.x - b * a.tiles;
+    }
+    a.M = min(16, a.M - 16 * b);
+    a.x += (int64_t)(16 * b) * a.K;
+    a.out += (int64_t)(16 * b) * a.N;
   } else {
     const int units = a.tiles * a.ks;
     if ((units & 7) == 0) unit = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
@@ -1066,8 +1083,8 @@ static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
   if constexpr (!decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV)) {
     return hipErrorInvalidValue;
   } else {
-    const size_t lds = decode_lds_bytes(a.n_experts > 0 ? 16 : a.M, a.pc, a.nw, CPL, PER_ELEM, a.G, a.cpg, a.phases,
-                                        a.bf16 != 0);
+    const size_t lds = decode_lds_bytes((a.n_experts > 0 || a.row_blocks > 1) ? 16 : a.M, a.pc, a.nw, CPL, PER_ELEM,
+                                        a.G, a.cpg, a.phases, a.bf16 != 0);
     auto kern = decode_kernel<BITS, PER_ELEM, MV, CPL, CPW, FOLD>;
     if constexpr (FOLD == 1 && decode_cpw_ok(BITS, PER_ELEM, CPL, CPW, MV, true)) {
       if (a.bf16) kern = decode_bf16_kernel<BITS, MV, CPL, CPW>;
@@ -1079,7 +1096,9 @@ static hipError_t launch_decode_k(const GemmArgs& a, hipStream_t stream) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    const int grid = a.n_experts > 0 ? a.n_experts * a.moe_blocks * a.tiles : a.tiles * a.ks;
+    if (a.row_blocks > 1 && (a.ks != 1 || a.n_experts > 0)) return hipErrorInvalidValue;
+    const int grid = a.n_experts > 0 ? a.n_experts * a.moe_blocks * a.tiles
+                                     : a.tiles * a.ks * (a.row_blocks > 1 ? a.row_blocks : 1);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * a.nw), lds, stream, a);
     return hipGetLastError();
   }

@@ -311,6 +311,21 @@ void plan_prefill_split(gptq::GemmArgs* a, bool allow_split, int64_t ws_cap) {
   a->cks = 2 * per;                                    // in 32-row chunks
 }
 
+// Per-element layers (act-order g_idx, or groups that are not whole 64-row
+// k tiles) at up to this many rows run the decode kernel over blocks of 16
+// rows: the prefill kernel's per-element path looks up g_idx, zeros and
+// scales per element in global memory, while the decode kernel stages the
+// layer's scale/zero table per workgroup and the row blocks of a column tile
+// share its weights through one XCD's L2.  Measured on MI355X (tiled, act
+// order unless noted), decode over row blocks vs the prefill kernel, us:
+// 4096 -> 12288 4-bit 22 / 39 / 128 / 253 / 1089 vs 111 / 149 / 354 / 678 /
+// 1441 at M = 17 / 64 / 256 / 512 / 2048; 3-bit 5120 -> 13824 38 / 205 /
+// 1694 vs 152 / 482 / 2288 at M = 17 / 256 / 2048; 4096 -> 4096 4-bit g32
+// (no g_idx) 8.6 / 81 / 325 vs 38 / 137 / 477 at M = 17 / 512 / 2048; 8192
+// -> 28672 4-bit at M = 2048 5254 vs 6072.  The bound keeps the grid (row
+// blocks x column tiles) far below 2^31.
+constexpr int64_t kRowBlockMaxRows = 4096;
+
 // Argument checks plus kernel choice and launch shape: pure host code.
 int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
@@ -339,6 +354,17 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
   a->bf16 = bf16 ? 1 : 0;
   *use_decode = (path == 1) || (path == 0 && M <= 16);
   if (M == 0) return GPTQ_OK;
+  if (path == 0 && M > 16 && M <= kRowBlockMaxRows && (g_idx != nullptr || group_size % 64 != 0)) {
+    // the prefill kernel would take its per-element path: the decode kernel
+    // over blocks of 16 rows instead (no K split)
+    bool pe = bf16 || g_idx != nullptr || group_size % 32 != 0;
+    if (decode_shape(bits, 16, a->N, a->K, a->G, decode_waves, false, tiled, &pe, a, bf16) == GPTQ_OK) {
+      *per_elem = pe;
+      *use_decode = true;
+      a->row_blocks = (int)((M + 15) / 16);
+      return GPTQ_OK;
+    }
+  }
   if (*use_decode) {
     // bfloat16: always the element-wise dequant (the fp16 exponent trick of
     // the fast path does not carry over)
@@ -555,15 +581,22 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
   const char* pe = per_elem ? "true" : "false";
   if (M == 0) {
     std::snprintf(buf, (size_t)buflen, "none (M = 0)");
-  } else if (use_decode && bf16) {
-    std::snprintf(buf, (size_t)buflen,
-                  "gptq::decode_bf16_kernel<%d, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d k_splits=%d",
-                  bits, M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles * a.ks, 64 * a.nw, a.phases, a.pc, a.ks);
   } else if (use_decode) {
-    std::snprintf(buf, (size_t)buflen,
-                  "gptq::decode_kernel<%d, %s, %d, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d "
-                  "k_splits=%d",
-                  bits, pe, M == 1 ? 1 : 4, a.cpl, a.cpw, a.fold, a.tiles * a.ks, 64 * a.nw, a.phases, a.pc, a.ks);
+    const int rb = a.row_blocks > 1 ? a.row_blocks : 1;
+    int len;
+    if (bf16)
+      len = std::snprintf(buf, (size_t)buflen,
+                          "gptq::decode_bf16_kernel<%d, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d "
+                          "k_splits=%d",
+                          bits, M == 1 ? 1 : 4, a.cpl, a.cpw, a.tiles * a.ks * rb, 64 * a.nw, a.phases, a.pc, a.ks);
+    else
+      len = std::snprintf(buf, (size_t)buflen,
+                          "gptq::decode_kernel<%d, %s, %d, %d, %d, %d> grid=%d block=%d phases=%d chunks_per_phase=%d "
+                          "k_splits=%d",
+                          bits, pe, M == 1 ? 1 : 4, a.cpl, a.cpw, a.fold, a.tiles * a.ks * rb, 64 * a.nw, a.phases,
+                          a.pc, a.ks);
+    if (rb > 1 && len > 0 && len < buflen)
+      std::snprintf(buf + len, (size_t)(buflen - len), " row_blocks=%d", rb);
   } else {
     // the pipelined full-tile body: fast path, K % 64 == 0, not 8-bit
     const bool full = !per_elem && K % 64 == 0 && bits != 8;

@@ -57,6 +57,10 @@ struct GemmArgs {
   const int32_t* moe_off;
   int n_experts, moe_blocks, moe_rows;
   int64_t qw_stride, qz_stride, sc_stride, gi_stride;
+  // decode over row blocks (M > 16 on a per-element layer): row_blocks x
+  // tiles workgroups, workgroup (b, t) computes rows [16 b, 16 b + 16) of
+  // column tile t (no K split); 0 or 1 otherwise
+  int row_blocks;
   // prefill launch shape: tiles_m x tiles_n workgroup tiles of pbm (32, 64,
   // 128 or 256) rows by 256 columns
   int tiles_m, tiles_n, pbm;

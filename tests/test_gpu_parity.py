@@ -259,9 +259,11 @@ PREFILL_SPLIT_CASES = [
     (2, 64, 50, 4096, 512, False, False), (4, 32, 40, 2048, 256, False, False),
     (4, 32, 24, 2080, 288, False, True), (3, 128, 130, 8192, 160, False, True),
     (4, 128, 17, 16384, 256, False, False),
-    # the sum kernel's four widths: up to 4, 8, 16 and 32 splits (4 and 8 here)
+    # the sum kernel's four widths: up to 4, 8, 16 and 32 splits (4 and 8 here;
+    # 28 and 26, below 32, repeat the last split's loads without adding them)
     (4, 128, 100, 1024, 8192, False, False), (3, 128, 48, 2048, 6144, False, True),
-    (4, 64, 24, 1024, 6144, False, True)]
+    (4, 64, 24, 1024, 6144, False, True), (4, 128, 24, 7168, 512, False, True),
+    (2, 128, 17, 6656, 512, False, False)]
 
 
 @pytest.mark.parametrize("bits,gs,M,K,N,act,tiled", PREFILL_SPLIT_CASES)

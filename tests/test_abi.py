@@ -158,11 +158,13 @@ def test_tiled_describe_shapes():
                                       (3, 128, 16, 5120, 13824, "<3, false, 4, ")):
         assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, bits, gs, 1, M, N, K, OUT, 0, 0, buf, 256) == 0
         assert buf.value.decode().startswith("gptq::decode_kernel" + want), buf.value
-    # 2048 x 8192: 8 x 32 tiles of 256 rows fit one round on 256 CUs (the 256-row tile);
-    # 2048 x 28672 needs several rounds (the 128-row tile); 8-bit always the 128-row tile
+    # 2048 x 8192: 8 x 32 tiles of 256 rows fit one round on 256 CUs (the 256-row tile,
+    # 8-bit with its pipelined body); 2048 x 28672 needs several rounds (the 128-row tile,
+    # 8-bit with the plain body)
     for (bits, N, want) in ((4, 8192, "gptq::prefill_big_kernel<4, true, true> grid=32x8"),
                             (4, 28672, "gptq::prefill_kernel<4, false, true, true> grid=112x16"),
-                            (8, 8192, "gptq::prefill_kernel<8, false, false, false> grid=32x16")):
+                            (8, 8192, "gptq::prefill_big_kernel<8, true, false> grid=32x8"),
+                            (8, 28672, "gptq::prefill_kernel<8, false, false, false> grid=112x16")):
         assert lib.gptq_gemm_tiled_describe(X, QW, QZ, SC, None, bits, 128, 1, 2048, N, 8192, OUT, 0, 0, buf, 256) == 0
         assert buf.value.decode().startswith(want), buf.value
 

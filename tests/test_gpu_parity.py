@@ -582,16 +582,17 @@ def test_gemm_tiled_shapes(dev, bits, gs, M, K, N, act):
 @pytest.mark.parametrize("M,K,N", [(1024, 512, 12288), (1057, 576, 12320), (2048, 1024, 6144)])
 def test_prefill_big_tiles(dev, bits, M, K, N):
     """Large M whose 256-row tiles fill one round of 3/4 .. all of the CUs
-    takes the 256-row prefill tile (not 8-bit):
-    ragged rows (M % 256) and columns (N % 256), both qweight layouts, against
-    the oracle on sampled columns; the two layouts give the same bits."""
+    takes the 256-row prefill tile (8-bit with its pipelined body, which only
+    this tile holds without spills): ragged rows (M % 256) and columns
+    (N % 256), both qweight layouts, against the oracle on sampled columns;
+    the two layouts give the same bits."""
     gs = 64
     d, L = quantized(K, N, M, bits, gs, False, True, False, seed=M + K + N + bits)
     qw, qz, sc, gi = upload(L, dev)
     qt = upload_tiled(L, dev)[0]
     x = torch.from_numpy(d.x).to(dev)
     desc = gq.describe(x, qw, qz, sc, gi, bits, gs, True)
-    assert ("prefill_big_kernel" in desc) == (bits != 8), desc
+    assert desc.startswith(f"gptq::prefill_big_kernel<{bits}, true,"), desc
     cols = np.unique(np.concatenate([np.arange(0, N, 7), [N - 1]]))
     ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N, cols=cols)
     yc = gq.gemm(x, qw, qz, sc, gi, bits, gs, True)

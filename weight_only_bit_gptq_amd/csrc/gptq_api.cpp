@@ -376,7 +376,10 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
     *use_decode = false;                             // very many groups: the prefill kernel
   }
   *per_elem = (g_idx != nullptr) || (group_size % 64 != 0);
-  gptq::prefill_shape(a->M, a->N, !*per_elem && !bf16 && bits != 8, &a->tiles_m, &a->tiles_n, &a->pbm);
+  // 256-row tiles: the fp16 fast path (8-bit only with whole 64-row k tiles,
+  // its pipelined body)
+  gptq::prefill_shape(a->M, a->N, !*per_elem && !bf16 && (bits != 8 || K % 64 == 0), &a->tiles_m, &a->tiles_n,
+                      &a->pbm);
   plan_prefill_split(a, allow_split, ws_cap);
   return GPTQ_OK;
 }
@@ -598,8 +601,9 @@ int describe_impl(const void* x, const int32_t* qweight, const int32_t* qzeros, 
     if (rb > 1 && len > 0 && len < buflen)
       std::snprintf(buf + len, (size_t)(buflen - len), " row_blocks=%d", rb);
   } else {
-    // the pipelined full-tile body: fast path, K % 64 == 0, not 8-bit
-    const bool full = !per_elem && K % 64 == 0 && bits != 8;
+    // the pipelined full-tile body: fast path, K % 64 == 0, 8-bit only on the
+    // 256-row tile
+    const bool full = !per_elem && K % 64 == 0 && (bits != 8 || a.pbm == 256);
     if (a.pbm < 128)         // 32- or 64-row tiles (M <= 64)
       std::snprintf(buf, (size_t)buflen, "gptq::%s<%d, %s, %s, %s, %d> grid=%dx%d block=256 k_splits=%d",
                     bf16 ? "prefill_bf16_small_kernel" : "prefill_small_kernel", bits, pe, full ? "true" : "false",

@@ -43,8 +43,9 @@ constexpr int kPrefillStages = 3;                 // x tiles in LDS: current + t
 // CUs (28672 -> 8192: 1159 -> 1207 TFLOP/s) but lose when the grid takes
 // several rounds, whose last one runs partly empty and, at one workgroup per
 // CU, exposes every workgroup's prologue and epilogue (8192 -> 28672: 1160 ->
-// 1107); 8-bit lost on both shapes (its B operand is not pipelined).  They
-// also lose when their one round leaves many CUs idle: 4096 -> 4096 at M =
+// 1107).  8-bit takes them with its pipelined body, which only they hold
+// without spills (28672 -> 8192: 993 -> 1042, 8192 -> 8192: 1009 -> 1083
+// TFLOP/s against the 128-row tile's plain body).  They also lose when their one round leaves many CUs idle: 4096 -> 4096 at M =
 // 1024 .. 2048 (64 .. 128 tiles) and 11008 -> 4096 ran at 340-710 TFLOP/s, so
 // they are taken only with at least 3/4 of the CUs busy.
 constexpr int kPrefillCUs = 256;
@@ -646,8 +647,16 @@ template <int BITS>
 static hipError_t launch_prefill_bits(bool per_elem, const GemmArgs& a, hipStream_t stream) {
   if (per_elem) return launch_prefill_pe<BITS, true, false>(a, stream);
   // 8-bit: the pipelined body needs more registers than 2 workgroups per CU
-  // leave (it spills), so it keeps the plain body
-  if constexpr (BITS == 8) return launch_prefill_pe<BITS, false, false>(a, stream);
+  // leave (it spills), so the 128-row and smaller tiles keep the plain body;
+  // the 256-row tile (one workgroup per CU, accumulators in AGPRs) holds it
+  if constexpr (BITS == 8) {
+    if (a.pbm == 256 && a.K % 64 == 0) {
+      if (a.ks > 1 || a.n_experts > 0) return hipErrorInvalidValue;   // never planned for 256-row tiles
+      hipLaunchKernelGGL((prefill_big_kernel<8, true, false>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
+    return launch_prefill_pe<BITS, false, false>(a, stream);
+  }
   else
     return a.K % 64 == 0 ? launch_prefill_pe<BITS, false, true>(a, stream)
                          : launch_prefill_pe<BITS, false, false>(a, stream);

@@ -390,7 +390,8 @@ def bench_small_batch(torch, gq, args, dev, outputs):
     """The Llama-7B layers at M = 17, 64, 128, 512 (tiled 4-bit) through
     gptq_gemm's automatic plan (prefill tiles of 32-128 rows, K split over
     workgroups when the grid is small): per-call median launch time over
-    rotated weight copies, weight GB/s and TFLOP/s."""
+    rotated weight copies, weight GB/s, TFLOP/s and the fraction of the
+    binding roofline (HBM for the bytes, fp16 MFMA for the flops)."""
     from workload import bench_cases
     res = []
     cur = sets = None
@@ -403,10 +404,14 @@ def bench_small_batch(torch, gq, args, dev, outputs):
         us, reps, out = time_decode_call(torch, P, dev, args, sets=sets)
         outputs[case.key] = out[:, torch.from_numpy(check_cols(P["layer"].N)).to(dev)].float().cpu().numpy()
         K, N = P["layer"].K, P["layer"].N
+        gbps = P["alg"] / (us * 1e-6) / 1e9
+        tf = 2.0 * case.M * K * N / (us * 1e-6) / 1e12
+        # the binding roofline at these sizes: the algorithmic bytes (weights,
+        # x, y) against HBM, or the flops against the fp16 MFMA peak
         res.append({"workload": case.workload, "layer": f"{case.layer} {K}->{N}", "M": case.M,
                     "kernel": P["desc"], "us": round(us, 3), "reps_us": reps,
-                    "weight_GBps": round(P["wbytes"] / (us * 1e-6) / 1e9, 1),
-                    "TFLOPs": round(2.0 * case.M * K * N / (us * 1e-6) / 1e12, 1)})
+                    "weight_GBps": round(P["wbytes"] / (us * 1e-6) / 1e9, 1), "TFLOPs": round(tf, 1),
+                    "roofline_frac": round(max(gbps / HBM_PEAK_GBPS, tf / MFMA_F16_PEAK_TFLOPS), 4)})
         del P
     return res
 

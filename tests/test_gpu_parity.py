@@ -342,6 +342,27 @@ def test_decode_row_blocks(dev, bits, gs, M, K, N, act, tiled):
         assert torch.equal(out.view(torch.int16), y1.view(torch.int16))
 
 
+@pytest.mark.parametrize("bits,gs,M,K,N,tiled,want", [
+    (4, 128, 24, 1024, 1024, True, "row_blocks=2"), (2, 64, 32, 2048, 512, False, "row_blocks=2"),
+    (8, 128, 17, 1024, 768, True, "row_blocks=2"), (4, 128, 17, 4096, 4096, True, "row_blocks=2"),
+    # excluded: two rounds of the CUs (checkpoint 4096 -> 4096), rows past 32, long K
+    (4, 128, 17, 4096, 4096, False, "gptq::prefill"), (4, 128, 33, 1024, 1024, True, "gptq::prefill"),
+    (4, 128, 17, 11008, 512, True, "gptq::prefill")])
+def test_small_layer_row_blocks(dev, bits, gs, M, K, N, tiled, want):
+    """Small fast-path layers at 17-32 rows take the decode kernel over two
+    row blocks when that grid fits one round of the CUs, else the prefill
+    kernel: the plan, and oracle parity on every output."""
+    d, L = quantized(K, N, M, bits, gs, False, True, False, seed=K + N + M + bits)
+    qw, qz, sc, gi = upload(L, dev)
+    if tiled:
+        qw = gq.repack_tiled(qw, bits)
+    x = torch.from_numpy(d.x).to(dev)
+    desc = gq.describe(x, qw, qz, sc, gi, bits, gs, True)
+    assert want in desc and (want != "row_blocks=2" or desc.startswith("gptq::decode_kernel")), desc
+    ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N)
+    assert_close(gq.gemm(x, qw, qz, sc, gi, bits, gs, True), ref, desc)
+
+
 def test_decode_row_blocks_full_size(dev):
     """Llama-7B qkv (4096 -> 12288, 4-bit g128) with act-order g_idx at 600
     rows, tiled: the decode kernel over 38 row blocks (the last of 8 rows);

@@ -326,6 +326,18 @@ void plan_prefill_split(gptq::GemmArgs* a, bool allow_split, int64_t ws_cap) {
 // blocks x column tiles) far below 2^31.
 constexpr int64_t kRowBlockMaxRows = 4096;
 
+// Small fast-path layers (N <= 4096, K <= 8192, fp16) at 17..32 rows: the
+// decode kernel over two row blocks when their grid fits one round of the
+// CUs.  The prefill grid there is 16 column tiles or fewer, so its split
+// launch's fixed costs dominate.  Measured on MI355X (tiled, 4-bit unless
+// noted, M = 17 / 32, us, decode vs prefill): 4096 -> 4096 8.1 / 8.2 vs
+// 10.9 / 13.5; 4096 -> 1024 6.7 / 6.9 vs 9.1 / 10.4; 2048 -> 4096 5.2 / 5.4
+// vs 9.6 / 10.6; 5120 -> 4096 9.7 / 9.8 vs 11.6 / 13.9; 2-bit and 8-bit
+// 4096 -> 4096 7.9 / 8.1 and 11.0 / 11.3 vs 10.9 / 13.1 and 12.5 / 15.6.
+// Ties at 11008 -> 4096, loses on the checkpoint layout of 4096 -> 4096
+// (whose 256 tiles take two rounds) and on 4096 -> 12288.
+constexpr int64_t kSmallLayerMaxN = 4096, kSmallLayerMaxK = 8192;
+
 // Argument checks plus kernel choice and launch shape: pure host code.
 int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales,
               const int32_t* g_idx, int bits, int group_size, int is_v2, int64_t M, int64_t N, int64_t K,
@@ -362,6 +374,18 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
       *per_elem = pe;
       *use_decode = true;
       a->row_blocks = (int)((M + 15) / 16);
+      return GPTQ_OK;
+    }
+  }
+  if (path == 0 && !bf16 && M > 16 && M <= 32 && N <= kSmallLayerMaxN && K <= kSmallLayerMaxK) {
+    gptq::GemmArgs b = *a;
+    bool pe = group_size % 32 != 0;
+    if (decode_shape(bits, 16, b.N, b.K, b.G, decode_waves, false, tiled, &pe, &b, false) == GPTQ_OK &&
+        2 * b.tiles <= kCUs) {
+      *a = b;
+      *per_elem = pe;
+      *use_decode = true;
+      a->row_blocks = 2;
       return GPTQ_OK;
     }
   }

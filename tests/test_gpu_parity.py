@@ -345,12 +345,13 @@ def test_decode_row_blocks(dev, bits, gs, M, K, N, act, tiled):
 @pytest.mark.parametrize("bits,gs,M,K,N,tiled,want", [
     (4, 128, 24, 1024, 1024, True, "row_blocks=2"), (2, 64, 32, 2048, 512, False, "row_blocks=2"),
     (8, 128, 17, 1024, 768, True, "row_blocks=2"), (4, 128, 17, 4096, 4096, True, "row_blocks=2"),
-    # excluded: two rounds of the CUs (checkpoint 4096 -> 4096), rows past 32, long K
-    (4, 128, 17, 4096, 4096, False, "gptq::prefill"), (4, 128, 33, 1024, 1024, True, "gptq::prefill"),
+    (4, 128, 50, 2048, 1024, True, "row_blocks=4"), (3, 128, 64, 1024, 512, False, "row_blocks=4"),
+    # excluded: more than 128 column tiles (checkpoint 4096 -> 4096), rows past 64, long K
+    (4, 128, 17, 4096, 4096, False, "gptq::prefill"), (4, 128, 65, 1024, 1024, True, "gptq::prefill"),
     (4, 128, 17, 11008, 512, True, "gptq::prefill")])
 def test_small_layer_row_blocks(dev, bits, gs, M, K, N, tiled, want):
-    """Small fast-path layers at 17-32 rows take the decode kernel over two
-    row blocks when that grid fits one round of the CUs, else the prefill
+    """Small fast-path layers at 17-64 rows take the decode kernel over row
+    blocks when its plan has at most 128 column tiles, else the prefill
     kernel: the plan, and oracle parity on every output."""
     d, L = quantized(K, N, M, bits, gs, False, True, False, seed=K + N + M + bits)
     qw, qz, sc, gi = upload(L, dev)
@@ -358,7 +359,7 @@ def test_small_layer_row_blocks(dev, bits, gs, M, K, N, tiled, want):
         qw = gq.repack_tiled(qw, bits)
     x = torch.from_numpy(d.x).to(dev)
     desc = gq.describe(x, qw, qz, sc, gi, bits, gs, True)
-    assert want in desc and (want != "row_blocks=2" or desc.startswith("gptq::decode_kernel")), desc
+    assert want in desc and (not want.startswith("row_blocks") or desc.startswith("gptq::decode_kernel")), desc
     ref = oracle.gptq_gemm_ref(d.x, L.qweight, L.qzeros, L.scales, None, bits, gs, True, K, N)
     assert_close(gq.gemm(x, qw, qz, sc, gi, bits, gs, True), ref, desc)
 

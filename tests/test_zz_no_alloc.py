@@ -76,7 +76,7 @@ def test_noalloc_prefill_split_within_scratch(dev):
     but not the 2 MiB scratch: the no-allocation call splits K less (here not
     at all), so it matches the oracle to the GEMM bar and gptq_gemm to the
     rounding of the fp32 sums' order; called twice, the second time smaller."""
-    for i, (K, N, M) in enumerate(((4096, 4096, 64), (4096, 1024, 40))):
+    for i, (K, N, M) in enumerate(((4096, 12288, 64), (4096, 1024, 80))):
         d, L = layer(K, N, M, 4, 128, seed=300 + i)
         x, qw, qz, sc, gi = upload(d, L, dev)
         desc = gq.describe(x, qw, qz, sc, gi, 4, 128, True)

@@ -326,16 +326,19 @@ void plan_prefill_split(gptq::GemmArgs* a, bool allow_split, int64_t ws_cap) {
 // blocks x column tiles) far below 2^31.
 constexpr int64_t kRowBlockMaxRows = 4096;
 
-// Small fast-path layers (N <= 4096, K <= 8192, fp16) at 17..32 rows: the
-// decode kernel over two row blocks when their grid fits one round of the
-// CUs.  The prefill grid there is 16 column tiles or fewer, so its split
-// launch's fixed costs dominate.  Measured on MI355X (tiled, 4-bit unless
-// noted, M = 17 / 32, us, decode vs prefill): 4096 -> 4096 8.1 / 8.2 vs
-// 10.9 / 13.5; 4096 -> 1024 6.7 / 6.9 vs 9.1 / 10.4; 2048 -> 4096 5.2 / 5.4
-// vs 9.6 / 10.6; 5120 -> 4096 9.7 / 9.8 vs 11.6 / 13.9; 2-bit and 8-bit
-// 4096 -> 4096 7.9 / 8.1 and 11.0 / 11.3 vs 10.9 / 13.1 and 12.5 / 15.6.
-// Ties at 11008 -> 4096, loses on the checkpoint layout of 4096 -> 4096
-// (whose 256 tiles take two rounds) and on 4096 -> 12288.
+// Small fast-path layers (N <= 4096, K <= 8192, fp16) at 17..64 rows: the
+// decode kernel over row blocks when its plan has at most 128 column tiles
+// (at most two rounds of the CUs for four blocks).  The prefill grid there
+// is 16 column tiles or fewer, so its split launch's fixed costs dominate.
+// Measured on MI355X (tiled, 4-bit unless noted, us, decode vs prefill, at
+// M = 17 / 32 / 64): 4096 -> 4096 8.1 / 8.2 / 12.7 vs 10.9 / 13.5 / 16.2;
+// 4096 -> 1024 6.7 / 6.9 / 6.9 vs 9.1 / 10.4 / 13.7; 2048 -> 4096 5.2 /
+// 5.4 / 7.7 vs 9.6 / 10.6 / 13.9; 5120 -> 4096 9.7 / 9.8 / 16.0 vs 11.6 /
+// 13.9 / 19.6; 8192 -> 4096 12.8 / 12.7 vs 12.7 / 15.4 at 17 / 32; 2-bit
+// and 8-bit 4096 -> 4096 alike.  Excluded by measurement: the checkpoint
+// layout of 4096 -> 4096 (256 tiles: 13.8 vs 11.4 at 17 rows), 11008 ->
+// 4096 (a tie at 17, 1.4x slower at 64) and wider layers (4096 -> 12288 /
+// 22016: up to 1.6x slower).
 constexpr int64_t kSmallLayerMaxN = 4096, kSmallLayerMaxK = 8192;
 
 // Argument checks plus kernel choice and launch shape: pure host code.
@@ -377,7 +380,7 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
       return GPTQ_OK;
     }
   }
-  if (path == 0 && !bf16 && M > 16 && M <= 32 && N <= kSmallLayerMaxN && K <= kSmallLayerMaxK) {
+  if (path == 0 && !bf16 && M > 16 && M <= 64 && N <= kSmallLayerMaxN && K <= kSmallLayerMaxK) {
     gptq::GemmArgs b = *a;
     bool pe = group_size % 32 != 0;
     if (decode_shape(bits, 16, b.N, b.K, b.G, decode_waves, false, tiled, &pe, &b, false) == GPTQ_OK &&
@@ -385,7 +388,7 @@ int plan_gemm(const void* x, const int32_t* qweight, const int32_t* qzeros, cons
       *a = b;
       *per_elem = pe;
       *use_decode = true;
-      a->row_blocks = 2;
+      a->row_blocks = (int)((M + 15) / 16);
       return GPTQ_OK;
     }
   }

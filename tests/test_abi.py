@@ -169,6 +169,45 @@ def test_tiled_describe_shapes():
         assert buf.value.decode().startswith(want), buf.value
 
 
+def test_row_block_plans():
+    """Host-only plan boundaries of the decode kernel over 16-row blocks:
+    per-element layers (act order, or groups that are not whole 64-row k
+    tiles) at 17..4096 rows; small fp16 fast-path layers (N, K bounded, at
+    most 128 decode column tiles) at 17..64 rows; a forced prefill path and
+    everything else keep the prefill kernel."""
+    lib = gq.library()
+    buf = ctypes.create_string_buffer(256)
+
+    def plan(bits, gs, M, K, N, gi=None, tiled=True, path=0, bf16=False):
+        if bf16:
+            fn = lib.gptq_gemm_tiled_bf16_describe if tiled else lib.gptq_gemm_bf16_describe
+        else:
+            fn = lib.gptq_gemm_tiled_describe if tiled else lib.gptq_gemm_describe
+        assert fn(X, QW, QZ, SC, gi, bits, gs, 1, M, N, K, OUT, path, 0, buf, 256) == 0
+        return buf.value.decode()
+
+    # per-element layers
+    assert plan(4, 128, 17, 4096, 12288, GI).startswith("gptq::decode_kernel<4, true,")
+    assert plan(4, 128, 17, 4096, 12288, GI).endswith("row_blocks=2")
+    assert plan(3, 128, 4096, 5120, 13824, GI, tiled=False).endswith("row_blocks=256")
+    assert plan(4, 128, 4097, 4096, 12288, GI).startswith("gptq::prefill_kernel<4, true,")
+    assert plan(4, 32, 40, 4096, 12288).startswith("gptq::decode_kernel<4, false,")
+    assert plan(4, 32, 40, 4096, 12288).endswith("row_blocks=3")
+    assert plan(4, 128, 40, 4096, 1024, GI, bf16=True).startswith("gptq::decode_bf16_kernel")
+    assert plan(4, 128, 17, 4096, 12288, GI, path=2).startswith("gptq::prefill_small_kernel<4, true,")
+    # small fp16 fast-path layers
+    assert plan(4, 128, 17, 4096, 4096).endswith("row_blocks=2")
+    assert plan(4, 128, 64, 4096, 4096).endswith("row_blocks=4")
+    assert plan(4, 128, 64, 8192, 1024).endswith("row_blocks=4")
+    assert plan(4, 128, 65, 4096, 4096).startswith("gptq::prefill")           # rows past 64
+    assert plan(4, 128, 17, 4096, 4096, tiled=False).startswith("gptq::prefill")   # 256 decode tiles
+    assert plan(4, 128, 17, 11008, 4096).startswith("gptq::prefill")          # K past 8192
+    assert plan(4, 128, 17, 4096, 8192).startswith("gptq::prefill")           # N past 4096
+    assert plan(4, 128, 17, 4096, 12288).startswith("gptq::prefill")
+    assert plan(4, 128, 17, 4096, 4096, bf16=True).startswith("gptq::prefill_bf16")
+    assert plan(4, 128, 17, 4096, 4096, path=2).startswith("gptq::prefill_small_kernel")
+
+
 def test_moe_argument_codes():
     """Bad grouped-GEMM arguments return before any launch (safe without a GPU)."""
     lib = gq.library()
